@@ -1,0 +1,198 @@
+"""CPU oracle of the FwPKM layer's hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never calls it, and it never calls the product path: the two
+share no code.  The arithmetic lives in ``fwpkm_oracle.c`` (plain C, fp64);
+this module only compiles it with gcc and marshals numpy arrays through
+ctypes.
+
+Configuration objects are duck-typed: anything with the attributes ``n,
+heads, d_q, d_v, k_half, k, chunk, store ('f32'|'bf16'), idw_eps, lr_v, lr_k,
+lookahead, znorm, znorm_eps, use_addr`` works.
+
+Storage-typed arrays (q, v, targets, K1, K2, V) are float32 arrays for
+``store='f32'`` and uint16 arrays holding bf16 bit patterns for
+``store='bf16'``; torch tensors are accepted and converted.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fwpkm_oracle.c")
+_SO = os.path.join(_HERE, "libfwpkm_oracle.so")
+
+_GCC_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libfwpkm_oracle.so``."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        cmd = ["gcc", *_GCC_FLAGS, _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_q", ctypes.c_int32),
+        ("d_v", ctypes.c_int32), ("k_half", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("store", ctypes.c_int32),
+        ("idw_eps", ctypes.c_double), ("lr_v", ctypes.c_double), ("lr_k", ctypes.c_double),
+        ("lookahead", ctypes.c_int32), ("znorm", ctypes.c_int32),
+        ("znorm_eps", ctypes.c_double), ("use_addr", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        lib.fwo_retrieve.argtypes = [ctypes.POINTER(_Cfg), i32, i32, P, P, P, P, P, P,
+                                     P, P, P, P, P, P, ctypes.c_double]
+        lib.fwo_chunk_update.argtypes = [ctypes.POINTER(_Cfg), i32, i32, i32, P, P, P,
+                                         P, P, P, P, P, P, P]
+        lib.fwo_forward_seq.argtypes = [ctypes.POINTER(_Cfg), i32, i32, i32, P, P, P, P,
+                                        P, P, P, P, P, i32]
+        lib.fwo_pair_p.argtypes = [ctypes.POINTER(_Cfg), i32, i32, i32, P, P, P, P, P]
+        lib.fwo_double_to_bf16.argtypes = [ctypes.c_double]
+        lib.fwo_double_to_bf16.restype = ctypes.c_uint16
+        lib.fwo_num_threads.restype = ctypes.c_int
+        for f in (lib.fwo_retrieve, lib.fwo_chunk_update, lib.fwo_forward_seq, lib.fwo_pair_p):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _cfg(c) -> _Cfg:
+    store = {"f32": 0, "bf16": 1}[c.store]
+    return _Cfg(int(c.n), int(c.heads), int(c.d_q), int(c.d_v), int(c.k_half), int(c.k),
+                int(c.chunk), store, float(c.idw_eps), float(c.lr_v), float(c.lr_k),
+                int(bool(c.lookahead)), int(bool(c.znorm)), float(c.znorm_eps),
+                int(bool(c.use_addr)))
+
+
+def _np(x, dtype):
+    """Contiguous numpy copy-or-view of x with the given dtype."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu()
+            if x.dtype == torch.bfloat16:
+                x = x.view(torch.int16).numpy().view(np.uint16)
+            else:
+                x = x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(x)
+    if a.dtype != dtype:
+        if dtype == np.uint16:
+            raise TypeError("bf16 storage arrays must hold uint16 bit patterns")
+        a = a.astype(dtype)
+    return a
+
+
+def _sdt(c):
+    return np.float32 if c.store == "f32" else np.uint16
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().fwo_num_threads())
+
+
+def double_to_bf16(x: float) -> int:
+    return int(_load().fwo_double_to_bf16(float(x)))
+
+
+def retrieve(c, q, v, g, K1, K2, V, tie_rel: float = 0.0):
+    """Frozen-state retrieval of every token.  Returns a dict with o, vhat
+    ([B,T,d_v] float64), idx ([B,T,H,k] int32), w and P ([B,T,H,k] float64)
+    and tie ([B,T,H] uint8)."""
+    lib = _load()
+    sdt = _sdt(c)
+    q, v, K1, K2, V = (_np(x, sdt) for x in (q, v, K1, K2, V))
+    g = _np(g, np.float32)
+    B, T = g.shape
+    H, k, dv = c.heads, c.k, c.d_v
+    o = np.zeros((B, T, dv)); vh = np.zeros((B, T, dv))
+    idx = np.zeros((B, T, H, k), np.int32); w = np.zeros((B, T, H, k)); P = np.zeros((B, T, H, k))
+    tie = np.zeros((B, T, H), np.uint8)
+    cc = _cfg(c)
+    rc = lib.fwo_retrieve(ctypes.byref(cc), B, T, _p(q), _p(v), _p(g), _p(K1), _p(K2), _p(V),
+                          _p(o), _p(vh), _p(idx), _p(w), _p(P), _p(tie), float(tie_rel))
+    if rc != 0:
+        raise ValueError("fwo_retrieve rejected its arguments")
+    return {"o": o, "vhat": vh, "idx": idx, "w": w, "P": P, "tie": tie}
+
+
+def chunk_update(c, q, g, tgt, n_tgt, idx, w, vhat, K1, K2, V, want_n_read: bool = True):
+    """One chunk's write.  Returns new copies (K1, K2, V, n_read)."""
+    lib = _load()
+    sdt = _sdt(c)
+    q = _np(q, sdt)
+    g = _np(g, np.float32)
+    B, Tc = g.shape
+    tgt = _np(tgt, sdt) if tgt is not None else None
+    idx = _np(idx, np.int32)
+    w = _np(w, np.float64)
+    vhat = _np(vhat, np.float64)
+    K1 = _np(K1, sdt).copy(); K2 = _np(K2, sdt).copy(); V = _np(V, sdt).copy()
+    N = c.n * c.n
+    nr = np.zeros((B, N), np.int32) if want_n_read else None
+    cc = _cfg(c)
+    rc = lib.fwo_chunk_update(ctypes.byref(cc), B, Tc, int(n_tgt), _p(q), _p(g), _p(tgt),
+                              _p(idx), _p(w), _p(vhat), _p(K1), _p(K2), _p(V), _p(nr))
+    if rc != 0:
+        raise ValueError("fwo_chunk_update rejected its arguments")
+    return K1, K2, V, nr
+
+
+def forward_seq(c, q, v, g, K1, K2, V, passes: int = 1, v_next=None, chunk_limit: int = 0):
+    """Whole sequences.  Returns dict(o, vhat, K1, K2, V) with new state copies."""
+    lib = _load()
+    sdt = _sdt(c)
+    q, v = _np(q, sdt), _np(v, sdt)
+    g = _np(g, np.float32)
+    vn = _np(v_next, sdt) if v_next is not None else None
+    K1 = _np(K1, sdt).copy(); K2 = _np(K2, sdt).copy(); V = _np(V, sdt).copy()
+    B, T = g.shape
+    o = np.zeros((B, T, c.d_v)); vh = np.zeros((B, T, c.d_v))
+    cc = _cfg(c)
+    rc = lib.fwo_forward_seq(ctypes.byref(cc), B, T, int(passes), _p(q), _p(v), _p(g), _p(vn),
+                             _p(K1), _p(K2), _p(V), _p(o), _p(vh), int(chunk_limit))
+    if rc != 0:
+        raise ValueError("fwo_forward_seq rejected its arguments")
+    return {"o": o, "vhat": vh, "K1": K1, "K2": K2, "V": V}
+
+
+def pair_p(c, q, K1, K2, slots):
+    """(eps+d1)(eps+d2) for slots[B,T,H,m] in double."""
+    lib = _load()
+    sdt = _sdt(c)
+    q, K1, K2 = _np(q, sdt), _np(K1, sdt), _np(K2, sdt)
+    slots = _np(slots, np.int32)
+    B, T, H, m = slots.shape
+    P = np.zeros((B, T, H, m))
+    cc = _cfg(c)
+    rc = lib.fwo_pair_p(ctypes.byref(cc), B, T, m, _p(q), _p(K1), _p(K2), _p(slots), _p(P))
+    if rc != 0:
+        raise ValueError("fwo_pair_p rejected its arguments")
+    return P
