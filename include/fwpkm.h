@@ -1,0 +1,196 @@
+/*
+ * fwpkm.h -- C ABI of the MI355X (gfx950) hot path of the Fast-weight Product
+ * Key Memory (FwPKM) layer.
+ *
+ * The layer ("Fast-weight Product Key Memory", Zhao & Jones, arXiv 2601.00671)
+ * keeps a value matrix V with N = n*n rows and two sub-key codebooks K1, K2
+ * of n rows each as fast weights.  Per token it reads V sparsely through a
+ * product-key search and, after every chunk of C tokens, writes V and the
+ * codebooks by one gradient step on chunk-local losses.
+ *
+ * Citations name the pages the method is taken from:
+ *   [digest]     paper.rainbus.top digest of the paper, "Method step details"
+ *                (steps 1-5) and "Prerequisites: product key memory";
+ *   [layer]      paperlayer.ai section summary of the paper (v2), by section;
+ *   [gist-es]    gist.science/es technical summary, "Memoria esparsa".
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP device memory), row-major,
+ *     densely packed in the layouts given below.  The caller owns every
+ *     buffer; the library never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued: outputs are valid once the stream reaches this point.
+ *   - "store dtype" is cfg->store: FWPKM_F32 (float) or FWPKM_BF16
+ *     (bfloat16 bit patterns, 2 bytes).  Arithmetic is fp32 throughout;
+ *     state written back to bf16 is rounded to nearest even.
+ *   - Return value: FWPKM_OK or a negative fwpkm_status.  Every argument is
+ *     validated before anything is enqueued; on error nothing is enqueued
+ *     and fwpkm_last_error() describes the problem.  FWPKM_EHIP means a HIP
+ *     launch reported an error; device faults surface at the caller's next
+ *     synchronisation on `stream`.
+ *   - B == 0 or a token count of 0 is a successful no-op.
+ *   - Calls on one stream are ordered; concurrent calls that share state
+ *     buffers or a workspace on different streams race.
+ */
+#ifndef FWPKM_H
+#define FWPKM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FWPKM_ABI_VERSION 1
+
+typedef enum { FWPKM_F32 = 0, FWPKM_BF16 = 1 } fwpkm_dtype;
+
+typedef enum {
+    FWPKM_OK = 0,
+    FWPKM_EINVAL = -1,      /* bad shape, value or NULL pointer */
+    FWPKM_EUNSUPPORTED = -2,/* valid for the method, outside this GPU path's limits */
+    FWPKM_EWORKSPACE = -3,  /* workspace NULL or smaller than fwpkm_workspace_bytes() */
+    FWPKM_EHIP = -4         /* a HIP call failed */
+} fwpkm_status;
+
+/*
+ * Layer configuration.
+ *   n        sub-keys per codebook; N = n*n value slots ([digest] prerequisites:
+ *            keys factorised into two smaller key matrices; [gist-es]: N ~ 10^6).
+ *            GPU limits: 16 <= n <= 2048, n % 16 == 0.
+ *   heads    H query heads.  Each head has its own query slice and its own
+ *            K1, K2; all heads read and write the one shared V, and the
+ *            retrieved value is the mean over heads ([layer] D.1, D.3: more
+ *            heads raise slot collisions).
+ *   d_q      per-head query dimension; the first d_q/2 dims are scored
+ *            against K1, the last d_q/2 against K2 ([digest] prerequisites).
+ *            GPU limit: d_q/2 in {32, 64, 128, 256}.
+ *   d_v      value dimension.  GPU limit: d_v in {64, 128, 256, 512}.
+ *   k_half   k': sub-keys kept per half, 1 <= k' <= min(n, 64).
+ *   k        final top-k, 1 <= k <= min(k'*k', 64), and the number of
+ *            candidate pairs (a, b) with (a+1)(b+1) <= k must be <= 256
+ *            (true for every k <= 48).  k <= k' makes the search exact over
+ *            all N slots.
+ *   chunk    C: tokens per fast-weight write (fwpkm_forward_seq only).
+ *   store    fwpkm_dtype of q, v, targets, K1, K2, V.
+ *   idw_eps  eps of the inverse-distance score s = -log(eps + ||q-k||^2)
+ *            ([layer] A.2; the constant is not given on the pages).  > 0.
+ *   lr_v     step size of the V write ([digest] step 4 uses 1).
+ *   lr_k     step size of the K1/K2 write (not given on the pages).
+ *   lookahead 1: token t is paired with v_{t+1} ([layer] A.1, default);
+ *            0: with v_t ([digest] step 4 as printed).
+ *   znorm    1: z-score each target over d_v ([layer] A.3).
+ *   znorm_eps variance epsilon of the z-score.
+ *   use_addr 1: apply the addressing step to K1, K2 ([digest] step 5).
+ */
+typedef struct {
+    int32_t n;
+    int32_t heads;
+    int32_t d_q;
+    int32_t d_v;
+    int32_t k_half;
+    int32_t k;
+    int32_t chunk;
+    int32_t store;
+    float idw_eps;
+    float lr_v;
+    float lr_k;
+    int32_t lookahead;
+    int32_t znorm;
+    float znorm_eps;
+    int32_t use_addr;
+} fwpkm_cfg;
+
+/* FWPKM_ABI_VERSION of the loaded library. */
+int32_t fwpkm_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread
+ * (thread-local; "" when none).  Never NULL. */
+const char* fwpkm_last_error(void);
+
+/*
+ * Workspace size in bytes that makes any of fwpkm_retrieve(B, T),
+ * fwpkm_chunk_update(B, Tc <= T) and fwpkm_forward_seq(B, T) valid for this
+ * configuration.  Writes *bytes and returns FWPKM_OK, or an error status if
+ * cfg, B or T is invalid.  The workspace is caller-owned device memory with
+ * at least 256-byte alignment; its contents need no initialisation and are
+ * not meaningful after a call.
+ */
+int fwpkm_workspace_bytes(const fwpkm_cfg* cfg, int32_t B, int32_t T, size_t* bytes);
+
+/*
+ * Sparse retrieval and gated output of T tokens against frozen state
+ * ([digest] steps 2-3; [layer] 2.2, 3.2, A.2):
+ *   per head h: split q into halves, score every sub-key of each half with
+ *   s = -log(eps + ||q_half - K_i||^2), keep the top-k' of each half (ties:
+ *   lower sub-key index), score the k'*k' pairs s1 + s2 with slot id
+ *   i*n + j, keep the top-k pairs (ties: lower slot id) in order of
+ *   decreasing score, weights w = softmax of their scores;
+ *   vhat_t = (1/H) sum_h sum_j w[h][j] V[idx[h][j]];
+ *   o_t = g_t * vhat_t + (1 - g_t) * v_t.
+ * Inputs:  q[B][T][H][d_q], v[B][T][d_v], K1, K2[B][H][n][d_q/2],
+ *          V[B][n*n][d_v] (store dtype); g[B][T] float, post-sigmoid gate.
+ * Outputs: o[B][T][d_v] float (required); vhat[B][T][d_v] float,
+ *          idx[B][T][H][k] int32, w[B][T][H][k] float (each nullable).
+ * State is not modified.
+ */
+int fwpkm_retrieve(const fwpkm_cfg* cfg, int32_t B, int32_t T,
+                   const void* q, const void* v, const float* g,
+                   const void* K1, const void* K2, const void* V,
+                   float* o, float* vhat, int32_t* idx, float* w,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One chunk's fast-weight write, given that chunk's retrieval results
+ * ([digest] steps 4-5; [layer] 3.3, 3.4, A.1, A.3-A.5):
+ *   memorisation (V): tokens t < n_tgt have raw targets tgt[b][t];
+ *     y_t = z-score(tgt_t) if znorm, r_t = g_t (vhat_t - y_t);
+ *     G_i = sum over reads (t, h, j) of row i, t < n_tgt, of (w/H) r_t;
+ *     N_read,i = number of such reads; rows with N_read,i > 0 get
+ *     V_i <- V_i - lr_v G_i / N_read,i; other rows are not touched.
+ *     The sum runs in a fixed order (no float atomics): results are
+ *     bitwise reproducible.
+ *   addressing (K1, K2), if use_addr: over all Tc tokens, per head and
+ *     half, p_t = softmax over all n sub-keys of s_t, pbar = mean_t p_t,
+ *     one step of lr_k on L = -H(pbar_1) - H(pbar_2).
+ * Inputs:  q[B][Tc][H][d_q], tgt[B][n_tgt][d_v] (store dtype; may be NULL
+ *          when n_tgt == 0), g[B][Tc] float, idx[B][Tc][H][k] int32 and
+ *          w[B][Tc][H][k] float and vhat[B][Tc][d_v] float as returned by
+ *          fwpkm_retrieve for this chunk with this state.
+ *          Slot ids must lie in [0, n*n) (checked on the device: an
+ *          out-of-range id is skipped, never dereferenced).
+ * In/out:  K1, K2, V updated in place.
+ * Output:  n_read[B][n*n] int32 (nullable): N_read of every row.
+ * 0 <= n_tgt <= Tc.
+ */
+int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tgt,
+                       const void* q, const float* g, const void* tgt,
+                       const int32_t* idx, const float* w, const float* vhat,
+                       void* K1, void* K2, void* V, int32_t* n_read,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Whole sequences: chunks of C tokens in causal order, each read with the
+ * state left by the previous chunk and then written ([layer] 3, 3.1), the
+ * whole input repeated `passes` times with state carried (iterative
+ * memorisation, [layer] 4.3).  Lookahead targets pair token t with v_{t+1};
+ * the last token pairs with v_next when given, else it has no target.
+ * Inputs:  q[B][T][H][d_q], v[B][T][d_v], v_next[B][d_v] (nullable)
+ *          (store dtype); g[B][T] float.
+ * In/out:  K1, K2, V.
+ * Outputs: o[B][T][d_v] float (required), vhat[B][T][d_v] float
+ *          (nullable), both from the last pass.
+ * passes >= 1.
+ */
+int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
+                      const void* q, const void* v, const float* g, const void* v_next,
+                      void* K1, void* K2, void* V,
+                      float* o, float* vhat,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FWPKM_H */

@@ -1,0 +1,418 @@
+// fwpkm_api.cpp -- the C ABI of include/fwpkm.h: argument validation,
+// workspace carving and the kernel sequence of each entry point.
+//
+// Per chunk of the causal loop ("Fast-weight Product Key Memory",
+// paperlayer.ai 3 and 3.1: read a chunk with the state left by the previous
+// one, then write):
+//   sweep(select|stats)  scores, top-k, weights, usage partial sums
+//   gather               v_hat, o, residual r
+//   sort passes          reads ordered by slot
+//   scatter + fixup      read-count-normalised V write
+//   pbar                 log pbar
+//   sweep(rowstat)       Z_t, m_t
+//   kgrad                K1/K2 step and their new norms
+#include "../../include/fwpkm.h"
+#include "fwpkm_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+using namespace fwpkm;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return FWPKM_OK;
+}
+
+struct Plan {
+    int n, H, dq, dh, dv, kh, k, C, store, es;
+    int64_t N;
+    float eps, lr_v, lr_k, zeps;
+    int look, znorm, addr;
+    CandTable cand;
+    int ncand;
+    int sort_passes;
+};
+
+int make_plan(const fwpkm_cfg* c, Plan* p) {
+    if (!c) return fail(FWPKM_EINVAL, "cfg is NULL");
+    if (c->n < 1) return fail(FWPKM_EINVAL, "n must be >= 1 (got %d)", c->n);
+    if (static_cast<int64_t>(c->n) * c->n > 2147483647LL) return fail(FWPKM_EINVAL, "n*n overflows int32");
+    if (c->heads < 1) return fail(FWPKM_EINVAL, "heads must be >= 1 (got %d)", c->heads);
+    if (c->d_q < 2 || (c->d_q & 1)) return fail(FWPKM_EINVAL, "d_q must be even and >= 2 (got %d)", c->d_q);
+    if (c->d_v < 1) return fail(FWPKM_EINVAL, "d_v must be >= 1 (got %d)", c->d_v);
+    if (c->k_half < 1 || c->k_half > c->n) return fail(FWPKM_EINVAL, "k_half must be in [1, n] (got %d)", c->k_half);
+    if (c->k < 1 || static_cast<int64_t>(c->k) > static_cast<int64_t>(c->k_half) * c->k_half)
+        return fail(FWPKM_EINVAL, "k must be in [1, k_half^2] (got %d)", c->k);
+    if (c->chunk < 1) return fail(FWPKM_EINVAL, "chunk must be >= 1 (got %d)", c->chunk);
+    if (c->store != FWPKM_F32 && c->store != FWPKM_BF16) return fail(FWPKM_EINVAL, "store must be FWPKM_F32 or FWPKM_BF16");
+    if (!(c->idw_eps > 0.f) || !std::isfinite(c->idw_eps)) return fail(FWPKM_EINVAL, "idw_eps must be finite and > 0");
+    if (!std::isfinite(c->lr_v) || !std::isfinite(c->lr_k)) return fail(FWPKM_EINVAL, "lr_v and lr_k must be finite");
+    if (!(c->znorm_eps >= 0.f) || !std::isfinite(c->znorm_eps)) return fail(FWPKM_EINVAL, "znorm_eps must be finite and >= 0");
+    // limits of this GPU path
+    if (c->n < 16 || c->n > 1024 || (c->n % 16))
+        return fail(FWPKM_EUNSUPPORTED, "GPU path needs 16 <= n <= 1024 and n %% 16 == 0 (got %d)", c->n);
+    const int dh = c->d_q / 2;
+    if (dh != 32 && dh != 64 && dh != 128 && dh != 256)
+        return fail(FWPKM_EUNSUPPORTED, "GPU path needs d_q/2 in {32, 64, 128, 256} (got %d)", dh);
+    if (c->d_v != 64 && c->d_v != 128 && c->d_v != 256 && c->d_v != 512)
+        return fail(FWPKM_EUNSUPPORTED, "GPU path needs d_v in {64, 128, 256, 512} (got %d)", c->d_v);
+    if (c->k_half > kMaxKHalf) return fail(FWPKM_EUNSUPPORTED, "GPU path needs k_half <= %d", kMaxKHalf);
+    if (c->k > kMaxK) return fail(FWPKM_EUNSUPPORTED, "GPU path needs k <= %d", kMaxK);
+    if (static_cast<int64_t>(c->heads) * c->k > 256) return fail(FWPKM_EUNSUPPORTED, "GPU path needs heads*k <= 256");
+
+    p->n = c->n; p->H = c->heads; p->dq = c->d_q; p->dh = dh; p->dv = c->d_v;
+    p->kh = c->k_half; p->k = c->k; p->C = c->chunk; p->store = c->store;
+    p->es = (c->store == FWPKM_BF16) ? 2 : 4;
+    p->N = static_cast<int64_t>(c->n) * c->n;
+    p->eps = c->idw_eps; p->lr_v = c->lr_v; p->lr_k = c->lr_k; p->zeps = c->znorm_eps;
+    p->look = c->lookahead != 0; p->znorm = c->znorm != 0; p->addr = c->use_addr != 0;
+    // product candidates: ranks (a, b) of the two sorted lists with (a+1)(b+1) <= k
+    int m = 0;
+    std::memset(&p->cand, 0, sizeof p->cand);
+    for (int a = 0; a < p->kh; ++a)
+        for (int b = 0; b < p->kh; ++b)
+            if (static_cast<int64_t>(a + 1) * (b + 1) <= p->k) {
+                if (m >= kMaxCand) return fail(FWPKM_EUNSUPPORTED, "too many product candidates for k=%d", p->k);
+                p->cand.ab[m++] = static_cast<uint16_t>(a * 64 + b);
+            }
+    p->ncand = m;
+    int bits = 1;
+    while ((int64_t{1} << bits) <= p->N) ++bits;  // keys 0..N inclusive (N = sentinel)
+    p->sort_passes = (bits + 7) / 8;
+    return FWPKM_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace carve-up for B sequences of Tt tokens per step.
+struct Layout {
+    size_t idx, w, knorm, qn, r, Z, m, part, lp, k0, v0, k1, v1, counts, ph, pt, pts, phe;
+    size_t total;
+};
+
+Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += up(bytes);
+        return at;
+    };
+    const size_t Bs = static_cast<size_t>(B), T = static_cast<size_t>(Tt);
+    const size_t ntiles = (T + kTileT - 1) / kTileT;
+    L.knorm = take(Bs * p.H * 2 * p.n * 4);
+    L.qn = take(Bs * p.H * 2 * T * 4);
+    if (with_iw) {
+        L.idx = take(Bs * T * p.H * p.k * 4);
+        L.w = take(Bs * T * p.H * p.k * 4);
+    }
+    if (with_update) {
+        const size_t M = T * p.H * p.k;
+        const size_t tiles = (M + kSortTile - 1) / kSortTile;
+        const size_t pieces = (M + kPiece - 1) / kPiece;
+        L.r = take(Bs * T * p.dv * 4);
+        L.Z = take(Bs * p.H * 2 * T * 4);
+        L.m = take(Bs * p.H * 2 * T * 4);
+        L.part = take(Bs * p.H * 2 * ntiles * p.n * 4);
+        L.lp = take(Bs * p.H * 2 * p.n * 4);
+        L.k0 = take(Bs * M * 4);
+        L.v0 = take(Bs * M * 4);
+        L.k1 = take(Bs * M * 4);
+        L.v1 = take(Bs * M * 4);
+        L.counts = take(Bs * 256 * std::max<size_t>(tiles, 1) * 4);
+        L.ph = take(Bs * pieces * p.dv * 4);
+        L.pt = take(Bs * pieces * p.dv * 4);
+        L.pts = take(Bs * pieces * 4);
+        L.phe = take(Bs * pieces * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+size_t need_retrieve(const Plan& p, int B, int T) { return layout(p, B, T, true, false).total; }
+size_t need_update(const Plan& p, int B, int T) { return layout(p, B, T, false, true).total; }
+size_t need_forward(const Plan& p, int B, int T) { return layout(p, B, std::min(T, p.C), true, true).total; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return FWPKM_OK;
+    if (!ws) return fail(FWPKM_EWORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(FWPKM_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(FWPKM_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return FWPKM_OK;
+}
+
+#define HIP_TRY(expr)                                                              \
+    do {                                                                           \
+        hipError_t e_ = (expr);                                                    \
+        if (e_ != hipSuccess) return fail(FWPKM_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+hipError_t knorm_launch(const Plan& p, int B, const void* K1, const void* K2, float* knorm, hipStream_t s) {
+    KnormArgs a{K1, K2, knorm, B, p.H, p.n, p.dh};
+    return launch_knorm(a, p.store, s);
+}
+
+// Sweep over Tc tokens (q with per-sequence stride q_bstride elements).
+SweepArgs sweep_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstride, const void* K1,
+                     const void* K2, const float* knorm, int mode) {
+    SweepArgs a{};
+    a.q = q; a.q_bstride = q_bstride; a.K1 = K1; a.K2 = K2; a.knorm = knorm;
+    a.B = B; a.Tc = Tc; a.n = p.n; a.H = p.H; a.dh = p.dh; a.kh = p.kh; a.k = p.k; a.ncand = p.ncand;
+    a.eps = p.eps; a.mode = mode; a.cand = p.cand;
+    return a;
+}
+
+// Memorisation write of one chunk from idx/w (per-sequence stride iw_bstride),
+// residual r [B][Tc][dv], n_tgt tokens with targets.
+int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt, const int32_t* idx,
+             const float* w, int64_t iw_bstride, void* V, int32_t* n_read, hipStream_t s) {
+    const int M = n_tgt * p.H * p.k;
+    if (n_read) HIP_TRY(launch_fill_i32(n_read, static_cast<int64_t>(B) * p.N, 0, s));
+    if (M == 0) return FWPKM_OK;
+    const int tiles = (M + kSortTile - 1) / kSortTile;
+    uint32_t* kb[2] = {at<uint32_t>(ws, L.k0), at<uint32_t>(ws, L.k1)};
+    uint32_t* vb[2] = {at<uint32_t>(ws, L.v0), at<uint32_t>(ws, L.v1)};
+    int cur = 0;
+    for (int pass = 0; pass < p.sort_passes; ++pass) {
+        SortArgs a{};
+        a.idx = idx; a.idx_bstride = iw_bstride;
+        a.kin = kb[cur]; a.vin = vb[cur];
+        a.kout = kb[cur ^ 1]; a.vout = vb[cur ^ 1];
+        a.counts = at<uint32_t>(ws, L.counts);
+        a.B = B; a.M = M; a.tiles = tiles; a.shift = 8 * pass; a.first = pass == 0;
+        a.N = static_cast<uint32_t>(p.N);
+        HIP_TRY(launch_sort_pass(a, s));
+        cur ^= 1;
+    }
+    ScatterArgs sa{};
+    sa.keys = kb[cur]; sa.vals = vb[cur];
+    sa.w = w; sa.w_bstride = iw_bstride;
+    sa.r = at<float>(ws, L.r);
+    sa.V = V; sa.n_read = n_read;
+    sa.ph = at<float>(ws, L.ph); sa.pt = at<float>(ws, L.pt);
+    sa.pt_start = at<int32_t>(ws, L.pts); sa.ph_end = at<int32_t>(ws, L.phe);
+    sa.B = B; sa.M = M; sa.pieces = (M + kPiece - 1) / kPiece; sa.H = p.H; sa.k = p.k; sa.dv = p.dv; sa.Tc = Tc;
+    sa.N = static_cast<uint32_t>(p.N); sa.lr = p.lr_v; sa.inv_h = 1.f / static_cast<float>(p.H);
+    HIP_TRY(launch_scatter(sa, p.store, s));
+    return FWPKM_OK;
+}
+
+// Addressing step of one chunk.  With `have_stats` the chunk's usage
+// partial sums (and ||q||^2) are already in the workspace from the select
+// sweep; otherwise a stats sweep computes them first.
+int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
+            void* K1, void* K2, bool have_stats, hipStream_t s) {
+    float* knorm = at<float>(ws, L.knorm);
+    if (!have_stats) {
+        SweepArgs a = sweep_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kSweepStats);
+        a.qn = at<float>(ws, L.qn);
+        a.part = at<float>(ws, L.part);
+        HIP_TRY(launch_sweep(a, p.store, s));
+    }
+    PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, (Tc + kTileT - 1) / kTileT, Tc};
+    HIP_TRY(launch_pbar(pa, s));
+    SweepArgs ra = sweep_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kSweepRowStat);
+    ra.lp = at<float>(ws, L.lp);
+    ra.Z = at<float>(ws, L.Z);
+    ra.m = at<float>(ws, L.m);
+    HIP_TRY(launch_sweep(ra, p.store, s));
+    KgradArgs ka{};
+    ka.q = q; ka.q_bstride = q_bstride; ka.K1 = K1; ka.K2 = K2; ka.knorm = knorm;
+    ka.qn = at<float>(ws, L.qn); ka.Z = at<float>(ws, L.Z); ka.m = at<float>(ws, L.m); ka.lp = at<float>(ws, L.lp);
+    ka.B = B; ka.Tc = Tc; ka.n = p.n; ka.H = p.H; ka.dh = p.dh; ka.eps = p.eps; ka.lr = p.lr_k;
+    HIP_TRY(launch_kgrad(ka, p.store, s));
+    return FWPKM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fwpkm_abi_version(void) { return FWPKM_ABI_VERSION; }
+
+const char* fwpkm_last_error(void) { return g_err.c_str(); }
+
+int fwpkm_workspace_bytes(const fwpkm_cfg* cfg, int32_t B, int32_t T, size_t* bytes) {
+    Plan p;
+    int rc = make_plan(cfg, &p);
+    if (rc) return rc;
+    if (B < 0 || T < 0) return fail(FWPKM_EINVAL, "B and T must be >= 0");
+    if (!bytes) return fail(FWPKM_EINVAL, "bytes is NULL");
+    if (B == 0 || T == 0) {
+        *bytes = 0;
+        return ok();
+    }
+    *bytes = std::max(need_retrieve(p, B, T), std::max(need_update(p, B, T), need_forward(p, B, T)));
+    return ok();
+}
+
+int fwpkm_retrieve(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, const void* v, const float* g,
+                   const void* K1, const void* K2, const void* V, float* o, float* vhat, int32_t* idx, float* w,
+                   void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int rc = make_plan(cfg, &p);
+    if (rc) return rc;
+    if (B < 0 || T < 0) return fail(FWPKM_EINVAL, "B and T must be >= 0");
+    if (static_cast<int64_t>(B) * T * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*T*heads*k too large");
+    if (B == 0 || T == 0) return ok();
+    if (!q || !v || !g || !K1 || !K2 || !V || !o) return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V and o are required");
+    const Layout L = layout(p, B, T, true, false);
+    rc = check_ws(ws, ws_bytes, L.total);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* knorm = at<float>(ws, L.knorm);
+    HIP_TRY(knorm_launch(p, B, K1, K2, knorm, s));
+    int32_t* ii = idx ? idx : at<int32_t>(ws, L.idx);
+    float* ww = w ? w : at<float>(ws, L.w);
+    SweepArgs a = sweep_args(p, B, T, q, static_cast<int64_t>(T) * p.H * p.dq, K1, K2, knorm, kSweepSelect);
+    a.idx = ii; a.w = ww; a.iw_bstride = static_cast<int64_t>(T) * p.H * p.k;
+    HIP_TRY(launch_sweep(a, p.store, s));
+    GatherArgs ga{};
+    ga.V = V; ga.idx = ii; ga.w = ww; ga.iw_bstride = a.iw_bstride;
+    ga.v = v; ga.v_bstride = static_cast<int64_t>(T) * p.dv;
+    ga.g = g; ga.g_bstride = T;
+    ga.o = o; ga.vhat = vhat; ga.o_bstride = static_cast<int64_t>(T) * p.dv;
+    ga.B = B; ga.Tc = T; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
+    HIP_TRY(launch_gather(ga, p.store, s));
+    return ok();
+}
+
+int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tgt, const void* q, const float* g,
+                       const void* tgt, const int32_t* idx, const float* w, const float* vhat, void* K1, void* K2,
+                       void* V, int32_t* n_read, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int rc = make_plan(cfg, &p);
+    if (rc) return rc;
+    if (B < 0 || Tc < 0) return fail(FWPKM_EINVAL, "B and Tc must be >= 0");
+    if (n_tgt < 0 || n_tgt > Tc) return fail(FWPKM_EINVAL, "n_tgt must be in [0, Tc] (got %d, Tc=%d)", n_tgt, Tc);
+    if (static_cast<int64_t>(B) * Tc * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*Tc*heads*k too large");
+    if (B == 0 || Tc == 0) return ok();
+    if (!q || !g || !idx || !w || !vhat || !K1 || !K2 || !V)
+        return fail(FWPKM_EINVAL, "q, g, idx, w, vhat, K1, K2 and V are required");
+    if (n_tgt > 0 && !tgt) return fail(FWPKM_EINVAL, "tgt is required when n_tgt > 0");
+    const Layout L = layout(p, B, Tc, false, true);
+    rc = check_ws(ws, ws_bytes, L.total);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
+    if (n_tgt > 0) {
+        ResidArgs ra{vhat, g, tgt, at<float>(ws, L.r), B, Tc, n_tgt, p.dv, p.znorm, p.zeps};
+        HIP_TRY(launch_resid(ra, p.store, s));
+    }
+    const int64_t iwb = static_cast<int64_t>(Tc) * p.H * p.k;
+    rc = memorise(p, L, ws, B, Tc, n_tgt, idx, w, iwb, V, n_read, s);
+    if (rc) return rc;
+    if (p.addr) {
+        rc = address(p, L, ws, B, Tc, q, static_cast<int64_t>(Tc) * p.H * p.dq, K1, K2, false, s);
+        if (rc) return rc;
+    }
+    return ok();
+}
+
+int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q, const void* v,
+                      const float* g, const void* v_next, void* K1, void* K2, void* V, float* o, float* vhat,
+                      void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int rc = make_plan(cfg, &p);
+    if (rc) return rc;
+    if (B < 0 || T < 0) return fail(FWPKM_EINVAL, "B and T must be >= 0");
+    if (passes < 1) return fail(FWPKM_EINVAL, "passes must be >= 1 (got %d)", passes);
+    if (B == 0 || T == 0) return ok();
+    if (!q || !v || !g || !K1 || !K2 || !V || !o) return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V and o are required");
+    const int Cm = std::min(T, p.C);
+    if (static_cast<int64_t>(B) * Cm * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*C*heads*k too large");
+    const Layout L = layout(p, B, Cm, true, true);
+    rc = check_ws(ws, ws_bytes, L.total);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* knorm = at<float>(ws, L.knorm);
+    HIP_TRY(knorm_launch(p, B, K1, K2, knorm, s));
+    const int64_t qb = static_cast<int64_t>(T) * p.H * p.dq;
+    const int64_t vbs = static_cast<int64_t>(T) * p.dv;
+    const int nchunks = (T + p.C - 1) / p.C;
+    int32_t* idx = at<int32_t>(ws, L.idx);
+    float* w = at<float>(ws, L.w);
+    for (int pass = 0; pass < passes; ++pass) {
+        const bool last_pass = pass == passes - 1;
+        for (int c = 0; c < nchunks; ++c) {
+            const int t0 = c * p.C;
+            const int Tc = std::min(p.C, T - t0);
+            const unsigned char* qc = static_cast<const unsigned char*>(q) + static_cast<size_t>(t0) * p.H * p.dq * p.es;
+            const unsigned char* vc = static_cast<const unsigned char*>(v) + static_cast<size_t>(t0) * p.dv * p.es;
+            const int64_t iwb = static_cast<int64_t>(Tc) * p.H * p.k;
+            // retrieval with the state left by the previous chunk
+            SweepArgs a = sweep_args(p, B, Tc, qc, qb, K1, K2, knorm, kSweepSelect | (p.addr ? kSweepStats : 0));
+            a.idx = idx; a.w = w; a.iw_bstride = iwb;
+            a.qn = at<float>(ws, L.qn);
+            a.part = at<float>(ws, L.part);
+            HIP_TRY(launch_sweep(a, p.store, s));
+            // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
+            int n_tgt;
+            const void* tgt;
+            const void* tgt_last = nullptr;
+            if (!p.look) {
+                n_tgt = Tc;
+                tgt = vc;
+            } else {
+                tgt = vc + static_cast<size_t>(p.dv) * p.es;
+                const bool at_end = t0 + Tc == T;
+                if (!at_end) {
+                    n_tgt = Tc;
+                } else if (v_next) {
+                    n_tgt = Tc;
+                    tgt_last = v_next;
+                } else {
+                    n_tgt = Tc - 1;
+                }
+            }
+            GatherArgs ga{};
+            ga.V = V; ga.idx = idx; ga.w = w; ga.iw_bstride = iwb;
+            ga.v = vc; ga.v_bstride = vbs;
+            ga.g = g + t0; ga.g_bstride = T;
+            ga.tgt = tgt; ga.tgt_bstride = vbs; ga.n_tgt = n_tgt;
+            ga.tgt_last = tgt_last; ga.tgt_last_bstride = p.dv;
+            ga.o = last_pass ? o + static_cast<size_t>(t0) * p.dv : nullptr;
+            ga.vhat = (last_pass && vhat) ? vhat + static_cast<size_t>(t0) * p.dv : nullptr;
+            ga.o_bstride = vbs;
+            ga.r = at<float>(ws, L.r);
+            ga.B = B; ga.Tc = Tc; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
+            ga.znorm = p.znorm; ga.znorm_eps = p.zeps;
+            HIP_TRY(launch_gather(ga, p.store, s));
+            // write
+            rc = memorise(p, L, ws, B, Tc, n_tgt, idx, w, iwb, V, nullptr, s);
+            if (rc) return rc;
+            if (p.addr) {
+                rc = address(p, L, ws, B, Tc, qc, qb, K1, K2, true, s);
+                if (rc) return rc;
+            }
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,263 @@
+// fwpkm_internal.h -- device helpers, kernel argument blocks and launch
+// entry points shared by the gfx950 HIP sources of the FwPKM library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fwpkm {
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+enum : int { kF32 = 0, kBF16 = 1 };
+
+template <int STORE> struct Store;
+template <> struct Store<kF32> {
+    using T = float;
+    static constexpr int kBytes = 4;
+};
+template <> struct Store<kBF16> {
+    using T = uint16_t;
+    static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+template <int STORE> __device__ __forceinline__ float ld_elem(const void* p, size_t i);
+template <> __device__ __forceinline__ float ld_elem<kF32>(const void* p, size_t i) {
+    return static_cast<const float*>(p)[i];
+}
+template <> __device__ __forceinline__ float ld_elem<kBF16>(const void* p, size_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+template <int STORE> __device__ __forceinline__ void st_elem(void* p, size_t i, float x);
+template <> __device__ __forceinline__ void st_elem<kF32>(void* p, size_t i, float x) {
+    static_cast<float*>(p)[i] = x;
+}
+template <> __device__ __forceinline__ void st_elem<kBF16>(void* p, size_t i, float x) {
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(x));
+}
+
+// Load 8 consecutive storage elements (16 B for bf16, 32 B for f32) as floats.
+template <int STORE> __device__ __forceinline__ void ld8(const void* p, size_t i, float (&x)[8]);
+template <> __device__ __forceinline__ void ld8<kF32>(const void* p, size_t i, float (&x)[8]) {
+    const float4* s = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    float4 a = s[0], b = s[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+template <> __device__ __forceinline__ void ld8<kBF16>(const void* p, size_t i, float (&x)[8]) {
+    uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    x[0] = __uint_as_float(a.x << 16); x[1] = __uint_as_float(a.x & 0xffff0000u);
+    x[2] = __uint_as_float(a.y << 16); x[3] = __uint_as_float(a.y & 0xffff0000u);
+    x[4] = __uint_as_float(a.z << 16); x[5] = __uint_as_float(a.z & 0xffff0000u);
+    x[6] = __uint_as_float(a.w << 16); x[7] = __uint_as_float(a.w & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------------------
+// wavefront helpers (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Orders LDS traffic of one wavefront: everything before is visible after.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o, 64);
+        if (l >= o) x += y;
+    }
+    return x;
+}
+
+// Map the hardware-linear workgroup id to a logical id so that the
+// workgroups the dispatcher sends to one XCD (linear id mod 8) receive a
+// contiguous range of logical ids: neighbouring tiles then share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t lin, uint32_t total) {
+    const uint32_t nx = 8;
+    const uint32_t x = lin % nx, i = lin / nx;
+    const uint32_t q = total / nx, r = total % nx;
+    return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// ---------------------------------------------------------------------------
+// kernel argument blocks
+// ---------------------------------------------------------------------------
+constexpr int kMaxCand = 256;   // product candidates per (token, head)
+constexpr int kTileT = 16;      // tokens per sweep workgroup
+constexpr int kMaxKHalf = 64;
+constexpr int kMaxK = 64;
+
+// Candidate pairs (a, b) of the two sorted top-k' lists that can reach the
+// final top-k: (a+1)(b+1) <= k.  Packed a*64 + b.
+struct CandTable {
+    uint16_t ab[kMaxCand];
+};
+
+enum SweepMode : int {
+    kSweepSelect = 1,   // per-half top-k', product top-k, weights -> idx, w
+    kSweepStats = 2,    // per-tile partial sums of p over tokens -> part
+    kSweepRowStat = 4,  // Z_t and m_t = sum_i p_ti log pbar_i -> Z, m
+};
+
+struct SweepArgs {
+    const void* q;        // token t of sequence b at q + b*q_bstride + t*H*d_q
+    int64_t q_bstride;
+    const void* K1;       // [B][H][n][dh]
+    const void* K2;
+    const float* knorm;   // [B][H][2][n]
+    int B, Tc, n, H, dh, kh, k, ncand;
+    float eps;
+    int mode;
+    int32_t* idx;         // [b*iw_bstride + (t*H + h)*k + j]
+    float* w;
+    int64_t iw_bstride;
+    float* qn;            // [B][H][2][Tc]  ||q_half||^2
+    float* part;          // [B][H][2][ntiles][n]
+    const float* lp;      // [B][H][2][n]   log pbar
+    float* Z;             // [B][H][2][Tc]
+    float* m;             // [B][H][2][Tc]
+    CandTable cand;
+};
+
+struct GatherArgs {
+    const void* V;        // [B][N][dv]
+    const int32_t* idx;   // [b*iw_bstride + t*H*k + e]
+    const float* w;
+    int64_t iw_bstride;
+    const void* v;        // residual path value: v + b*v_bstride + t*dv
+    int64_t v_bstride;
+    const float* g;       // g + b*g_bstride + t
+    int64_t g_bstride;
+    const void* tgt;      // raw target of token t: tgt + b*tgt_bstride + t*dv, t < n_tgt
+    int64_t tgt_bstride;
+    int n_tgt;            // tokens with a target (per sequence)
+    const void* tgt_last; // nullable: target of token Tc-1 at tgt_last + b*tgt_last_bstride
+    int64_t tgt_last_bstride;
+    float* o;             // o + b*o_bstride + t*dv
+    float* vhat;          // nullable, same layout as o
+    int64_t o_bstride;
+    float* r;             // nullable: residual [B][Tc][dv] when given
+    int B, Tc, H, k, dv;
+    int64_t N;
+    int znorm;
+    float znorm_eps;
+};
+
+struct ResidArgs {        // r = g (vhat - z(tgt)) for t < n_tgt
+    const float* vhat;    // [B][Tc][dv]
+    const float* g;       // [B][Tc]
+    const void* tgt;      // [B][n_tgt][dv]
+    float* r;             // [B][Tc][dv]
+    int B, Tc, n_tgt, dv, znorm;
+    float znorm_eps;
+};
+
+struct SortArgs {
+    const int32_t* idx;   // first pass source: slot of entry e = idx[b*idx_bstride + e]
+    int64_t idx_bstride;
+    const uint32_t* kin;  // later passes: keys / values in
+    const uint32_t* vin;
+    uint32_t* kout;
+    uint32_t* vout;
+    uint32_t* counts;     // [B][256][tiles]
+    int B, M;             // entries per sequence
+    int tiles;
+    int shift;
+    int first;
+    uint32_t N;           // slot ids >= N (or < 0) become the sentinel key N
+};
+
+struct ScatterArgs {
+    const uint32_t* keys; // sorted slot per position [B][M]
+    const uint32_t* vals; // entry id per position [B][M]
+    const float* w;       // weights by entry id: w[b*w_bstride + e]
+    int64_t w_bstride;
+    const float* r;       // residual [B][Tc][dv]
+    void* V;              // [B][N][dv]
+    int32_t* n_read;      // nullable [B][N]
+    float* ph;            // [B][pieces][dv] partial of the run continuing into the piece
+    float* pt;            // [B][pieces][dv] partial of the run leaving the piece
+    int32_t* pt_start;    // [B][pieces] start position of the leaving run, or -1
+    int32_t* ph_end;      // [B][pieces] end position (exclusive) of the entering run, or -1
+    int B, M, pieces, H, k, dv, Tc;
+    uint32_t N;
+    float lr, inv_h;
+};
+
+struct PbarArgs {
+    const float* part;    // [B][H][2][ntiles][n]
+    float* lp;            // [B][H][2][n]
+    int B, H, n, ntiles, Tc;
+};
+
+struct KgradArgs {
+    const void* q;
+    int64_t q_bstride;
+    void* K1;
+    void* K2;
+    float* knorm;         // [B][H][2][n], rewritten with the new keys
+    const float* qn;      // [B][H][2][Tc]
+    const float* Z;
+    const float* m;
+    const float* lp;      // [B][H][2][n]
+    int B, Tc, n, H, dh;
+    float eps, lr;
+};
+
+struct KnormArgs {
+    const void* K1;
+    const void* K2;
+    float* knorm;
+    int B, H, n, dh;
+};
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipGetLastError() after enqueueing)
+// ---------------------------------------------------------------------------
+hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s);
+hipError_t launch_sweep(const SweepArgs& a, int store, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int store, hipStream_t s);
+hipError_t launch_resid(const ResidArgs& a, int store, hipStream_t s);
+hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s);
+hipError_t launch_scatter(const ScatterArgs& a, int store, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t s);
+hipError_t launch_pbar(const PbarArgs& a, hipStream_t s);
+hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s);
+
+constexpr int kSortItems = 8;                  // entries per thread
+constexpr int kSortTile = 256 * kSortItems;    // entries per sort workgroup
+constexpr int kPiece = 64;                     // sorted positions per scatter wavefront
+
+}  // namespace fwpkm

@@ -1,0 +1,283 @@
+// k_scatter.hip -- read-count-normalised value-row write of one chunk.
+//
+// With the chunk's reads sorted by slot, every value row read at least once
+// is one run of equal keys.  Its gradient is the sum over the run of
+// (w/H) r_t, and the write is V_i <- V_i - lr (sum) / N_read,i, N_read,i
+// being the run length ("Fast-weight Product Key Memory", rainbus digest
+// step 4: aggregated gradient divided by the row's read count; paperlayer.ai
+// 3.3: read-count consensus; A.3: no clipping; A.4: sum reduction).  Rows
+// that nobody read are never touched.
+//
+// The sorted list is cut into pieces of 64 positions, one wavefront each;
+// lane l owns elements [l*EPL, (l+1)*EPL) of a d_v row.  A wavefront sums
+// each run of its piece in list order.  Runs inside the piece are written
+// straight away; a run that crosses a piece boundary leaves per-piece
+// partial sums, which k_fixup adds in piece order.  Fixed order everywhere:
+// no float atomics, bitwise reproducible results.
+#include "fwpkm_internal.h"
+
+namespace fwpkm {
+
+namespace {
+
+template <int STORE, int EPL>
+__device__ __forceinline__ void ld_row(const void* base, size_t off, float (&x)[EPL]) {
+    if constexpr (STORE == kF32) {
+        const float* p = static_cast<const float*>(base) + off;
+        if constexpr (EPL % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < EPL; i += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(p + i);
+                x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+            }
+        } else if constexpr (EPL == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(p);
+            x[0] = v.x; x[1] = v.y;
+        } else {
+            x[0] = p[0];
+        }
+    } else {
+        const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+        if constexpr (EPL == 8) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __uint_as_float(w[i] << 16);
+                x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        } else if constexpr (EPL == 4) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            x[0] = __uint_as_float(v.x << 16); x[1] = __uint_as_float(v.x & 0xffff0000u);
+            x[2] = __uint_as_float(v.y << 16); x[3] = __uint_as_float(v.y & 0xffff0000u);
+        } else if constexpr (EPL == 2) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+            x[0] = __uint_as_float(v << 16); x[1] = __uint_as_float(v & 0xffff0000u);
+        } else {
+            x[0] = bf16_to_f32(p[0]);
+        }
+    }
+}
+
+template <int STORE, int EPL>
+__device__ __forceinline__ void st_row(void* base, size_t off, const float (&x)[EPL]) {
+    if constexpr (STORE == kF32) {
+        float* p = static_cast<float*>(base) + off;
+        if constexpr (EPL % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < EPL; i += 4)
+                *reinterpret_cast<float4*>(p + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+        } else if constexpr (EPL == 2) {
+            *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+        } else {
+            p[0] = x[0];
+        }
+    } else {
+        uint16_t* p = static_cast<uint16_t*>(base) + off;
+        uint32_t h[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) h[i] = f32_to_bf16(x[i]);
+        if constexpr (EPL == 8) {
+            *reinterpret_cast<uint4*>(p) = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                                      h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        } else if constexpr (EPL == 4) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else if constexpr (EPL == 2) {
+            *reinterpret_cast<uint32_t*>(p) = h[0] | (h[1] << 16);
+        } else {
+            p[0] = static_cast<uint16_t>(h[0]);
+        }
+    }
+}
+
+template <int EPL>
+__device__ __forceinline__ void ld_f32(const float* p, float (&x)[EPL]) {
+    if constexpr (EPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < EPL; i += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(p + i);
+            x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+        }
+    } else if constexpr (EPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        x[0] = v.x; x[1] = v.y;
+    } else {
+        x[0] = p[0];
+    }
+}
+
+template <int EPL>
+__device__ __forceinline__ void st_f32(float* p, const float (&x)[EPL]) {
+    if constexpr (EPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < EPL; i += 4)
+            *reinterpret_cast<float4*>(p + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    } else if constexpr (EPL == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    } else {
+        p[0] = x[0];
+    }
+}
+
+// V_slot <- V_slot - lr * acc / count, one row, lanes across d_v.
+template <int STORE, int EPL>
+__device__ __forceinline__ void apply_row(const ScatterArgs& a, int b, uint32_t slot, int count,
+                                          const float (&acc)[EPL]) {
+    const size_t off = (static_cast<size_t>(b) * a.N + slot) * a.dv + static_cast<size_t>(lane_id()) * EPL;
+    float v[EPL];
+    ld_row<STORE, EPL>(a.V, off, v);
+    const float c = static_cast<float>(count);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = v[i] - a.lr * acc[i] / c;
+    st_row<STORE, EPL>(a.V, off, v);
+    if (a.n_read && lane_id() == 0) a.n_read[static_cast<size_t>(b) * a.N + slot] = count;
+}
+
+template <int STORE, int EPL>
+__global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
+    const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t wid = static_cast<int64_t>(blk) * 4 + wave;
+    if (wid >= static_cast<int64_t>(a.B) * a.pieces) return;
+    const int b = static_cast<int>(wid / a.pieces), p = static_cast<int>(wid % a.pieces);
+    const int p0 = p * kPiece;
+    const int pos = p0 + lane;
+    const bool valid = pos < a.M;
+    const uint32_t* keys = a.keys + static_cast<size_t>(b) * a.M;
+    const uint32_t* vals = a.vals + static_cast<size_t>(b) * a.M;
+    const uint32_t key = valid ? keys[pos] : 0xffffffffu;
+    const uint32_t ent = valid ? vals[pos] : 0u;
+    uint32_t prev = __shfl_up(key, 1, 64);
+    uint32_t next = __shfl_down(key, 1, 64);
+    if (lane == 0) prev = (p0 > 0) ? keys[p0 - 1] : 0xfffffffeu;
+    if (lane == 63) next = (pos + 1 < a.M) ? keys[pos + 1] : 0xfffffffeu;
+    const bool head = valid && (pos == 0 || prev != key);
+    const bool tail = valid && (pos == a.M - 1 || next != key);
+    const int HK = a.H * a.k;
+    const int tok = static_cast<int>(ent / static_cast<uint32_t>(HK));
+    const float wv = valid ? a.w[static_cast<size_t>(b) * a.w_bstride + ent] * a.inv_h : 0.f;
+    const uint64_t hb = ballot(head), tb = ballot(tail);
+    const int nvalid = __popcll(ballot(valid));
+    const size_t pidx = static_cast<size_t>(b) * a.pieces + p;
+    if (lane == 0) {
+        a.pt_start[pidx] = -1;
+        a.ph_end[pidx] = -1;
+    }
+    const float* rb = a.r + static_cast<size_t>(b) * a.Tc * a.dv + static_cast<size_t>(lane) * EPL;
+
+    int s = 0;
+    while (s < nvalid) {
+        const uint64_t tm = tb & (~0ull << s);
+        const bool ends_here = tm != 0ull;
+        const int e = ends_here ? (__ffsll(static_cast<unsigned long long>(tm)) - 1) : nvalid - 1;
+        const bool starts_here = (hb >> s) & 1ull;
+        const uint32_t slot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), s));
+        float acc[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+        int j = s;
+        for (; j + 4 <= e + 1; j += 4) {
+            float x[4][EPL];
+            float ww[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = __builtin_amdgcn_readlane(tok, j + u);
+                ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), j + u));
+                ld_f32<EPL>(rb + static_cast<size_t>(t) * a.dv, x[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww[u], x[u][i], acc[i]);
+        }
+        for (; j <= e; ++j) {
+            float x[EPL];
+            const int t = __builtin_amdgcn_readlane(tok, j);
+            const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), j));
+            ld_f32<EPL>(rb + static_cast<size_t>(t) * a.dv, x);
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, x[i], acc[i]);
+        }
+        if (starts_here && ends_here) {
+            if (slot < a.N) apply_row<STORE, EPL>(a, b, slot, e - s + 1, acc);
+        } else if (!starts_here) {
+            // run entering from the previous piece (it starts at lane 0)
+            st_f32<EPL>(a.ph + pidx * a.dv + static_cast<size_t>(lane) * EPL, acc);
+            if (lane == 0) a.ph_end[pidx] = ends_here ? p0 + e + 1 : -1;
+        } else {
+            // run leaving into the next piece
+            st_f32<EPL>(a.pt + pidx * a.dv + static_cast<size_t>(lane) * EPL, acc);
+            if (lane == 0) a.pt_start[pidx] = p0 + s;
+        }
+        s = e + 1;
+    }
+}
+
+// Runs that cross piece boundaries: the piece a run starts in adds the
+// partials of the following pieces in order, then writes the row.
+template <int STORE, int EPL>
+__global__ __launch_bounds__(256) void k_fixup(ScatterArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (wid >= static_cast<int64_t>(a.B) * a.pieces) return;
+    const int b = static_cast<int>(wid / a.pieces), p = static_cast<int>(wid % a.pieces);
+    const size_t base = static_cast<size_t>(b) * a.pieces;
+    const int start = a.pt_start[base + p];
+    if (start < 0) return;
+    float acc[EPL];
+    ld_f32<EPL>(a.pt + (base + p) * a.dv + static_cast<size_t>(lane) * EPL, acc);
+    int end = -1;
+    for (int q = p + 1; q < a.pieces; ++q) {
+        float x[EPL];
+        ld_f32<EPL>(a.ph + (base + q) * a.dv + static_cast<size_t>(lane) * EPL, x);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[i] += x[i];
+        end = a.ph_end[base + q];
+        if (end >= 0) break;
+    }
+    if (end < 0) return;  // unreachable for a well-formed list: the last position ends a run
+    const uint32_t slot = a.keys[static_cast<size_t>(b) * a.M + start];
+    if (slot < a.N) apply_row<STORE, EPL>(a, b, slot, end - start, acc);
+}
+
+__global__ void k_fill_i32(int32_t* p, int64_t count, int32_t value) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t j = i; j < count; j += stride) p[j] = value;
+}
+
+template <int STORE, int EPL>
+hipError_t scatter_t(const ScatterArgs& a, hipStream_t s) {
+    const int64_t waves = static_cast<int64_t>(a.B) * a.pieces;
+    const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
+    hipLaunchKernelGGL((k_scatter<STORE, EPL>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_fixup<STORE, EPL>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int STORE>
+hipError_t scatter_s(const ScatterArgs& a, hipStream_t s) {
+    switch (a.dv / 64) {
+        case 1: return scatter_t<STORE, 1>(a, s);
+        case 2: return scatter_t<STORE, 2>(a, s);
+        case 4: return scatter_t<STORE, 4>(a, s);
+        case 8: return scatter_t<STORE, 8>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_scatter(const ScatterArgs& a, int store, hipStream_t s) {
+    return store == kBF16 ? scatter_s<kBF16>(a, s) : scatter_s<kF32>(a, s);
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, count, value);
+    return hipGetLastError();
+}
+
+}  // namespace fwpkm

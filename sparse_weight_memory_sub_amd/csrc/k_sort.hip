@@ -1,0 +1,133 @@
+// k_sort.hip -- stable LSD radix sort of one chunk's read list by slot id,
+// per sequence, 8 bits per pass.
+//
+// The memorisation write sums, for every value row, the contributions of
+// all reads of that row in the chunk and divides by their count N_read
+// ("Fast-weight Product Key Memory", rainbus digest step 4; paperlayer.ai
+// 3.3).  Sorting the reads by slot turns that into a segmented reduction
+// whose order is fixed (reads of a row stay in (token, head, rank) order),
+// so the write is bitwise reproducible and needs no float atomics.
+//
+// Entry e = (t*H + h)*k + j of a sequence carries key = slot id (ids outside
+// [0, N) become the sentinel N, which the scatter skips) and value = e.
+// Each pass: count (per-tile digit histograms), scan (digit-major exclusive
+// prefix over tiles), scatter (stable rank inside the tile from wavefront
+// ballots, wavefronts in order).
+#include "fwpkm_internal.h"
+
+namespace fwpkm {
+
+namespace {
+
+__device__ __forceinline__ uint32_t load_key(const SortArgs& a, int b, int pos) {
+    if (a.first) {
+        const int32_t s = a.idx[static_cast<size_t>(b) * a.idx_bstride + pos];
+        return (s < 0 || static_cast<uint32_t>(s) >= a.N) ? a.N : static_cast<uint32_t>(s);
+    }
+    return a.kin[static_cast<size_t>(b) * a.M + pos];
+}
+
+__global__ __launch_bounds__(256) void k_sort_count(SortArgs a) {
+    __shared__ uint32_t hist[256];
+    const int tile = blockIdx.x, b = blockIdx.y;
+    hist[threadIdx.x] = 0u;
+    __syncthreads();
+    const int base = tile * kSortTile;
+#pragma unroll
+    for (int it = 0; it < kSortItems; ++it) {
+        const int pos = base + it * 256 + threadIdx.x;
+        if (pos < a.M) atomicAdd(&hist[(load_key(a, b, pos) >> a.shift) & 255u], 1u);
+    }
+    __syncthreads();
+    a.counts[(static_cast<size_t>(b) * 256 + threadIdx.x) * a.tiles + tile] = hist[threadIdx.x];
+}
+
+// Exclusive prefix of counts[b][digit][tile] in (digit, tile) order.
+__global__ __launch_bounds__(256) void k_sort_scan(SortArgs a) {
+    __shared__ uint32_t wsum[4];
+    const int b = blockIdx.x, d = threadIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint32_t* row = a.counts + (static_cast<size_t>(b) * 256 + d) * a.tiles;
+    uint32_t s = 0u;
+    for (int t = 0; t < a.tiles; ++t) s += row[t];
+    const uint32_t incl = wave_incl_scan_u32(s);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0u;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    uint32_t run = off + incl - s;
+    for (int t = 0; t < a.tiles; ++t) {
+        const uint32_t c = row[t];
+        row[t] = run;
+        run += c;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
+    __shared__ uint32_t cnt[4][256];
+    __shared__ uint32_t toff[256];
+    const int tile = blockIdx.x, b = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) cnt[w][threadIdx.x] = 0u;
+    toff[threadIdx.x] = a.counts[(static_cast<size_t>(b) * 256 + threadIdx.x) * a.tiles + tile];
+    __syncthreads();
+
+    constexpr int kPerWave = kSortTile / 4;
+    const int wbase = tile * kSortTile + wave * kPerWave;
+    const uint64_t lt = lanemask_lt();
+    uint32_t key[kSortItems], val[kSortItems], loc[kSortItems];
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int pos = wbase + r * 64 + lane;
+        const bool valid = pos < a.M;
+        key[r] = valid ? load_key(a, b, pos) : 0u;
+        val[r] = valid ? (a.first ? static_cast<uint32_t>(pos) : a.vin[static_cast<size_t>(b) * a.M + pos]) : 0u;
+        const uint32_t d = (key[r] >> a.shift) & 255u;
+        uint64_t peers = ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool on = (d >> bit) & 1u;
+            const uint64_t bb = ballot(valid && on);
+            peers &= on ? bb : ~bb;
+        }
+        const uint32_t rank = __popcll(peers & lt);
+        const uint32_t before = valid ? cnt[wave][d] : 0u;
+        wave_sync();
+        if (valid && rank == 0) cnt[wave][d] = before + __popcll(peers);
+        wave_sync();
+        loc[r] = before + rank;
+    }
+    __syncthreads();
+    {
+        const int d = threadIdx.x;
+        const uint32_t c0 = cnt[0][d], c1 = cnt[1][d], c2 = cnt[2][d];
+        cnt[0][d] = 0u;
+        cnt[1][d] = c0;
+        cnt[2][d] = c0 + c1;
+        cnt[3][d] = c0 + c1 + c2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int pos = wbase + r * 64 + lane;
+        if (pos < a.M) {
+            const uint32_t d = (key[r] >> a.shift) & 255u;
+            const uint32_t g = toff[d] + cnt[wave][d] + loc[r];
+            a.kout[static_cast<size_t>(b) * a.M + g] = key[r];
+            a.vout[static_cast<size_t>(b) * a.M + g] = val[r];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.tiles), static_cast<unsigned>(a.B));
+    hipLaunchKernelGGL(k_sort_count, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_sort_scan, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_sort_scatter, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace fwpkm

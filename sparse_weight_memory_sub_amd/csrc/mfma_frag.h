@@ -1,0 +1,79 @@
+// mfma_frag.h -- 16x16 MFMA tiles over 32-wide k-blocks for bf16 and fp32
+// operands on gfx950.
+//
+// Lane l of a wavefront owns row/column (l % 16) of a 16-wide operand tile
+// and k-group g = l / 16.  Within a 32-wide k-block s, lane group g holds the
+// 8 consecutive k-elements 32*s + 8*g + j (j = 0..7) of its row.  A and B
+// use the same (g, j) -> k map, so the products pair up whatever order the
+// instruction sums them in.  The 16x16 fp32 result is spread as
+// acc[i] = C[row 4*(l/16) + i][column l % 16].
+#pragma once
+
+#include "fwpkm_internal.h"
+
+namespace fwpkm {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+template <int STORE> struct Frag;
+template <> struct Frag<kBF16> {
+    u32x4_t v;  // 8 bf16, element j in bits 16*(j%2) of word j/2
+};
+template <> struct Frag<kF32> {
+    float v[8];
+};
+
+template <int STORE> __device__ __forceinline__ void frag_zero(Frag<STORE>& f);
+template <> __device__ __forceinline__ void frag_zero<kBF16>(Frag<kBF16>& f) {
+    f.v = u32x4_t{0u, 0u, 0u, 0u};
+}
+template <> __device__ __forceinline__ void frag_zero<kF32>(Frag<kF32>& f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = 0.f;
+}
+
+// 8 consecutive storage elements starting at p (16-byte aligned for bf16,
+// 32-byte aligned for fp32).
+template <int STORE> __device__ __forceinline__ void frag_load(Frag<STORE>& f, const void* p);
+template <> __device__ __forceinline__ void frag_load<kBF16>(Frag<kBF16>& f, const void* p) {
+    f.v = *reinterpret_cast<const u32x4_t*>(p);
+}
+template <> __device__ __forceinline__ void frag_load<kF32>(Frag<kF32>& f, const void* p) {
+    const float4* s = reinterpret_cast<const float4*>(p);
+    float4 a = s[0], b = s[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// Sum of squares of the fragment's elements (fp32).
+template <int STORE> __device__ __forceinline__ float frag_sumsq(const Frag<STORE>& f);
+template <> __device__ __forceinline__ float frag_sumsq<kBF16>(const Frag<kBF16>& f) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float lo = __uint_as_float(f.v[j] << 16), hi = __uint_as_float(f.v[j] & 0xffff0000u);
+        s = fmaf(lo, lo, s);
+        s = fmaf(hi, hi, s);
+    }
+    return s;
+}
+template <> __device__ __forceinline__ float frag_sumsq<kF32>(const Frag<kF32>& f) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = fmaf(f.v[j], f.v[j], s);
+    return s;
+}
+
+// acc += A * B over one 32-wide k-block.
+__device__ __forceinline__ void mma(const Frag<kBF16>& a, const Frag<kBF16>& b, f32x4_t& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                   __builtin_bit_cast(bf16x8_t, b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(const Frag<kF32>& a, const Frag<kF32>& b, f32x4_t& acc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+}  // namespace fwpkm

@@ -1,0 +1,201 @@
+"""Thin ctypes binding of libfwpkm.so (include/fwpkm.h).
+
+The functions keep the C entry points' names.  They only check and marshal
+torch tensors (device pointers, the current HIP stream, a workspace from the
+torch allocator); every step of the layer runs in the library's HIP kernels.
+Nothing here falls back to another implementation: if the library or a GPU
+is missing, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .workloads import FwpkmConfig
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfwpkm.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+_STATUS = {OK: "FWPKM_OK", EINVAL: "FWPKM_EINVAL", EUNSUPPORTED: "FWPKM_EUNSUPPORTED",
+           EWORKSPACE: "FWPKM_EWORKSPACE", EHIP: "FWPKM_EHIP"}
+
+EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
+           "fwpkm_retrieve", "fwpkm_chunk_update", "fwpkm_forward_seq")
+
+
+class FwpkmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_q", ctypes.c_int32),
+        ("d_v", ctypes.c_int32), ("k_half", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("store", ctypes.c_int32),
+        ("idw_eps", ctypes.c_float), ("lr_v", ctypes.c_float), ("lr_k", ctypes.c_float),
+        ("lookahead", ctypes.c_int32), ("znorm", ctypes.c_int32),
+        ("znorm_eps", ctypes.c_float), ("use_addr", ctypes.c_int32),
+    ]
+
+
+def cfg_struct(c: FwpkmConfig) -> Cfg:
+    return Cfg(int(c.n), int(c.heads), int(c.d_q), int(c.d_v), int(c.k_half), int(c.k), int(c.chunk),
+               {"f32": 0, "bf16": 1}[c.store], float(c.idw_eps), float(c.lr_v), float(c.lr_k),
+               int(bool(c.lookahead)), int(bool(c.znorm)), float(c.znorm_eps), int(bool(c.use_addr)))
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libfwpkm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m sparse_weight_memory_sub_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        C = ctypes.POINTER(Cfg)
+        lib.fwpkm_abi_version.restype = i32
+        lib.fwpkm_last_error.restype = ctypes.c_char_p
+        lib.fwpkm_workspace_bytes.argtypes = [C, i32, i32, ctypes.POINTER(sz)]
+        lib.fwpkm_retrieve.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        lib.fwpkm_chunk_update.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        lib.fwpkm_forward_seq.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P]
+        for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise FwpkmError(rc, load().fwpkm_last_error().decode())
+
+
+def abi_version() -> int:
+    return int(load().fwpkm_abi_version())
+
+
+def workspace_bytes(cfg: FwpkmConfig, B: int, T: int) -> int:
+    out = ctypes.c_size_t(0)
+    c = cfg_struct(cfg)
+    _check(load().fwpkm_workspace_bytes(ctypes.byref(c), int(B), int(T), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _workspace(cfg, B, T, ws, device):
+    need = workspace_bytes(cfg, B, T)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def fwpkm_retrieve(cfg: FwpkmConfig, q, v, g, K1, K2, V, o=None, vhat=None, idx=None, w=None,
+                   ws=None, stream=None, want=("vhat", "idx", "w")):
+    """Frozen-state retrieval.  Returns dict(o, vhat, idx, w) (outputs are
+    allocated when not given and wanted)."""
+    sd = cfg.torch_dtype
+    B, T = g.shape
+    H, dq, dv, k = cfg.heads, cfg.d_q, cfg.d_v, cfg.k
+    dev = g.device
+    _dev(q, "q", sd, (B, T, H, dq)); _dev(v, "v", sd, (B, T, dv)); _dev(g, "g", torch.float32, (B, T))
+    _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
+    _dev(V, "V", sd, (B, cfg.N, dv))
+    o = torch.empty((B, T, dv), dtype=torch.float32, device=dev) if o is None else o
+    if vhat is None and "vhat" in want:
+        vhat = torch.empty((B, T, dv), dtype=torch.float32, device=dev)
+    if idx is None and "idx" in want:
+        idx = torch.empty((B, T, H, k), dtype=torch.int32, device=dev)
+    if w is None and "w" in want:
+        w = torch.empty((B, T, H, k), dtype=torch.float32, device=dev)
+    _dev(o, "o", torch.float32, (B, T, dv))
+    if vhat is not None: _dev(vhat, "vhat", torch.float32, (B, T, dv))
+    if idx is not None: _dev(idx, "idx", torch.int32, (B, T, H, k))
+    if w is not None: _dev(w, "w", torch.float32, (B, T, H, k))
+    ws, wsb = _workspace(cfg, B, T, ws, dev)
+    c = cfg_struct(cfg)
+    _check(load().fwpkm_retrieve(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2), _ptr(V),
+                                 _ptr(o), _ptr(vhat), _ptr(idx), _ptr(w), _ptr(ws), wsb, _stream(stream)))
+    return {"o": o, "vhat": vhat, "idx": idx, "w": w}
+
+
+def fwpkm_chunk_update(cfg: FwpkmConfig, q, g, tgt, n_tgt: int, idx, w, vhat, K1, K2, V, n_read=None,
+                       ws=None, stream=None):
+    """One chunk's write; K1, K2, V are updated in place.  Returns n_read (or None)."""
+    sd = cfg.torch_dtype
+    B, Tc = g.shape
+    H, dq, dv, k = cfg.heads, cfg.d_q, cfg.d_v, cfg.k
+    _dev(q, "q", sd, (B, Tc, H, dq)); _dev(g, "g", torch.float32, (B, Tc))
+    if n_tgt > 0:
+        _dev(tgt, "tgt", sd, (B, n_tgt, dv))
+    _dev(idx, "idx", torch.int32, (B, Tc, H, k)); _dev(w, "w", torch.float32, (B, Tc, H, k))
+    _dev(vhat, "vhat", torch.float32, (B, Tc, dv))
+    _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
+    _dev(V, "V", sd, (B, cfg.N, dv))
+    if n_read is not None:
+        _dev(n_read, "n_read", torch.int32, (B, cfg.N))
+    ws, wsb = _workspace(cfg, B, Tc, ws, g.device)
+    c = cfg_struct(cfg)
+    _check(load().fwpkm_chunk_update(ctypes.byref(c), B, Tc, int(n_tgt), _ptr(q), _ptr(g),
+                                     _ptr(tgt) if n_tgt > 0 else None, _ptr(idx), _ptr(w), _ptr(vhat),
+                                     _ptr(K1), _ptr(K2), _ptr(V), _ptr(n_read), _ptr(ws), wsb, _stream(stream)))
+    return n_read
+
+
+def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_next=None, o=None, vhat=None,
+                      ws=None, stream=None, want_vhat: bool = False):
+    """Whole sequences, chunk-causal, `passes` times; K1, K2, V updated in place.
+    Returns dict(o, vhat) of the last pass."""
+    sd = cfg.torch_dtype
+    B, T = g.shape
+    H, dq, dv = cfg.heads, cfg.d_q, cfg.d_v
+    dev = g.device
+    _dev(q, "q", sd, (B, T, H, dq)); _dev(v, "v", sd, (B, T, dv)); _dev(g, "g", torch.float32, (B, T))
+    if v_next is not None:
+        _dev(v_next, "v_next", sd, (B, dv))
+    _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
+    _dev(V, "V", sd, (B, cfg.N, dv))
+    o = torch.empty((B, T, dv), dtype=torch.float32, device=dev) if o is None else o
+    _dev(o, "o", torch.float32, (B, T, dv))
+    if vhat is None and want_vhat:
+        vhat = torch.empty((B, T, dv), dtype=torch.float32, device=dev)
+    if vhat is not None:
+        _dev(vhat, "vhat", torch.float32, (B, T, dv))
+    ws, wsb = _workspace(cfg, B, T, ws, dev)
+    c = cfg_struct(cfg)
+    _check(load().fwpkm_forward_seq(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g), _ptr(v_next),
+                                    _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat), _ptr(ws), wsb,
+                                    _stream(stream)))
+    return {"o": o, "vhat": vhat}

@@ -1,0 +1,312 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case prints its name before touching the GPU.  Inputs are seeded and
+synthetic; the oracle and the GPU read the same bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import TIE_REL, close, compare_indices, rtol_for, token_set_match
+from sparse_weight_memory_sub_amd import fwpkm
+from sparse_weight_memory_sub_amd.workloads import WORKLOADS, FwpkmConfig, make_state, make_tokens
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] {request.node.name}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def problem(cfg, B, T, seed, kind="gauss", kstd=0.02, **kw):
+    q, v, g, extra = make_tokens(cfg, B, T, seed, kind, **kw)
+    K1, K2, V = make_state(cfg, B, seed, std=kstd)
+    return q, v, g, K1, K2, V
+
+
+def dev(*ts):
+    return [t.to(DEV).contiguous() for t in ts]
+
+
+def as_f64(x, cfg=None):
+    """GPU tensor / oracle storage array -> float64 numpy."""
+    if isinstance(x, torch.Tensor):
+        return x.detach().float().cpu().numpy().astype(np.float64)
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    return x.astype(np.float64)
+
+
+def C(n, H, dq, dv, kh, k, chunk=64, store="f32", **kw):
+    return FwpkmConfig(n=n, heads=H, d_q=dq, d_v=dv, k_half=kh, k=k, chunk=chunk, store=store, **kw)
+
+
+RETRIEVE_CASES = [
+    ("f32_n64_h1", C(64, 1, 64, 64, 8, 8), 2, 37, 0.02),
+    ("f32_n128_h2_k12", C(128, 2, 128, 128, 16, 12), 1, 50, 0.5),
+    ("f32_n48_ragged", C(48, 1, 64, 64, 5, 3), 2, 17, 0.5),
+    ("f32_k_gt_khalf", C(32, 1, 64, 64, 4, 10), 1, 20, 0.5),
+    ("bf16_n128_h4", C(128, 4, 256, 256, 16, 16, store="bf16"), 2, 40, 0.02),
+    ("bf16_n256_h2_d512", C(256, 2, 512, 512, 32, 32, store="bf16"), 1, 33, 0.02),
+    ("bf16_n1024_h1", C(1024, 1, 512, 512, 32, 32, store="bf16"), 1, 24, 0.02),
+    ("bf16_n64_h3_kstd", C(64, 3, 64, 128, 12, 20, store="bf16"), 2, 19, 0.5),
+]
+
+
+def run_retrieve(cfg, q, v, g, K1, K2, V):
+    out = fwpkm.fwpkm_retrieve(cfg, *dev(q, v, g, K1, K2, V))
+    torch.cuda.synchronize()
+    return {k: x.cpu().numpy() for k, x in out.items()}
+
+
+@pytest.mark.parametrize("case", RETRIEVE_CASES, ids=[c[0] for c in RETRIEVE_CASES])
+def test_retrieve_parity(case):
+    name, cfg, B, T, kstd = case
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=len(name), kstd=kstd)
+    gpu = run_retrieve(cfg, q, v, g, K1, K2, V)
+    ora = oracle.retrieve(cfg, q, v, g, K1, K2, V, tie_rel=TIE_REL)
+    exact, near = compare_indices(cfg, q, K1, K2, gpu["idx"], ora)
+    print(f"  tokens*heads={exact.size} exact={int(exact.sum())} near_ties={near} oracle_flagged={int(ora['tie'].sum())}")
+    assert near <= max(2, 0.1 * exact.size)
+    m = token_set_match(gpu["idx"], ora["idx"])
+    close(gpu["w"], ora["w"], 1e-4, mask=exact, what="w")
+    close(gpu["vhat"], ora["vhat"], 1e-4, mask=m, what="vhat")
+    close(gpu["o"], ora["o"], 1e-4, mask=m, what="o")
+
+
+def test_gate_extremes_exact():
+    cfg = C(64, 2, 64, 128, 8, 8)
+    q, v, g, K1, K2, V = problem(cfg, 1, 21, seed=3)
+    for gv in (0.0, 1.0):
+        gg = torch.full_like(g, gv)
+        out = run_retrieve(cfg, q, v, gg, K1, K2, V)
+        if gv == 0.0:
+            assert np.array_equal(out["o"], v.numpy())
+        else:
+            assert np.array_equal(out["o"], out["vhat"])
+    np.testing.assert_allclose(out["w"].sum(-1), 1.0, rtol=1e-6)
+
+
+UPDATE_CASES = [
+    ("f32_n64", C(64, 1, 64, 64, 8, 8, lr_k=50.0), 2, 37, 0.5, "gauss"),
+    ("f32_n128_h2", C(128, 2, 128, 128, 16, 12, lr_k=50.0), 1, 70, 0.5, "gauss"),
+    ("f32_collide", C(64, 2, 64, 64, 8, 8, lr_k=50.0), 2, 300, 0.5, "same"),
+    ("bf16_n128_h4", C(128, 4, 256, 256, 16, 16, store="bf16"), 2, 40, 0.02, "gauss"),
+    ("bf16_n256_d512", C(256, 2, 512, 512, 32, 32, store="bf16", lr_k=1e3), 1, 64, 0.5, "gauss"),
+    ("bf16_zipf", C(128, 4, 256, 256, 16, 16, store="bf16"), 2, 200, 0.02, "zipf"),
+]
+
+
+def _update_problem(case):
+    name, cfg, B, T, kstd, kind = case
+    if kind == "same":
+        q, v, g, K1, K2, V = problem(cfg, B, T, seed=7, kstd=kstd)
+        q[:] = q[:, :1].clone()  # every token reads the same rows: runs span many pieces
+    elif kind == "zipf":
+        q, v, g, K1, K2, V = problem(cfg, B, T, seed=8, kind="zipf", kstd=kstd, n_centres=16)
+    else:
+        q, v, g, K1, K2, V = problem(cfg, B, T, seed=len(name), kstd=kstd)
+    return cfg, B, T, q, v, g, K1, K2, V
+
+
+@pytest.mark.parametrize("case", UPDATE_CASES, ids=[c[0] for c in UPDATE_CASES])
+def test_chunk_update_parity_teacher_forced(case):
+    cfg, B, T, q, v, g, K1, K2, V = _update_problem(case)
+    qd, vd, gd, K1d, K2d, Vd = dev(q, v, g, K1, K2, V)
+    r = fwpkm.fwpkm_retrieve(cfg, qd, vd, gd, K1d, K2d, Vd)
+    n_tgt = T - 1
+    tgt = v[:, 1:].contiguous()
+    nr = torch.empty((B, cfg.N), dtype=torch.int32, device=DEV)
+    fwpkm.fwpkm_chunk_update(cfg, qd, gd, tgt.to(DEV), n_tgt, r["idx"], r["w"], r["vhat"], K1d, K2d, Vd, n_read=nr)
+    torch.cuda.synchronize()
+    idx = r["idx"].cpu().numpy()
+    w = r["w"].cpu().numpy().astype(np.float64)
+    vh = r["vhat"].cpu().numpy().astype(np.float64)
+    K1o, K2o, Vo, nro = oracle.chunk_update(cfg, q, g, tgt, n_tgt, idx, w, vh, K1, K2, V)
+    nrg = nr.cpu().numpy()
+    assert np.array_equal(nrg, nro), "N_read differs"
+    print(f"  rows written={int((nro > 0).sum())} max N_read={int(nro.max())}")
+    rt = rtol_for(cfg)
+    Vg = as_f64(Vd)
+    V0 = as_f64(V)
+    unread = nro == 0
+    assert np.array_equal(Vg[unread], V0[unread]), "unread rows changed"
+    close(Vg, as_f64(Vo), rt, what="V")
+    # the write itself (V_new - V_old) on the rows that were read
+    close((Vg - V0)[~unread], (as_f64(Vo) - V0)[~unread], 1e-3 if cfg.store == "f32" else 0.1, what="dV")
+    for Kg, Ko, K0, nm in ((K1d, K1o, K1, "K1"), (K2d, K2o, K2, "K2")):
+        close(as_f64(Kg), as_f64(Ko), rt, what=nm)
+        if cfg.store == "f32":
+            close(as_f64(Kg) - as_f64(K0), as_f64(Ko) - as_f64(K0), 1e-3, what="d" + nm)
+
+
+def test_chunk_update_is_bitwise_deterministic():
+    cfg, B, T, q, v, g, K1, K2, V = _update_problem(UPDATE_CASES[5])
+    outs = []
+    for _ in range(2):
+        qd, vd, gd, K1d, K2d, Vd = dev(q, v, g, K1, K2, V)
+        r = fwpkm.fwpkm_retrieve(cfg, qd, vd, gd, K1d, K2d, Vd)
+        fwpkm.fwpkm_chunk_update(cfg, qd, gd, v[:, 1:].contiguous().to(DEV), T - 1, r["idx"], r["w"], r["vhat"],
+                                 K1d, K2d, Vd)
+        torch.cuda.synchronize()
+        outs.append([x.cpu() for x in (K1d, K2d, Vd)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_chunk_update_edge_cases():
+    cfg = C(64, 2, 64, 64, 8, 8)
+    B, T = 2, 9
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=11, kstd=0.5)
+    qd, vd, gd, K1d, K2d, Vd = dev(q, v, g, K1, K2, V)
+    r = fwpkm.fwpkm_retrieve(cfg, qd, vd, gd, K1d, K2d, Vd)
+    # n_tgt = 0: V untouched, keys still take their step
+    nr = torch.full((B, cfg.N), 7, dtype=torch.int32, device=DEV)
+    fwpkm.fwpkm_chunk_update(cfg, qd, gd, None, 0, r["idx"], r["w"], r["vhat"], K1d, K2d, Vd, n_read=nr)
+    torch.cuda.synchronize()
+    assert torch.equal(Vd.cpu(), V) and int(nr.abs().sum()) == 0
+    K1o, K2o, _, _ = oracle.chunk_update(cfg, q, g, None, 0, r["idx"].cpu().numpy(),
+                                         r["w"].cpu().numpy().astype(np.float64),
+                                         r["vhat"].cpu().numpy().astype(np.float64), K1, K2, V)
+    close(as_f64(K1d), as_f64(K1o), 1e-4, what="K1")
+    # out-of-range slot ids are skipped, never dereferenced
+    qd, vd, gd, K1d, K2d, Vd = dev(q, v, g, K1, K2, V)
+    bad = r["idx"].clone()
+    bad[:, :, :, 0] = -5
+    bad[:, :, :, 1] = cfg.N + 3
+    c0 = cfg.replace(use_addr=False)
+    fwpkm.fwpkm_chunk_update(c0, qd, gd, v[:, 1:].contiguous().to(DEV), T - 1, bad, r["w"], r["vhat"], K1d, K2d, Vd)
+    torch.cuda.synchronize()
+    # expected: the same write with the two invalid reads of every (token, head) removed
+    c2 = c0.replace(k=cfg.k - 2)
+    _, _, Vo, _ = oracle.chunk_update(c2, q, g, v[:, 1:].contiguous(), T - 1, bad.cpu().numpy()[..., 2:],
+                                      r["w"].cpu().numpy().astype(np.float64)[..., 2:],
+                                      r["vhat"].cpu().numpy().astype(np.float64), K1, K2, V)
+    close(as_f64(Vd), as_f64(Vo), 1e-4, what="V with invalid ids skipped")
+    assert torch.equal(K1d.cpu(), K1)
+
+
+def _chunked_gpu(cfg, q, v, g, K1d, K2d, Vd, v_next=None):
+    """Chunk-by-chunk retrieve + chunk_update on the GPU (state updated in place)."""
+    B, T = g.shape
+    outs = []
+    for t0 in range(0, T, cfg.chunk):
+        t1 = min(T, t0 + cfg.chunk)
+        qc, vc, gc = (x[:, t0:t1].contiguous().to(DEV) for x in (q, v, g))
+        r = fwpkm.fwpkm_retrieve(cfg, qc, vc, gc, K1d, K2d, Vd)
+        if cfg.lookahead:
+            if t1 < T:
+                tgt, n_tgt = v[:, t0 + 1:t1 + 1], t1 - t0
+            elif v_next is not None:
+                tgt, n_tgt = torch.cat([v[:, t0 + 1:t1], v_next[:, None]], 1), t1 - t0
+            else:
+                tgt, n_tgt = v[:, t0 + 1:t1], t1 - t0 - 1
+        else:
+            tgt, n_tgt = v[:, t0:t1], t1 - t0
+        fwpkm.fwpkm_chunk_update(cfg, qc, gc, tgt.contiguous().to(DEV), n_tgt, r["idx"], r["w"], r["vhat"],
+                                 K1d, K2d, Vd)
+        outs.append(r)
+    return outs
+
+
+@pytest.mark.parametrize("store,v_next", [("f32", False), ("bf16", False), ("f32", True)])
+def test_forward_seq_equals_chunked_calls_bitwise(store, v_next):
+    cfg = C(64, 2, 64, 128, 8, 8, chunk=24, store=store, lr_k=20.0)
+    B, T = 2, 100
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=21, kstd=0.5)
+    vn = torch.randn((B, cfg.d_v), generator=torch.Generator().manual_seed(5)).to(cfg.torch_dtype) if v_next else None
+    qd, vd, gd, K1a, K2a, Va = dev(q, v, g, K1, K2, V)
+    out = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1a, K2a, Va, v_next=vn.to(DEV) if v_next else None,
+                                  want_vhat=True)
+    K1b, K2b, Vb = dev(K1, K2, V)
+    outs = _chunked_gpu(cfg, q, v, g, K1b, K2b, Vb, v_next=vn)
+    torch.cuda.synchronize()
+    o_chunked = torch.cat([r["o"] for r in outs], 1)
+    vh_chunked = torch.cat([r["vhat"] for r in outs], 1)
+    assert torch.equal(out["o"], o_chunked)
+    assert torch.equal(out["vhat"], vh_chunked)
+    for a, b in ((K1a, K1b), (K2a, K2b), (Va, Vb)):
+        assert torch.equal(a, b)
+
+
+def test_forward_seq_passes_carry_state():
+    cfg = C(64, 1, 64, 64, 8, 8, chunk=16)
+    B, T = 1, 40
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=4, kstd=0.5)
+    qd, vd, gd, K1a, K2a, Va = dev(q, v, g, K1, K2, V)
+    two = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1a, K2a, Va, passes=2)
+    K1b, K2b, Vb = dev(K1, K2, V)
+    fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1b, K2b, Vb, passes=1)
+    again = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1b, K2b, Vb, passes=1)
+    torch.cuda.synchronize()
+    assert torch.equal(two["o"], again["o"])
+    assert torch.equal(Va, Vb) and torch.equal(K1a, K1b)
+
+
+def _resync_parity(cfg, q, v, g, K1, K2, V):
+    """Chunk-by-chunk GPU run; each chunk checked against the oracle started
+    from the GPU's own state before that chunk (so a near-tie flip in one
+    chunk cannot cascade into the next)."""
+    B, T = g.shape
+    K1d, K2d, Vd = dev(K1, K2, V)
+    rt = rtol_for(cfg)
+    near_total = 0
+    for t0 in range(0, T, cfg.chunk):
+        t1 = min(T, t0 + cfg.chunk)
+        s_K1, s_K2, s_V = (x.cpu() for x in (K1d, K2d, Vd))
+        qc, vc, gc = (x[:, t0:t1].contiguous() for x in (q, v, g))
+        r = fwpkm.fwpkm_retrieve(cfg, qc.to(DEV), vc.to(DEV), gc.to(DEV), K1d, K2d, Vd)
+        torch.cuda.synchronize()
+        ora = oracle.retrieve(cfg, qc, vc, gc, s_K1, s_K2, s_V, tie_rel=TIE_REL)
+        exact, near = compare_indices(cfg, qc, s_K1, s_K2, r["idx"].cpu().numpy(), ora)
+        near_total += near
+        m = token_set_match(r["idx"].cpu().numpy(), ora["idx"])
+        close(r["o"].cpu().numpy(), ora["o"], 1e-4, mask=m, what=f"o chunk@{t0}")
+        n_tgt = (t1 - t0) if t1 < T else (t1 - t0 - 1)
+        tgt = v[:, t0 + 1:t0 + 1 + n_tgt].contiguous()
+        fwpkm.fwpkm_chunk_update(cfg, qc.to(DEV), gc.to(DEV), tgt.to(DEV), n_tgt, r["idx"], r["w"], r["vhat"],
+                                 K1d, K2d, Vd)
+        torch.cuda.synchronize()
+        K1o, K2o, Vo, _ = oracle.chunk_update(cfg, qc, gc, tgt, n_tgt, r["idx"].cpu().numpy(),
+                                              r["w"].cpu().numpy().astype(np.float64),
+                                              r["vhat"].cpu().numpy().astype(np.float64), s_K1, s_K2, s_V)
+        close(as_f64(Vd), as_f64(Vo), rt, what=f"V chunk@{t0}")
+        close(as_f64(K1d), as_f64(K1o), rt, what=f"K1 chunk@{t0}")
+        close(as_f64(K2d), as_f64(K2o), rt, what=f"K2 chunk@{t0}")
+    return near_total
+
+
+def test_tiny_workload_resync_parity():
+    wl = WORKLOADS["tiny"]
+    q, v, g, extra = make_tokens(wl.cfg, wl.B, wl.T, wl.seed, wl.kind)
+    K1, K2, V = make_state(wl.cfg, wl.B, wl.seed)
+    near = _resync_parity(wl.cfg, q, v, g, K1, K2, V)
+    print(f"  near-tie tokens over the run: {near}")
+
+
+def test_tiny_workload_end_to_end():
+    """forward_seq (the benchmarked call) against the oracle's whole run."""
+    wl = WORKLOADS["tiny"]
+    cfg = wl.cfg
+    q, v, g, extra = make_tokens(cfg, wl.B, wl.T, wl.seed, wl.kind)
+    K1, K2, V = make_state(cfg, wl.B, wl.seed)
+    qd, vd, gd, K1d, K2d, Vd = dev(q, v, g, K1, K2, V)
+    out = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1d, K2d, Vd, want_vhat=True)
+    torch.cuda.synchronize()
+    ora = oracle.forward_seq(cfg, q, v, g, K1, K2, V)
+    o = out["o"].cpu().numpy()
+    err = np.abs(o - ora["o"]) / (np.abs(ora["o"]) + np.sqrt(np.mean(ora["o"] ** 2)))
+    bad_tok = (err > 1e-4).any(-1)
+    print(f"  tokens beyond 1e-4: {int(bad_tok.sum())} of {bad_tok.size}; worst {err.max():.3g}")
+    # a near-tie flip can move later reads of the rows it wrote; allow at most 1% of tokens
+    assert bad_tok.mean() <= 0.01
+    close(as_f64(Vd), as_f64(ora["V"]), 1e-3, what="final V")
