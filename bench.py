@@ -1,0 +1,240 @@
+"""Benchmark of the FwPKM layer hot path on one MI355X.
+
+A step is one fwpkm_forward_seq over one batch of the workload: every chunk
+of every sequence read (scoring, top-k, gather, gated output) and then
+written (value rows and sub-key codebooks), in causal order.  Inputs are
+seeded synthetic data already resident in HBM; the fast-weight state carries
+over from step to step, as it does across sequences of a stream.
+
+Prints one JSON line: tokens/s of the whole job, the roofline of the
+dominant kernel (its algorithmic bytes or flops per launch over its average
+launch time, measured with HIP events on the library's stream), and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--workload million] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FwPKM layer tokens/s (retrieve+chunk update) on one GPU; gather/scatter HBM GB/s"
+HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E, GB/s
+MFMA_PEAK_TFS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="million")
+    ap.add_argument("--passes", type=int, default=None)
+    ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the oracle sample")
+    ap.add_argument("--cpu-chunks", type=int, default=None, help="chunks per sequence of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="only the timed steps (for profilers): no kernel timing pass, no CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, B, Tc, n_tgt, U, passes_write_o=True):
+    """Algorithmic bytes / flops of one launch of each kernel family for one
+    chunk step of B sequences (Tc tokens, n_tgt with targets, U unique rows
+    written per sequence)."""
+    es = 2 if cfg.store == "bf16" else 4
+    H, k, dv, n, dh = cfg.heads, cfg.k, cfg.d_v, cfg.n, cfg.d_h
+    tok = B * Tc
+    M = B * n_tgt * H * k
+    gather = tok * (H * k * dv * es      # selected value rows
+                    + H * k * 8          # slot ids and weights
+                    + dv * es + 4        # residual-path value and gate
+                    + dv * es            # lookahead target
+                    + 4 * dv             # residual r written
+                    + (4 * dv if passes_write_o else 0))  # o written
+    scatter = (B * U * dv * es * 2       # read-modify-write of each written row
+               + B * n_tgt * dv * 4      # residual rows (read once)
+               + M * 12)                 # sorted slot, entry, weight per read
+    sweep_flops = 2.0 * tok * H * 2 * n * dh        # q.K for both halves
+    kgrad_flops = 2.0 * 2 * B * H * 2 * n * Tc * dh  # distance recompute + a^T q
+    return {"gather": gather, "scatter": scatter, "sweep_select": sweep_flops,
+            "sweep_rowstat": sweep_flops, "kgrad": kgrad_flops}
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(ROOT, "sparse_weight_memory_sub_amd", "csrc", nm), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SRC = {"gather": ("k_gather.hip",), "scatter": ("k_scatter.hip",),
+              "sweep_select": ("k_sweep.hip", "mfma_frag.h"), "kgrad": ("k_addr.hip", "mfma_frag.h")}
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, when
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SRC:
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("src_hash") != src_hash(*KERNEL_SRC[kernel]):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from sparse_weight_memory_sub_amd import fwpkm
+    from sparse_weight_memory_sub_amd.workloads import WORKLOADS, make_state, make_tokens
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    wl = WORKLOADS[args.workload]
+    cfg, B, T = wl.cfg, wl.B, wl.T
+    passes = args.passes or wl.passes
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    q, v, g, _ = make_tokens(cfg, B, T, wl.seed, wl.kind)
+    K1, K2, V = make_state(cfg, B, wl.seed, device=dev)
+    q, v, g = q.to(dev), v.to(dev), g.to(dev)
+    log(f"workload {wl.name}: B={B} T={T} N={cfg.N} H={cfg.heads} d_q={cfg.d_q} d_v={cfg.d_v} "
+        f"k={cfg.k} C={cfg.chunk} {cfg.store}; inputs ready in {time.time() - t0:.1f}s")
+
+    want_cpu = not (args.no_cpu_baseline or args.profile_only)
+    if want_cpu:
+        ns = args.cpu_seqs or 1
+        pristine = [x[:ns].cpu() for x in (K1, K2, V)]
+
+    o = torch.empty((B, T, cfg.d_v), dtype=torch.float32, device=dev)
+    ws = torch.empty(fwpkm.workspace_bytes(cfg, B, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fwpkm.fwpkm_forward_seq(cfg, q, v, g, K1, K2, V, passes=passes, o=o, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    tokens_step = B * T * passes
+    value = tokens_step / (ms_step / 1e3)
+    log(f"{args.steps} steps: {ms_step:.3f} ms/step, {value:.4g} tokens/s")
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.store, "data": "synthetic",
+        "config": {"workload": wl.name, "n_slots": cfg.N, "heads": cfg.heads, "d_q": cfg.d_q, "d_v": cfg.d_v,
+                   "k_half": cfg.k_half, "k": cfg.k, "chunk": cfg.chunk, "batch": B, "seq_len": T,
+                   "passes": passes, "storage": cfg.store, "accumulate": "f32", "state": "carried across steps"},
+    }
+    if args.profile_only:
+        print(json.dumps(result), flush=True)
+        return
+
+    # --- per-kernel timing pass (events around each kernel family launch) ---
+    fwpkm.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    tk = fwpkm.timing_read()
+    fwpkm.timing_enable(False)
+
+    # --- unique rows written per chunk, measured on sampled chunks ---
+    nchunks = (T + cfg.chunk - 1) // cfg.chunk
+    Us = []
+    Ks = [x.clone() for x in (K1, K2, V)]
+    for c in sorted({0, nchunks // 2, nchunks - 1}):
+        c0, c1 = c * cfg.chunk, min(T, (c + 1) * cfg.chunk)
+        r = fwpkm.fwpkm_retrieve(cfg, q[:, c0:c1].contiguous(), v[:, c0:c1].contiguous(), g[:, c0:c1].contiguous(),
+                                 *Ks, want=("idx",))
+        n_t = (c1 - c0) if c1 < T else (c1 - c0 - 1)
+        idx = r["idx"][:, :n_t].reshape(B, -1)
+        Us.append(float(sum(torch.unique(idx[b]).numel() for b in range(B))) / B)
+    del Ks
+    U = sum(Us) / len(Us)
+    n_tgt = cfg.chunk  # all but the sequence's last chunk
+    alg = algorithmic(cfg, B, min(cfg.chunk, T), n_tgt, U)
+    kernels = {}
+    for name, (ms, n) in tk.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        entry = {"avg_ms": avg, "launches": n, "share": ms / sum(x[0] for x in tk.values())}
+        if name in ("gather", "scatter"):
+            entry["algorithmic_bytes"] = alg[name]
+            entry["GB/s"] = alg[name] / (avg / 1e3) / 1e9
+            entry["frac_hbm_peak"] = entry["GB/s"] / HBM_PEAK_GBS
+        elif name in ("sweep_select", "sweep_rowstat", "kgrad"):
+            entry["algorithmic_flops"] = alg[name]
+            entry["TFLOP/s"] = alg[name] / (avg / 1e3) / 1e12
+            entry["frac_mfma_peak"] = entry["TFLOP/s"] / MFMA_PEAK_TFS[cfg.store]
+        kernels[name] = entry
+    dom = max(("gather", "scatter"), key=lambda k: tk[k][0])
+    d = kernels[dom]
+    traffic = traffic_from_profiles(dom, wl.name)
+    result["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": d["frac_hbm_peak"], "traffic": traffic,
+                          "bytes_per_launch": d["algorithmic_bytes"], "avg_launch_ms": d["avg_ms"]}
+    result["kernels"] = kernels
+    result["unique_rows_per_chunk_seq"] = U
+    result["reads_per_chunk_seq"] = n_tgt * cfg.heads * cfg.k
+    log(f"dominant kernel {dom}: {d['GB/s']:.1f} GB/s ({100 * d['frac_hbm_peak']:.1f}% of HBM peak); U={U:.0f}")
+
+    # --- CPU oracle on a bounded sample of the same workload ---
+    if want_cpu:
+        import oracle
+        ns = args.cpu_seqs or 1
+        nc = args.cpu_chunks or nchunks
+        qs, vs, gs = (x[:ns].cpu() for x in (q, v, g))
+        threads = oracle.num_threads()
+        t1 = time.perf_counter()
+        oracle.forward_seq(cfg, qs, vs, gs, *pristine, passes=1, chunk_limit=nc)
+        dt = time.perf_counter() - t1
+        tok = ns * min(T, nc * cfg.chunk)
+        result["cpu_baseline"] = {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "sample": f"{ns} sequence(s) x first {nc} chunk(s) of pass 1 "
+                                            f"({tok} tokens, {dt:.1f} s, fp64 C oracle, OpenMP)"}
+        log(f"cpu oracle: {tok / dt:.4g} tokens/s on {threads} threads ({dt:.1f} s)")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

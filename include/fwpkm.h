@@ -189,6 +189,41 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
                       float* o, float* vhat,
                       void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Kernel timing (observability; not part of the method).  Kernel families
+ * of the entry points above, for fwpkm_timing_read.
+ */
+typedef enum {
+    FWPKM_K_KNORM = 0,          /* sub-key norms at the start of a call            */
+    FWPKM_K_SWEEP_SELECT = 1,   /* scoring + top-k' + product top-k (+ usage sums)  */
+    FWPKM_K_GATHER = 2,         /* value-row gather, gated output, residual        */
+    FWPKM_K_RESID = 3,          /* residual of fwpkm_chunk_update                  */
+    FWPKM_K_SORT = 4,           /* radix sort of the read list (all passes)        */
+    FWPKM_K_SCATTER = 5,        /* read-count-normalised value-row write           */
+    FWPKM_K_PBAR = 6,           /* log of the usage marginals                      */
+    FWPKM_K_SWEEP_STATS = 7,    /* usage sums of fwpkm_chunk_update                */
+    FWPKM_K_SWEEP_ROWSTAT = 8,  /* row statistic of the entropy gradient           */
+    FWPKM_K_KGRAD = 9,          /* sub-key gradient step                           */
+    FWPKM_K_FILL = 10,          /* zero fill of n_read                             */
+    FWPKM_K_COUNT = 11
+} fwpkm_kernel;
+
+/*
+ * on != 0: from now on every kernel family launch of the calling process is
+ * bracketed by a pair of HIP events recorded on the launch's stream, and the
+ * accumulated totals are reset.  on == 0 stops recording (totals are kept).
+ * Recording adds two event records per launch; leave it off when timing a
+ * whole call.  Not thread-safe against concurrent entry-point calls.
+ */
+int fwpkm_timing_enable(int32_t on);
+
+/*
+ * Waits for every recorded event, then writes the summed elapsed time in
+ * milliseconds and the number of timed launches of family `kernel` since the
+ * last fwpkm_timing_enable(1).
+ */
+int fwpkm_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

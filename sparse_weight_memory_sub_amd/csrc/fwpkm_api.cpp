@@ -19,7 +19,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 using namespace fwpkm;
 
@@ -41,6 +43,72 @@ int ok() {
     g_err.clear();
     return FWPKM_OK;
 }
+
+// ---------------------------------------------------------------------------
+// opt-in kernel timing: HIP events around each kernel family launch
+// ---------------------------------------------------------------------------
+struct TimedPair {
+    int family;
+    hipEvent_t start, stop;
+};
+
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    std::vector<TimedPair> pending;
+    double ms[FWPKM_K_COUNT] = {};
+    int64_t launches[FWPKM_K_COUNT] = {};
+
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+};
+
+Timing& timing() {
+    static Timing t;
+    return t;
+}
+
+// Brackets one kernel family launch with events when timing is on.
+class TimedLaunch {
+  public:
+    TimedLaunch(int family, hipStream_t s) : family_(family), s_(s) {
+        Timing& t = timing();
+        if (!t.on) return;
+        std::lock_guard<std::mutex> lk(t.mu);
+        start_ = t.get();
+        stop_ = t.get();
+        if (!start_ || !stop_ || hipEventRecord(start_, s_) != hipSuccess) drop(t);
+    }
+    ~TimedLaunch() {
+        if (!start_ || !stop_) return;
+        Timing& t = timing();
+        std::lock_guard<std::mutex> lk(t.mu);
+        if (hipEventRecord(stop_, s_) != hipSuccess) {
+            drop(t);
+            return;
+        }
+        t.pending.push_back({family_, start_, stop_});
+    }
+
+  private:
+    void drop(Timing& t) {
+        if (start_) t.pool.push_back(start_);
+        if (stop_) t.pool.push_back(stop_);
+        start_ = stop_ = nullptr;
+    }
+    int family_;
+    hipStream_t s_;
+    hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
 
 struct Plan {
     int n, H, dq, dh, dv, kh, k, C, store, es;
@@ -173,6 +241,7 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
     } while (0)
 
 hipError_t knorm_launch(const Plan& p, int B, const void* K1, const void* K2, float* knorm, hipStream_t s) {
+    TimedLaunch tl(FWPKM_K_KNORM, s);
     KnormArgs a{K1, K2, knorm, B, p.H, p.n, p.dh};
     return launch_knorm(a, p.store, s);
 }
@@ -192,12 +261,17 @@ SweepArgs sweep_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstr
 int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt, const int32_t* idx,
              const float* w, int64_t iw_bstride, void* V, int32_t* n_read, hipStream_t s) {
     const int M = n_tgt * p.H * p.k;
-    if (n_read) HIP_TRY(launch_fill_i32(n_read, static_cast<int64_t>(B) * p.N, 0, s));
+    if (n_read) {
+        TimedLaunch tl(FWPKM_K_FILL, s);
+        HIP_TRY(launch_fill_i32(n_read, static_cast<int64_t>(B) * p.N, 0, s));
+    }
     if (M == 0) return FWPKM_OK;
     const int tiles = (M + kSortTile - 1) / kSortTile;
     uint32_t* kb[2] = {at<uint32_t>(ws, L.k0), at<uint32_t>(ws, L.k1)};
     uint32_t* vb[2] = {at<uint32_t>(ws, L.v0), at<uint32_t>(ws, L.v1)};
     int cur = 0;
+    {
+    TimedLaunch tl(FWPKM_K_SORT, s);
     for (int pass = 0; pass < p.sort_passes; ++pass) {
         SortArgs a{};
         a.idx = idx; a.idx_bstride = iw_bstride;
@@ -209,6 +283,7 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
         HIP_TRY(launch_sort_pass(a, s));
         cur ^= 1;
     }
+    }
     ScatterArgs sa{};
     sa.keys = kb[cur]; sa.vals = vb[cur];
     sa.w = w; sa.w_bstride = iw_bstride;
@@ -218,7 +293,10 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
     sa.pt_start = at<int32_t>(ws, L.pts); sa.ph_end = at<int32_t>(ws, L.phe);
     sa.B = B; sa.M = M; sa.pieces = (M + kPiece - 1) / kPiece; sa.H = p.H; sa.k = p.k; sa.dv = p.dv; sa.Tc = Tc;
     sa.N = static_cast<uint32_t>(p.N); sa.lr = p.lr_v; sa.inv_h = 1.f / static_cast<float>(p.H);
-    HIP_TRY(launch_scatter(sa, p.store, s));
+    {
+        TimedLaunch tl(FWPKM_K_SCATTER, s);
+        HIP_TRY(launch_scatter(sa, p.store, s));
+    }
     return FWPKM_OK;
 }
 
@@ -232,20 +310,30 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
         SweepArgs a = sweep_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kSweepStats);
         a.qn = at<float>(ws, L.qn);
         a.part = at<float>(ws, L.part);
+        TimedLaunch tl(FWPKM_K_SWEEP_STATS, s);
         HIP_TRY(launch_sweep(a, p.store, s));
     }
     PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, (Tc + kTileT - 1) / kTileT, Tc};
-    HIP_TRY(launch_pbar(pa, s));
+    {
+        TimedLaunch tl(FWPKM_K_PBAR, s);
+        HIP_TRY(launch_pbar(pa, s));
+    }
     SweepArgs ra = sweep_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kSweepRowStat);
     ra.lp = at<float>(ws, L.lp);
     ra.Z = at<float>(ws, L.Z);
     ra.m = at<float>(ws, L.m);
-    HIP_TRY(launch_sweep(ra, p.store, s));
+    {
+        TimedLaunch tl(FWPKM_K_SWEEP_ROWSTAT, s);
+        HIP_TRY(launch_sweep(ra, p.store, s));
+    }
     KgradArgs ka{};
     ka.q = q; ka.q_bstride = q_bstride; ka.K1 = K1; ka.K2 = K2; ka.knorm = knorm;
     ka.qn = at<float>(ws, L.qn); ka.Z = at<float>(ws, L.Z); ka.m = at<float>(ws, L.m); ka.lp = at<float>(ws, L.lp);
     ka.B = B; ka.Tc = Tc; ka.n = p.n; ka.H = p.H; ka.dh = p.dh; ka.eps = p.eps; ka.lr = p.lr_k;
-    HIP_TRY(launch_kgrad(ka, p.store, s));
+    {
+        TimedLaunch tl(FWPKM_K_KGRAD, s);
+        HIP_TRY(launch_kgrad(ka, p.store, s));
+    }
     return FWPKM_OK;
 }
 
@@ -291,14 +379,20 @@ int fwpkm_retrieve(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, co
     float* ww = w ? w : at<float>(ws, L.w);
     SweepArgs a = sweep_args(p, B, T, q, static_cast<int64_t>(T) * p.H * p.dq, K1, K2, knorm, kSweepSelect);
     a.idx = ii; a.w = ww; a.iw_bstride = static_cast<int64_t>(T) * p.H * p.k;
-    HIP_TRY(launch_sweep(a, p.store, s));
+    {
+        TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
+        HIP_TRY(launch_sweep(a, p.store, s));
+    }
     GatherArgs ga{};
     ga.V = V; ga.idx = ii; ga.w = ww; ga.iw_bstride = a.iw_bstride;
     ga.v = v; ga.v_bstride = static_cast<int64_t>(T) * p.dv;
     ga.g = g; ga.g_bstride = T;
     ga.o = o; ga.vhat = vhat; ga.o_bstride = static_cast<int64_t>(T) * p.dv;
     ga.B = B; ga.Tc = T; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
-    HIP_TRY(launch_gather(ga, p.store, s));
+    {
+        TimedLaunch tl(FWPKM_K_GATHER, s);
+        HIP_TRY(launch_gather(ga, p.store, s));
+    }
     return ok();
 }
 
@@ -322,6 +416,7 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
     HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     if (n_tgt > 0) {
         ResidArgs ra{vhat, g, tgt, at<float>(ws, L.r), B, Tc, n_tgt, p.dv, p.znorm, p.zeps};
+        TimedLaunch tl(FWPKM_K_RESID, s);
         HIP_TRY(launch_resid(ra, p.store, s));
     }
     const int64_t iwb = static_cast<int64_t>(Tc) * p.H * p.k;
@@ -370,7 +465,10 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             a.idx = idx; a.w = w; a.iw_bstride = iwb;
             a.qn = at<float>(ws, L.qn);
             a.part = at<float>(ws, L.part);
-            HIP_TRY(launch_sweep(a, p.store, s));
+            {
+                TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
+                HIP_TRY(launch_sweep(a, p.store, s));
+            }
             // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
             int n_tgt;
             const void* tgt;
@@ -402,7 +500,10 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             ga.r = at<float>(ws, L.r);
             ga.B = B; ga.Tc = Tc; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
             ga.znorm = p.znorm; ga.znorm_eps = p.zeps;
-            HIP_TRY(launch_gather(ga, p.store, s));
+            {
+                TimedLaunch tl(FWPKM_K_GATHER, s);
+                HIP_TRY(launch_gather(ga, p.store, s));
+            }
             // write
             rc = memorise(p, L, ws, B, Tc, n_tgt, idx, w, iwb, V, nullptr, s);
             if (rc) return rc;
@@ -412,6 +513,44 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             }
         }
     }
+    return ok();
+}
+
+int fwpkm_timing_enable(int32_t on) {
+    Timing& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (on) {
+        for (const TimedPair& p : t.pending) {
+            t.pool.push_back(p.start);
+            t.pool.push_back(p.stop);
+        }
+        t.pending.clear();
+        for (int i = 0; i < FWPKM_K_COUNT; ++i) {
+            t.ms[i] = 0.0;
+            t.launches[i] = 0;
+        }
+    }
+    t.on = on != 0;
+    return ok();
+}
+
+int fwpkm_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
+    if (kernel < 0 || kernel >= FWPKM_K_COUNT) return fail(FWPKM_EINVAL, "unknown kernel family %d", kernel);
+    if (!total_ms || !launches) return fail(FWPKM_EINVAL, "total_ms and launches are required");
+    Timing& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    for (const TimedPair& p : t.pending) {
+        HIP_TRY(hipEventSynchronize(p.stop));
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, p.start, p.stop));
+        t.ms[p.family] += ms;
+        t.launches[p.family] += 1;
+        t.pool.push_back(p.start);
+        t.pool.push_back(p.stop);
+    }
+    t.pending.clear();
+    *total_ms = t.ms[kernel];
+    *launches = t.launches[kernel];
     return ok();
 }
 

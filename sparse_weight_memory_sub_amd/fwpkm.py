@@ -23,7 +23,12 @@ _STATUS = {OK: "FWPKM_OK", EINVAL: "FWPKM_EINVAL", EUNSUPPORTED: "FWPKM_EUNSUPPO
            EWORKSPACE: "FWPKM_EWORKSPACE", EHIP: "FWPKM_EHIP"}
 
 EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
-           "fwpkm_retrieve", "fwpkm_chunk_update", "fwpkm_forward_seq")
+           "fwpkm_retrieve", "fwpkm_chunk_update", "fwpkm_forward_seq",
+           "fwpkm_timing_enable", "fwpkm_timing_read")
+
+# kernel families of fwpkm_timing_read, in fwpkm_kernel order
+KERNELS = ("knorm", "sweep_select", "gather", "resid", "sort", "scatter", "pbar",
+           "sweep_stats", "sweep_rowstat", "kgrad", "fill")
 
 
 class FwpkmError(RuntimeError):
@@ -67,7 +72,10 @@ def load(path: str = LIB_PATH):
         lib.fwpkm_retrieve.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_chunk_update.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_forward_seq.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P]
-        for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq):
+        lib.fwpkm_timing_enable.argtypes = [i32]
+        lib.fwpkm_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq,
+                  lib.fwpkm_timing_enable, lib.fwpkm_timing_read):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -80,6 +88,21 @@ def _check(rc: int):
 
 def abi_version() -> int:
     return int(load().fwpkm_abi_version())
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every kernel family launch with HIP events (resets totals when on)."""
+    _check(load().fwpkm_timing_enable(1 if on else 0))
+
+
+def timing_read() -> dict:
+    """{family: (total_ms, launches)} of the launches timed since timing_enable(True)."""
+    out = {}
+    for i, name in enumerate(KERNELS):
+        ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+        _check(load().fwpkm_timing_read(i, ctypes.byref(ms), ctypes.byref(n)))
+        out[name] = (float(ms.value), int(n.value))
+    return out
 
 
 def workspace_bytes(cfg: FwpkmConfig, B: int, T: int) -> int:

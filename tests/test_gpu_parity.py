@@ -141,12 +141,23 @@ def test_chunk_update_parity_teacher_forced(case):
     unread = nro == 0
     assert np.array_equal(Vg[unread], V0[unread]), "unread rows changed"
     close(Vg, as_f64(Vo), rt, what="V")
-    # the write itself (V_new - V_old) on the rows that were read
-    close((Vg - V0)[~unread], (as_f64(Vo) - V0)[~unread], 1e-3 if cfg.store == "f32" else 0.1, what="dV")
+    # the write itself (new - old): elementwise for fp32; for bf16 storage a
+    # step of a few ulps can differ by one rounding, so compare it as a norm
+    delta_check(Vg - V0, as_f64(Vo) - V0, cfg, "dV")
     for Kg, Ko, K0, nm in ((K1d, K1o, K1, "K1"), (K2d, K2o, K2, "K2")):
         close(as_f64(Kg), as_f64(Ko), rt, what=nm)
-        if cfg.store == "f32":
-            close(as_f64(Kg) - as_f64(K0), as_f64(Ko) - as_f64(K0), 1e-3, what="d" + nm)
+        delta_check(as_f64(Kg) - as_f64(K0), as_f64(Ko) - as_f64(K0), cfg, "d" + nm)
+
+
+def delta_check(dg, do, cfg, what):
+    if cfg.store == "f32":
+        close(dg, do, 1e-3, what=what)
+    else:
+        den = np.linalg.norm(do)
+        if den > 0:
+            rel = np.linalg.norm(dg - do) / den
+            print(f"  {what}: relative norm error {rel:.3g}")
+            assert rel <= 2e-2, f"{what}: relative norm error {rel:.3g}"
 
 
 def test_chunk_update_is_bitwise_deterministic():
