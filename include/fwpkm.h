@@ -58,7 +58,7 @@ typedef enum {
  * Layer configuration.
  *   n        sub-keys per codebook; N = n*n value slots ([digest] prerequisites:
  *            keys factorised into two smaller key matrices; [gist-es]: N ~ 10^6).
- *            GPU limits: 16 <= n <= 2048, n % 16 == 0.
+ *            GPU limits: 16 <= n <= 1024, n % 16 == 0.
  *   heads    H query heads.  Each head has its own query slice and its own
  *            K1, K2; all heads read and write the one shared V, and the
  *            retrieved value is the mean over heads ([layer] D.1, D.3: more
@@ -195,7 +195,7 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
  */
 typedef enum {
     FWPKM_K_KNORM = 0,          /* sub-key norms at the start of a call            */
-    FWPKM_K_SWEEP_SELECT = 1,   /* scoring + top-k' + product top-k (+ usage sums)  */
+    FWPKM_K_SWEEP_SELECT = 1,   /* scoring: top-k' candidate lists (+ usage sums)   */
     FWPKM_K_GATHER = 2,         /* value-row gather, gated output, residual        */
     FWPKM_K_RESID = 3,          /* residual of fwpkm_chunk_update                  */
     FWPKM_K_SORT = 4,           /* radix sort of the read list (all passes)        */
@@ -205,7 +205,8 @@ typedef enum {
     FWPKM_K_SWEEP_ROWSTAT = 8,  /* row statistic of the entropy gradient           */
     FWPKM_K_KGRAD = 9,          /* sub-key gradient step                           */
     FWPKM_K_FILL = 10,          /* zero fill of n_read                             */
-    FWPKM_K_COUNT = 11
+    FWPKM_K_SELECT = 11,        /* per-half top-k', product top-k, weights         */
+    FWPKM_K_COUNT = 12
 } fwpkm_kernel;
 
 /*

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfwpkm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["fwpkm_api.cpp", "k_sweep.hip", "k_gather.hip", "k_sort.hip", "k_scatter.hip", "k_addr.hip"]
+SOURCES = ["fwpkm_api.cpp", "k_score.hip", "k_gather.hip", "k_sort.hip", "k_scatter.hip", "k_addr.hip"]
 
 ARCH = os.environ.get("FWPKM_OFFLOAD_ARCH", "gfx950")
 

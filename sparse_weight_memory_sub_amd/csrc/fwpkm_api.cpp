@@ -174,7 +174,7 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, knorm, qn, r, Z, m, part, lp, k0, v0, k1, v1, counts, ph, pt, pts, phe;
+    size_t idx, w, knorm, qn, cand, cnt, r, Z, m, part, lp, k0, v0, k1, v1, counts, ph, pt, pts, phe;
     size_t total;
 };
 
@@ -187,12 +187,14 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update) {
         return at;
     };
     const size_t Bs = static_cast<size_t>(B), T = static_cast<size_t>(Tt);
-    const size_t ntiles = (T + kTileT - 1) / kTileT;
+    const size_t ntiles = (T + kScoreTok - 1) / kScoreTok;
     L.knorm = take(Bs * p.H * 2 * p.n * 4);
     L.qn = take(Bs * p.H * 2 * T * 4);
     if (with_iw) {
         L.idx = take(Bs * T * p.H * p.k * 4);
         L.w = take(Bs * T * p.H * p.k * 4);
+        L.cand = take(Bs * p.H * 2 * T * static_cast<size_t>(score_cap(p.kh)) * 8);
+        L.cnt = take(Bs * p.H * 2 * T * 4);
     }
     if (with_update) {
         const size_t M = T * p.H * p.k;
@@ -246,14 +248,41 @@ hipError_t knorm_launch(const Plan& p, int B, const void* K1, const void* K2, fl
     return launch_knorm(a, p.store, s);
 }
 
-// Sweep over Tc tokens (q with per-sequence stride q_bstride elements).
-SweepArgs sweep_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstride, const void* K1,
+// Scoring of Tc tokens (q with per-sequence stride q_bstride elements).
+ScoreArgs score_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstride, const void* K1,
                      const void* K2, const float* knorm, int mode) {
-    SweepArgs a{};
+    ScoreArgs a{};
     a.q = q; a.q_bstride = q_bstride; a.K1 = K1; a.K2 = K2; a.knorm = knorm;
-    a.B = B; a.Tc = Tc; a.n = p.n; a.H = p.H; a.dh = p.dh; a.kh = p.kh; a.k = p.k; a.ncand = p.ncand;
-    a.eps = p.eps; a.mode = mode; a.cand = p.cand;
+    a.B = B; a.Tc = Tc; a.n = p.n; a.H = p.H; a.dh = p.dh; a.kh = p.kh;
+    a.eps = p.eps; a.mode = mode; a.cap = score_cap(p.kh);
     return a;
+}
+
+// Retrieval's selection of Tc tokens: candidate scoring, then per (token,
+// head) top-k' of each half and the product top-k into idx / w.
+int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
+                const void* K1, const void* K2, int32_t* idx, float* w, int64_t iw_bstride, bool stats,
+                hipStream_t s) {
+    ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, at<float>(ws, L.knorm),
+                             kScoreSelect | (stats ? kScoreStats : 0));
+    a.cand = at<uint64_t>(ws, L.cand);
+    a.cnt = at<int32_t>(ws, L.cnt);
+    a.qn = at<float>(ws, L.qn);
+    if (stats) a.part = at<float>(ws, L.part);
+    {
+        TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
+        HIP_TRY(launch_score(a, p.store, s));
+    }
+    SelectArgs sa{};
+    sa.cand = a.cand; sa.cnt = a.cnt; sa.cap = a.cap;
+    sa.q = q; sa.q_bstride = q_bstride; sa.K1 = K1; sa.K2 = K2;
+    sa.B = B; sa.Tc = Tc; sa.n = p.n; sa.H = p.H; sa.dh = p.dh; sa.kh = p.kh; sa.k = p.k; sa.ncand = p.ncand;
+    sa.eps = p.eps; sa.idx = idx; sa.w = w; sa.iw_bstride = iw_bstride; sa.cand_ab = p.cand;
+    {
+        TimedLaunch tl(FWPKM_K_SELECT, s);
+        HIP_TRY(launch_select(sa, p.store, s));
+    }
+    return FWPKM_OK;
 }
 
 // Memorisation write of one chunk from idx/w (per-sequence stride iw_bstride),
@@ -301,30 +330,30 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
 }
 
 // Addressing step of one chunk.  With `have_stats` the chunk's usage
-// partial sums (and ||q||^2) are already in the workspace from the select
-// sweep; otherwise a stats sweep computes them first.
+// partial sums (and ||q||^2) are already in the workspace from the
+// retrieval's scoring; otherwise a stats scoring pass computes them first.
 int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
             void* K1, void* K2, bool have_stats, hipStream_t s) {
     float* knorm = at<float>(ws, L.knorm);
     if (!have_stats) {
-        SweepArgs a = sweep_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kSweepStats);
+        ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreStats);
         a.qn = at<float>(ws, L.qn);
         a.part = at<float>(ws, L.part);
         TimedLaunch tl(FWPKM_K_SWEEP_STATS, s);
-        HIP_TRY(launch_sweep(a, p.store, s));
+        HIP_TRY(launch_score(a, p.store, s));
     }
-    PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, (Tc + kTileT - 1) / kTileT, Tc};
+    PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, (Tc + kScoreTok - 1) / kScoreTok, Tc};
     {
         TimedLaunch tl(FWPKM_K_PBAR, s);
         HIP_TRY(launch_pbar(pa, s));
     }
-    SweepArgs ra = sweep_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kSweepRowStat);
+    ScoreArgs ra = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreRowStat);
     ra.lp = at<float>(ws, L.lp);
     ra.Z = at<float>(ws, L.Z);
     ra.m = at<float>(ws, L.m);
     {
         TimedLaunch tl(FWPKM_K_SWEEP_ROWSTAT, s);
-        HIP_TRY(launch_sweep(ra, p.store, s));
+        HIP_TRY(launch_score(ra, p.store, s));
     }
     KgradArgs ka{};
     ka.q = q; ka.q_bstride = q_bstride; ka.K1 = K1; ka.K2 = K2; ka.knorm = knorm;
@@ -373,18 +402,14 @@ int fwpkm_retrieve(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, co
     rc = check_ws(ws, ws_bytes, L.total);
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float* knorm = at<float>(ws, L.knorm);
-    HIP_TRY(knorm_launch(p, B, K1, K2, knorm, s));
+    HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     int32_t* ii = idx ? idx : at<int32_t>(ws, L.idx);
     float* ww = w ? w : at<float>(ws, L.w);
-    SweepArgs a = sweep_args(p, B, T, q, static_cast<int64_t>(T) * p.H * p.dq, K1, K2, knorm, kSweepSelect);
-    a.idx = ii; a.w = ww; a.iw_bstride = static_cast<int64_t>(T) * p.H * p.k;
-    {
-        TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
-        HIP_TRY(launch_sweep(a, p.store, s));
-    }
+    const int64_t iwb = static_cast<int64_t>(T) * p.H * p.k;
+    rc = select_topk(p, L, ws, B, T, q, static_cast<int64_t>(T) * p.H * p.dq, K1, K2, ii, ww, iwb, false, s);
+    if (rc) return rc;
     GatherArgs ga{};
-    ga.V = V; ga.idx = ii; ga.w = ww; ga.iw_bstride = a.iw_bstride;
+    ga.V = V; ga.idx = ii; ga.w = ww; ga.iw_bstride = iwb;
     ga.v = v; ga.v_bstride = static_cast<int64_t>(T) * p.dv;
     ga.g = g; ga.g_bstride = T;
     ga.o = o; ga.vhat = vhat; ga.o_bstride = static_cast<int64_t>(T) * p.dv;
@@ -445,8 +470,7 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
     rc = check_ws(ws, ws_bytes, L.total);
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float* knorm = at<float>(ws, L.knorm);
-    HIP_TRY(knorm_launch(p, B, K1, K2, knorm, s));
+    HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     const int64_t qb = static_cast<int64_t>(T) * p.H * p.dq;
     const int64_t vbs = static_cast<int64_t>(T) * p.dv;
     const int nchunks = (T + p.C - 1) / p.C;
@@ -461,14 +485,8 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             const unsigned char* vc = static_cast<const unsigned char*>(v) + static_cast<size_t>(t0) * p.dv * p.es;
             const int64_t iwb = static_cast<int64_t>(Tc) * p.H * p.k;
             // retrieval with the state left by the previous chunk
-            SweepArgs a = sweep_args(p, B, Tc, qc, qb, K1, K2, knorm, kSweepSelect | (p.addr ? kSweepStats : 0));
-            a.idx = idx; a.w = w; a.iw_bstride = iwb;
-            a.qn = at<float>(ws, L.qn);
-            a.part = at<float>(ws, L.part);
-            {
-                TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
-                HIP_TRY(launch_sweep(a, p.store, s));
-            }
+            rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, idx, w, iwb, p.addr, s);
+            if (rc) return rc;
             // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
             int n_tgt;
             const void* tgt;

@@ -24,12 +24,17 @@ template <> struct Store<kBF16> {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) float f2_t;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf2_t;
+    const f2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2_t));
 }
 
 template <int STORE> __device__ __forceinline__ float ld_elem(const void* p, size_t i);
@@ -115,7 +120,6 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t lin, uint32_t total) {
 // kernel argument blocks
 // ---------------------------------------------------------------------------
 constexpr int kMaxCand = 256;   // product candidates per (token, head)
-constexpr int kTileT = 16;      // tokens per sweep workgroup
 constexpr int kMaxKHalf = 64;
 constexpr int kMaxK = 64;
 
@@ -125,31 +129,50 @@ struct CandTable {
     uint16_t ab[kMaxCand];
 };
 
-enum SweepMode : int {
-    kSweepSelect = 1,   // per-half top-k', product top-k, weights -> idx, w
-    kSweepStats = 2,    // per-tile partial sums of p over tokens -> part
-    kSweepRowStat = 4,  // Z_t and m_t = sum_i p_ti log pbar_i -> Z, m
+enum ScoreMode : int {
+    kScoreSelect = 1,   // candidate lists of the per-half top-k' -> cand, cnt
+    kScoreStats = 2,    // per-64-token partial sums of p over tokens -> part
+    kScoreRowStat = 4,  // Z_t and m_t = sum_i p_ti log pbar_i -> Z, m
 };
+constexpr int kScoreTok = 64;   // tokens per scoring workgroup
 
-struct SweepArgs {
+struct ScoreArgs {
     const void* q;        // token t of sequence b at q + b*q_bstride + t*H*d_q
     int64_t q_bstride;
     const void* K1;       // [B][H][n][dh]
     const void* K2;
     const float* knorm;   // [B][H][2][n]
-    int B, Tc, n, H, dh, kh, k, ncand;
+    int B, Tc, n, H, dh, kh;
     float eps;
     int mode;
-    int32_t* idx;         // [b*iw_bstride + (t*H + h)*k + j]
-    float* w;
-    int64_t iw_bstride;
+    uint64_t* cand;       // [B][H][2][Tc][cap]  (e bits << 32 | sub-key)
+    int32_t* cnt;         // [B][H][2][Tc]       candidates found (may exceed cap)
+    int cap;
     float* qn;            // [B][H][2][Tc]  ||q_half||^2
-    float* part;          // [B][H][2][ntiles][n]
+    float* part;          // [B][H][2][ceil(Tc/64)][n]
     const float* lp;      // [B][H][2][n]   log pbar
     float* Z;             // [B][H][2][Tc]
     float* m;             // [B][H][2][Tc]
-    CandTable cand;
 };
+
+struct SelectArgs {
+    const uint64_t* cand;
+    const int32_t* cnt;
+    int cap;
+    const void* q;        // for the exact recompute of an overflowed list
+    int64_t q_bstride;
+    const void* K1;
+    const void* K2;
+    int B, Tc, n, H, dh, kh, k, ncand;
+    float eps;
+    int32_t* idx;         // [b*iw_bstride + (t*H + h)*k + j]
+    float* w;
+    int64_t iw_bstride;
+    CandTable cand_ab;
+};
+
+int score_keep(int kh);   // smallest e kept per lane in the first scoring pass
+int score_cap(int kh);    // candidate list capacity per (token, head, half)
 
 struct GatherArgs {
     const void* V;        // [B][N][dv]
@@ -191,7 +214,7 @@ struct SortArgs {
     const uint32_t* vin;
     uint32_t* kout;
     uint32_t* vout;
-    uint32_t* counts;     // [B][256][tiles]
+    uint32_t* counts;     // [B][tiles][256]
     int B, M;             // entries per sequence
     int tiles;
     int shift;
@@ -247,7 +270,8 @@ struct KnormArgs {
 // launchers (each returns hipGetLastError() after enqueueing)
 // ---------------------------------------------------------------------------
 hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s);
-hipError_t launch_sweep(const SweepArgs& a, int store, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int store, hipStream_t s);
 hipError_t launch_resid(const ResidArgs& a, int store, hipStream_t s);
 hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s);

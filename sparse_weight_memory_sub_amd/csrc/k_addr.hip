@@ -105,8 +105,7 @@ __global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
     Frag<STORE> Bk[DHS];
     float kn = 0.f, lpv = 0.f;
     if (active) {
-#pragma unroll
-        for (int s = 0; s < DHS; ++s) frag_load<STORE>(Bk[s], Kb + (static_cast<size_t>(key) * dh + 32 * s + 8 * g) * ES);
+        load_row_frags<STORE, DHS>(Bk, Kb + static_cast<size_t>(key) * dh * ES, g);
         kn = a.knorm[static_cast<size_t>(bhh) * n + key];
         lpv = a.lp[static_cast<size_t>(bhh) * n + key];
     }
@@ -117,7 +116,12 @@ __global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
     float colsum = 0.f;
     const float inv_tc2 = 2.f / static_cast<float>(a.Tc);
 
-    for (int tb = 0; tb < a.Tc; tb += 32) {
+    // key blocks of one (sequence, head, half) run side by side and read the
+    // same query rows: start each at a different token block (fixed order per
+    // block, so the sums stay reproducible)
+    const int nblk = (a.Tc + 31) / 32;
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int tb = ((bi + kb) % nblk) * 32;
         __syncthreads();
         // stage the query halves of tokens tb .. tb+31 (zeros past Tc)
         const int chunks = dh / 8;  // 8-element pieces per row
@@ -147,7 +151,9 @@ __global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
             const int which = threadIdx.x / 32, row = threadIdx.x % 32;
             const int t = tb + row;
             const float* src = which == 0 ? a.qn : (which == 1 ? a.Z : a.m);
-            tq[which * 32 + row] = (t < a.Tc) ? src[static_cast<size_t>(bhh) * a.Tc + t] : 1.f;
+            float x = (t < a.Tc) ? src[static_cast<size_t>(bhh) * a.Tc + t] : 1.f;
+            if (which == 1) x = __builtin_amdgcn_rcpf(x);  // stored as 1/Z
+            tq[which * 32 + row] = x;
         }
         __syncthreads();
         if (!active) continue;
@@ -155,24 +161,34 @@ __global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
         float av[8];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
+            Frag<STORE> A[DHS];
+            load_row_frags<STORE, DHS>(A, qs + static_cast<size_t>(sub * 16 + r) * qstride * ES, g);
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < DHS; ++s) {
-                Frag<STORE> A;
-                frag_load<STORE>(A, qs + (static_cast<size_t>(sub * 16 + r) * qstride + 32 * s + 8 * g) * ES);
-                mma(A, Bk[s], acc);
-            }
+            for (int s = 0; s < DHS; ++s) mma(A[s], Bk[s], acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = sub * 16 + 4 * g + i;
                 const float d = tq[row] + kn - 2.f * acc[i];
-                const float e = a.eps + fmaxf(d, 0.f);
-                const float val = (tb + row < a.Tc) ? inv_tc2 * (lpv - tq[64 + row]) / (tq[32 + row] * e * e) : 0.f;
+                const float ie = __builtin_amdgcn_rcpf(a.eps + fmaxf(d, 0.f));
+                const float val = (tb + row < a.Tc) ? inv_tc2 * (lpv - tq[64 + row]) * tq[32 + row] * ie * ie : 0.f;
                 av[sub * 4 + i] = val;
                 colsum += val;
             }
         }
         // sum_t a_ti q_t: keys x tokens (A) times tokens x d_h (B)
+        Frag<kBF16> Ahi, Alo;
+        if constexpr (STORE == kBF16) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hi[j] = pack_bf16x2(av[2 * j], av[2 * j + 1]);
+                lo[j] = pack_bf16x2(av[2 * j] - __uint_as_float(hi[j] << 16),
+                                    av[2 * j + 1] - __uint_as_float(hi[j] & 0xffff0000u));
+            }
+            Ahi.v = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+            Alo.v = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+        }
 #pragma unroll
         for (int c = 0; c < NCT; ++c) {
             const int col = c * 16 + r;
@@ -181,16 +197,8 @@ __global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
                 uint32_t bq[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) bq[j] = qb[tok_of(g, j) * qstride + col];
-                Frag<kBF16> B, Ahi, Alo;
+                Frag<kBF16> B;
                 B.v = u32x4_t{bq[0] | (bq[1] << 16), bq[2] | (bq[3] << 16), bq[4] | (bq[5] << 16), bq[6] | (bq[7] << 16)};
-                uint32_t hi[8], lo[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    hi[j] = bf16_bits(av[j]);
-                    lo[j] = bf16_bits(av[j] - bf16_to_f32(hi[j]));
-                }
-                Ahi.v = u32x4_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-                Alo.v = u32x4_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
                 mma(Ahi, B, gacc[c]);
                 mma(Alo, B, gacc[c]);
             } else {

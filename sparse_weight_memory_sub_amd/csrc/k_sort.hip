@@ -39,17 +39,17 @@ __global__ __launch_bounds__(256) void k_sort_count(SortArgs a) {
         if (pos < a.M) atomicAdd(&hist[(load_key(a, b, pos) >> a.shift) & 255u], 1u);
     }
     __syncthreads();
-    a.counts[(static_cast<size_t>(b) * 256 + threadIdx.x) * a.tiles + tile] = hist[threadIdx.x];
+    a.counts[(static_cast<size_t>(b) * a.tiles + tile) * 256 + threadIdx.x] = hist[threadIdx.x];
 }
 
-// Exclusive prefix of counts[b][digit][tile] in (digit, tile) order.
+// Exclusive prefix of counts[b][tile][digit] taken in (digit, tile) order.
 __global__ __launch_bounds__(256) void k_sort_scan(SortArgs a) {
     __shared__ uint32_t wsum[4];
     const int b = blockIdx.x, d = threadIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    uint32_t* row = a.counts + (static_cast<size_t>(b) * 256 + d) * a.tiles;
+    uint32_t* col = a.counts + static_cast<size_t>(b) * a.tiles * 256 + d;
     uint32_t s = 0u;
-    for (int t = 0; t < a.tiles; ++t) s += row[t];
+    for (int t = 0; t < a.tiles; ++t) s += col[static_cast<size_t>(t) * 256];
     const uint32_t incl = wave_incl_scan_u32(s);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void k_sort_scan(SortArgs a) {
     for (int w = 0; w < wave; ++w) off += wsum[w];
     uint32_t run = off + incl - s;
     for (int t = 0; t < a.tiles; ++t) {
-        const uint32_t c = row[t];
-        row[t] = run;
+        const uint32_t c = col[static_cast<size_t>(t) * 256];
+        col[static_cast<size_t>(t) * 256] = run;
         run += c;
     }
 }
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int w = 0; w < 4; ++w) cnt[w][threadIdx.x] = 0u;
-    toff[threadIdx.x] = a.counts[(static_cast<size_t>(b) * 256 + threadIdx.x) * a.tiles + tile];
+    toff[threadIdx.x] = a.counts[(static_cast<size_t>(b) * a.tiles + tile) * 256 + threadIdx.x];
     __syncthreads();
 
     constexpr int kPerWave = kSortTile / 4;

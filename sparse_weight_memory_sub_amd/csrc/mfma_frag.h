@@ -2,10 +2,14 @@
 // operands on gfx950.
 //
 // Lane l of a wavefront owns row/column (l % 16) of a 16-wide operand tile
-// and k-group g = l / 16.  Within a 32-wide k-block s, lane group g holds the
-// 8 consecutive k-elements 32*s + 8*g + j (j = 0..7) of its row.  A and B
-// use the same (g, j) -> k map, so the products pair up whatever order the
-// instruction sums them in.  The 16x16 fp32 result is spread as
+// and k-group g = l / 16.  A k-block is 32 wide; each lane holds 8 of its
+// k-elements.  For an operand row of d elements (d/32 k-blocks) the blocks
+// are taken in pairs: lane group g reads the 16 consecutive elements
+// [64*s2 + 16*g, +16) of its row with one 32-byte (bf16) load, the first 8
+// for block 2*s2 and the last 8 for block 2*s2 + 1, so the four groups of a
+// row cover a whole 128-byte line.  (A single block, d = 32, uses
+// [8*g, +8).)  A and B use the same map, so the products pair up whatever
+// order the instruction sums them in.  The 16x16 fp32 result is spread as
 // acc[i] = C[row 4*(l/16) + i][column l % 16].
 #pragma once
 
@@ -45,6 +49,23 @@ template <> __device__ __forceinline__ void frag_load<kF32>(Frag<kF32>& f, const
     float4 a = s[0], b = s[1];
     f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// All DHS fragments of one operand row (d = 32*DHS storage elements starting
+// at `row`, 16-byte aligned) for lane group g, in the k-block map above.
+template <int STORE, int DHS>
+__device__ __forceinline__ void load_row_frags(Frag<STORE> (&f)[DHS], const unsigned char* row, int g) {
+    constexpr int ES = Store<STORE>::kBytes;
+    if constexpr (DHS == 1) {
+        frag_load<STORE>(f[0], row + 8 * g * ES);
+    } else {
+#pragma unroll
+        for (int s2 = 0; s2 < DHS / 2; ++s2) {
+            const unsigned char* p = row + (64 * s2 + 16 * g) * ES;
+            frag_load<STORE>(f[2 * s2], p);
+            frag_load<STORE>(f[2 * s2 + 1], p + 8 * ES);
+        }
+    }
 }
 
 // Sum of squares of the fragment's elements (fp32).

@@ -27,8 +27,8 @@ EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
            "fwpkm_timing_enable", "fwpkm_timing_read")
 
 # kernel families of fwpkm_timing_read, in fwpkm_kernel order
-KERNELS = ("knorm", "sweep_select", "gather", "resid", "sort", "scatter", "pbar",
-           "sweep_stats", "sweep_rowstat", "kgrad", "fill")
+KERNELS = ("knorm", "score_select", "gather", "resid", "sort", "scatter", "pbar",
+           "score_stats", "score_rowstat", "kgrad", "fill", "select")
 
 
 class FwpkmError(RuntimeError):
