@@ -182,6 +182,11 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
  * Outputs: o[B][T][d_v] float (required), vhat[B][T][d_v] float
  *          (nullable), both from the last pass.
  * passes >= 1.
+ * Streams: the key path of each chunk is enqueued on `stream`, its value
+ * path (gather, sort, value write) on a second stream the library creates
+ * once per host thread and device (default priority); events fork it from
+ * and join it back to `stream`, so when `stream` reaches the end of this
+ * call everything is done.
  */
 int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                       const void* q, const void* v, const float* g, const void* v_next,

@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -110,6 +111,32 @@ class TimedLaunch {
     hipEvent_t start_ = nullptr, stop_ = nullptr;
 };
 
+// Second stream and fork/join events of fwpkm_forward_seq, one set per
+// (host thread, device), created on first use and never released.
+struct Aux {
+    hipStream_t sv = nullptr;
+    hipEvent_t ev_start = nullptr, ev_sel = nullptr, ev_end = nullptr;
+    hipEvent_t ev_write[2] = {nullptr, nullptr};
+};
+
+hipError_t aux_streams(Aux** out) {
+    thread_local std::vector<Aux*> per_dev;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1, nullptr);
+    if (!per_dev[dev]) {
+        Aux* a = new Aux();
+        if ((e = hipStreamCreateWithFlags(&a->sv, hipStreamNonBlocking)) != hipSuccess) return e;
+        hipEvent_t* evs[5] = {&a->ev_start, &a->ev_sel, &a->ev_end, &a->ev_write[0], &a->ev_write[1]};
+        for (hipEvent_t* ev : evs)
+            if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+        per_dev[dev] = a;
+    }
+    *out = per_dev[dev];
+    return hipSuccess;
+}
+
 struct Plan {
     int n, H, dq, dh, dv, kh, k, C, store, es;
     int64_t N;
@@ -174,11 +201,12 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, knorm, qn, cand, cnt, r, Z, m, part, lp, k0, v0, k1, v1, counts, ph, pt, pts, phe;
+    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, r, Z, m, part, lp, k0, v0, k1, v1, counts, ph, pt, pts, phe;
     size_t total;
 };
 
-Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update) {
+// iw_copies = 2 double-buffers the slot/weight lists across chunks (forward_seq).
+Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int iw_copies = 1) {
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -193,6 +221,10 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update) {
     if (with_iw) {
         L.idx = take(Bs * T * p.H * p.k * 4);
         L.w = take(Bs * T * p.H * p.k * 4);
+        if (iw_copies > 1) {
+            L.idx2 = take(Bs * T * p.H * p.k * 4);
+            L.w2 = take(Bs * T * p.H * p.k * 4);
+        }
         L.cand = take(Bs * p.H * 2 * T * static_cast<size_t>(score_cap(p.kh)) * 8);
         L.cnt = take(Bs * p.H * 2 * T * 4);
     }
@@ -221,7 +253,7 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update) {
 
 size_t need_retrieve(const Plan& p, int B, int T) { return layout(p, B, T, true, false).total; }
 size_t need_update(const Plan& p, int B, int T) { return layout(p, B, T, false, true).total; }
-size_t need_forward(const Plan& p, int B, int T) { return layout(p, B, std::min(T, p.C), true, true).total; }
+size_t need_forward(const Plan& p, int B, int T) { return layout(p, B, std::min(T, p.C), true, true, 2).total; }
 
 template <class T>
 T* at(void* ws, size_t off) {
@@ -466,27 +498,49 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
     if (!q || !v || !g || !K1 || !K2 || !V || !o) return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V and o are required");
     const int Cm = std::min(T, p.C);
     if (static_cast<int64_t>(B) * Cm * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*C*heads*k too large");
-    const Layout L = layout(p, B, Cm, true, true);
+    const Layout L = layout(p, B, Cm, true, true, 2);
     rc = check_ws(ws, ws_bytes, L.total);
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // The key path (scoring, selection, usage statistics, key step) stays on
+    // the caller's stream; the value path (gather, sort, value write) of the
+    // same chunk runs on a second stream of the library.  They meet at the
+    // selection of each chunk, and the slot/weight lists alternate between
+    // two buffers so chunk c+1's selection only waits for chunk c-1's write.
+    // FWPKM_SINGLE_STREAM=1 keeps both paths on `stream` (same work, one queue).
+    Aux* ax = nullptr;
+    HIP_TRY(aux_streams(&ax));
+    static const bool single = [] {
+        const char* e = std::getenv("FWPKM_SINGLE_STREAM");
+        return e && e[0] == '1';
+    }();
+    hipStream_t sv = single ? s : ax->sv;
+    HIP_TRY(hipEventRecord(ax->ev_start, s));
+    HIP_TRY(hipStreamWaitEvent(sv, ax->ev_start, 0));
     HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     const int64_t qb = static_cast<int64_t>(T) * p.H * p.dq;
     const int64_t vbs = static_cast<int64_t>(T) * p.dv;
     const int nchunks = (T + p.C - 1) / p.C;
-    int32_t* idx = at<int32_t>(ws, L.idx);
-    float* w = at<float>(ws, L.w);
+    int32_t* idxs[2] = {at<int32_t>(ws, L.idx), at<int32_t>(ws, L.idx2)};
+    float* ws_w[2] = {at<float>(ws, L.w), at<float>(ws, L.w2)};
+    int64_t step = 0;
     for (int pass = 0; pass < passes; ++pass) {
         const bool last_pass = pass == passes - 1;
-        for (int c = 0; c < nchunks; ++c) {
+        for (int c = 0; c < nchunks; ++c, ++step) {
             const int t0 = c * p.C;
             const int Tc = std::min(p.C, T - t0);
             const unsigned char* qc = static_cast<const unsigned char*>(q) + static_cast<size_t>(t0) * p.H * p.dq * p.es;
             const unsigned char* vc = static_cast<const unsigned char*>(v) + static_cast<size_t>(t0) * p.dv * p.es;
             const int64_t iwb = static_cast<int64_t>(Tc) * p.H * p.k;
+            const int buf = static_cast<int>(step & 1);
+            int32_t* idx = idxs[buf];
+            float* w = ws_w[buf];
+            // this buffer was last read by the value write two chunks ago
+            if (step >= 2) HIP_TRY(hipStreamWaitEvent(s, ax->ev_write[buf], 0));
             // retrieval with the state left by the previous chunk
             rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, idx, w, iwb, p.addr, s);
             if (rc) return rc;
+            HIP_TRY(hipEventRecord(ax->ev_sel, s));
             // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
             int n_tgt;
             const void* tgt;
@@ -506,6 +560,8 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
                     n_tgt = Tc - 1;
                 }
             }
+            // value path of this chunk
+            HIP_TRY(hipStreamWaitEvent(sv, ax->ev_sel, 0));
             GatherArgs ga{};
             ga.V = V; ga.idx = idx; ga.w = w; ga.iw_bstride = iwb;
             ga.v = vc; ga.v_bstride = vbs;
@@ -519,18 +575,22 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             ga.B = B; ga.Tc = Tc; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
             ga.znorm = p.znorm; ga.znorm_eps = p.zeps;
             {
-                TimedLaunch tl(FWPKM_K_GATHER, s);
-                HIP_TRY(launch_gather(ga, p.store, s));
+                TimedLaunch tl(FWPKM_K_GATHER, sv);
+                HIP_TRY(launch_gather(ga, p.store, sv));
             }
-            // write
-            rc = memorise(p, L, ws, B, Tc, n_tgt, idx, w, iwb, V, nullptr, s);
+            rc = memorise(p, L, ws, B, Tc, n_tgt, idx, w, iwb, V, nullptr, sv);
             if (rc) return rc;
+            HIP_TRY(hipEventRecord(ax->ev_write[buf], sv));
+            // key path: addressing step of this chunk
             if (p.addr) {
                 rc = address(p, L, ws, B, Tc, qc, qb, K1, K2, true, s);
                 if (rc) return rc;
             }
         }
     }
+    // join: the caller's stream sees every write
+    HIP_TRY(hipEventRecord(ax->ev_end, sv));
+    HIP_TRY(hipStreamWaitEvent(s, ax->ev_end, 0));
     return ok();
 }
 
