@@ -300,7 +300,10 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     a.cand = at<uint64_t>(ws, L.cand);
     a.cnt = at<int32_t>(ws, L.cnt);
     a.qn = at<float>(ws, L.qn);
-    if (stats) a.part = at<float>(ws, L.part);
+    if (stats) {
+        a.part = at<float>(ws, L.part);
+        a.Z = at<float>(ws, L.Z);
+    }
     {
         TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
         HIP_TRY(launch_score(a, p.store, s));
@@ -371,6 +374,7 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
         ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreStats);
         a.qn = at<float>(ws, L.qn);
         a.part = at<float>(ws, L.part);
+        a.Z = at<float>(ws, L.Z);
         TimedLaunch tl(FWPKM_K_SWEEP_STATS, s);
         HIP_TRY(launch_score(a, p.store, s));
     }

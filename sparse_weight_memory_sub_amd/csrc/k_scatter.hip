@@ -59,6 +59,50 @@ __device__ __forceinline__ void ld_row(const void* base, size_t off, float (&x)[
     }
 }
 
+// A row piece in its storage form, so a load can be issued early and unpacked
+// only where it is used (after other loads have been waited for).
+template <int STORE, int EPL>
+struct RawRow {
+    static constexpr int kWords = (STORE == kF32) ? EPL : (EPL + 1) / 2;
+    uint32_t w[kWords];
+};
+
+template <int STORE, int EPL>
+__device__ __forceinline__ void ld_raw(const void* base, size_t off, RawRow<STORE, EPL>& x) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const unsigned char*>(base) +
+                                                           off * Store<STORE>::kBytes);
+    if constexpr (RawRow<STORE, EPL>::kWords % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < RawRow<STORE, EPL>::kWords; i += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p + i);
+            x.w[i] = v.x; x.w[i + 1] = v.y; x.w[i + 2] = v.z; x.w[i + 3] = v.w;
+        }
+    } else if constexpr (RawRow<STORE, EPL>::kWords == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        x.w[0] = v.x; x.w[1] = v.y;
+    } else if constexpr (STORE == kF32 || EPL == 2) {
+        x.w[0] = p[0];
+    } else {
+        x.w[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+}
+
+template <int STORE, int EPL>
+__device__ __forceinline__ void unpack(const RawRow<STORE, EPL>& x, float (&v)[EPL]) {
+    if constexpr (STORE == kF32) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) v[i] = __uint_as_float(x.w[i]);
+    } else if constexpr (EPL == 1) {
+        v[0] = __uint_as_float(x.w[0] << 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL / 2; ++i) {
+            v[2 * i] = __uint_as_float(x.w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(x.w[i] & 0xffff0000u);
+        }
+    }
+}
+
 template <int STORE, int EPL>
 __device__ __forceinline__ void st_row(void* base, size_t off, const float (&x)[EPL]) {
     if constexpr (STORE == kF32) {
@@ -119,18 +163,29 @@ __device__ __forceinline__ void st_f32(float* p, const float (&x)[EPL]) {
     }
 }
 
-// V_slot <- V_slot - lr * acc / count, one row, lanes across d_v.
+__device__ __forceinline__ size_t row_off(const ScatterArgs& a, int b, uint32_t slot, int epl) {
+    return (static_cast<size_t>(b) * a.N + slot) * a.dv + static_cast<size_t>(lane_id()) * epl;
+}
+
+// V_slot <- V_slot - lr * acc / count from the row's old value v (loaded by
+// the caller), one row, lanes across d_v.
+template <int STORE, int EPL>
+__device__ __forceinline__ void finish_row(const ScatterArgs& a, int b, uint32_t slot, int count, float (&v)[EPL],
+                                           const float (&acc)[EPL]) {
+    // one division per row; the elements take a multiply-add
+    const float sc = a.lr / static_cast<float>(count);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = fmaf(-sc, acc[i], v[i]);
+    st_row<STORE, EPL>(a.V, row_off(a, b, slot, EPL), v);
+    if (a.n_read && lane_id() == 0) a.n_read[static_cast<size_t>(b) * a.N + slot] = count;
+}
+
 template <int STORE, int EPL>
 __device__ __forceinline__ void apply_row(const ScatterArgs& a, int b, uint32_t slot, int count,
                                           const float (&acc)[EPL]) {
-    const size_t off = (static_cast<size_t>(b) * a.N + slot) * a.dv + static_cast<size_t>(lane_id()) * EPL;
     float v[EPL];
-    ld_row<STORE, EPL>(a.V, off, v);
-    const float c = static_cast<float>(count);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = v[i] - a.lr * acc[i] / c;
-    st_row<STORE, EPL>(a.V, off, v);
-    if (a.n_read && lane_id() == 0) a.n_read[static_cast<size_t>(b) * a.N + slot] = count;
+    ld_row<STORE, EPL>(a.V, row_off(a, b, slot, EPL), v);
+    finish_row<STORE, EPL>(a, b, slot, count, v, acc);
 }
 
 template <int STORE, int EPL>
@@ -172,6 +227,12 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
         const int e = ends_here ? (__ffsll(static_cast<unsigned long long>(tm)) - 1) : nvalid - 1;
         const bool starts_here = (hb >> s) & 1ull;
         const uint32_t slot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), s));
+        // a run wholly inside the piece: fetch its row now, so the load overlaps
+        // the residual reads below
+        // (row 0 stands in for the others; it is read, never written, for them)
+        const bool whole = starts_here && ends_here && slot < a.N;
+        RawRow<STORE, EPL> vraw;
+        ld_raw<STORE, EPL>(a.V, row_off(a, b, whole ? slot : 0u, EPL), vraw);
         float acc[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
@@ -199,7 +260,11 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
             for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, x[i], acc[i]);
         }
         if (starts_here && ends_here) {
-            if (slot < a.N) apply_row<STORE, EPL>(a, b, slot, e - s + 1, acc);
+            if (whole) {
+                float vrow[EPL];
+                unpack<STORE, EPL>(vraw, vrow);
+                finish_row<STORE, EPL>(a, b, slot, e - s + 1, vrow, acc);
+            }
         } else if (!starts_here) {
             // run entering from the previous piece (it starts at lane 0)
             st_f32<EPL>(a.ph + pidx * a.dv + static_cast<size_t>(lane) * EPL, acc);

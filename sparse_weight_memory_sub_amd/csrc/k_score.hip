@@ -8,21 +8,26 @@
 // paperlayer.ai 3.4) use p_ti = (1/e_ti) / Z_t, e = eps + d, Z_t = sum_i 1/e_ti.
 //
 // k_score streams the codebook through LDS like a GEMM: a workgroup owns 64
-// tokens of one (sequence, head) -- 16 per wavefront, the MFMA rows -- and
-// walks the sub-keys in blocks of kKB, double-buffered, so every sub-key row
-// is read from L2 once per 64 tokens.  Nothing of the distance matrix is
-// stored; each mode reduces it in registers:
+// tokens of one (sequence, head, half) -- 16 per wavefront, the MFMA rows --
+// and walks the sub-keys in blocks of kKB, double-buffered and copied by
+// direct global-to-LDS loads, so every sub-key row is read from L2 once per
+// 64 tokens.  The accumulators start at ||q||^2 + ||K_i||^2 + eps and the
+// query is scaled by -2, so the MFMAs leave e = eps + d directly.  Nothing
+// of the distance matrix is stored; each mode (a template argument) reduces
+// it in registers:
 //
-//  kScoreSelect   pass 1: Z_t, and for each lane the MK smallest e of the
-//                 sub-keys it sees; tau_t = k'-th smallest of those 16*MK
-//                 values is an upper bound of the k'-th smallest e of the row
-//                 (at least k' values are <= tau_t).  Pass 2 recomputes the
-//                 tile and appends every (e, sub-key) with e <= tau_t to the
-//                 token's candidate list in the workspace; k_select then
-//                 sorts the few candidates.
-//  kScoreStats    pass 2 also forms the per-64-token partial sums over tokens
-//                 of p_ti, the pieces of the chunk's marginal usage pbar.
-//  kScoreRowStat  one pass: Z_t and m_t = sum_i p_ti log pbar_i.
+//  kScoreSelect   pass 1: for each lane the MK smallest e of the sub-keys it
+//                 sees; tau_t = k'-th smallest of those 16*MK values is an
+//                 upper bound of the k'-th smallest e of the row (at least
+//                 k' values are <= tau_t).  Pass 2 recomputes the tile and
+//                 appends every (e, sub-key) with e <= tau_t to the token's
+//                 candidate list in the workspace (positions from an LDS
+//                 counter, so the list order varies; k_select sorts it).
+//  kScoreStats    pass 1 also sums Z_t = sum_i 1/e_ti (written out); pass 2
+//                 forms the per-64-token partial sums over tokens of p_ti,
+//                 the pieces of the chunk's marginal usage pbar.
+//  kScoreRowStat  one pass: m_t = sum_i p_ti log pbar_i, with Z_t from the
+//                 stats pass of the same chunk.
 //
 // k_select: one wavefront per (token, head): sorts each half's candidates
 // by (e, sub-key) for the top-k' (ties to the lower sub-key index), then the
@@ -93,195 +98,282 @@ __device__ __forceinline__ void bitonic_sort(K (&x)[R]) {
 // ---------------------------------------------------------------------------
 // k_score
 // ---------------------------------------------------------------------------
-template <int STORE, int DHS, int MK>
-__global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
-    constexpr int ES = Store<STORE>::kBytes;
-    constexpr int PADK = 16 / ES;  // LDS row padding (elements): 16 bytes
-    constexpr int KB = kKB<STORE>;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int n = a.n, H = a.H, dh = a.dh;
-    const int kstride = dh + PADK;
-    unsigned char* kbuf = smem;                                                  // [2][KB][kstride]
-    float* colbuf = reinterpret_cast<float*>(kbuf + 2 * KB * kstride * ES);     // [2][4][KB]
-    float* lps = colbuf + 2 * 4 * KB;                                            // [n] (rowstat)
 
-    const int ntiles = (a.Tc + kTok - 1) / kTok;
+// LDS image of a block of KB sub-key rows, in 16-byte chunks: chunk c of
+// block row R sits at position R*CPR + (c ^ (R & M)), M = min(CPR, 8) - 1.
+// The swizzle moves only the low three chunk bits, so the eight rows of a
+// fragment read that share a bank group land on distinct banks while the
+// fragment offsets stay a per-lane base plus constants.
+template <int CPR>
+__host__ __device__ constexpr int swz_mask() {
+    return (CPR < 8 ? CPR : 8) - 1;
+}
+
+// Per-lane byte offsets of the fragments of block row r (0..15) for lane
+// group g: fragment s of tile ct is at base[s & 1] (bf16) or base[2*(s & 1)
+// + j] (the two halves of an fp32 fragment) plus frag_imm(ct, s).
+template <int STORE, int DHS>
+struct FragBase {
+    static constexpr int CPR = 32 * DHS * Store<STORE>::kBytes / 16;
+    static constexpr int NB = (STORE == kBF16) ? 2 : 4;
+    uint32_t base[NB];
+    __device__ __forceinline__ FragBase(int r, int g) {
+        const int f = r & swz_mask<CPR>();
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            // chunk within the row for s = 0 / 1 (and half j of an fp32 fragment)
+            int c;
+            if constexpr (STORE == kBF16) c = (DHS == 1) ? g : 2 * g + q;
+            else c = (DHS == 1) ? 2 * g + (q & 1) : 4 * g + q;
+            base[q] = static_cast<uint32_t>(r * CPR + (c ^ f)) * 16u;
+        }
+    }
+    // the part of a fragment's offset that does not depend on the lane
+    static __device__ __forceinline__ constexpr uint32_t imm(int ct, int s) {
+        if constexpr (STORE == kBF16) return static_cast<uint32_t>(ct * 16 * CPR + (DHS == 1 ? 0 : 8 * (s >> 1))) * 16u;
+        else return static_cast<uint32_t>(ct * 16 * CPR + (DHS == 1 ? 0 : 16 * (s >> 1))) * 16u;
+    }
+};
+
+// Fragment s of tile ct (block rows ct*16 .. +15) from the LDS image at kb.
+template <int STORE, int DHS>
+__device__ __forceinline__ void lds_frag(Frag<STORE>& f, const unsigned char* kb, const FragBase<STORE, DHS>& fb,
+                                         int ct, int s) {
+    const uint32_t im = FragBase<STORE, DHS>::imm(ct, s);
+    if constexpr (STORE == kBF16) {
+        f.v = *reinterpret_cast<const u32x4_t*>(kb + fb.base[(DHS == 1) ? 0 : (s & 1)] + im);
+    } else {
+        const int q = (DHS == 1) ? 0 : 2 * (s & 1);
+        const float4 x = *reinterpret_cast<const float4*>(kb + fb.base[q] + im);
+        const float4 y = *reinterpret_cast<const float4*>(kb + fb.base[q + 1] + im);
+        f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
+        f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
+    }
+}
+
+// Copies sub-key rows [row0, row0 + KB) of one codebook (rows >= n are
+// skipped) into the swizzled LDS image at dst with direct global-to-LDS
+// loads: each wavefront instruction fills 64 consecutive chunk positions,
+// lane L position 64*j + L, from whatever global chunk belongs there.
+template <int STORE, int DHS, int KB>
+__device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned char* Kg, int row0, int n, int wave,
+                                          int lane) {
+    constexpr int CPR = 32 * DHS * Store<STORE>::kBytes / 16;
+    constexpr int M = swz_mask<CPR>();
+    constexpr int NINST = KB * CPR / 64;
+    const unsigned char* src = Kg + static_cast<size_t>(row0) * CPR * 16;
+    const bool full = row0 + KB <= n;
+#pragma unroll
+    for (int j = 0; j < NINST; j += 4) {
+        const int jj = j + wave;
+        if (NINST % 4 == 0 || jj < NINST) {
+            const int p = 64 * jj + lane;
+            const int R = p / CPR, cs = p % CPR;
+            const uint32_t off = static_cast<uint32_t>(R * CPR + (cs ^ (R & M))) * 16u;
+            if (full || row0 + R < n)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + off), dst + 64 * jj * 16, 16,
+                                                 0, 0);
+        }
+    }
+}
+
+// f <- -2 f, exactly (a power-of-two scaling of representable values).
+__device__ __forceinline__ void frag_scale_m2(Frag<kBF16>& f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = -2.f * __uint_as_float(f.v[j] << 16);
+        const float hi = -2.f * __uint_as_float(f.v[j] & 0xffff0000u);
+        f.v[j] = pack_bf16x2(lo, hi);
+    }
+}
+__device__ __forceinline__ void frag_scale_m2(Frag<kF32>& f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] *= -2.f;
+}
+
+// One sweep of 64 tokens of one (sequence, head, half) against all n
+// sub-keys of that half.  MODE is a combination of kScoreSelect,
+// kScoreStats and kScoreRowStat (the latter alone).  The MFMA accumulators
+// start at ||q||^2 + ||K_i||^2 + eps and the query fragments are scaled by
+// -2, so each accumulator ends as e = eps + d before the clamp at eps.
+template <int STORE, int DHS, int MK, int MODE>
+__global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
+    constexpr int ES = Store<STORE>::kBytes;
+    constexpr int KB = kKB<STORE>;
+    constexpr int CPR = 32 * DHS * ES / 16;
+    constexpr int BLK_BYTES = KB * CPR * 16;
+    constexpr bool SEL = (MODE & kScoreSelect) != 0;
+    constexpr bool STATS = (MODE & kScoreStats) != 0;
+    constexpr bool ROW = (MODE & kScoreRowStat) != 0;
+    constexpr int NPASS = (SEL || STATS) ? 2 : 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* kbuf = smem;                                            // [2][BLK_BYTES]
+    float* kns = reinterpret_cast<float*>(smem + 2 * BLK_BYTES);           // [n]  ||K_i||^2
+    float* colbuf = kns + a.n;                                             // [2][4][KB] (stats)
+    uint32_t* ccnt = reinterpret_cast<uint32_t*>(colbuf + (STATS ? 2 * 4 * KB : 0));  // [kTok] (select)
+    float* lps = reinterpret_cast<float*>(ccnt + (SEL ? kTok : 0));        // [n]  log pbar (row statistic)
+
+    const int n = a.n, H = a.H, Tc = a.Tc;
+    const int ntiles = (Tc + kTok - 1) / kTok;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = static_cast<int>(lid % ntiles);
-    const int bh = static_cast<int>(lid / ntiles);
+    const int bhh = static_cast<int>(lid / ntiles);  // (b*H + h)*2 + half
+    const int half = bhh & 1, bh = bhh >> 1;
     const int h = bh % H, b = bh / H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int tw0 = tile * kTok + wave * 16;       // first token of this wavefront
-    const int dq = 2 * dh;
-    const bool sel = (a.mode & kScoreSelect) != 0;
-    const bool stats = (a.mode & kScoreStats) != 0;
-    const bool rowstat = (a.mode & kScoreRowStat) != 0;
-    const int npass = (sel || stats) ? 2 : 1;
+    const int tw0 = tile * kTok + wave * 16;  // first token of this wavefront
     const int nblk = (n + KB - 1) / KB;
-    // cooperative block load: each thread moves 16-byte pieces of a block
-    const int row_pieces = dh * ES / 16;            // 16-byte pieces per sub-key row
-    const int blk_pieces = KB * row_pieces;
-    const int my_pieces = (blk_pieces + 255) / 256; // <= 4
+    const unsigned char* Kg = static_cast<const unsigned char*>(half ? a.K2 : a.K1) +
+                              static_cast<size_t>(bh) * n * (32 * DHS) * ES;
+    const size_t rowbase = static_cast<size_t>(bhh) * Tc;
+    for (int i = threadIdx.x; i < n; i += 256) kns[i] = a.knorm[static_cast<size_t>(bhh) * n + i];
 
-    for (int half = 0; half < 2; ++half) {
-        const int bhh = (b * H + h) * 2 + half;
-        const unsigned char* Kg = static_cast<const unsigned char*>(half ? a.K2 : a.K1) +
-                                  static_cast<size_t>(b * H + h) * n * dh * ES;
-        const float* kn = a.knorm + static_cast<size_t>(bhh) * n;
-        // query fragments: token tw0 + r of this half (zero past the chunk)
-        Frag<STORE> A[DHS];
-        const int tok = tw0 + r;
-        const bool tv = tok < a.Tc;
+    // query fragments of token tw0 + r (zero past the chunk), then -2 q
+    Frag<STORE> A[DHS];
+    const int tok = tw0 + r;
+    const bool tv = tok < Tc;
+    {
         const unsigned char* qrow = static_cast<const unsigned char*>(a.q) +
-            (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(tv ? tok : 0) * H * dq + h * dq + half * dh) * ES;
+            (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(tv ? tok : 0) * H * (64 * DHS) +
+             h * (64 * DHS) + half * (32 * DHS)) * ES;
         load_row_frags<STORE, DHS>(A, qrow, g);
-        float qsq = 0.f;
+    }
+    float qsq = 0.f;
 #pragma unroll
-        for (int s = 0; s < DHS; ++s) {
-            if (!tv) frag_zero<STORE>(A[s]);
-            qsq += frag_sumsq<STORE>(A[s]);
-        }
-        qsq += __shfl_xor(qsq, 16, 64);
-        qsq += __shfl_xor(qsq, 32, 64);
-        if (a.qn && (sel || stats) && g == 0 && tv) a.qn[static_cast<size_t>(bhh) * a.Tc + tok] = qsq;
-        // this lane's output rows: tokens tw0 + 4g + i
-        float qn_row[4];
-        bool rv[4];
+    for (int s = 0; s < DHS; ++s) {
+        if (!tv) frag_zero<STORE>(A[s]);
+        qsq += frag_sumsq<STORE>(A[s]);
+        frag_scale_m2(A[s]);
+    }
+    qsq += __shfl_xor(qsq, 16, 64);
+    qsq += __shfl_xor(qsq, 32, 64);
+    if ((SEL || STATS) && a.qn && g == 0 && tv) a.qn[rowbase + tok] = qsq;
+    // this lane's output rows: tokens tw0 + 4g + i
+    const int eps_bits = __float_as_int(a.eps);
+    const FragBase<STORE, DHS> fb(r, g);
+    float qe[4];
+    bool rv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qn_row[i] = __shfl(qsq, 4 * g + i, 64);
-            rv[i] = tw0 + 4 * g + i < a.Tc;
-        }
-        if (rowstat) {
-            __syncthreads();
-            for (int i = threadIdx.x; i < n; i += 256) lps[i] = a.lp[static_cast<size_t>(bhh) * n + i];
-        }
+    for (int i = 0; i < 4; ++i) {
+        qe[i] = __shfl(qsq, 4 * g + i, 64) + a.eps;
+        rv[i] = tw0 + 4 * g + i < Tc;
+    }
 
-        float zinv[4] = {0.f, 0.f, 0.f, 0.f};
-        uint32_t tau[4] = {0u, 0u, 0u, 0u};
-        for (int pass = 0; pass < npass; ++pass) {
-            const bool last = pass == npass - 1;
-            float zacc[4] = {0.f, 0.f, 0.f, 0.f}, macc[4] = {0.f, 0.f, 0.f, 0.f};
-            uint32_t keep[4][MK];
-            uint32_t cnt[4] = {0u, 0u, 0u, 0u};
+    float zinv[4] = {0.f, 0.f, 0.f, 0.f};  // 1/Z_t of the selection pass (0 past the chunk)
+    float zrow[4] = {1.f, 1.f, 1.f, 1.f};  // Z_t from the workspace (row statistic)
+    uint32_t tau[4] = {0u, 0u, 0u, 0u};
+    if constexpr (ROW) {
+        for (int i = threadIdx.x; i < n; i += 256) lps[i] = a.lp[static_cast<size_t>(bhh) * n + i];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int m = 0; m < MK; ++m) keep[i][m] = 0xffffffffu;
+        for (int i = 0; i < 4; ++i)
+            if (rv[i]) zrow[i] = a.Z[rowbase + tw0 + 4 * g + i];
+    }
 
-            // prologue: block 0 -> buffer 0
-            __syncthreads();
-            for (int c = 0; c < my_pieces; ++c) {
-                const int piece = threadIdx.x + 256 * c;
-                if (piece < blk_pieces && piece / row_pieces < n) {
-                    const int kr = piece / row_pieces, kc = piece % row_pieces;
-                    *reinterpret_cast<uint4*>(kbuf + (kr * kstride) * ES + kc * 16) =
-                        *reinterpret_cast<const uint4*>(Kg + static_cast<size_t>(kr) * dh * ES + kc * 16);
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        float zacc[4] = {0.f, 0.f, 0.f, 0.f}, macc[4] = {0.f, 0.f, 0.f, 0.f};
+        uint32_t keep[4][MK];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int m = 0; m < MK; ++m) keep[i][m] = 0xffffffffu;
+
+        __syncthreads();  // the previous pass is done with kbuf / ccnt
+        if (SEL && pass == 1 && threadIdx.x < kTok) ccnt[threadIdx.x] = 0u;
+        dma_block<STORE, DHS, KB>(kbuf, Kg, 0, n, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int cur = blk & 1;
+            if (blk + 1 < nblk)
+                dma_block<STORE, DHS, KB>(kbuf + (cur ^ 1) * BLK_BYTES, Kg, (blk + 1) * KB, n, wave, lane);
+            const unsigned char* kb = kbuf + cur * BLK_BYTES;
+            float colv[KB / 16];
+#pragma unroll
+            for (int ct = 0; ct < KB / 16; ++ct) {
+                colv[ct] = 0.f;
+                if (blk * KB + ct * 16 >= n) continue;  // partial last block (n % 16 == 0)
+                const int key = blk * KB + ct * 16 + r;
+                const float knv = kns[key];
+                f32x4_t acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = qe[i] + knv;
+                // k-blocks in pairs, the next pair's LDS reads in flight under
+                // this pair's MFMAs
+                constexpr int NP = (DHS + 1) / 2;
+                Frag<STORE> Bf[2][2];
+                lds_frag<STORE, DHS>(Bf[0][0], kb, fb, ct, 0);
+                if (DHS > 1) lds_frag<STORE, DHS>(Bf[0][1], kb, fb, ct, 1);
+#pragma unroll
+                for (int sp = 0; sp < NP; ++sp) {
+                    if (sp + 1 < NP) {
+                        lds_frag<STORE, DHS>(Bf[(sp + 1) & 1][0], kb, fb, ct, 2 * sp + 2);
+                        lds_frag<STORE, DHS>(Bf[(sp + 1) & 1][1], kb, fb, ct, 2 * sp + 3);
+                    }
+                    mma(A[2 * sp], Bf[sp & 1][0], acc);
+                    if (2 * sp + 1 < DHS) mma(A[2 * sp + 1], Bf[sp & 1][1], acc);
                 }
-            }
-            __syncthreads();
-
-            for (int blk = 0; blk < nblk; ++blk) {
-                const int cur = blk & 1;
-                // prefetch the next block into registers
-                uint4 pre[4] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u),
-                                make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-                const bool has_next = blk + 1 < nblk;
-                if (has_next) {
+                float lpk = 0.f;
+                if constexpr (ROW) lpk = lps[key];
+                float cs = 0.f;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int piece = threadIdx.x + 256 * c;
-                        if (c < my_pieces && piece < blk_pieces && (blk + 1) * KB + piece / row_pieces < n) {
-                            const int kr = piece / row_pieces, kc = piece % row_pieces;
-                            pre[c] = *reinterpret_cast<const uint4*>(
-                                Kg + static_cast<size_t>((blk + 1) * KB + kr) * dh * ES + kc * 16);
+                for (int i = 0; i < 4; ++i) {
+                    // e = max(eps + d, eps): a signed-integer max of the bit
+                    // patterns orders these floats exactly (eps > 0)
+                    const uint32_t eb = static_cast<uint32_t>(max(__float_as_int(acc[i]), eps_bits));
+                    const float e = __uint_as_float(eb);
+                    if (pass == 0) {
+                        if constexpr (STATS) zacc[i] += fast_rcp(e);
+                        if constexpr (ROW) macc[i] = fmaf(fast_rcp(e), lpk, macc[i]);
+                        if constexpr (SEL) {
+                            // keep the MK smallest of this lane, ascending
+                            uint32_t x = eb;
+#pragma unroll
+                            for (int m = 0; m < MK; ++m) {
+                                const uint32_t lo = min(keep[i][m], x);
+                                x = max(keep[i][m], x);
+                                keep[i][m] = lo;
+                            }
+                        }
+                    } else {
+                        if constexpr (STATS) cs = fmaf(fast_rcp(e), zinv[i], cs);
+                        if constexpr (SEL) {
+                            if (eb <= tau[i]) {
+                                const uint32_t pos = atomicAdd(&ccnt[wave * 16 + 4 * g + i], 1u);
+                                if (pos < static_cast<uint32_t>(a.cap))
+                                    a.cand[(rowbase + tw0 + 4 * g + i) * a.cap + pos] =
+                                        (static_cast<uint64_t>(eb) << 32) | static_cast<uint32_t>(key);
+                            }
                         }
                     }
                 }
-                const unsigned char* kb = kbuf + cur * KB * kstride * ES;
-                float colv[KB / 16];
+                colv[ct] = cs;
+            }
+            if (STATS && pass == 1) {
+                // sum over this wavefront's 16 tokens: across the four lane groups
 #pragma unroll
                 for (int ct = 0; ct < KB / 16; ++ct) {
-                    colv[ct] = 0.f;
-                    if (blk * KB + ct * 16 >= n) continue;  // partial last block (n % 16 == 0)
-                    Frag<STORE> B[DHS];
-                    load_row_frags<STORE, DHS>(B, kb + (ct * 16 + r) * kstride * ES, g);
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < DHS; ++s) mma(A[s], B[s], acc);
-                    const int key = blk * KB + ct * 16 + r;
-                    const float knv = kn[key];
-                    float cs = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = a.eps + fmaxf(qn_row[i] + knv - 2.f * acc[i], 0.f);
-                        const uint32_t eb = __float_as_uint(e);
-                        if (pass == 0 && (sel || stats || rowstat)) {
-                            const float u = rv[i] ? fast_rcp(e) : 0.f;
-                            zacc[i] += u;
-                            if (rowstat) macc[i] = fmaf(u, lps[key], macc[i]);
-                            if (sel && rv[i]) {
-                                // keep the MK smallest of this lane, ascending
-                                uint32_t x = eb;
-#pragma unroll
-                                for (int m = 0; m < MK; ++m) {
-                                    const uint32_t lo = min(keep[i][m], x);
-                                    x = max(keep[i][m], x);
-                                    keep[i][m] = lo;
-                                }
-                            }
-                        }
-                        if (pass == 1) {
-                            if (stats && rv[i]) cs = fmaf(fast_rcp(e), zinv[i], cs);
-                            if (sel) {
-                                const bool pred = rv[i] && eb <= tau[i];
-                                const uint32_t m16 = static_cast<uint32_t>(ballot(pred) >> (16 * g)) & 0xffffu;
-                                const uint32_t pos = cnt[i] + __popc(m16 & ((1u << r) - 1u));
-                                if (pred && pos < static_cast<uint32_t>(a.cap)) {
-                                    const size_t o = (static_cast<size_t>(bhh) * a.Tc + tw0 + 4 * g + i) * a.cap + pos;
-                                    a.cand[o] = (static_cast<uint64_t>(eb) << 32) | static_cast<uint32_t>(key);
-                                }
-                                cnt[i] += __popc(m16);
-                            }
-                        }
-                    }
-                    colv[ct] = cs;
-                }
-                if (pass == 1 && stats) {
-                    // sum over this wavefront's 16 tokens: across the four lane groups
-#pragma unroll
-                    for (int ct = 0; ct < KB / 16; ++ct) {
-                        float x = colv[ct];
-                        x += __shfl_xor(x, 16, 64);
-                        x += __shfl_xor(x, 32, 64);
-                        if (g == 0) colbuf[(cur * 4 + wave) * KB + ct * 16 + r] = x;
-                    }
-                }
-                // stage the prefetched block into the other buffer
-                if (has_next) {
-                    unsigned char* nb = kbuf + (cur ^ 1) * KB * kstride * ES;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int piece = threadIdx.x + 256 * c;
-                        if (c < my_pieces && piece < blk_pieces && (blk + 1) * KB + piece / row_pieces < n) {
-                            const int kr = piece / row_pieces, kc = piece % row_pieces;
-                            *reinterpret_cast<uint4*>(nb + (kr * kstride) * ES + kc * 16) = pre[c];
-                        }
-                    }
-                }
-                __syncthreads();
-                if (pass == 1 && stats && threadIdx.x < KB && blk * KB + static_cast<int>(threadIdx.x) < n) {
-                    // this tile's partial of pbar for the block's sub-keys, waves in order
-                    const float* cb = colbuf + cur * 4 * KB + threadIdx.x;
-                    const float s = ((cb[0] + cb[KB]) + cb[2 * KB]) + cb[3 * KB];
-                    a.part[(static_cast<size_t>(bhh) * ntiles + tile) * n + blk * KB + threadIdx.x] = s;
+                    float x = colv[ct];
+                    x += __shfl_xor(x, 16, 64);
+                    x += __shfl_xor(x, 32, 64);
+                    if (g == 0) colbuf[(cur * 4 + wave) * KB + ct * 16 + r] = x;
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next block has landed
+            __syncthreads();
+            if (STATS && pass == 1 && threadIdx.x < KB && blk * KB + static_cast<int>(threadIdx.x) < n) {
+                // this tile's partial of pbar for the block's sub-keys, waves in order
+                const float* cb = colbuf + cur * 4 * KB + threadIdx.x;
+                const float s = ((cb[0] + cb[KB]) + cb[2 * KB]) + cb[3 * KB];
+                a.part[(static_cast<size_t>(bhh) * ntiles + tile) * n + blk * KB + threadIdx.x] = s;
+            }
+        }
 
-            if (pass == 0) {
+        if (pass == 0) {
+            if constexpr (STATS) {
                 // Z_t over the sixteen lanes that share token 4g+i
-                float zt[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = zacc[i];
@@ -289,48 +381,45 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
                     x += __shfl_xor(x, 2, 64);
                     x += __shfl_xor(x, 4, 64);
                     x += __shfl_xor(x, 8, 64);
-                    zt[i] = x;
-                    zinv[i] = fast_rcp(x);
-                }
-                if (rowstat) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float x = macc[i];
-                        x += __shfl_xor(x, 1, 64);
-                        x += __shfl_xor(x, 2, 64);
-                        x += __shfl_xor(x, 4, 64);
-                        x += __shfl_xor(x, 8, 64);
-                        if (r == 0 && rv[i]) {
-                            const size_t o = static_cast<size_t>(bhh) * a.Tc + tw0 + 4 * g + i;
-                            a.Z[o] = zt[i];
-                            a.m[o] = x / zt[i];
-                        }
-                    }
-                }
-                if (sel) {
-                    // tau = k'-th smallest of the 16*MK values kept by the token's lanes
-                    constexpr int RS = (MK <= 1) ? 1 : (MK <= 2 ? 2 : 4);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        uint32_t v[RS];
-#pragma unroll
-                        for (int m = 0; m < RS; ++m) v[m] = (m < MK) ? keep[i][m] : 0xffffffffu;
-                        bitonic_sort<RS, 16>(v);
-                        const int kth = a.kh - 1;
-                        uint32_t t = 0u;
-#pragma unroll
-                        for (int m = 0; m < RS; ++m)
-                            if (m == kth / 16) t = v[m];
-                        tau[i] = static_cast<uint32_t>(__shfl(static_cast<int>(t), 16 * g + (kth % 16), 64));
-                    }
+                    zinv[i] = rv[i] ? fast_rcp(x) : 0.f;
+                    if (r == 0 && rv[i]) a.Z[rowbase + tw0 + 4 * g + i] = x;
                 }
             }
-            if (last && sel && r == 0) {
+            if constexpr (ROW) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (rv[i]) a.cnt[static_cast<size_t>(bhh) * a.Tc + tw0 + 4 * g + i] = static_cast<int32_t>(cnt[i]);
+                for (int i = 0; i < 4; ++i) {
+                    float x = macc[i];
+                    x += __shfl_xor(x, 1, 64);
+                    x += __shfl_xor(x, 2, 64);
+                    x += __shfl_xor(x, 4, 64);
+                    x += __shfl_xor(x, 8, 64);
+                    if (r == 0 && rv[i]) a.m[rowbase + tw0 + 4 * g + i] = x / zrow[i];
+                }
+            }
+            if constexpr (SEL) {
+                // tau = k'-th smallest of the 16*MK values kept by the token's lanes
+                constexpr int RS = (MK <= 1) ? 1 : (MK <= 2 ? 2 : 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t v[RS];
+#pragma unroll
+                    for (int m = 0; m < RS; ++m) v[m] = (m < MK) ? keep[i][m] : 0xffffffffu;
+                    bitonic_sort<RS, 16>(v);
+                    const int kth = a.kh - 1;
+                    uint32_t t = 0u;
+#pragma unroll
+                    for (int m = 0; m < RS; ++m)
+                        if (m == kth / 16) t = v[m];
+                    t = static_cast<uint32_t>(__shfl(static_cast<int>(t), 16 * g + (kth % 16), 64));
+                    tau[i] = rv[i] ? t : 0u;  // rows past the chunk collect nothing
+                }
             }
         }
+    }
+    if constexpr (SEL) {
+        __syncthreads();
+        const int t = tile * kTok + static_cast<int>(threadIdx.x);
+        if (threadIdx.x < kTok && t < Tc) a.cnt[rowbase + t] = static_cast<int32_t>(ccnt[threadIdx.x]);
     }
 }
 
@@ -508,31 +597,45 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
 }
 
-template <int STORE, int DHS, int MK>
+template <int STORE, int DHS, int MK, int MODE>
 hipError_t score_t(const ScoreArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int KB = kKB<STORE>;
-    const size_t lds = static_cast<size_t>(2) * KB * (a.dh + 16 / ES) * ES + 2 * 4 * KB * 4 +
-                       ((a.mode & kScoreRowStat) ? static_cast<size_t>(a.n) * 4 : 0);
+    constexpr size_t BLK_BYTES = static_cast<size_t>(KB) * DHS * 32 * ES;
+    const size_t lds = 2 * BLK_BYTES + static_cast<size_t>(a.n) * 4 + ((MODE & kScoreStats) ? 2 * 4 * KB * 4 : 0) +
+                       ((MODE & kScoreSelect) ? kTok * 4 : 0) +
+                       ((MODE & kScoreRowStat) ? static_cast<size_t>(a.n) * 4 : 0);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK, MODE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int ntiles = (a.Tc + kTok - 1) / kTok;
-    const unsigned grid = static_cast<unsigned>(a.B) * a.H * ntiles;
-    hipLaunchKernelGGL((k_score<STORE, DHS, MK>), dim3(grid), dim3(256), lds, s, a);
+    const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * ntiles;
+    hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE>), dim3(grid), dim3(256), lds, s, a);
     return hipGetLastError();
+}
+
+template <int STORE, int DHS, int MK>
+hipError_t score_mode(const ScoreArgs& a, hipStream_t s) {
+    switch (a.mode) {
+        case kScoreSelect: return score_t<STORE, DHS, MK, kScoreSelect>(a, s);
+        case kScoreSelect | kScoreStats: return score_t<STORE, DHS, MK, kScoreSelect | kScoreStats>(a, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int STORE, int DHS>
 hipError_t score_mk(const ScoreArgs& a, hipStream_t s) {
+    // modes without selection do not keep per-lane minima
+    if (a.mode == kScoreStats) return score_t<STORE, DHS, 1, kScoreStats>(a, s);
+    if (a.mode == kScoreRowStat) return score_t<STORE, DHS, 1, kScoreRowStat>(a, s);
     switch (score_keep(a.kh)) {
-        case 2: return score_t<STORE, DHS, 2>(a, s);
-        case 3: return score_t<STORE, DHS, 3>(a, s);
-        case 4: return score_t<STORE, DHS, 4>(a, s);
+        case 2: return score_mode<STORE, DHS, 2>(a, s);
+        case 3: return score_mode<STORE, DHS, 3>(a, s);
+        case 4: return score_mode<STORE, DHS, 4>(a, s);
     }
     return hipErrorInvalidValue;
 }
