@@ -211,7 +211,8 @@ typedef enum {
     FWPKM_K_KGRAD = 9,          /* sub-key gradient step                           */
     FWPKM_K_FILL = 10,          /* zero fill of n_read                             */
     FWPKM_K_SELECT = 11,        /* per-half top-k', product top-k, weights         */
-    FWPKM_K_COUNT = 12
+    FWPKM_K_QT = 12,            /* transposed query halves for the sub-key step    */
+    FWPKM_K_COUNT = 13
 } fwpkm_kernel;
 
 /*

@@ -201,7 +201,7 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, r, Z, m, part, lp, k0, v0, k1, v1, counts, ph, pt, pts, phe;
+    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, r, Z, m, part, lp, qT, k0, v0, k1, v1, counts, ph, pt, pts, phe;
     size_t total;
 };
 
@@ -237,6 +237,7 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         L.m = take(Bs * p.H * 2 * T * 4);
         L.part = take(Bs * p.H * 2 * ntiles * p.n * 4);
         L.lp = take(Bs * p.H * 2 * p.n * 4);
+        L.qT = take(Bs * p.H * 2 * p.dh * ((T + 31) / 32 * 32) * p.es);
         L.k0 = take(Bs * M * 4);
         L.v0 = take(Bs * M * 4);
         L.k1 = take(Bs * M * 4);
@@ -391,8 +392,15 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
         TimedLaunch tl(FWPKM_K_SWEEP_ROWSTAT, s);
         HIP_TRY(launch_score(ra, p.store, s));
     }
+    const int Tp = (Tc + 31) / 32 * 32;
+    {
+        QtArgs qa{q, q_bstride, at<void>(ws, L.qT), B, Tc, Tp, p.H, p.dh};
+        TimedLaunch tl(FWPKM_K_QT, s);
+        HIP_TRY(launch_qt(qa, p.store, s));
+    }
     KgradArgs ka{};
-    ka.q = q; ka.q_bstride = q_bstride; ka.K1 = K1; ka.K2 = K2; ka.knorm = knorm;
+    ka.q = q; ka.q_bstride = q_bstride; ka.qT = at<void>(ws, L.qT); ka.Tp = Tp;
+    ka.K1 = K1; ka.K2 = K2; ka.knorm = knorm;
     ka.qn = at<float>(ws, L.qn); ka.Z = at<float>(ws, L.Z); ka.m = at<float>(ws, L.m); ka.lp = at<float>(ws, L.lp);
     ka.B = B; ka.Tc = Tc; ka.n = p.n; ka.H = p.H; ka.dh = p.dh; ka.eps = p.eps; ka.lr = p.lr_k;
     {

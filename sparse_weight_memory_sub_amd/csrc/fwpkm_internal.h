@@ -245,9 +245,18 @@ struct PbarArgs {
     int B, H, n, ntiles, Tc;
 };
 
+struct QtArgs {
+    const void* q;        // token t of sequence b at q + b*q_bstride + t*H*2*dh
+    int64_t q_bstride;
+    void* qT;             // [B][H][2][dh][Tp]
+    int B, Tc, Tp, H, dh;
+};
+
 struct KgradArgs {
     const void* q;
     int64_t q_bstride;
+    const void* qT;       // [B][H][2][dh][Tp] (k_qt)
+    int Tp;
     void* K1;
     void* K2;
     float* knorm;         // [B][H][2][n], rewritten with the new keys
@@ -278,6 +287,7 @@ hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, int store, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t s);
 hipError_t launch_pbar(const PbarArgs& a, hipStream_t s);
+hipError_t launch_qt(const QtArgs& a, int store, hipStream_t s);
 hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s);
 
 constexpr int kSortItems = 8;                  // entries per thread

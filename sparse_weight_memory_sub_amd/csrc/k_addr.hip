@@ -69,7 +69,34 @@ __global__ __launch_bounds__(256) void k_knorm(KnormArgs a) {
     if (valid && r == 0) a.knorm[key] = x;
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float x) { return f32_to_bf16(x); }
+// Transposed query halves of a chunk, qT[bhh][d][t] for t < Tp (Tp = Tc
+// rounded up to 32; zeros past Tc), the token-contiguous operand of the
+// sum over tokens in k_kgrad.  64x64 tiles through LDS.
+template <int STORE>
+__global__ __launch_bounds__(256) void k_qt(QtArgs a) {
+    using E = typename Store<STORE>::T;
+    __shared__ E tile[64][65];
+    const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+    const int bhh = blockIdx.z;
+    const int half = bhh & 1, bh = bhh >> 1;
+    const int h = bh % a.H, b = bh / a.H;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const E* q = static_cast<const E*>(a.q) + static_cast<size_t>(b) * a.q_bstride + h * 2 * a.dh + half * a.dh;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+        const int tl = ty * 16 + i, t = t0 + tl, d = d0 + tx;
+        E v{};
+        if (t < a.Tc && d < a.dh) v = q[static_cast<size_t>(t) * a.H * 2 * a.dh + d];
+        tile[tl][tx] = v;
+    }
+    __syncthreads();
+    E* out = static_cast<E*>(a.qT) + static_cast<size_t>(bhh) * a.dh * a.Tp;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+        const int dl = ty * 16 + i, d = d0 + dl, t = t0 + tx;
+        if (d < a.dh && t < a.Tp) out[static_cast<size_t>(d) * a.Tp + t] = tile[tx][dl];
+    }
+}
 
 // token of element j of lane group g in the 32-token block: the first four
 // from the 16-token sub-tile 0, the last four from sub-tile 1, matching the
@@ -77,141 +104,174 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) { return f32_to_bf16(x); 
 __device__ __forceinline__ int tok_of(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4); }
 
 template <int STORE, int DHS>
-__global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
+__global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int ES = Store<STORE>::kBytes;
-    constexpr int PAD = (STORE == kBF16) ? 8 : 4;  // row padding in elements (LDS banks)
-    const int dh = a.dh, n = a.n, H = a.H;
-    const int qstride = dh + PAD;
-    unsigned char* qs = smem;                                            // [32][qstride]
-    float* tq = reinterpret_cast<float*>(smem + 32 * qstride * ES);     // qn, Z, m: [3][32]
+    constexpr int DH = 32 * DHS;
+    constexpr int CPRQ = DH * ES / 16;        // chunks per query row (wide image, 32 rows)
+    constexpr int CPRT = 32 * ES / 16;        // chunks per transposed row (narrow image, DH rows)
+    constexpr int QB = 32 * CPRQ * 16;        // bytes of one query tile
+    constexpr int TB = DH * CPRT * 16;        // bytes of one transposed tile
+    constexpr int BUF = QB + TB + 3 * 32 * 4; // + qn, 1/Z, m of the 32 tokens
+    const int n = a.n, H = a.H, Tc = a.Tc;
 
     const int nkb = (n + 63) / 64;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int kb = static_cast<int>(lid % nkb);
-    int rest = static_cast<int>(lid / nkb);
-    const int half = rest % 2;
-    rest /= 2;
-    const int h = rest % H, b = rest / H;
-    const int bhh = (b * H + h) * 2 + half;
+    const int bhh = static_cast<int>(lid / nkb);  // (b*H + h)*2 + half
+    const int half = bhh & 1, bh = bhh >> 1;
+    const int h = bh % H, b = bh / H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int key0 = kb * 64 + wave * 16;
     const bool active = key0 < n;
     const int key = key0 + r;
-    unsigned char* Kb = static_cast<unsigned char*>(half ? a.K2 : a.K1) + static_cast<size_t>(b * H + h) * n * dh * ES;
-    const int dq = 2 * dh;
+    unsigned char* Kb = static_cast<unsigned char*>(half ? a.K2 : a.K1) + static_cast<size_t>(bh) * n * DH * ES;
+    const unsigned char* qbase = static_cast<const unsigned char*>(a.q) +
+        (static_cast<size_t>(b) * a.q_bstride + h * 2 * DH + half * DH) * ES;
+    const uint32_t qstride = static_cast<uint32_t>(H * 2 * DH * ES);
+    const unsigned char* tbase = static_cast<const unsigned char*>(a.qT) + static_cast<size_t>(bhh) * DH * a.Tp * ES;
+    const uint32_t tstride = static_cast<uint32_t>(a.Tp * ES);
 
+    // this wave's 16 keys as the B operand of the distance tiles, scaled by -2
     Frag<STORE> Bk[DHS];
     float kn = 0.f, lpv = 0.f;
     if (active) {
-        load_row_frags<STORE, DHS>(Bk, Kb + static_cast<size_t>(key) * dh * ES, g);
+        load_row_frags<STORE, DHS>(Bk, Kb + static_cast<size_t>(key) * DH * ES, g);
+#pragma unroll
+        for (int s = 0; s < DHS; ++s) frag_scale_m2(Bk[s]);
         kn = a.knorm[static_cast<size_t>(bhh) * n + key];
         lpv = a.lp[static_cast<size_t>(bhh) * n + key];
     }
+    const int eps_bits = __float_as_int(a.eps);
+    const FragBase<STORE, DHS> fq(r, g);
+    // transposed-tile offsets of the operand column d = 16c + r: tokens 4g..4g+3
+    // and 16+4g..16+4g+3 of the block
+    uint32_t tb0, tb1;
+    {
+        const int f = swz<CPRT, true>(r);
+        if constexpr (STORE == kBF16) {
+            tb0 = static_cast<uint32_t>(r * CPRT + ((g >> 1) ^ f)) * 16u + 8u * (g & 1);
+            tb1 = static_cast<uint32_t>(r * CPRT + ((2 + (g >> 1)) ^ f)) * 16u + 8u * (g & 1);
+        } else {
+            tb0 = static_cast<uint32_t>(r * CPRT + (g ^ f)) * 16u;
+            tb1 = static_cast<uint32_t>(r * CPRT + ((4 + g) ^ f)) * 16u;
+        }
+    }
+
     constexpr int NCT = DHS * 2;  // 16-wide column tiles of d_h
     f32x4_t gacc[NCT];
 #pragma unroll
     for (int c = 0; c < NCT; ++c) gacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float colsum = 0.f;
-    const float inv_tc2 = 2.f / static_cast<float>(a.Tc);
+    const float inv_tc2 = 2.f / static_cast<float>(Tc);
 
-    // key blocks of one (sequence, head, half) run side by side and read the
-    // same query rows: start each at a different token block (fixed order per
-    // block, so the sums stay reproducible)
-    const int nblk = (a.Tc + 31) / 32;
-    for (int bi = 0; bi < nblk; ++bi) {
-        const int tb = ((bi + kb) % nblk) * 32;
-        __syncthreads();
-        // stage the query halves of tokens tb .. tb+31 (zeros past Tc)
-        const int chunks = dh / 8;  // 8-element pieces per row
-        for (int c = threadIdx.x; c < 32 * chunks; c += 256) {
-            const int row = c / chunks, col = (c % chunks) * 8;
-            const int t = tb + row;
-            unsigned char* dst = qs + (static_cast<size_t>(row) * qstride + col) * ES;
-            if (t < a.Tc) {
-                const unsigned char* src = static_cast<const unsigned char*>(a.q) +
-                    (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(t) * H * dq + h * dq + half * dh + col) * ES;
-                if constexpr (STORE == kBF16) {
-                    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-                } else {
-                    reinterpret_cast<float4*>(dst)[0] = reinterpret_cast<const float4*>(src)[0];
-                    reinterpret_cast<float4*>(dst)[1] = reinterpret_cast<const float4*>(src)[1];
-                }
-            } else {
-                if constexpr (STORE == kBF16) {
-                    *reinterpret_cast<uint4*>(dst) = make_uint4(0u, 0u, 0u, 0u);
-                } else {
-                    reinterpret_cast<float4*>(dst)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    reinterpret_cast<float4*>(dst)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
-        }
+    // Token blocks of 32.  Key blocks of one (sequence, head, half) run side by
+    // side and read the same query rows: each starts at a different block
+    // (fixed order per key block, so the sums stay reproducible).
+    const int nblk = (Tc + 31) / 32;
+    auto tok_block = [&](int bi) { return ((bi + kb) % nblk) * 32; };
+    auto stage = [&](unsigned char* buf, int tb) {
+        dma_rows<CPRQ, 32, 4, false>(buf, qbase + static_cast<size_t>(tb) * qstride, qstride, Tc - tb, wave, lane);
+        dma_rows<CPRT, DH, 4, true>(buf + QB, tbase + static_cast<size_t>(tb) * ES, tstride, DH, wave, lane);
+    };
+    // qn, 1/Z, m of tokens tb..tb+31 (zeros past the chunk), threads 0..95
+    auto tq_load = [&](int tb) {
+        float x = 0.f;
         if (threadIdx.x < 96) {
-            const int which = threadIdx.x / 32, row = threadIdx.x % 32;
-            const int t = tb + row;
-            const float* src = which == 0 ? a.qn : (which == 1 ? a.Z : a.m);
-            float x = (t < a.Tc) ? src[static_cast<size_t>(bhh) * a.Tc + t] : 1.f;
-            if (which == 1) x = __builtin_amdgcn_rcpf(x);  // stored as 1/Z
-            tq[which * 32 + row] = x;
+            const int which = threadIdx.x >> 5, t = tb + (threadIdx.x & 31);
+            if (t < Tc) {
+                const size_t o = static_cast<size_t>(bhh) * Tc + t;
+                x = which == 0 ? a.qn[o] : (which == 1 ? __builtin_amdgcn_rcpf(a.Z[o]) : a.m[o]);
+            }
         }
-        __syncthreads();
-        if (!active) continue;
+        return x;
+    };
+    auto tq_store = [&](unsigned char* buf, float x) {
+        if (threadIdx.x < 96) reinterpret_cast<float*>(buf + QB + TB)[threadIdx.x] = x;
+    };
 
-        float av[8];
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            Frag<STORE> A[DHS];
-            load_row_frags<STORE, DHS>(A, qs + static_cast<size_t>(sub * 16 + r) * qstride * ES, g);
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < DHS; ++s) mma(A[s], Bk[s], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = sub * 16 + 4 * g + i;
-                const float d = tq[row] + kn - 2.f * acc[i];
-                const float ie = __builtin_amdgcn_rcpf(a.eps + fmaxf(d, 0.f));
-                const float val = (tb + row < a.Tc) ? inv_tc2 * (lpv - tq[64 + row]) * tq[32 + row] * ie * ie : 0.f;
-                av[sub * 4 + i] = val;
-                colsum += val;
-            }
+    stage(smem, tok_block(0));
+    tq_store(smem, tq_load(tok_block(0)));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int bi = 0; bi < nblk; ++bi) {
+        unsigned char* cur = smem + (bi & 1) * BUF;
+        unsigned char* nxt = smem + ((bi + 1) & 1) * BUF;
+        const int tb = tok_block(bi);
+        float tqn = 0.f;
+        if (bi + 1 < nblk) {
+            stage(nxt, tok_block(bi + 1));
+            tqn = tq_load(tok_block(bi + 1));
         }
-        // sum_t a_ti q_t: keys x tokens (A) times tokens x d_h (B)
-        Frag<kBF16> Ahi, Alo;
-        if constexpr (STORE == kBF16) {
-            uint32_t hi[4], lo[4];
+        if (active) {
+            const float* tq = reinterpret_cast<const float*>(cur + QB + TB);
+            float av[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hi[j] = pack_bf16x2(av[2 * j], av[2 * j + 1]);
-                lo[j] = pack_bf16x2(av[2 * j] - __uint_as_float(hi[j] << 16),
-                                    av[2 * j + 1] - __uint_as_float(hi[j] & 0xffff0000u));
-            }
-            Ahi.v = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
-            Alo.v = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
-        }
+            for (int sub = 0; sub < 2; ++sub) {
+                f32x4_t acc;
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-            const int col = c * 16 + r;
-            if constexpr (STORE == kBF16) {
-                const uint16_t* qb = reinterpret_cast<const uint16_t*>(qs);
-                uint32_t bq[8];
+                for (int i = 0; i < 4; ++i) acc[i] = (tq[sub * 16 + 4 * g + i] + a.eps) + kn;
+                Frag<STORE> A[2];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) bq[j] = qb[tok_of(g, j) * qstride + col];
-                Frag<kBF16> B;
-                B.v = u32x4_t{bq[0] | (bq[1] << 16), bq[2] | (bq[3] << 16), bq[4] | (bq[5] << 16), bq[6] | (bq[7] << 16)};
-                mma(Ahi, B, gacc[c]);
-                mma(Alo, B, gacc[c]);
-            } else {
-                const float* qf = reinterpret_cast<const float*>(qs);
-                Frag<kF32> B, A;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    B.v[j] = qf[tok_of(g, j) * qstride + col];
-                    A.v[j] = av[j];
+                for (int s = 0; s < DHS; ++s) {
+                    lds_frag<STORE, DHS>(A[s & 1], cur, fq, sub, s);
+                    mma(A[s & 1], Bk[s], acc);
                 }
-                mma(A, B, gacc[c]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = sub * 16 + 4 * g + i;
+                    const float e = __int_as_float(max(__float_as_int(acc[i]), eps_bits));
+                    const float ie = __builtin_amdgcn_rcpf(e);
+                    // tokens past the chunk have 1/Z = 0; the select also drops
+                    // whatever their (unfilled) query rows produced
+                    const float val = inv_tc2 * (lpv - tq[64 + row]) * tq[32 + row] * ie * ie;
+                    av[sub * 4 + i] = (tb + row < Tc) ? val : 0.f;
+                    colsum += av[sub * 4 + i];
+                }
+            }
+            // sum_t a_ti q_t: keys x tokens (A) times tokens x d_h (B)
+            if constexpr (STORE == kBF16) {
+                Frag<kBF16> Ahi, Alo;
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    hi[j] = pack_bf16x2(av[2 * j], av[2 * j + 1]);
+                    lo[j] = pack_bf16x2(av[2 * j] - __uint_as_float(hi[j] << 16),
+                                        av[2 * j + 1] - __uint_as_float(hi[j] & 0xffff0000u));
+                }
+                Ahi.v = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+                Alo.v = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    const unsigned char* tp = cur + QB + static_cast<uint32_t>(c * 16 * CPRT * 16);
+                    const uint2 x0 = *reinterpret_cast<const uint2*>(tp + tb0);
+                    const uint2 x1 = *reinterpret_cast<const uint2*>(tp + tb1);
+                    Frag<kBF16> Bq;
+                    Bq.v = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+                    mma(Ahi, Bq, gacc[c]);
+                    mma(Alo, Bq, gacc[c]);
+                }
+            } else {
+                Frag<kF32> A;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) A.v[j] = av[j];
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    const unsigned char* tp = cur + QB + static_cast<uint32_t>(c * 16 * CPRT * 16);
+                    const float4 x0 = *reinterpret_cast<const float4*>(tp + tb0);
+                    const float4 x1 = *reinterpret_cast<const float4*>(tp + tb1);
+                    Frag<kF32> Bq;
+                    Bq.v[0] = x0.x; Bq.v[1] = x0.y; Bq.v[2] = x0.z; Bq.v[3] = x0.w;
+                    Bq.v[4] = x1.x; Bq.v[5] = x1.y; Bq.v[6] = x1.z; Bq.v[7] = x1.w;
+                    mma(A, Bq, gacc[c]);
+                }
             }
         }
+        if (bi + 1 < nblk) tq_store(nxt, tqn);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next block has landed
+        __syncthreads();
     }
     if (!active) return;
 
@@ -230,7 +290,7 @@ __global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int k = key0 + 4 * g + i;
-            const size_t off = static_cast<size_t>(k) * dh + col;
+            const size_t off = static_cast<size_t>(k) * DH + col;
             const float kv = ld_elem<STORE>(Kb, off);
             const float grad = gacc[c][i] - cs[i] * kv;
             float kn2 = kv - a.lr * grad;
@@ -253,11 +313,18 @@ __global__ __launch_bounds__(256) void k_kgrad(KgradArgs a) {
 template <int STORE, int DHS>
 hipError_t kgrad_t(const KgradArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
-    constexpr int PAD = (STORE == kBF16) ? 8 : 4;
-    const size_t lds = static_cast<size_t>(32) * (a.dh + PAD) * ES + 3 * 32 * 4;
+    constexpr int DH = 32 * DHS;
+    constexpr size_t BUF = static_cast<size_t>(32) * DH * ES + static_cast<size_t>(DH) * 32 * ES + 3 * 32 * 4;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_kgrad<STORE, DHS>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
     const int nkb = (a.n + 63) / 64;
     const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * nkb;
-    hipLaunchKernelGGL((k_kgrad<STORE, DHS>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_kgrad<STORE, DHS>), dim3(grid), dim3(256), 2 * BUF, s, a);
     return hipGetLastError();
 }
 
@@ -285,6 +352,14 @@ hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>((keys + 15) / 16);
     if (store == kBF16) hipLaunchKernelGGL(k_knorm<kBF16>, dim3(grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_knorm<kF32>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_qt(const QtArgs& a, int store, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>((a.Tp + 63) / 64), static_cast<unsigned>((a.dh + 63) / 64),
+                    static_cast<unsigned>(a.B * a.H * 2));
+    if (store == kBF16) hipLaunchKernelGGL(k_qt<kBF16>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_qt<kF32>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

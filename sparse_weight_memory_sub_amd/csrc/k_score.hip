@@ -99,98 +99,6 @@ __device__ __forceinline__ void bitonic_sort(K (&x)[R]) {
 // k_score
 // ---------------------------------------------------------------------------
 
-// LDS image of a block of KB sub-key rows, in 16-byte chunks: chunk c of
-// block row R sits at position R*CPR + (c ^ (R & M)), M = min(CPR, 8) - 1.
-// The swizzle moves only the low three chunk bits, so the eight rows of a
-// fragment read that share a bank group land on distinct banks while the
-// fragment offsets stay a per-lane base plus constants.
-template <int CPR>
-__host__ __device__ constexpr int swz_mask() {
-    return (CPR < 8 ? CPR : 8) - 1;
-}
-
-// Per-lane byte offsets of the fragments of block row r (0..15) for lane
-// group g: fragment s of tile ct is at base[s & 1] (bf16) or base[2*(s & 1)
-// + j] (the two halves of an fp32 fragment) plus frag_imm(ct, s).
-template <int STORE, int DHS>
-struct FragBase {
-    static constexpr int CPR = 32 * DHS * Store<STORE>::kBytes / 16;
-    static constexpr int NB = (STORE == kBF16) ? 2 : 4;
-    uint32_t base[NB];
-    __device__ __forceinline__ FragBase(int r, int g) {
-        const int f = r & swz_mask<CPR>();
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            // chunk within the row for s = 0 / 1 (and half j of an fp32 fragment)
-            int c;
-            if constexpr (STORE == kBF16) c = (DHS == 1) ? g : 2 * g + q;
-            else c = (DHS == 1) ? 2 * g + (q & 1) : 4 * g + q;
-            base[q] = static_cast<uint32_t>(r * CPR + (c ^ f)) * 16u;
-        }
-    }
-    // the part of a fragment's offset that does not depend on the lane
-    static __device__ __forceinline__ constexpr uint32_t imm(int ct, int s) {
-        if constexpr (STORE == kBF16) return static_cast<uint32_t>(ct * 16 * CPR + (DHS == 1 ? 0 : 8 * (s >> 1))) * 16u;
-        else return static_cast<uint32_t>(ct * 16 * CPR + (DHS == 1 ? 0 : 16 * (s >> 1))) * 16u;
-    }
-};
-
-// Fragment s of tile ct (block rows ct*16 .. +15) from the LDS image at kb.
-template <int STORE, int DHS>
-__device__ __forceinline__ void lds_frag(Frag<STORE>& f, const unsigned char* kb, const FragBase<STORE, DHS>& fb,
-                                         int ct, int s) {
-    const uint32_t im = FragBase<STORE, DHS>::imm(ct, s);
-    if constexpr (STORE == kBF16) {
-        f.v = *reinterpret_cast<const u32x4_t*>(kb + fb.base[(DHS == 1) ? 0 : (s & 1)] + im);
-    } else {
-        const int q = (DHS == 1) ? 0 : 2 * (s & 1);
-        const float4 x = *reinterpret_cast<const float4*>(kb + fb.base[q] + im);
-        const float4 y = *reinterpret_cast<const float4*>(kb + fb.base[q + 1] + im);
-        f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
-        f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
-    }
-}
-
-// Copies sub-key rows [row0, row0 + KB) of one codebook (rows >= n are
-// skipped) into the swizzled LDS image at dst with direct global-to-LDS
-// loads: each wavefront instruction fills 64 consecutive chunk positions,
-// lane L position 64*j + L, from whatever global chunk belongs there.
-template <int STORE, int DHS, int KB>
-__device__ __forceinline__ void dma_block(unsigned char* dst, const unsigned char* Kg, int row0, int n, int wave,
-                                          int lane) {
-    constexpr int CPR = 32 * DHS * Store<STORE>::kBytes / 16;
-    constexpr int M = swz_mask<CPR>();
-    constexpr int NINST = KB * CPR / 64;
-    const unsigned char* src = Kg + static_cast<size_t>(row0) * CPR * 16;
-    const bool full = row0 + KB <= n;
-#pragma unroll
-    for (int j = 0; j < NINST; j += 4) {
-        const int jj = j + wave;
-        if (NINST % 4 == 0 || jj < NINST) {
-            const int p = 64 * jj + lane;
-            const int R = p / CPR, cs = p % CPR;
-            const uint32_t off = static_cast<uint32_t>(R * CPR + (cs ^ (R & M))) * 16u;
-            if (full || row0 + R < n)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + off), dst + 64 * jj * 16, 16,
-                                                 0, 0);
-        }
-    }
-}
-
-// f <- -2 f, exactly (a power-of-two scaling of representable values).
-__device__ __forceinline__ void frag_scale_m2(Frag<kBF16>& f) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float lo = -2.f * __uint_as_float(f.v[j] << 16);
-        const float hi = -2.f * __uint_as_float(f.v[j] & 0xffff0000u);
-        f.v[j] = pack_bf16x2(lo, hi);
-    }
-}
-__device__ __forceinline__ void frag_scale_m2(Frag<kF32>& f) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f.v[j] *= -2.f;
-}
-
 // One sweep of 64 tokens of one (sequence, head, half) against all n
 // sub-keys of that half.  MODE is a combination of kScoreSelect,
 // kScoreStats and kScoreRowStat (the latter alone).  The MFMA accumulators
@@ -281,14 +189,15 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
 
         __syncthreads();  // the previous pass is done with kbuf / ccnt
         if (SEL && pass == 1 && threadIdx.x < kTok) ccnt[threadIdx.x] = 0u;
-        dma_block<STORE, DHS, KB>(kbuf, Kg, 0, n, wave, lane);
+        dma_rows<CPR, KB, 4, false>(kbuf, Kg, CPR * 16, n, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
         for (int blk = 0; blk < nblk; ++blk) {
             const int cur = blk & 1;
             if (blk + 1 < nblk)
-                dma_block<STORE, DHS, KB>(kbuf + (cur ^ 1) * BLK_BYTES, Kg, (blk + 1) * KB, n, wave, lane);
+                dma_rows<CPR, KB, 4, false>(kbuf + (cur ^ 1) * BLK_BYTES, Kg + static_cast<size_t>(blk + 1) * KB * CPR * 16,
+                                            CPR * 16, n - (blk + 1) * KB, wave, lane);
             const unsigned char* kb = kbuf + cur * BLK_BYTES;
             float colv[KB / 16];
 #pragma unroll

@@ -97,4 +97,109 @@ __device__ __forceinline__ void mma(const Frag<kF32>& a, const Frag<kF32>& b, f3
     for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Swizzled LDS images of operand tiles, filled by direct global-to-LDS loads
+// ---------------------------------------------------------------------------
+//
+// A tile of ROWS rows of CPR 16-byte chunks is stored row after row, with
+// the chunk index of row R permuted by an xor so that the sixteen rows a
+// fragment read touches fall on distinct LDS banks:
+//   wide rows (CPR >= 8, operand rows along the MFMA k dimension):
+//     chunk c of row R at R*CPR + (c ^ (R & (min(CPR, 8) - 1)));
+//   narrow rows (CPR = 4 or 8, a transposed tile read 8 or 16 bytes at a time):
+//     chunk c of row R at R*CPR + (c ^ ((R / (16 / CPR)) & (CPR - 1))).
+
+template <int CPR>
+__host__ __device__ constexpr int swz_mask() {
+    return (CPR < 8 ? CPR : 8) - 1;
+}
+
+template <int CPR, bool NARROW>
+__device__ __forceinline__ int swz(int R) {
+    if constexpr (NARROW) return (R / (16 / CPR)) & (CPR - 1);
+    else return R & swz_mask<CPR>();
+}
+
+// Copies rows [0, ROWS) of a strided source (row R at src + R*stride bytes;
+// rows R >= nvalid are skipped and keep whatever the image held) into the
+// image at dst.  Each wavefront instruction fills 64 consecutive chunk
+// positions, lane L position 64*j + L, from the global chunk that belongs
+// there; the NW wavefronts of the workgroup take instructions in turn.
+template <int CPR, int ROWS, int NW, bool NARROW>
+__device__ __forceinline__ void dma_rows(unsigned char* dst, const unsigned char* src, uint32_t stride, int nvalid,
+                                         int wave, int lane) {
+    constexpr int NINST = ROWS * CPR / 64;
+    static_assert(NINST >= 1 && (ROWS * CPR) % 64 == 0, "tile must be a whole number of 1 KiB pieces");
+#pragma unroll
+    for (int j = 0; j < NINST; j += NW) {
+        const int jj = j + wave;
+        if (NINST % NW == 0 || jj < NINST) {
+            const int p = 64 * jj + lane;
+            const int R = p / CPR, cs = p % CPR;
+            const int c = cs ^ swz<CPR, NARROW>(R);
+            if (R < nvalid)
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const void*>(src + (static_cast<uint32_t>(R) * stride + static_cast<uint32_t>(c) * 16u)),
+                    dst + 64 * jj * 16, 16, 0, 0);
+        }
+    }
+}
+
+// Per-lane byte offsets of the k-block fragments of row r (0..15) of a wide
+// image of 32*DHS-element rows, for lane group g: fragment s of row tile ct
+// (rows 16*ct .. +15) is at base[s & 1] (bf16) or base[2*(s & 1) + j] (the
+// two 16-byte halves of an fp32 fragment) plus imm(ct, s).
+template <int STORE, int DHS>
+struct FragBase {
+    static constexpr int CPR = 32 * DHS * Store<STORE>::kBytes / 16;
+    static constexpr int NB = (STORE == kBF16) ? 2 : 4;
+    uint32_t base[NB];
+    __device__ __forceinline__ FragBase(int r, int g) {
+        const int f = swz<CPR, false>(r);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            int c;  // chunk within the row for s = 0 / 1 (and half j of an fp32 fragment)
+            if constexpr (STORE == kBF16) c = (DHS == 1) ? g : 2 * g + q;
+            else c = (DHS == 1) ? 2 * g + (q & 1) : 4 * g + q;
+            base[q] = static_cast<uint32_t>(r * CPR + (c ^ f)) * 16u;
+        }
+    }
+    static __device__ __forceinline__ constexpr uint32_t imm(int ct, int s) {
+        if constexpr (STORE == kBF16)
+            return static_cast<uint32_t>(ct * 16 * CPR + (DHS == 1 ? 0 : 8 * (s >> 1))) * 16u;
+        else
+            return static_cast<uint32_t>(ct * 16 * CPR + (DHS == 1 ? 0 : 16 * (s >> 1))) * 16u;
+    }
+};
+
+// Fragment s of row tile ct from the wide image at img.
+template <int STORE, int DHS>
+__device__ __forceinline__ void lds_frag(Frag<STORE>& f, const unsigned char* img, const FragBase<STORE, DHS>& fb,
+                                         int ct, int s) {
+    const uint32_t im = FragBase<STORE, DHS>::imm(ct, s);
+    if constexpr (STORE == kBF16) {
+        f.v = *reinterpret_cast<const u32x4_t*>(img + fb.base[(DHS == 1) ? 0 : (s & 1)] + im);
+    } else {
+        const int q = (DHS == 1) ? 0 : 2 * (s & 1);
+        const float4 x = *reinterpret_cast<const float4*>(img + fb.base[q] + im);
+        const float4 y = *reinterpret_cast<const float4*>(img + fb.base[q + 1] + im);
+        f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
+        f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
+    }
+}
+
+// f <- -2 f, exactly (a power-of-two scaling of representable values).
+__device__ __forceinline__ void frag_scale_m2(Frag<kBF16>& f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = -2.f * __uint_as_float(f.v[j] << 16);
+        const float hi = -2.f * __uint_as_float(f.v[j] & 0xffff0000u);
+        f.v[j] = pack_bf16x2(lo, hi);
+    }
+}
+__device__ __forceinline__ void frag_scale_m2(Frag<kF32>& f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] *= -2.f;
+}
+
 }  // namespace fwpkm

@@ -28,7 +28,7 @@ EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
 
 # kernel families of fwpkm_timing_read, in fwpkm_kernel order
 KERNELS = ("knorm", "score_select", "gather", "resid", "sort", "scatter", "pbar",
-           "score_stats", "score_rowstat", "kgrad", "fill", "select")
+           "score_stats", "score_rowstat", "kgrad", "fill", "select", "qt")
 
 
 class FwpkmError(RuntimeError):
