@@ -118,18 +118,15 @@ __device__ __forceinline__ void st_row(void* base, size_t off, const float (&x)[
         }
     } else {
         uint16_t* p = static_cast<uint16_t*>(base) + off;
-        uint32_t h[EPL];
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) h[i] = f32_to_bf16(x[i]);
         if constexpr (EPL == 8) {
-            *reinterpret_cast<uint4*>(p) = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                                      h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
         } else if constexpr (EPL == 4) {
-            *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
         } else if constexpr (EPL == 2) {
-            *reinterpret_cast<uint32_t*>(p) = h[0] | (h[1] << 16);
+            *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(x[0], x[1]);
         } else {
-            p[0] = static_cast<uint16_t>(h[0]);
+            p[0] = static_cast<uint16_t>(f32_to_bf16(x[0]));
         }
     }
 }
@@ -172,8 +169,8 @@ __device__ __forceinline__ size_t row_off(const ScatterArgs& a, int b, uint32_t 
 template <int STORE, int EPL>
 __device__ __forceinline__ void finish_row(const ScatterArgs& a, int b, uint32_t slot, int count, float (&v)[EPL],
                                            const float (&acc)[EPL]) {
-    // one division per row; the elements take a multiply-add
-    const float sc = a.lr / static_cast<float>(count);
+    // lr / count once per row; the elements take a multiply-add
+    const float sc = a.lr * __builtin_amdgcn_rcpf(static_cast<float>(count));
 #pragma unroll
     for (int i = 0; i < EPL; ++i) v[i] = fmaf(-sc, acc[i], v[i]);
     st_row<STORE, EPL>(a.V, row_off(a, b, slot, EPL), v);
@@ -191,7 +188,7 @@ __device__ __forceinline__ void apply_row(const ScatterArgs& a, int b, uint32_t 
 template <int STORE, int EPL>
 __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
     const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t wid = static_cast<int64_t>(blk) * 4 + wave;
     if (wid >= static_cast<int64_t>(a.B) * a.pieces) return;
     const int b = static_cast<int>(wid / a.pieces), p = static_cast<int>(wid % a.pieces);
@@ -218,52 +215,93 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
         a.pt_start[pidx] = -1;
         a.ph_end[pidx] = -1;
     }
-    const float* rb = a.r + static_cast<size_t>(b) * a.Tc * a.dv + static_cast<size_t>(lane) * EPL;
+    // per-sequence bases; row offsets within a sequence fit 32 bits
+    constexpr int ES = Store<STORE>::kBytes;
+    unsigned char* Vb = static_cast<unsigned char*>(a.V) + static_cast<size_t>(b) * a.N * a.dv * ES;
+    const unsigned char* rb = reinterpret_cast<const unsigned char*>(a.r + static_cast<size_t>(b) * a.Tc * a.dv);
+    const uint32_t vrow = static_cast<uint32_t>(a.dv * ES), rrow = static_cast<uint32_t>(a.dv * 4);
+    const uint32_t vlane = static_cast<uint32_t>(lane * EPL * ES), rlane = static_cast<uint32_t>(lane * EPL * 4);
+    auto rrow_at = [&](int j) {
+        const uint32_t t = static_cast<uint32_t>(__builtin_amdgcn_readlane(tok, j));
+        return reinterpret_cast<const float*>(rb + (t * rrow + rlane));
+    };
+    auto w_at = [&](int j) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), j)); };
 
-    int s = 0;
-    while (s < nvalid) {
-        const uint64_t tm = tb & (~0ull << s);
-        const bool ends_here = tm != 0ull;
-        const int e = ends_here ? (__ffsll(static_cast<unsigned long long>(tm)) - 1) : nvalid - 1;
-        const bool starts_here = (hb >> s) & 1ull;
-        const uint32_t slot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), s));
-        // a run wholly inside the piece: fetch its row now, so the load overlaps
-        // the residual reads below
-        // (row 0 stands in for the others; it is read, never written, for them)
+    // Runs are processed in order, software-pipelined: the row and first
+    // residual of run j+1 are requested before run j is computed and stored,
+    // so the loads do not queue behind run j's store.  Two register sets,
+    // used alternately, hold the requested data.
+    struct Pending {
+        RawRow<STORE, EPL> v;
+        float x[EPL];
+    };
+    auto run_end = [&](int s0) {
+        const uint64_t tm = tb & (~0ull << s0);
+        return tm != 0ull ? (__ffsll(static_cast<unsigned long long>(tm)) - 1) : nvalid - 1;
+    };
+    auto row_of = [&](int s0) {
+        // a run wholly inside the piece writes its row; row 0 stands in for the
+        // others (it is read, never written, for them)
+        const uint32_t slot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), s0));
+        const int e0 = run_end(s0);
+        const bool whole = ((hb >> s0) & 1ull) && ((tb >> e0) & 1ull) && slot < a.N;
+        return whole ? slot : 0u;
+    };
+    auto request = [&](int s0, Pending& pd) {
+        ld_raw<STORE, EPL>(Vb + (row_of(s0) * vrow + vlane), 0, pd.v);
+        ld_f32<EPL>(rrow_at(s0), pd.x);
+    };
+    auto finish = [&](int s0, int e, Pending& pd) {
+        const bool ends_here = (tb >> e) & 1ull;
+        const bool starts_here = (hb >> s0) & 1ull;
+        const uint32_t slot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), s0));
         const bool whole = starts_here && ends_here && slot < a.N;
-        RawRow<STORE, EPL> vraw;
-        ld_raw<STORE, EPL>(a.V, row_off(a, b, whole ? slot : 0u, EPL), vraw);
+        unsigned char* vp = Vb + (slot * vrow + vlane);
+        const float w0 = w_at(s0);
+        if (whole && e == s0) {
+            // a row read once: V - lr w r
+            float v[EPL];
+            unpack<STORE, EPL>(pd.v, v);
+            const float sw = a.lr * w0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) v[i] = fmaf(-sw, pd.x[i], v[i]);
+            st_row<STORE, EPL>(vp, 0, v);
+            if (a.n_read && lane == 0) a.n_read[static_cast<size_t>(b) * a.N + slot] = 1;
+            return;
+        }
         float acc[EPL];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-        int j = s;
+        for (int i = 0; i < EPL; ++i) acc[i] = w0 * pd.x[i];
+        int j = s0 + 1;
         for (; j + 4 <= e + 1; j += 4) {
-            float x[4][EPL];
+            float y[4][EPL];
             float ww[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int t = __builtin_amdgcn_readlane(tok, j + u);
-                ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), j + u));
-                ld_f32<EPL>(rb + static_cast<size_t>(t) * a.dv, x[u]);
+                ww[u] = w_at(j + u);
+                ld_f32<EPL>(rrow_at(j + u), y[u]);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww[u], x[u][i], acc[i]);
+                for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww[u], y[u][i], acc[i]);
         }
         for (; j <= e; ++j) {
-            float x[EPL];
-            const int t = __builtin_amdgcn_readlane(tok, j);
-            const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), j));
-            ld_f32<EPL>(rb + static_cast<size_t>(t) * a.dv, x);
+            float y[EPL];
+            const float ww = w_at(j);
+            ld_f32<EPL>(rrow_at(j), y);
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, x[i], acc[i]);
+            for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, y[i], acc[i]);
         }
         if (starts_here && ends_here) {
             if (whole) {
-                float vrow[EPL];
-                unpack<STORE, EPL>(vraw, vrow);
-                finish_row<STORE, EPL>(a, b, slot, e - s + 1, vrow, acc);
+                float v[EPL];
+                unpack<STORE, EPL>(pd.v, v);
+                const float sc = a.lr * __builtin_amdgcn_rcpf(static_cast<float>(e - s0 + 1));
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) v[i] = fmaf(-sc, acc[i], v[i]);
+                st_row<STORE, EPL>(vp, 0, v);
+                if (a.n_read && lane == 0) a.n_read[static_cast<size_t>(b) * a.N + slot] = e - s0 + 1;
             }
         } else if (!starts_here) {
             // run entering from the previous piece (it starts at lane 0)
@@ -272,8 +310,24 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
         } else {
             // run leaving into the next piece
             st_f32<EPL>(a.pt + pidx * a.dv + static_cast<size_t>(lane) * EPL, acc);
-            if (lane == 0) a.pt_start[pidx] = p0 + s;
+            if (lane == 0) a.pt_start[pidx] = p0 + s0;
         }
+    };
+
+    // (the request after the last run repeats it: every iteration issues the
+    // same loads, so the waits before a run's use count only the newer ones)
+    Pending pa, pb;
+    int s = 0;
+    if (s < nvalid) request(s, pa);
+    while (s < nvalid) {
+        int e = run_end(s);
+        request(e + 1 < nvalid ? e + 1 : s, pb);
+        finish(s, e, pa);
+        s = e + 1;
+        if (s >= nvalid) break;
+        e = run_end(s);
+        request(e + 1 < nvalid ? e + 1 : s, pa);
+        finish(s, e, pb);
         s = e + 1;
     }
 }
