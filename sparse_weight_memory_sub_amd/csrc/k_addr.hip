@@ -10,13 +10,18 @@
 //   dL/dK_i = sum_t a_ti (q_t - K_i),   a_ti = 2 (log pbar_i - m_t) / (Tc Z_t e_ti^2).
 //
 // k_kgrad: one workgroup per 64 sub-keys of one (sequence, head, half); each
-// wavefront owns 16 keys and walks the chunk's tokens in blocks of 32:
-//  1. recompute the 32x16 distance tile on the matrix cores (same fragments
-//     and order as the scoring sweep, so the values are bitwise the same);
+// wavefront owns 16 keys and walks the chunk's tokens in blocks of 32.  Each
+// block is staged in LDS twice by direct global-to-LDS loads, double-buffered:
+// the query rows (d_h-contiguous) and the same rows transposed
+// (token-contiguous, written once per chunk by k_qt).  Per block:
+//  1. recompute the 32x16 distance tile on the matrix cores (same operands,
+//     order and roundings as the scoring sweep, so the values are bitwise
+//     the same);
 //  2. form a_ti for its keys;
 //  3. accumulate sum_t a_ti q_t on the matrix cores (keys x tokens times
-//     tokens x d_h; for bf16 storage a_ti is split into a bf16 high part and
-//     a bf16 low part, two MFMAs, about 16 bits of a_ti).
+//     tokens x d_h from the transposed tile; for bf16 storage a_ti is split
+//     into a bf16 high part and a bf16 low part, two MFMAs, about 16 bits of
+//     a_ti).
 // Then K_i <- K_i - lr (sum_t a_ti q_t - (sum_t a_ti) K_i), rounded to the
 // storage type, and ||K_i||^2 of the stored key is written for the next
 // chunk's scoring.  Every key is read and written by one wavefront only.
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
             for (int sub = 0; sub < 2; ++sub) {
                 f32x4_t acc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = (tq[sub * 16 + 4 * g + i] + a.eps) + kn;
+                for (int i = 0; i < 4; ++i) acc[i] = kn;
                 Frag<STORE> A[2];
 #pragma unroll
                 for (int s = 0; s < DHS; ++s) {
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = sub * 16 + 4 * g + i;
-                    const float e = __int_as_float(max(__float_as_int(acc[i]), eps_bits));
+                    const float e = __int_as_float(max(__float_as_int((tq[row] + a.eps) + acc[i]), eps_bits));
                     const float ie = __builtin_amdgcn_rcpf(e);
                     // tokens past the chunk have 1/Z = 0; the select also drops
                     // whatever their (unfilled) query rows produced

@@ -11,8 +11,10 @@
 // tokens of one (sequence, head, half) -- 16 per wavefront, the MFMA rows --
 // and walks the sub-keys in blocks of kKB, double-buffered and copied by
 // direct global-to-LDS loads, so every sub-key row is read from L2 once per
-// 64 tokens.  The accumulators start at ||q||^2 + ||K_i||^2 + eps and the
-// query is scaled by -2, so the MFMAs leave e = eps + d directly.  Nothing
+// 64 tokens.  The accumulators start at ||K_i||^2 and the query is scaled by
+// -2, so the MFMAs leave ||K_i||^2 - 2 q.K_i, summed at the small magnitude
+// of the dot products; ||q||^2 + eps is added once at the end (one rounding
+// at the scale of ||q||^2, which may dwarf the spread of the distances).  Nothing
 // of the distance matrix is stored; each mode (a template argument) reduces
 // it in registers:
 //
@@ -101,9 +103,7 @@ __device__ __forceinline__ void bitonic_sort(K (&x)[R]) {
 
 // One sweep of 64 tokens of one (sequence, head, half) against all n
 // sub-keys of that half.  MODE is a combination of kScoreSelect,
-// kScoreStats and kScoreRowStat (the latter alone).  The MFMA accumulators
-// start at ||q||^2 + ||K_i||^2 + eps and the query fragments are scaled by
-// -2, so each accumulator ends as e = eps + d before the clamp at eps.
+// kScoreStats and kScoreRowStat (the latter alone).
 template <int STORE, int DHS, int MK, int MODE>
 __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
     constexpr int ES = Store<STORE>::kBytes;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
                 const float knv = kns[key];
                 f32x4_t acc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = qe[i] + knv;
+                for (int i = 0; i < 4; ++i) acc[i] = knv;
                 // k-blocks in pairs, the next pair's LDS reads in flight under
                 // this pair's MFMAs
                 constexpr int NP = (DHS + 1) / 2;
@@ -229,9 +229,10 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
                 float cs = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    // e = max(eps + d, eps): a signed-integer max of the bit
+                    // e = max(eps + d, eps): the large ||q||^2 enters with one
+                    // rounding at the end; a signed-integer max of the bit
                     // patterns orders these floats exactly (eps > 0)
-                    const uint32_t eb = static_cast<uint32_t>(max(__float_as_int(acc[i]), eps_bits));
+                    const uint32_t eb = static_cast<uint32_t>(max(__float_as_int(qe[i] + acc[i]), eps_bits));
                     const float e = __uint_as_float(eb);
                     if (pass == 0) {
                         if constexpr (STATS) zacc[i] += fast_rcp(e);
