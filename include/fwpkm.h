@@ -186,7 +186,9 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
  * path (gather, sort, value write) on a second stream the library creates
  * once per host thread and device (default priority); events fork it from
  * and join it back to `stream`, so when `stream` reaches the end of this
- * call everything is done.
+ * call everything is done.  While kernel timing is on (fwpkm_timing_enable),
+ * or when the environment variable FWPKM_SINGLE_STREAM is "1", both paths
+ * stay on `stream`: the same kernels in the same order, one at a time.
  */
 int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                       const void* q, const void* v, const float* g, const void* v_next,
@@ -219,8 +221,10 @@ typedef enum {
  * on != 0: from now on every kernel family launch of the calling process is
  * bracketed by a pair of HIP events recorded on the launch's stream, and the
  * accumulated totals are reset.  on == 0 stops recording (totals are kept).
- * Recording adds two event records per launch; leave it off when timing a
- * whole call.  Not thread-safe against concurrent entry-point calls.
+ * While it is on, fwpkm_forward_seq runs one kernel at a time on the caller's
+ * stream, so each recorded duration is that kernel's own.  Recording adds
+ * two event records per launch; leave it off when timing a whole call.  Not
+ * thread-safe against concurrent entry-point calls.
  */
 int fwpkm_timing_enable(int32_t on);
 

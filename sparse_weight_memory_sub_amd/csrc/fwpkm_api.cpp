@@ -519,13 +519,12 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
     // same chunk runs on a second stream of the library.  They meet at the
     // selection of each chunk, and the slot/weight lists alternate between
     // two buffers so chunk c+1's selection only waits for chunk c-1's write.
-    // FWPKM_SINGLE_STREAM=1 keeps both paths on `stream` (same work, one queue).
+    // With kernel timing on, or FWPKM_SINGLE_STREAM=1, both paths stay on
+    // `stream` (same work, one kernel at a time).
     Aux* ax = nullptr;
     HIP_TRY(aux_streams(&ax));
-    static const bool single = [] {
-        const char* e = std::getenv("FWPKM_SINGLE_STREAM");
-        return e && e[0] == '1';
-    }();
+    const char* env_single = std::getenv("FWPKM_SINGLE_STREAM");
+    const bool single = timing().on || (env_single && env_single[0] == '1');
     hipStream_t sv = single ? s : ax->sv;
     HIP_TRY(hipEventRecord(ax->ev_start, s));
     HIP_TRY(hipStreamWaitEvent(sv, ax->ev_start, 0));
