@@ -24,6 +24,28 @@ template <> struct Store<kBF16> {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// 16-byte global load / store; NT marks it non-temporal (streamed data that
+// should not displace reused lines from the caches).
+typedef __attribute__((ext_vector_type(4))) unsigned int nt_u32x4;
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    if constexpr (NT) {
+        const nt_u32x4 v = __builtin_nontemporal_load(static_cast<const nt_u32x4*>(p));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+        return *static_cast<const uint4*>(p);
+    }
+}
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+    if constexpr (NT) {
+        const nt_u32x4 x = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(x, static_cast<nt_u32x4*>(p));
+    } else {
+        *static_cast<uint4*>(p) = v;
+    }
+}
+
 // fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));

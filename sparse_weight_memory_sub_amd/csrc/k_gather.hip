@@ -17,15 +17,16 @@ namespace fwpkm {
 
 namespace {
 
-template <int STORE, int EPL>
+template <int STORE, int EPL, bool NT = false>
 __device__ __forceinline__ void ldrow(const void* base, size_t off, float (&x)[EPL]) {
     if constexpr (STORE == kF32) {
         const float* p = static_cast<const float*>(base) + off;
         if constexpr (EPL % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < EPL; i += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(p + i);
-                x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+                const uint4 v = ld16<NT>(p + i);
+                x[i] = __uint_as_float(v.x); x[i + 1] = __uint_as_float(v.y);
+                x[i + 2] = __uint_as_float(v.z); x[i + 3] = __uint_as_float(v.w);
             }
         } else if constexpr (EPL == 2) {
             const float2 v = *reinterpret_cast<const float2*>(p);
@@ -36,7 +37,7 @@ __device__ __forceinline__ void ldrow(const void* base, size_t off, float (&x)[E
     } else {
         const uint16_t* p = static_cast<const uint16_t*>(base) + off;
         if constexpr (EPL == 8) {
-            const uint4 v = *reinterpret_cast<const uint4*>(p);
+            const uint4 v = ld16<NT>(p);
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
             for (int u = 0; u < 8; ++u) {
                 const int s = __builtin_amdgcn_readlane(sl[r], j + u);
                 ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt[r]), j + u));
-                ldrow<STORE, EPL>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
+                ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
             float x[EPL];
             const int s = __builtin_amdgcn_readlane(sl[r], j);
             const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt[r]), j));
-            ldrow<STORE, EPL>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
+            ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
 #pragma unroll
             for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, x[i], acc[i]);
         }

@@ -74,7 +74,7 @@ __device__ __forceinline__ void ld_raw(const void* base, size_t off, RawRow<STOR
     if constexpr (RawRow<STORE, EPL>::kWords % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < RawRow<STORE, EPL>::kWords; i += 4) {
-            const uint4 v = *reinterpret_cast<const uint4*>(p + i);
+            const uint4 v = ld16<true>(p + i);  // each row is touched once: streamed
             x.w[i] = v.x; x.w[i + 1] = v.y; x.w[i + 2] = v.z; x.w[i + 3] = v.w;
         }
     } else if constexpr (RawRow<STORE, EPL>::kWords == 2) {
@@ -119,8 +119,8 @@ __device__ __forceinline__ void st_row(void* base, size_t off, const float (&x)[
     } else {
         uint16_t* p = static_cast<uint16_t*>(base) + off;
         if constexpr (EPL == 8) {
-            *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+            st16<true>(p, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                     pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
         } else if constexpr (EPL == 4) {
             *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
         } else if constexpr (EPL == 2) {
