@@ -74,9 +74,18 @@ __global__ __launch_bounds__(256) void k_knorm(KnormArgs a) {
     if (valid && r == 0) a.knorm[key] = x;
 }
 
-// Transposed query halves of a chunk, qT[bhh][d][t] for t < Tp (Tp = Tc
-// rounded up to 32; zeros past Tc), the token-contiguous operand of the
-// sum over tokens in k_kgrad.  64x64 tiles through LDS.
+// Transposed query halves of a chunk, qT[bhh][d][t'] for t' < Tp (Tp = Tc
+// rounded up to 32; zeros past Tc), the token-contiguous operand of the sum
+// over tokens in k_kgrad.  Within each 32-token block the tokens are stored
+// in groups of four in the order 0, 4, 1, 5, 2, 6, 3, 7 (group j = tokens
+// 4j..4j+3), so that tokens 4g..4g+3 and 16+4g..16+4g+3 -- the eight
+// k-elements lane group g of an MFMA operand holds -- are adjacent.  64x64
+// tiles through LDS.
+__host__ __device__ constexpr int qt_pos(int t) {
+    const int blk = t & ~31, grp = (t >> 2) & 7;
+    return blk + (((grp & 3) << 1) | (grp >> 2)) * 4 + (t & 3);
+}
+
 template <int STORE>
 __global__ __launch_bounds__(256) void k_qt(QtArgs a) {
     using E = typename Store<STORE>::T;
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(256) void k_qt(QtArgs a) {
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
         const int dl = ty * 16 + i, d = d0 + dl, t = t0 + tx;
-        if (d < a.dh && t < a.Tp) out[static_cast<size_t>(d) * a.Tp + t] = tile[tx][dl];
+        if (d < a.dh && t < a.Tp) out[static_cast<size_t>(d) * a.Tp + qt_pos(t)] = tile[tx][dl];
     }
 }
 
@@ -151,16 +160,17 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
     const int eps_bits = __float_as_int(a.eps);
     const FragBase<STORE, DHS> fq(r, g);
     // transposed-tile offsets of the operand column d = 16c + r: tokens 4g..4g+3
-    // and 16+4g..16+4g+3 of the block
+    // and 16+4g..16+4g+3 of the block, adjacent in the k_qt order (one 16-byte
+    // chunk for bf16, two for fp32)
     uint32_t tb0, tb1;
     {
         const int f = swz<CPRT, true>(r);
         if constexpr (STORE == kBF16) {
-            tb0 = static_cast<uint32_t>(r * CPRT + ((g >> 1) ^ f)) * 16u + 8u * (g & 1);
-            tb1 = static_cast<uint32_t>(r * CPRT + ((2 + (g >> 1)) ^ f)) * 16u + 8u * (g & 1);
-        } else {
             tb0 = static_cast<uint32_t>(r * CPRT + (g ^ f)) * 16u;
-            tb1 = static_cast<uint32_t>(r * CPRT + ((4 + g) ^ f)) * 16u;
+            tb1 = tb0;
+        } else {
+            tb0 = static_cast<uint32_t>(r * CPRT + ((2 * g) ^ f)) * 16u;
+            tb1 = static_cast<uint32_t>(r * CPRT + ((2 * g + 1) ^ f)) * 16u;
         }
     }
 
@@ -251,10 +261,8 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
                     const unsigned char* tp = cur + QB + static_cast<uint32_t>(c * 16 * CPRT * 16);
-                    const uint2 x0 = *reinterpret_cast<const uint2*>(tp + tb0);
-                    const uint2 x1 = *reinterpret_cast<const uint2*>(tp + tb1);
                     Frag<kBF16> Bq;
-                    Bq.v = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+                    Bq.v = *reinterpret_cast<const u32x4_t*>(tp + tb0);
                     mma(Ahi, Bq, gacc[c]);
                     mma(Alo, Bq, gacc[c]);
                 }

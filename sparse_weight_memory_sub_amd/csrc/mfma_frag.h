@@ -130,6 +130,7 @@ __device__ __forceinline__ void dma_rows(unsigned char* dst, const unsigned char
                                          int wave, int lane) {
     constexpr int NINST = ROWS * CPR / 64;
     static_assert(NINST >= 1 && (ROWS * CPR) % 64 == 0, "tile must be a whole number of 1 KiB pieces");
+    const bool full = nvalid >= ROWS;  // the usual case: no per-lane row check
 #pragma unroll
     for (int j = 0; j < NINST; j += NW) {
         const int jj = j + wave;
@@ -137,10 +138,13 @@ __device__ __forceinline__ void dma_rows(unsigned char* dst, const unsigned char
             const int p = 64 * jj + lane;
             const int R = p / CPR, cs = p % CPR;
             const int c = cs ^ swz<CPR, NARROW>(R);
-            if (R < nvalid)
-                __builtin_amdgcn_global_load_lds(
-                    reinterpret_cast<const void*>(src + (static_cast<uint32_t>(R) * stride + static_cast<uint32_t>(c) * 16u)),
-                    dst + 64 * jj * 16, 16, 0, 0);
+            const void* g = reinterpret_cast<const void*>(
+                src + (static_cast<uint32_t>(R) * stride + static_cast<uint32_t>(c) * 16u));
+            if (full) {
+                __builtin_amdgcn_global_load_lds(g, dst + 64 * jj * 16, 16, 0, 0);
+            } else if (R < nvalid) {
+                __builtin_amdgcn_global_load_lds(g, dst + 64 * jj * 16, 16, 0, 0);
+            }
         }
     }
 }
