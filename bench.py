@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="million")
     ap.add_argument("--passes", type=int, default=None)
-    ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the oracle sample (default 3)")
+    ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the oracle sample (default 5)")
     ap.add_argument("--cpu-chunks", type=int, default=None, help="chunks per sequence of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
@@ -129,7 +129,7 @@ def main():
 
     want_cpu = not (args.no_cpu_baseline or args.profile_only)
     if want_cpu:
-        ns = args.cpu_seqs or 3
+        ns = args.cpu_seqs or 5
         pristine = [x[:ns].cpu() for x in (K1, K2, V)]
 
     o = torch.empty((B, T, cfg.d_v), dtype=torch.float32, device=dev)
@@ -248,7 +248,7 @@ def main():
     # --- CPU oracle on a bounded sample of the same workload ---
     if want_cpu:
         import oracle
-        ns = args.cpu_seqs or 3
+        ns = args.cpu_seqs or 5
         nc = args.cpu_chunks or nchunks
         qs, vs, gs = (x[:ns].cpu() for x in (q, v, g))
         threads = oracle.num_threads()
