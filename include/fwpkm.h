@@ -183,7 +183,8 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
  *          (nullable), both from the last pass.
  * passes >= 1.
  * Streams: the key path of each chunk is enqueued on `stream`, its value
- * path (gather, sort, value write) on a second stream the library creates
+ * path (sort of the reads, then gather and value write as two half-batch
+ * launches each) on a second stream the library creates
  * once per host thread and device (default priority); events fork it from
  * and join it back to `stream`, so when `stream` reaches the end of this
  * call everything is done.  While kernel timing is on (fwpkm_timing_enable),
