@@ -10,9 +10,11 @@
 //
 // Entry e = (t*H + h)*k + j of a sequence carries key = slot id (ids outside
 // [0, N) become the sentinel N, which the scatter skips) and value = e.
-// Each pass: count (per-tile digit histograms), scan (digit-major exclusive
-// prefix over tiles), scatter (stable rank inside the tile from wavefront
-// ballots, wavefronts in order).
+// Each pass: count (per-tile digit histograms), then scatter: each tile's
+// workgroup derives its digit offsets from all tiles' histograms (elements
+// of smaller digits anywhere, plus elements of its digit in earlier tiles)
+// and places its elements by a stable rank inside the tile from wavefront
+// ballots, wavefronts in order.
 #include "fwpkm_internal.h"
 
 namespace fwpkm {
@@ -42,35 +44,42 @@ __global__ __launch_bounds__(256) void k_sort_count(SortArgs a) {
     a.counts[(static_cast<size_t>(b) * a.tiles + tile) * 256 + threadIdx.x] = hist[threadIdx.x];
 }
 
-// Exclusive prefix of counts[b][tile][digit] taken in (digit, tile) order.
-__global__ __launch_bounds__(256) void k_sort_scan(SortArgs a) {
-    __shared__ uint32_t wsum[4];
-    const int b = blockIdx.x, d = threadIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    uint32_t* col = a.counts + static_cast<size_t>(b) * a.tiles * 256 + d;
-    uint32_t s = 0u;
-    for (int t = 0; t < a.tiles; ++t) s += col[static_cast<size_t>(t) * 256];
-    const uint32_t incl = wave_incl_scan_u32(s);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t off = 0u;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    uint32_t run = off + incl - s;
-    for (int t = 0; t < a.tiles; ++t) {
-        const uint32_t c = col[static_cast<size_t>(t) * 256];
-        col[static_cast<size_t>(t) * 256] = run;
-        run += c;
-    }
-}
-
 __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
     __shared__ uint32_t cnt[4][256];
     __shared__ uint32_t toff[256];
+    __shared__ uint32_t wsum[4];
     const int tile = blockIdx.x, b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int w = 0; w < 4; ++w) cnt[w][threadIdx.x] = 0u;
-    toff[threadIdx.x] = a.counts[(static_cast<size_t>(b) * a.tiles + tile) * 256 + threadIdx.x];
+    {
+        // digit d = threadIdx.x: its total over all tiles and over the tiles
+        // before this one, then the exclusive prefix of the totals over digits
+        const uint32_t* col = a.counts + static_cast<size_t>(b) * a.tiles * 256 + threadIdx.x;
+        uint32_t tot = 0u, before = 0u;
+        int t = 0;
+        for (; t + 8 <= a.tiles; t += 8) {
+            uint32_t c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = col[static_cast<size_t>(t + u) * 256];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                tot += c[u];
+                before += (t + u < tile) ? c[u] : 0u;
+            }
+        }
+        for (; t < a.tiles; ++t) {
+            const uint32_t c = col[static_cast<size_t>(t) * 256];
+            tot += c;
+            before += (t < tile) ? c : 0u;
+        }
+        const uint32_t incl = wave_incl_scan_u32(tot);
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        uint32_t off = 0u;
+        for (int w = 0; w < wave; ++w) off += wsum[w];
+        toff[threadIdx.x] = off + incl - tot + before;
+    }
     __syncthreads();
 
     constexpr int kPerWave = kSortTile / 4;
@@ -125,7 +134,6 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
 hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.tiles), static_cast<unsigned>(a.B));
     hipLaunchKernelGGL(k_sort_count, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_sort_scan, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_sort_scatter, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
