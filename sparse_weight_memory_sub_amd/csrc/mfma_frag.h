@@ -102,22 +102,17 @@ __device__ __forceinline__ void mma(const Frag<kF32>& a, const Frag<kF32>& b, f3
 // ---------------------------------------------------------------------------
 //
 // A tile of ROWS rows of CPR 16-byte chunks is stored row after row, with
-// the chunk index of row R permuted by an xor so that the sixteen rows a
-// fragment read touches fall on distinct LDS banks:
-//   wide rows (CPR >= 8, operand rows along the MFMA k dimension):
-//     chunk c of row R at R*CPR + (c ^ (R & (min(CPR, 8) - 1)));
-//   narrow rows (CPR = 4 or 8, a transposed tile read 8 or 16 bytes at a time):
-//     chunk c of row R at R*CPR + (c ^ ((R / (16 / CPR)) & (CPR - 1))).
+// the chunk index of row R permuted by an xor, chunk c at R*CPR + (c ^ swz(R)),
+// swz(R) = R & 15 for CPR >= 16 and (R / (16 / CPR)) & (CPR - 1) for CPR = 4
+// or 8.  A 16-byte read is served sixteen lanes at a time across all banks
+// (sixteen 16-byte bank groups), and these sixteen lanes read the same chunk
+// of sixteen consecutive rows; with the swizzle those land in sixteen
+// distinct bank groups for every row width.
 
-template <int CPR>
-__host__ __device__ constexpr int swz_mask() {
-    return (CPR < 8 ? CPR : 8) - 1;
-}
-
-template <int CPR, bool NARROW>
+template <int CPR, bool NARROW = false>
 __device__ __forceinline__ int swz(int R) {
-    if constexpr (NARROW) return (R / (16 / CPR)) & (CPR - 1);
-    else return R & swz_mask<CPR>();
+    if constexpr (CPR >= 16) return R & 15;
+    else return (R / (16 / CPR)) & (CPR - 1);
 }
 
 // Copies rows [0, ROWS) of a strided source (row R at src + R*stride bytes;
@@ -137,7 +132,7 @@ __device__ __forceinline__ void dma_rows(unsigned char* dst, const unsigned char
         if (NINST % NW == 0 || jj < NINST) {
             const int p = 64 * jj + lane;
             const int R = p / CPR, cs = p % CPR;
-            const int c = cs ^ swz<CPR, NARROW>(R);
+            const int c = cs ^ swz<CPR>(R);
             const void* g = reinterpret_cast<const void*>(
                 src + (static_cast<uint32_t>(R) * stride + static_cast<uint32_t>(c) * 16u));
             if (full) {
@@ -149,23 +144,39 @@ __device__ __forceinline__ void dma_rows(unsigned char* dst, const unsigned char
     }
 }
 
-// Per-lane byte offsets of the k-block fragments of row r (0..15) of a wide
-// image of 32*DHS-element rows, for lane group g: fragment s of row tile ct
-// (rows 16*ct .. +15) is at base[s & 1] (bf16) or base[2*(s & 1) + j] (the
-// two 16-byte halves of an fp32 fragment) plus imm(ct, s).
+// Per-lane byte offsets of the k-block fragments of row r (0..15) of an
+// image of 32*DHS-element rows, for lane group g.  Fragment s = 2*sp + (s & 1)
+// (k-block pair sp) of row tile ct (rows 16*ct .. +15) starts at
+//   bf16: base[2*(s & 1) + (sp & 1)] + imm(ct, s)
+//   fp32: its two 16-byte halves at base[2*(s & 1) + j] + imm(ct, s), j = 0, 1.
+// For bf16 rows of 16 or more chunks the xor also flips bit 3 of the chunk
+// index (the low bit of sp) in rows 8..15; that is +8 or -8 chunks depending
+// on the parity of sp, so it is folded into the two bases of each parity.
 template <int STORE, int DHS>
 struct FragBase {
     static constexpr int CPR = 32 * DHS * Store<STORE>::kBytes / 16;
-    static constexpr int NB = (STORE == kBF16) ? 2 : 4;
-    uint32_t base[NB];
+    uint32_t base[4];
     __device__ __forceinline__ FragBase(int r, int g) {
-        const int f = swz<CPR, false>(r);
+        const int f = swz<CPR>(r);
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            int c;  // chunk within the row for s = 0 / 1 (and half j of an fp32 fragment)
-            if constexpr (STORE == kBF16) c = (DHS == 1) ? g : 2 * g + q;
-            else c = (DHS == 1) ? 2 * g + (q & 1) : 4 * g + q;
-            base[q] = static_cast<uint32_t>(r * CPR + (c ^ f)) * 16u;
+        for (int q = 0; q < 4; ++q) {
+            int pos;
+            if constexpr (STORE == kBF16) {
+                const int s1 = q >> 1, spp = q & 1;
+                if constexpr (DHS == 1) {
+                    pos = r * CPR + (g ^ f);
+                } else if constexpr (CPR < 16) {
+                    pos = r * CPR + ((2 * g + s1) ^ f);
+                } else {
+                    const int hb = (r >> 3) & 1;
+                    pos = r * CPR + ((2 * g + s1) ^ (r & 7)) + 8 * ((spp ^ hb) - spp);
+                }
+            } else {
+                const int s1 = q >> 1, j = q & 1;
+                if constexpr (DHS == 1) pos = r * CPR + ((2 * g + j) ^ f);
+                else pos = r * CPR + ((4 * g + 2 * s1 + j) ^ f);
+            }
+            base[q] = static_cast<uint32_t>(pos) * 16u;
         }
     }
     static __device__ __forceinline__ constexpr uint32_t imm(int ct, int s) {
@@ -176,13 +187,14 @@ struct FragBase {
     }
 };
 
-// Fragment s of row tile ct from the wide image at img.
+// Fragment s of row tile ct from the image at img.
 template <int STORE, int DHS>
 __device__ __forceinline__ void lds_frag(Frag<STORE>& f, const unsigned char* img, const FragBase<STORE, DHS>& fb,
                                          int ct, int s) {
     const uint32_t im = FragBase<STORE, DHS>::imm(ct, s);
     if constexpr (STORE == kBF16) {
-        f.v = *reinterpret_cast<const u32x4_t*>(img + fb.base[(DHS == 1) ? 0 : (s & 1)] + im);
+        const int q = (DHS == 1) ? 0 : 2 * (s & 1) + ((s >> 1) & 1);
+        f.v = *reinterpret_cast<const u32x4_t*>(img + fb.base[q] + im);
     } else {
         const int q = (DHS == 1) ? 0 : 2 * (s & 1);
         const float4 x = *reinterpret_cast<const float4*>(img + fb.base[q] + im);
