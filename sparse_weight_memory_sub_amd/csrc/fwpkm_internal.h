@@ -24,6 +24,30 @@ template <> struct Store<kBF16> {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Value of lane (lane ^ m) of a wavefront, for a stride m known at compile
+// time after unrolling: data-parallel-primitive moves inside a 16-lane row
+// for m = 1, 2, 4, 8 (quad permutes and row rotates; row_ror:n reads lane
+// (i - n) mod 16), a bit-mask swizzle for 16, a permute through the LDS
+// crossbar otherwise.
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int m) {
+    const int v = static_cast<int>(x);
+    switch (m) {
+        case 1: return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+        case 2: return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+        case 4: {
+            const int down = __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false);  // lane i - 4
+            const int up = __builtin_amdgcn_mov_dpp(v, 0x12C, 0xF, 0xF, false);    // lane i + 4
+            return static_cast<uint32_t>((__lane_id() & 4) ? down : up);
+        }
+        case 8: return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
+        case 16: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(v, 0x401F));
+        default: return static_cast<uint32_t>(__shfl_xor(v, m, 64));
+    }
+}
+__device__ __forceinline__ float xor_lane(float x, int m) {
+    return __uint_as_float(xor_lane(__float_as_uint(x), m));
+}
+
 // 16-byte global load / store; NT marks it non-temporal (streamed data that
 // should not displace reused lines from the caches).
 typedef __attribute__((ext_vector_type(4))) unsigned int nt_u32x4;

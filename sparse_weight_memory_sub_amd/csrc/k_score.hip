@@ -51,8 +51,8 @@ constexpr int kNplMax = 16;    // sub-keys per lane in a row: n <= 1024
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), m, 64);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), m, 64);
+    const uint32_t lo = xor_lane(static_cast<uint32_t>(x), m);
+    const uint32_t hi = xor_lane(static_cast<uint32_t>(x >> 32), m);
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
@@ -84,7 +84,7 @@ __device__ __forceinline__ void bitonic_sort(K (&x)[R]) {
                 for (int r = 0; r < R; ++r) {
                     K y;
                     if constexpr (sizeof(K) == 8) y = shfl_xor_u64(x[r], stride);
-                    else y = __shfl_xor(x[r], stride, 64);
+                    else y = xor_lane(x[r], stride);
                     const int p = r * W + ln;
                     const bool up = (p & size) == 0;
                     const bool lower = (ln & stride) == 0;
@@ -154,8 +154,8 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
         qsq += frag_sumsq<STORE>(A[s]);
         frag_scale_m2(A[s]);
     }
-    qsq += __shfl_xor(qsq, 16, 64);
-    qsq += __shfl_xor(qsq, 32, 64);
+    qsq += xor_lane(qsq, 16);
+    qsq += xor_lane(qsq, 32);
     if ((SEL || STATS) && a.qn && g == 0 && tv) a.qn[rowbase + tok] = qsq;
     // this lane's output rows: tokens tw0 + 4g + i
     const int eps_bits = __float_as_int(a.eps);
@@ -266,8 +266,8 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
 #pragma unroll
                 for (int ct = 0; ct < KB / 16; ++ct) {
                     float x = colv[ct];
-                    x += __shfl_xor(x, 16, 64);
-                    x += __shfl_xor(x, 32, 64);
+                    x += xor_lane(x, 16);
+                    x += xor_lane(x, 32);
                     if (g == 0) colbuf[(cur * 4 + wave) * KB + ct * 16 + r] = x;
                 }
             }
@@ -287,10 +287,10 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = zacc[i];
-                    x += __shfl_xor(x, 1, 64);
-                    x += __shfl_xor(x, 2, 64);
-                    x += __shfl_xor(x, 4, 64);
-                    x += __shfl_xor(x, 8, 64);
+                    x += xor_lane(x, 1);
+                    x += xor_lane(x, 2);
+                    x += xor_lane(x, 4);
+                    x += xor_lane(x, 8);
                     zinv[i] = rv[i] ? fast_rcp(x) : 0.f;
                     if (r == 0 && rv[i]) a.Z[rowbase + tw0 + 4 * g + i] = x;
                 }
@@ -299,10 +299,10 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = macc[i];
-                    x += __shfl_xor(x, 1, 64);
-                    x += __shfl_xor(x, 2, 64);
-                    x += __shfl_xor(x, 4, 64);
-                    x += __shfl_xor(x, 8, 64);
+                    x += xor_lane(x, 1);
+                    x += xor_lane(x, 2);
+                    x += xor_lane(x, 4);
+                    x += xor_lane(x, 8);
                     if (r == 0 && rv[i]) a.m[rowbase + tw0 + 4 * g + i] = x / zrow[i];
                 }
             }
