@@ -97,6 +97,29 @@ __device__ __forceinline__ void bitonic_sort(K (&x)[R]) {
     }
 }
 
+// Ascending bitonic sort of L independent 64-element lists, list l in x[l]
+// (element = lane).  The lists go through the network side by side, so the
+// lane exchanges of one list fill the latency of the other's.
+template <int L>
+__device__ __forceinline__ void bitonic_sort_lists(uint64_t (&x)[L]) {
+    const int ln = lane_id();
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const bool up = (ln & size) == 0;
+            const bool lower = (ln & stride) == 0;
+#pragma unroll
+            for (int l = 0; l < L; ++l) {
+                const uint64_t y = shfl_xor_u64(x[l], stride);
+                const uint64_t mn = x[l] < y ? x[l] : y;
+                const uint64_t mx = x[l] < y ? y : x[l];
+                x[l] = (lower == up) ? mn : mx;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // k_score
 // ---------------------------------------------------------------------------
@@ -499,8 +522,27 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     const int h = static_cast<int>(item % a.H);
     const int64_t bt = item / a.H;
     const int t = static_cast<int>(bt % a.Tc), b = static_cast<int>(bt / a.Tc);
-    for (int half = 0; half < 2; ++half)
-        half_topk<STORE>(a, b, t, h, half, hist[wave], buf[wave], se[wave][half], si[wave][half]);
+    const size_t row0 = (static_cast<size_t>(b * a.H + h) * 2) * a.Tc + t;  // half 0; half 1 is Tc further
+    const int c0 = a.cnt[row0], c1 = a.cnt[row0 + a.Tc];
+    if (c0 <= 64 && c1 <= 64 && a.cap >= 64) {
+        // the usual case: both lists fit one register; sort them together
+        const int lane = threadIdx.x & 63;
+        uint64_t key[2];
+        key[0] = (lane < c0) ? a.cand[row0 * a.cap + lane] : ~0ull;
+        key[1] = (lane < c1) ? a.cand[(row0 + a.Tc) * a.cap + lane] : ~0ull;
+        bitonic_sort_lists<2>(key);
+        if (lane < a.kh) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                se[wave][half][lane] = __uint_as_float(static_cast<uint32_t>(key[half] >> 32));
+                si[wave][half][lane] = static_cast<int>(key[half] & 0xffffffffu);
+            }
+        }
+        wave_sync();
+    } else {
+        for (int half = 0; half < 2; ++half)
+            half_topk<STORE>(a, b, t, h, half, hist[wave], buf[wave], se[wave][half], si[wave][half]);
+    }
     const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
     if (a.ncand <= 64) product_topk<1>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
     else if (a.ncand <= 128) product_topk<2>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
