@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void k_qt(QtArgs a) {
 __device__ __forceinline__ int tok_of(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4); }
 
 template <int STORE, int DHS>
-__global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
+__global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int DH = 32 * DHS;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
     constexpr int CPRT = 32 * ES / 16;        // chunks per transposed row (narrow image, DH rows)
     constexpr int QB = 32 * CPRQ * 16;        // bytes of one query tile
     constexpr int TB = DH * CPRT * 16;        // bytes of one transposed tile
-    constexpr int BUF = QB + TB + 3 * 32 * 4; // + qn, 1/Z, m of the 32 tokens
+    constexpr int QBUF = QB + 3 * 32 * 4;     // a query tile + qn, 1/Z, m of its 32 tokens
     const int n = a.n, H = a.H, Tc = a.Tc;
 
     const int nkb = (n + 63) / 64;
@@ -186,9 +186,14 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
     // (fixed order per key block, so the sums stay reproducible).
     const int nblk = (Tc + 31) / 32;
     auto tok_block = [&](int bi) { return ((bi + kb) % nblk) * 32; };
-    auto stage = [&](unsigned char* buf, int tb) {
+    // LDS: two query tiles (with their token statistics), used in turn, and
+    // one transposed tile
+    unsigned char* tbuf = smem + 2 * QBUF;
+    auto stage_q = [&](unsigned char* buf, int tb) {
         dma_rows<CPRQ, 32, 4, false>(buf, qbase + static_cast<size_t>(tb) * qstride, qstride, Tc - tb, wave, lane);
-        dma_rows<CPRT, DH, 4, true>(buf + QB, tbase + static_cast<size_t>(tb) * ES, tstride, DH, wave, lane);
+    };
+    auto stage_t = [&](int tb) {
+        dma_rows<CPRT, DH, 4, true>(tbuf, tbase + static_cast<size_t>(tb) * ES, tstride, DH, wave, lane);
     };
     // qn, 1/Z, m of tokens tb..tb+31 (zeros past the chunk), threads 0..95
     auto tq_load = [&](int tb) {
@@ -203,26 +208,32 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
         return x;
     };
     auto tq_store = [&](unsigned char* buf, float x) {
-        if (threadIdx.x < 96) reinterpret_cast<float*>(buf + QB + TB)[threadIdx.x] = x;
+        if (threadIdx.x < 96) reinterpret_cast<float*>(buf + QB)[threadIdx.x] = x;
     };
 
-    stage(smem, tok_block(0));
+    stage_q(smem, tok_block(0));
+    stage_t(tok_block(0));
     tq_store(smem, tq_load(tok_block(0)));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // Per block: the next query tile is requested first; the distance tile
+    // uses the current one; once every wave's part of the transposed tile
+    // has landed (barrier 1) the sum over tokens reads it; after barrier 2
+    // the next transposed tile is requested, to land under the next block's
+    // distance recompute.
     for (int bi = 0; bi < nblk; ++bi) {
-        unsigned char* cur = smem + (bi & 1) * BUF;
-        unsigned char* nxt = smem + ((bi + 1) & 1) * BUF;
+        unsigned char* cur = smem + (bi & 1) * QBUF;
+        unsigned char* nxt = smem + ((bi + 1) & 1) * QBUF;
         const int tb = tok_block(bi);
         float tqn = 0.f;
         if (bi + 1 < nblk) {
-            stage(nxt, tok_block(bi + 1));
+            stage_q(nxt, tok_block(bi + 1));
             tqn = tq_load(tok_block(bi + 1));
         }
+        float av[8];  // a_ti of this wave's keys for the block's tokens
         if (active) {
-            const float* tq = reinterpret_cast<const float*>(cur + QB + TB);
-            float av[8];
+            const float* tq = reinterpret_cast<const float*>(cur + QB);
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
                 f32x4_t acc;
@@ -246,6 +257,10 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
                     colsum += av[sub * 4 + i];
                 }
             }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the transposed tile has landed
+        __syncthreads();
+        if (active) {
             // sum_t a_ti q_t: keys x tokens (A) times tokens x d_h (B)
             if constexpr (STORE == kBF16) {
                 Frag<kBF16> Ahi, Alo;
@@ -260,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
                 Alo.v = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
-                    const unsigned char* tp = cur + QB + static_cast<uint32_t>(c * 16 * CPRT * 16);
+                    const unsigned char* tp = tbuf + static_cast<uint32_t>(c * 16 * CPRT * 16);
                     Frag<kBF16> Bq;
                     Bq.v = *reinterpret_cast<const u32x4_t*>(tp + tb0);
                     mma(Ahi, Bq, gacc[c]);
@@ -272,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
                 for (int j = 0; j < 8; ++j) A.v[j] = av[j];
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
-                    const unsigned char* tp = cur + QB + static_cast<uint32_t>(c * 16 * CPRT * 16);
+                    const unsigned char* tp = tbuf + static_cast<uint32_t>(c * 16 * CPRT * 16);
                     const float4 x0 = *reinterpret_cast<const float4*>(tp + tb0);
                     const float4 x1 = *reinterpret_cast<const float4*>(tp + tb1);
                     Frag<kF32> Bq;
@@ -283,8 +298,8 @@ __global__ __launch_bounds__(256, 2) void k_kgrad(KgradArgs a) {
             }
         }
         if (bi + 1 < nblk) tq_store(nxt, tqn);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next block has landed
-        __syncthreads();
+        __syncthreads();  // every wave is done with the transposed tile
+        if (bi + 1 < nblk) stage_t(tok_block(bi + 1));
     }
     if (!active) return;
 
@@ -327,7 +342,7 @@ template <int STORE, int DHS>
 hipError_t kgrad_t(const KgradArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int DH = 32 * DHS;
-    constexpr size_t BUF = static_cast<size_t>(32) * DH * ES + static_cast<size_t>(DH) * 32 * ES + 3 * 32 * 4;
+    constexpr size_t LDS = 2 * (static_cast<size_t>(32) * DH * ES + 3 * 32 * 4) + static_cast<size_t>(DH) * 32 * ES;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_kgrad<STORE, DHS>),
@@ -337,7 +352,7 @@ hipError_t kgrad_t(const KgradArgs& a, hipStream_t s) {
     }
     const int nkb = (a.n + 63) / 64;
     const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * nkb;
-    hipLaunchKernelGGL((k_kgrad<STORE, DHS>), dim3(grid), dim3(256), 2 * BUF, s, a);
+    hipLaunchKernelGGL((k_kgrad<STORE, DHS>), dim3(grid), dim3(256), LDS, s, a);
     return hipGetLastError();
 }
 
