@@ -153,7 +153,10 @@ int fwpkm_retrieve(const fwpkm_cfg* cfg, int32_t B, int32_t T,
  *     bitwise reproducible.
  *   addressing (K1, K2), if use_addr: over all Tc tokens, per head and
  *     half, p_t = softmax over all n sub-keys of s_t, pbar = mean_t p_t,
- *     one step of lr_k on L = -H(pbar_1) - H(pbar_2).
+ *     one step of lr_k on L = -H(pbar_1) - H(pbar_2).  pbar is summed in
+ *     tiles of 64 to 256 tokens picked from B, H, Tc and the device's
+ *     compute-unit count, so K is reproducible bit for bit for one shape
+ *     on one kind of device, and agrees to rounding across shapes.
  * Inputs:  q[B][Tc][H][d_q], tgt[B][n_tgt][d_v] (store dtype; may be NULL
  *          when n_tgt == 0), g[B][Tc] float, idx[B][Tc][H][k] int32 and
  *          w[B][Tc][H][k] float and vhat[B][Tc][d_v] float as returned by

@@ -215,7 +215,7 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         return at;
     };
     const size_t Bs = static_cast<size_t>(B), T = static_cast<size_t>(Tt);
-    const size_t ntiles = (T + kScoreTok - 1) / kScoreTok;
+    const size_t ntiles = (T + kScoreTokMin - 1) / kScoreTokMin;
     L.knorm = take(Bs * p.H * 2 * p.n * 4);
     L.qn = take(Bs * p.H * 2 * T * 4);
     if (with_iw) {
@@ -399,7 +399,11 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
         TimedLaunch tl(FWPKM_K_SWEEP_STATS, s);
         HIP_TRY(launch_score(a, p.store, s));
     }
-    PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, (Tc + kScoreTok - 1) / kScoreTok, Tc};
+    PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, 0, Tc};
+    {
+        const int tile = score_tile(B, p.H, Tc);
+        pa.ntiles = (Tc + tile - 1) / tile;
+    }
     {
         TimedLaunch tl(FWPKM_K_PBAR, s);
         HIP_TRY(launch_pbar(pa, s));

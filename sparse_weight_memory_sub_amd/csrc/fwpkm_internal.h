@@ -177,10 +177,13 @@ struct CandTable {
 
 enum ScoreMode : int {
     kScoreSelect = 1,   // candidate lists of the per-half top-k' -> cand, cnt
-    kScoreStats = 2,    // per-64-token partial sums of p over tokens -> part
+    kScoreStats = 2,    // per-tile partial sums of p over tokens -> part
     kScoreRowStat = 4,  // Z_t and m_t = sum_i p_ti log pbar_i -> Z, m
 };
-constexpr int kScoreTok = 64;   // tokens per scoring workgroup
+// Tokens per scoring workgroup, 16 per wavefront: 64, 128 or 256, chosen
+// per launch by score_tile().
+constexpr int kScoreTokMin = 64;
+constexpr int kScoreTokMax = 256;
 
 struct ScoreArgs {
     const void* q;        // token t of sequence b at q + b*q_bstride + t*H*d_q
@@ -195,10 +198,11 @@ struct ScoreArgs {
     int32_t* cnt;         // [B][H][2][Tc]       candidates found (may exceed cap)
     int cap;
     float* qn;            // [B][H][2][Tc]  ||q_half||^2
-    float* part;          // [B][H][2][ceil(Tc/64)][n]
+    float* part;          // [B][H][2][ceil(Tc/tile)][n]
     const float* lp;      // [B][H][2][n]   log pbar
     float* Z;             // [B][H][2][Tc]
     float* m;             // [B][H][2][Tc]
+    int tile;             // tokens per workgroup (set by launch_score)
 };
 
 struct SelectArgs {
@@ -325,6 +329,10 @@ struct KnormArgs {
 // launchers (each returns hipGetLastError() after enqueueing)
 // ---------------------------------------------------------------------------
 hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s);
+// Tokens per scoring workgroup for B sequences of H heads and Tc tokens on
+// the current device: the largest tile whose grid still covers every
+// compute unit, else the smallest.
+int score_tile(int B, int H, int Tc);
 hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int store, hipStream_t s);

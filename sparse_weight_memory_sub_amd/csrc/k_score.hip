@@ -7,12 +7,15 @@
 // is s = -log(eps + d).  Statistics of the addressing step (digest step 5,
 // paperlayer.ai 3.4) use p_ti = (1/e_ti) / Z_t, e = eps + d, Z_t = sum_i 1/e_ti.
 //
-// k_score streams the codebook through LDS like a GEMM: a workgroup owns 64
-// tokens of one (sequence, head, half) -- 16 per wavefront, the MFMA rows --
-// and walks the sub-keys in blocks of kKB, double-buffered and copied by
-// direct global-to-LDS loads, so every sub-key row is read from L2 once per
-// 64 tokens.  The accumulators start at ||K_i||^2 and the query is scaled by
-// -2, so the MFMAs leave ||K_i||^2 - 2 q.K_i, summed at the small magnitude
+// k_score streams the codebook through LDS like a GEMM: a workgroup owns a
+// tile of 64, 128 or 256 tokens of one (sequence, head, half) -- 16 per
+// wavefront, the MFMA rows -- and walks the sub-keys in blocks of kKB,
+// double-buffered and copied by direct global-to-LDS loads, so every sub-key
+// row is read from L2 once per tile.  The tile is the widest that still gives
+// every compute unit a workgroup: wide tiles share each staged block (and its
+// barrier) among more tokens, narrow ones spread a small batch over more CUs.
+// The accumulators start at ||K_i||^2 and the query is scaled by -2, so the
+// MFMAs leave ||K_i||^2 - 2 q.K_i, summed at the small magnitude
 // of the dot products; ||q||^2 + eps is added once at the end (one rounding
 // at the scale of ||q||^2, which may dwarf the spread of the distances).  Nothing
 // of the distance matrix is stored; each mode (a template argument) reduces
@@ -26,7 +29,7 @@
 //                 candidate list in the workspace (positions from an LDS
 //                 counter, so the list order varies; k_select sorts it).
 //  kScoreStats    pass 1 also sums Z_t = sum_i 1/e_ti (written out); pass 2
-//                 forms the per-64-token partial sums over tokens of p_ti,
+//                 forms the per-tile partial sums over tokens of p_ti,
 //                 the pieces of the chunk's marginal usage pbar.
 //  kScoreRowStat  one pass: m_t = sum_i p_ti log pbar_i, with Z_t from the
 //                 stats pass of the same chunk.
@@ -45,7 +48,6 @@ namespace {
 
 // sub-keys per LDS block: 32 bf16 or 16 fp32 rows (at most 16 KiB for d_h <= 256)
 template <int STORE> constexpr int kKB = (STORE == kBF16) ? 32 : 16;
-constexpr int kTok = 64;       // tokens per k_score workgroup
 constexpr int kNplMax = 16;    // sub-keys per lane in a row: n <= 1024
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -124,11 +126,11 @@ __device__ __forceinline__ void bitonic_sort_lists(uint64_t (&x)[L]) {
 // k_score
 // ---------------------------------------------------------------------------
 
-// One sweep of 64 tokens of one (sequence, head, half) against all n
+// One sweep of a.tile tokens of one (sequence, head, half) against all n
 // sub-keys of that half.  MODE is a combination of kScoreSelect,
 // kScoreStats and kScoreRowStat (the latter alone).
-template <int STORE, int DHS, int MK, int MODE>
-__global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
+template <int STORE, int DHS, int MK, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int KB = kKB<STORE>;
     constexpr int CPR = 32 * DHS * ES / 16;
@@ -140,12 +142,13 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* kbuf = smem;                                            // [2][BLK_BYTES]
     float* kns = reinterpret_cast<float*>(smem + 2 * BLK_BYTES);           // [n]  ||K_i||^2
-    float* colbuf = kns + a.n;                                             // [2][4][KB] (stats)
-    uint32_t* ccnt = reinterpret_cast<uint32_t*>(colbuf + (STATS ? 2 * 4 * KB : 0));  // [kTok] (select)
-    float* lps = reinterpret_cast<float*>(ccnt + (SEL ? kTok : 0));        // [n]  log pbar (row statistic)
+    constexpr int TT = 16 * NW;  // tokens of the workgroup, 16 per wavefront
+    float* colbuf = kns + a.n;                                             // [2][NW][KB] (stats)
+    uint32_t* ccnt = reinterpret_cast<uint32_t*>(colbuf + (STATS ? 2 * NW * KB : 0));  // [TT] (select)
+    float* lps = reinterpret_cast<float*>(ccnt + (SEL ? TT : 0));         // [n]  log pbar (row statistic)
 
     const int n = a.n, H = a.H, Tc = a.Tc;
-    const int ntiles = (Tc + kTok - 1) / kTok;
+    const int ntiles = (Tc + TT - 1) / TT;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = static_cast<int>(lid % ntiles);
     const int bhh = static_cast<int>(lid / ntiles);  // (b*H + h)*2 + half
@@ -153,12 +156,12 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
     const int h = bh % H, b = bh / H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int tw0 = tile * kTok + wave * 16;  // first token of this wavefront
+    const int tw0 = tile * TT + wave * 16;  // first token of this wavefront
     const int nblk = (n + KB - 1) / KB;
     const unsigned char* Kg = static_cast<const unsigned char*>(half ? a.K2 : a.K1) +
                               static_cast<size_t>(bh) * n * (32 * DHS) * ES;
     const size_t rowbase = static_cast<size_t>(bhh) * Tc;
-    for (int i = threadIdx.x; i < n; i += 256) kns[i] = a.knorm[static_cast<size_t>(bhh) * n + i];
+    for (int i = threadIdx.x; i < n; i += 64 * NW) kns[i] = a.knorm[static_cast<size_t>(bhh) * n + i];
 
     // query fragments of token tw0 + r (zero past the chunk), then -2 q
     Frag<STORE> A[DHS];
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
     float zrow[4] = {1.f, 1.f, 1.f, 1.f};  // Z_t from the workspace (row statistic)
     uint32_t tau[4] = {0u, 0u, 0u, 0u};
     if constexpr (ROW) {
-        for (int i = threadIdx.x; i < n; i += 256) lps[i] = a.lp[static_cast<size_t>(bhh) * n + i];
+        for (int i = threadIdx.x; i < n; i += 64 * NW) lps[i] = a.lp[static_cast<size_t>(bhh) * n + i];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (rv[i]) zrow[i] = a.Z[rowbase + tw0 + 4 * g + i];
@@ -211,16 +214,16 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
             for (int m = 0; m < MK; ++m) keep[i][m] = 0xffffffffu;
 
         __syncthreads();  // the previous pass is done with kbuf / ccnt
-        if (SEL && pass == 1 && threadIdx.x < kTok) ccnt[threadIdx.x] = 0u;
-        dma_rows<CPR, KB, 4, false>(kbuf, Kg, CPR * 16, n, wave, lane);
+        if (SEL && pass == 1 && static_cast<int>(threadIdx.x) < TT) ccnt[threadIdx.x] = 0u;
+        dma_rows<CPR, KB, NW, false>(kbuf, Kg, CPR * 16, n, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
         for (int blk = 0; blk < nblk; ++blk) {
             const int cur = blk & 1;
             if (blk + 1 < nblk)
-                dma_rows<CPR, KB, 4, false>(kbuf + (cur ^ 1) * BLK_BYTES, Kg + static_cast<size_t>(blk + 1) * KB * CPR * 16,
-                                            CPR * 16, n - (blk + 1) * KB, wave, lane);
+                dma_rows<CPR, KB, NW, false>(kbuf + (cur ^ 1) * BLK_BYTES, Kg + static_cast<size_t>(blk + 1) * KB * CPR * 16,
+                                             CPR * 16, n - (blk + 1) * KB, wave, lane);
             const unsigned char* kb = kbuf + cur * BLK_BYTES;
             float colv[KB / 16];
 #pragma unroll
@@ -291,15 +294,17 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
                     float x = colv[ct];
                     x += xor_lane(x, 16);
                     x += xor_lane(x, 32);
-                    if (g == 0) colbuf[(cur * 4 + wave) * KB + ct * 16 + r] = x;
+                    if (g == 0) colbuf[(cur * NW + wave) * KB + ct * 16 + r] = x;
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next block has landed
             __syncthreads();
             if (STATS && pass == 1 && threadIdx.x < KB && blk * KB + static_cast<int>(threadIdx.x) < n) {
                 // this tile's partial of pbar for the block's sub-keys, waves in order
-                const float* cb = colbuf + cur * 4 * KB + threadIdx.x;
-                const float s = ((cb[0] + cb[KB]) + cb[2 * KB]) + cb[3 * KB];
+                const float* cb = colbuf + cur * NW * KB + threadIdx.x;
+                float s = cb[0];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) s += cb[w * KB];
                 a.part[(static_cast<size_t>(bhh) * ntiles + tile) * n + blk * KB + threadIdx.x] = s;
             }
         }
@@ -351,8 +356,8 @@ __global__ __launch_bounds__(256, 4) void k_score(ScoreArgs a) {
     }
     if constexpr (SEL) {
         __syncthreads();
-        const int t = tile * kTok + static_cast<int>(threadIdx.x);
-        if (threadIdx.x < kTok && t < Tc) a.cnt[rowbase + t] = static_cast<int32_t>(ccnt[threadIdx.x]);
+        const int t = tile * TT + static_cast<int>(threadIdx.x);
+        if (static_cast<int>(threadIdx.x) < TT && t < Tc) a.cnt[rowbase + t] = static_cast<int32_t>(ccnt[threadIdx.x]);
     }
 }
 
@@ -549,25 +554,35 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
 }
 
-template <int STORE, int DHS, int MK, int MODE>
-hipError_t score_t(const ScoreArgs& a, hipStream_t s) {
+template <int STORE, int DHS, int MK, int MODE, int NW>
+hipError_t score_w(const ScoreArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int KB = kKB<STORE>;
     constexpr size_t BLK_BYTES = static_cast<size_t>(KB) * DHS * 32 * ES;
-    const size_t lds = 2 * BLK_BYTES + static_cast<size_t>(a.n) * 4 + ((MODE & kScoreStats) ? 2 * 4 * KB * 4 : 0) +
-                       ((MODE & kScoreSelect) ? kTok * 4 : 0) +
+    const size_t lds = 2 * BLK_BYTES + static_cast<size_t>(a.n) * 4 + ((MODE & kScoreStats) ? 2 * NW * KB * 4 : 0) +
+                       ((MODE & kScoreSelect) ? 16 * NW * 4 : 0) +
                        ((MODE & kScoreRowStat) ? static_cast<size_t>(a.n) * 4 : 0);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK, MODE>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK, MODE, NW>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int ntiles = (a.Tc + kTok - 1) / kTok;
+    const int ntiles = (a.Tc + 16 * NW - 1) / (16 * NW);
     const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * ntiles;
-    hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE, NW>), dim3(grid), dim3(64 * NW), lds, s, a);
     return hipGetLastError();
+}
+
+template <int STORE, int DHS, int MK, int MODE>
+hipError_t score_t(const ScoreArgs& a, hipStream_t s) {
+    switch (a.tile) {
+        case 64: return score_w<STORE, DHS, MK, MODE, 4>(a, s);
+        case 128: return score_w<STORE, DHS, MK, MODE, 8>(a, s);
+        case 256: return score_w<STORE, DHS, MK, MODE, 16>(a, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int STORE, int DHS, int MK>
@@ -612,8 +627,34 @@ int score_keep(int kh) {
 
 int score_cap(int kh) { return kh <= 32 ? 128 : 256; }
 
+int score_tile(int B, int H, int Tc) {
+    // compute units of the current device, looked up once per device
+    static int cus[64] = {};
+    int dev = 0;
+    int ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        if (cus[dev] == 0) {
+            int v = 0;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+                cus[dev] = v;
+            else
+                cus[dev] = ncu;
+        }
+        ncu = cus[dev];
+    }
+    const int span = (Tc + 15) / 16 * 16;  // no wider than the chunk
+    for (int tile = kScoreTokMax; tile > kScoreTokMin; tile >>= 1) {
+        if (tile > span) continue;
+        const long long wgs = static_cast<long long>(B) * H * 2 * ((Tc + tile - 1) / tile);
+        if (wgs >= ncu) return tile;
+    }
+    return kScoreTokMin;
+}
+
 hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s) {
-    return store == kBF16 ? score_s<kBF16>(a, s) : score_s<kF32>(a, s);
+    ScoreArgs b = a;
+    b.tile = score_tile(a.B, a.H, a.Tc);
+    return store == kBF16 ? score_s<kBF16>(b, s) : score_s<kF32>(b, s);
 }
 
 hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s) {
