@@ -196,3 +196,78 @@ def pair_p(c, q, K1, K2, slots):
     if rc != 0:
         raise ValueError("fwo_pair_p rejected its arguments")
     return P
+
+
+class Stream:
+    """Streaming (inference) reading of the layer, token by token.
+
+    [layer] A.1: a prediction never waits for its own lookahead target;
+    inference collects (q_t, target) pairs until a chunk of C is full, then
+    writes it.  [layer] E.1: the memory state carries over from one
+    sequence to the next.  Steps, per arriving token x_j:
+
+      1. with lookahead, v_j completes the pending token before it;
+      2. a pending chunk that is complete (C tokens, each with its target)
+         is written (chunk_update) before anything else reads the state;
+      3. x_j is read against the current state (retrieve) and joins the
+         pending chunk, with target v_j when lookahead is off.
+
+    flush() ends the sequences: the pending tokens are written, the last
+    one pairing with v_next when given, else without a target.  Plain
+    Python over single tokens: for small cases only.
+    """
+
+    def __init__(self, c, K1, K2, V):
+        sdt = _sdt(c)
+        self.c = c
+        self.K1 = _np(K1, sdt).copy()
+        self.K2 = _np(K2, sdt).copy()
+        self.V = _np(V, sdt).copy()
+        self.pend = []  # per pending token: dict(q, g, idx, w, vhat, tgt)
+
+    def _write(self, n_tgt):
+        c, P = self.c, self.pend
+        q = np.stack([e["q"] for e in P], axis=1)
+        g = np.stack([e["g"] for e in P], axis=1)
+        idx = np.stack([e["idx"] for e in P], axis=1)
+        w = np.stack([e["w"] for e in P], axis=1)
+        vh = np.stack([e["vhat"] for e in P], axis=1)
+        tgt = np.stack([e["tgt"] for e in P[:n_tgt]], axis=1) if n_tgt > 0 else None
+        self.K1, self.K2, self.V, _ = chunk_update(c, q, g, tgt, n_tgt, idx, w, vh, self.K1, self.K2, self.V,
+                                                   want_n_read=False)
+        self.pend = []
+
+    def step(self, q, v, g):
+        """q[B,T,H,d_q], v[B,T,d_v], g[B,T] -> dict(o, vhat) of the T tokens."""
+        c = self.c
+        sdt = _sdt(c)
+        q, v = _np(q, sdt), _np(v, sdt)
+        g = _np(g, np.float32)
+        B, T = g.shape
+        o = np.zeros((B, T, c.d_v))
+        vh = np.zeros((B, T, c.d_v))
+        for j in range(T):
+            if c.lookahead and self.pend:
+                self.pend[-1]["tgt"] = v[:, j]
+            if len(self.pend) == c.chunk:
+                self._write(c.chunk)
+            r = retrieve(c, q[:, j:j + 1], v[:, j:j + 1], g[:, j:j + 1], self.K1, self.K2, self.V)
+            o[:, j] = r["o"][:, 0]
+            vh[:, j] = r["vhat"][:, 0]
+            self.pend.append({"q": q[:, j], "g": g[:, j], "idx": r["idx"][:, 0], "w": r["w"][:, 0],
+                              "vhat": r["vhat"][:, 0], "tgt": None if c.lookahead else v[:, j]})
+            if not c.lookahead and len(self.pend) == c.chunk:
+                self._write(c.chunk)
+        return {"o": o, "vhat": vh}
+
+    def flush(self, v_next=None):
+        c = self.c
+        if not self.pend:
+            return
+        n_tgt = len(self.pend)
+        if c.lookahead:
+            if v_next is not None:
+                self.pend[-1]["tgt"] = _np(v_next, _sdt(c))
+            else:
+                n_tgt -= 1
+        self._write(n_tgt)

@@ -422,6 +422,79 @@ def test_no_lookahead_uses_own_value():
     assert np.array_equal(out["V"], vv) and np.array_equal(out["K1"], k1)
 
 
+# ---------------------------------------------------------------- streaming
+def _stream_run(cfg, q, v, g, K1, K2, V, cuts, v_next=None):
+    st = oracle.Stream(cfg, K1, K2, V)
+    outs, vhs = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        r = st.step(q[:, a:b], v[:, a:b], g[:, a:b])
+        outs.append(r["o"]); vhs.append(r["vhat"])
+    st.flush(v_next)
+    return np.concatenate(outs, 1), np.concatenate(vhs, 1), st
+
+
+@pytest.mark.parametrize("look,store", [(True, "f32"), (False, "f32"), (True, "bf16")])
+def test_stream_equals_forward_seq(look, store):
+    """[layer] A.1: streaming token by token (pairs collected until the chunk
+    is full) reads and writes exactly what the chunked pass does."""
+    cfg, q, v, g, K1, K2, V = _seq_problem(T=29, C=8, store=store)
+    cfg = cfg.replace(lookahead=look)
+    full = oracle.forward_seq(cfg, q, v, g, K1, K2, V)
+    for cuts in (list(range(30)), [0, 3, 8, 9, 17, 29]):
+        o, vh, st = _stream_run(cfg, q, v, g, K1, K2, V, cuts)
+        assert np.array_equal(o, full["o"]) and np.array_equal(vh, full["vhat"])
+        for k in ("K1", "K2", "V"):
+            assert np.array_equal(getattr(st, k), full[k])
+
+
+def test_stream_writes_a_chunk_only_when_its_last_target_arrives():
+    cfg, q, v, g, K1, K2, V = _seq_problem(T=10, C=4)
+    st = oracle.Stream(cfg, K1, K2, V)
+    st.step(q[:, :4], v[:, :4], g[:, :4])
+    assert np.array_equal(st.V, V.numpy())  # chunk full, its last target not yet known
+    st.step(q[:, 4:5], v[:, 4:5], g[:, 4:5])
+    assert not np.array_equal(st.V, V.numpy())
+    c0 = cfg.replace(lookahead=False)
+    st = oracle.Stream(c0, K1, K2, V)
+    st.step(q[:, :3], v[:, :3], g[:, :3])
+    assert np.array_equal(st.V, V.numpy())
+    st.step(q[:, 3:4], v[:, 3:4], g[:, 3:4])
+    assert not np.array_equal(st.V, V.numpy())  # own-value targets: written once full
+
+
+def test_stream_prediction_does_not_wait_for_its_target():
+    """A token's output depends on tokens up to itself only."""
+    cfg, q, v, g, K1, K2, V = _seq_problem(T=12, C=4)
+    o1, _, _ = _stream_run(cfg, q, v, g, K1, K2, V, list(range(13)))
+    v2 = v.clone()
+    v2[:, 6] += 3.0
+    o2, _, _ = _stream_run(cfg, q, v2, g, K1, K2, V, list(range(13)))
+    assert np.array_equal(o1[:, :6], o2[:, :6])
+    assert not np.array_equal(o1[:, 6], o2[:, 6])
+
+
+def test_stream_carries_state_across_sequences():
+    """[layer] E.1: memory state carried over a sequence boundary."""
+    cfg, q, v, g, K1, K2, V = _seq_problem(T=30, C=8)
+    a = oracle.forward_seq(cfg, q[:, :13], v[:, :13], g[:, :13], K1, K2, V)
+    b = oracle.forward_seq(cfg, q[:, 13:], v[:, 13:], g[:, 13:], a["K1"], a["K2"], a["V"])
+    st = oracle.Stream(cfg, K1, K2, V)
+    oa = st.step(q[:, :13], v[:, :13], g[:, :13])["o"]
+    st.flush()
+    ob = np.concatenate([st.step(q[:, t:t + 1], v[:, t:t + 1], g[:, t:t + 1])["o"] for t in range(13, 30)], 1)
+    st.flush()
+    assert np.array_equal(oa, a["o"]) and np.array_equal(ob, b["o"])
+    for k in ("K1", "K2", "V"):
+        assert np.array_equal(getattr(st, k), b[k])
+    # v_next at the flush pairs the last token, as forward_seq's v_next does
+    c = oracle.forward_seq(cfg, q[:, :13], v[:, :13], g[:, :13], K1, K2, V, v_next=v[:, 13])
+    st = oracle.Stream(cfg, K1, K2, V)
+    st.step(q[:, :13], v[:, :13], g[:, :13])
+    st.flush(v[:, 13])
+    assert np.array_equal(st.V, c["V"])
+    assert not np.array_equal(st.V, a["V"])
+
+
 def test_near_tie_flag_on_duplicate_keys():
     cfg = FwpkmConfig(n=6, heads=1, d_q=4, d_v=2, k_half=2, k=2, chunk=4)
     q, v, g, K1, K2, V = _rand_problem(cfg, 1, 4, seed=6)
