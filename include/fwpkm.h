@@ -201,6 +201,65 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Streaming (inference) mode ([layer] A.1: lookahead pairs are collected
+ * until a chunk is full, so a token's prediction never waits for its own
+ * target; [layer] E.1: memory state carried across sequence boundaries).
+ *
+ * B sequences decode in lockstep, T >= 1 new tokens per call.  Each token
+ * is read against the state left by the last completed chunk write and
+ * joins the pending chunk.  With lookahead, the chunk of C pending tokens
+ * is written when the token after it arrives (that token's v is the last
+ * target), before that token is read; without lookahead it is written as
+ * soon as it is full.  fwpkm_stream_flush ends the sequences: it writes the
+ * pending tokens (the last one pairs with v_next, or has no target).  The
+ * outputs and the state after every call are those of fwpkm_forward_seq
+ * over the same tokens (one pass), whatever the split into calls.
+ *
+ * state: caller-owned device memory of fwpkm_stream_state_bytes() bytes,
+ *   256-byte aligned: the sub-key norms and the pending chunk (q, g,
+ *   targets, slot ids, weights and vhat of up to C tokens per sequence).
+ *   Needs no initialisation; keep it for the life of the stream.
+ * pos: HOST memory, read and updated at enqueue time.  pending = tokens in
+ *   the pending chunk (0 to start a stream); norms_valid = 0 makes the next
+ *   call recompute the sub-key norms (set it to 0 to start, and whenever
+ *   the caller itself changes K1 or K2).
+ * ws: at least fwpkm_workspace_bytes(cfg, B, cfg->chunk) bytes.
+ * Calls of one stream must be enqueued in order on one HIP stream.  After
+ * an FWPKM_EHIP error the stream's state is undefined.
+ */
+typedef struct {
+    int32_t pending;
+    int32_t norms_valid;
+} fwpkm_stream_pos;
+
+/* Bytes of the streaming state for B sequences. */
+int fwpkm_stream_state_bytes(const fwpkm_cfg* cfg, int32_t B, size_t* bytes);
+
+/*
+ * T new tokens of B sequences: q[B][T][H][d_q], v[B][T][d_v] (store dtype),
+ * g[B][T] float.  Outputs o[B][T][d_v] float (required), vhat[B][T][d_v]
+ * float (nullable).  K1, K2, V are updated in place by every chunk write
+ * the call triggers.
+ */
+int fwpkm_stream_step(const fwpkm_cfg* cfg, int32_t B, int32_t T,
+                      const void* q, const void* v, const float* g,
+                      void* K1, void* K2, void* V,
+                      float* o, float* vhat,
+                      void* state, fwpkm_stream_pos* pos,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * End of the B sequences: writes the pending tokens, if any.  v_next[B][d_v]
+ * (store dtype, nullable) is the value after the last token, its lookahead
+ * target.  Leaves pos->pending = 0; the state carries into the next
+ * sequences.
+ */
+int fwpkm_stream_flush(const fwpkm_cfg* cfg, int32_t B, const void* v_next,
+                       void* K1, void* K2, void* V,
+                       void* state, fwpkm_stream_pos* pos,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing (observability; not part of the method).  Kernel families
  * of the entry points above, for fwpkm_timing_read.
  */
@@ -218,7 +277,8 @@ typedef enum {
     FWPKM_K_FILL = 10,          /* zero fill of n_read                             */
     FWPKM_K_SELECT = 11,        /* per-half top-k', product top-k, weights         */
     FWPKM_K_QT = 12,            /* transposed query halves for the sub-key step    */
-    FWPKM_K_COUNT = 13
+    FWPKM_K_PEND = 13,          /* copies into a stream's pending chunk            */
+    FWPKM_K_COUNT = 14
 } fwpkm_kernel;
 
 /*

@@ -294,10 +294,9 @@ ScoreArgs score_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstr
 // Retrieval's selection of Tc tokens: candidate scoring, then per (token,
 // head) top-k' of each half and the product top-k into idx / w.
 int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
-                const void* K1, const void* K2, int32_t* idx, float* w, int64_t iw_bstride, bool stats,
-                hipStream_t s) {
-    ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, at<float>(ws, L.knorm),
-                             kScoreSelect | (stats ? kScoreStats : 0));
+                const void* K1, const void* K2, const float* knorm, int32_t* idx, float* w, int64_t iw_bstride,
+                bool stats, hipStream_t s) {
+    ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreSelect | (stats ? kScoreStats : 0));
     a.cand = at<uint64_t>(ws, L.cand);
     a.cnt = at<int32_t>(ws, L.cnt);
     a.qn = at<float>(ws, L.qn);
@@ -388,9 +387,9 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
 // Addressing step of one chunk.  With `have_stats` the chunk's usage
 // partial sums (and ||q||^2) are already in the workspace from the
 // retrieval's scoring; otherwise a stats scoring pass computes them first.
+// knorm holds ||K_i||^2 of the current codebooks; the key step rewrites it.
 int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
-            void* K1, void* K2, bool have_stats, hipStream_t s) {
-    float* knorm = at<float>(ws, L.knorm);
+            void* K1, void* K2, bool have_stats, float* knorm, hipStream_t s) {
     if (!have_stats) {
         ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreStats);
         a.qn = at<float>(ws, L.qn);
@@ -434,6 +433,122 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     return FWPKM_OK;
 }
 
+// Streaming state carve-up: sub-key norms and the pending chunk, C token
+// slots per sequence.
+struct StreamLayout {
+    size_t knorm, q, g, tgt, idx, w, vhat;
+    size_t total;
+};
+
+StreamLayout stream_layout(const Plan& p, int B) {
+    StreamLayout S{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += up(bytes);
+        return at;
+    };
+    const size_t Bs = static_cast<size_t>(B), C = static_cast<size_t>(p.C);
+    S.knorm = take(Bs * p.H * 2 * p.n * 4);
+    S.q = take(Bs * C * p.H * p.dq * p.es);
+    S.g = take(Bs * C * 4);
+    S.tgt = take(Bs * C * p.dv * p.es);
+    S.idx = take(Bs * C * p.H * p.k * 4);
+    S.w = take(Bs * C * p.H * p.k * 4);
+    S.vhat = take(Bs * C * p.dv * 4);
+    S.total = off;
+    return S;
+}
+
+size_t need_stream(const Plan& p, int B) {
+    return std::max(need_retrieve(p, B, p.C), need_update(p, B, p.C));
+}
+
+// The write of the pending chunk's first Tc tokens, n_tgt of them with
+// targets: residual, memorisation and addressing, as fwpkm_chunk_update.
+int stream_fire(const Plan& p, const StreamLayout& S, void* st, int B, int Tc, int n_tgt, void* K1, void* K2,
+                void* V, void* ws, hipStream_t s) {
+    const Layout L = layout(p, B, Tc, false, true);
+    const int64_t C = p.C;
+    if (n_tgt > 0) {
+        ResidArgs ra{at<float>(st, S.vhat), at<float>(st, S.g), at<void>(st, S.tgt), at<float>(ws, L.r),
+                     C * p.dv, C, C * p.dv, B, Tc, n_tgt, p.dv, p.znorm, p.zeps};
+        TimedLaunch tl(FWPKM_K_RESID, s);
+        HIP_TRY(launch_resid(ra, p.store, s));
+    }
+    int rc = memorise(p, L, ws, B, Tc, n_tgt, at<int32_t>(st, S.idx), at<float>(st, S.w), C * p.H * p.k, V, nullptr, s);
+    if (rc) return rc;
+    if (p.addr) {
+        rc = address(p, L, ws, B, Tc, at<void>(st, S.q), C * p.H * p.dq, K1, K2, false, at<float>(st, S.knorm), s);
+        if (rc) return rc;
+    }
+    return FWPKM_OK;
+}
+
+// Retrieval of tokens [j, j + seg) of this call (T tokens per sequence)
+// into the pending slots [pend, pend + seg), with the copies of q, g and the
+// targets that the chunk's write will need.
+int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T, int j, int seg, int pend,
+                    const void* q, const void* v, const float* g, const void* K1, const void* K2, const void* V,
+                    float* o, float* vhat, void* ws, hipStream_t s) {
+    const Layout L = layout(p, B, seg, true, false);
+    const int64_t C = p.C;
+    const size_t qrow = static_cast<size_t>(p.H) * p.dq * p.es, vrow = static_cast<size_t>(p.dv) * p.es;
+    const auto* qb = static_cast<const unsigned char*>(q);
+    const auto* vb = static_cast<const unsigned char*>(v);
+    auto* sq = at<unsigned char>(st, S.q);
+    auto* stg = at<unsigned char>(st, S.tgt);
+    const int64_t iwb = C * p.H * p.k;
+    int32_t* idx = at<int32_t>(st, S.idx) + static_cast<size_t>(pend) * p.H * p.k;
+    float* w = at<float>(st, S.w) + static_cast<size_t>(pend) * p.H * p.k;
+    int rc = select_topk(p, L, ws, B, seg, qb + j * qrow, static_cast<int64_t>(T) * p.H * p.dq, K1, K2,
+                         at<float>(st, S.knorm), idx, w, iwb, false, s);
+    if (rc) return rc;
+    GatherArgs ga{};
+    ga.V = V; ga.idx = idx; ga.w = w; ga.iw_bstride = iwb;
+    ga.v = vb + j * vrow; ga.v_bstride = static_cast<int64_t>(T) * p.dv;
+    ga.g = g + j; ga.g_bstride = T;
+    ga.o = o + static_cast<size_t>(j) * p.dv;
+    ga.vhat = vhat ? vhat + static_cast<size_t>(j) * p.dv : nullptr;
+    ga.o_bstride = static_cast<int64_t>(T) * p.dv;
+    ga.vhat2 = at<float>(st, S.vhat) + static_cast<size_t>(pend) * p.dv; ga.vhat2_bstride = C * p.dv;
+    ga.B = B; ga.Tc = seg; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
+    {
+        TimedLaunch tl(FWPKM_K_GATHER, s);
+        HIP_TRY(launch_gather(ga, p.store, s));
+    }
+    TimedLaunch tl(FWPKM_K_PEND, s);
+    HIP_TRY(launch_copy2d(sq + pend * qrow, C * qrow, qb + j * qrow, T * qrow, seg * qrow, B, s));
+    HIP_TRY(launch_copy2d(at<float>(st, S.g) + pend, C * 4, g + j, T * 4, seg * 4, B, s));
+    if (!p.look) {
+        HIP_TRY(launch_copy2d(stg + pend * vrow, C * vrow, vb + j * vrow, T * vrow, seg * vrow, B, s));
+    } else if (pend > 0) {
+        // token j completes the pair of pending token pend-1
+        HIP_TRY(launch_copy2d(stg + (pend - 1) * vrow, C * vrow, vb + j * vrow, T * vrow, seg * vrow, B, s));
+    } else if (seg > 1) {
+        HIP_TRY(launch_copy2d(stg, C * vrow, vb + (j + 1) * vrow, T * vrow, (seg - 1) * vrow, B, s));
+    }
+    return FWPKM_OK;
+}
+
+int stream_args(const fwpkm_cfg* cfg, int32_t B, void* state, fwpkm_stream_pos* pos, Plan* p) {
+    int rc = make_plan(cfg, p);
+    if (rc) return rc;
+    if (B < 0) return fail(FWPKM_EINVAL, "B must be >= 0");
+    if (!pos) return fail(FWPKM_EINVAL, "pos is NULL");
+    if (pos->pending < 0 || pos->pending > p->C)
+        return fail(FWPKM_EINVAL, "pos->pending must be in [0, chunk] (got %d)", pos->pending);
+    if (static_cast<int64_t>(B) * p->C * p->H * p->k > 2147483647LL)
+        return fail(FWPKM_EUNSUPPORTED, "B*C*heads*k too large");
+    return FWPKM_OK;
+}
+
+int check_state(const void* state) {
+    if (!state) return fail(FWPKM_EINVAL, "state is NULL");
+    if (reinterpret_cast<uintptr_t>(state) % kAlign) return fail(FWPKM_EINVAL, "state must be 256-byte aligned");
+    return FWPKM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -474,7 +589,8 @@ int fwpkm_retrieve(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, co
     int32_t* ii = idx ? idx : at<int32_t>(ws, L.idx);
     float* ww = w ? w : at<float>(ws, L.w);
     const int64_t iwb = static_cast<int64_t>(T) * p.H * p.k;
-    rc = select_topk(p, L, ws, B, T, q, static_cast<int64_t>(T) * p.H * p.dq, K1, K2, ii, ww, iwb, false, s);
+    rc = select_topk(p, L, ws, B, T, q, static_cast<int64_t>(T) * p.H * p.dq, K1, K2, at<float>(ws, L.knorm), ii, ww,
+                     iwb, false, s);
     if (rc) return rc;
     GatherArgs ga{};
     ga.V = V; ga.idx = ii; ga.w = ww; ga.iw_bstride = iwb;
@@ -508,7 +624,8 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
     hipStream_t s = static_cast<hipStream_t>(stream);
     HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     if (n_tgt > 0) {
-        ResidArgs ra{vhat, g, tgt, at<float>(ws, L.r), B, Tc, n_tgt, p.dv, p.znorm, p.zeps};
+        ResidArgs ra{vhat, g, tgt, at<float>(ws, L.r), static_cast<int64_t>(Tc) * p.dv, Tc,
+                     static_cast<int64_t>(n_tgt) * p.dv, B, Tc, n_tgt, p.dv, p.znorm, p.zeps};
         TimedLaunch tl(FWPKM_K_RESID, s);
         HIP_TRY(launch_resid(ra, p.store, s));
     }
@@ -516,7 +633,8 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
     rc = memorise(p, L, ws, B, Tc, n_tgt, idx, w, iwb, V, n_read, s);
     if (rc) return rc;
     if (p.addr) {
-        rc = address(p, L, ws, B, Tc, q, static_cast<int64_t>(Tc) * p.H * p.dq, K1, K2, false, s);
+        rc = address(p, L, ws, B, Tc, q, static_cast<int64_t>(Tc) * p.H * p.dq, K1, K2, false, at<float>(ws, L.knorm),
+                     s);
         if (rc) return rc;
     }
     return ok();
@@ -577,7 +695,7 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             // this buffer was last read by the value write two chunks ago
             if (step >= 2) HIP_TRY(hipStreamWaitEvent(s, ax->ev_write[buf], 0));
             // retrieval with the state left by the previous chunk
-            rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, idx, w, iwb, p.addr, s);
+            rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, at<float>(ws, L.knorm), idx, w, iwb, p.addr, s);
             if (rc) return rc;
             HIP_TRY(hipEventRecord(ax->ev_sel, s));
             // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
@@ -633,7 +751,7 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             HIP_TRY(hipEventRecord(ax->ev_write[buf], sv));
             // key path: addressing step of this chunk
             if (p.addr) {
-                rc = address(p, L, ws, B, Tc, qc, qb, K1, K2, true, s);
+                rc = address(p, L, ws, B, Tc, qc, qb, K1, K2, true, at<float>(ws, L.knorm), s);
                 if (rc) return rc;
             }
         }
@@ -641,6 +759,102 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
     // join: the caller's stream sees every write
     HIP_TRY(hipEventRecord(ax->ev_end, sv));
     HIP_TRY(hipStreamWaitEvent(s, ax->ev_end, 0));
+    return ok();
+}
+
+int fwpkm_stream_state_bytes(const fwpkm_cfg* cfg, int32_t B, size_t* bytes) {
+    Plan p;
+    int rc = make_plan(cfg, &p);
+    if (rc) return rc;
+    if (B < 0) return fail(FWPKM_EINVAL, "B must be >= 0");
+    if (!bytes) return fail(FWPKM_EINVAL, "bytes is NULL");
+    *bytes = B == 0 ? 0 : stream_layout(p, B).total;
+    return ok();
+}
+
+int fwpkm_stream_step(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, const void* v, const float* g,
+                      void* K1, void* K2, void* V, float* o, float* vhat, void* state, fwpkm_stream_pos* pos,
+                      void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int rc = stream_args(cfg, B, state, pos, &p);
+    if (rc) return rc;
+    if (T < 0) return fail(FWPKM_EINVAL, "T must be >= 0");
+    if (B == 0 || T == 0) return ok();
+    if (!q || !v || !g || !K1 || !K2 || !V || !o) return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V and o are required");
+    rc = check_state(state);
+    if (rc) return rc;
+    rc = check_ws(ws, ws_bytes, need_stream(p, B));
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const StreamLayout S = stream_layout(p, B);
+    if (!pos->norms_valid) {
+        HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(state, S.knorm), s));
+        pos->norms_valid = 1;
+    }
+    const size_t vrow = static_cast<size_t>(p.dv) * p.es;
+    int pend = pos->pending;
+    for (int j = 0; j < T;) {
+        if (pend == p.C) {
+            // a full chunk; with lookahead token j is its last token's target
+            if (p.look)
+                HIP_TRY(launch_copy2d(at<unsigned char>(state, S.tgt) + (pend - 1) * vrow,
+                                      static_cast<int64_t>(p.C) * vrow,
+                                      static_cast<const unsigned char*>(v) + static_cast<size_t>(j) * vrow,
+                                      static_cast<int64_t>(T) * vrow, vrow, B, s));
+            rc = stream_fire(p, S, state, B, p.C, p.C, K1, K2, V, ws, s);
+            if (rc) return rc;
+            pend = 0;
+        }
+        const int seg = std::min(T - j, p.C - pend);
+        rc = stream_retrieve(p, S, state, B, T, j, seg, pend, q, v, g, K1, K2, V, o, vhat, ws, s);
+        if (rc) return rc;
+        pend += seg;
+        j += seg;
+        pos->pending = pend;
+        if (!p.look && pend == p.C) {
+            rc = stream_fire(p, S, state, B, p.C, p.C, K1, K2, V, ws, s);
+            if (rc) return rc;
+            pend = 0;
+            pos->pending = 0;
+        }
+    }
+    return ok();
+}
+
+int fwpkm_stream_flush(const fwpkm_cfg* cfg, int32_t B, const void* v_next, void* K1, void* K2, void* V,
+                       void* state, fwpkm_stream_pos* pos, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int rc = stream_args(cfg, B, state, pos, &p);
+    if (rc) return rc;
+    if (B == 0 || pos->pending == 0) {
+        pos->pending = 0;
+        return ok();
+    }
+    if (!K1 || !K2 || !V) return fail(FWPKM_EINVAL, "K1, K2 and V are required");
+    rc = check_state(state);
+    if (rc) return rc;
+    rc = check_ws(ws, ws_bytes, need_stream(p, B));
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const StreamLayout S = stream_layout(p, B);
+    if (!pos->norms_valid) {
+        HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(state, S.knorm), s));
+        pos->norms_valid = 1;
+    }
+    const int pend = pos->pending;
+    int n_tgt = pend;
+    if (p.look) {
+        if (v_next) {
+            const size_t vrow = static_cast<size_t>(p.dv) * p.es;
+            HIP_TRY(launch_copy2d(at<unsigned char>(state, S.tgt) + (pend - 1) * vrow,
+                                  static_cast<int64_t>(p.C) * vrow, v_next, static_cast<int64_t>(vrow), vrow, B, s));
+        } else {
+            n_tgt = pend - 1;
+        }
+    }
+    rc = stream_fire(p, S, state, B, pend, n_tgt, K1, K2, V, ws, s);
+    if (rc) return rc;
+    pos->pending = 0;
     return ok();
 }
 

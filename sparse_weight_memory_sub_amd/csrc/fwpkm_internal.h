@@ -242,6 +242,8 @@ struct GatherArgs {
     float* vhat;          // nullable, same layout as o
     int64_t o_bstride;
     float* r;             // nullable: residual [B][Tc][dv] when given
+    float* vhat2;         // nullable: a second copy of vhat at vhat2 + b*vhat2_bstride + t*dv
+    int64_t vhat2_bstride;
     int B, Tc, H, k, dv;
     int64_t N;
     int znorm;
@@ -249,10 +251,11 @@ struct GatherArgs {
 };
 
 struct ResidArgs {        // r = g (vhat - z(tgt)) for t < n_tgt
-    const float* vhat;    // [B][Tc][dv]
-    const float* g;       // [B][Tc]
-    const void* tgt;      // [B][n_tgt][dv]
+    const float* vhat;    // vhat + b*vhat_bstride + t*dv
+    const float* g;       // g + b*g_bstride + t
+    const void* tgt;      // tgt + b*tgt_bstride + t*dv
     float* r;             // [B][Tc][dv]
+    int64_t vhat_bstride, g_bstride, tgt_bstride;
     int B, Tc, n_tgt, dv, znorm;
     float znorm_eps;
 };
@@ -340,6 +343,9 @@ hipError_t launch_resid(const ResidArgs& a, int store, hipStream_t s);
 hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, int store, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t s);
+// height rows of width_bytes (a multiple of 4) from src + y*spitch to dst + y*dpitch
+hipError_t launch_copy2d(void* dst, int64_t dpitch, const void* src, int64_t spitch, int64_t width_bytes,
+                         int64_t height, hipStream_t s);
 hipError_t launch_pbar(const PbarArgs& a, hipStream_t s);
 hipError_t launch_qt(const QtArgs& a, int store, hipStream_t s);
 hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s);

@@ -156,6 +156,8 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
         stf<EPL>(a.o + oo, o);
         if (a.vhat) stf<EPL>(a.vhat + oo, vh);
     }
+    if (a.vhat2)
+        stf<EPL>(a.vhat2 + static_cast<size_t>(b) * a.vhat2_bstride + static_cast<size_t>(t) * a.dv + col, vh);
     if (a.r && t < a.n_tgt) {
         float y[EPL];
         if (a.tgt_last && t == a.Tc - 1)
@@ -178,10 +180,10 @@ __global__ __launch_bounds__(256) void k_resid(ResidArgs a) {
     const int b = static_cast<int>(tok / a.n_tgt), t = static_cast<int>(tok % a.n_tgt);
     const size_t col = static_cast<size_t>(lane) * EPL;
     float y[EPL], vh[EPL];
-    ldrow<STORE, EPL>(a.tgt, (static_cast<size_t>(b) * a.n_tgt + t) * a.dv + col, y);
+    ldrow<STORE, EPL>(a.tgt, static_cast<size_t>(b) * a.tgt_bstride + static_cast<size_t>(t) * a.dv + col, y);
     if (a.znorm) zscore<EPL>(y, a.dv, a.znorm_eps);
-    ldrow<kF32, EPL>(a.vhat, (static_cast<size_t>(b) * a.Tc + t) * a.dv + col, vh);
-    const float gt = a.g[static_cast<size_t>(b) * a.Tc + t];
+    ldrow<kF32, EPL>(a.vhat, static_cast<size_t>(b) * a.vhat_bstride + static_cast<size_t>(t) * a.dv + col, vh);
+    const float gt = a.g[static_cast<size_t>(b) * a.g_bstride + t];
     float rr[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) rr[i] = gt * (vh[i] - y[i]);

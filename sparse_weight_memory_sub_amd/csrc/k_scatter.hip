@@ -365,6 +365,19 @@ __global__ void k_fill_i32(int32_t* p, int64_t count, int32_t value) {
     for (int64_t j = i; j < count; j += stride) p[j] = value;
 }
 
+// 2-D copy in 16-byte or 4-byte words (grid-stride over height x words).
+template <typename W>
+__global__ void k_copy2d(unsigned char* dst, int64_t dpitch, const unsigned char* src, int64_t spitch,
+                         int64_t words, int64_t height) {
+    const int64_t total = words * height;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t y = i / words, x = i - y * words;
+        *reinterpret_cast<W*>(dst + y * dpitch + x * static_cast<int64_t>(sizeof(W))) =
+            *reinterpret_cast<const W*>(src + y * spitch + x * static_cast<int64_t>(sizeof(W)));
+    }
+}
+
 template <int STORE, int EPL>
 hipError_t scatter_t(const ScatterArgs& a, hipStream_t s) {
     const int64_t waves = static_cast<int64_t>(a.B) * a.pieces;
@@ -396,6 +409,26 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t
     int64_t blocks = (count + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, count, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy2d(void* dst, int64_t dpitch, const void* src, int64_t spitch, int64_t width_bytes,
+                         int64_t height, hipStream_t s) {
+    if (width_bytes <= 0 || height <= 0) return hipSuccess;
+    if (width_bytes % 4) return hipErrorInvalidValue;
+    auto* d = static_cast<unsigned char*>(dst);
+    const auto* sp = static_cast<const unsigned char*>(src);
+    const bool wide = width_bytes % 16 == 0 && dpitch % 16 == 0 && spitch % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(d) % 16 == 0 && reinterpret_cast<uintptr_t>(sp) % 16 == 0;
+    const int64_t words = width_bytes / (wide ? 16 : 4);
+    int64_t blocks = (words * height + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (wide)
+        hipLaunchKernelGGL(k_copy2d<uint4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, d, dpitch, sp,
+                           spitch, words, height);
+    else
+        hipLaunchKernelGGL(k_copy2d<uint32_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, d, dpitch, sp,
+                           spitch, words, height);
     return hipGetLastError();
 }
 

@@ -24,11 +24,12 @@ _STATUS = {OK: "FWPKM_OK", EINVAL: "FWPKM_EINVAL", EUNSUPPORTED: "FWPKM_EUNSUPPO
 
 EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
            "fwpkm_retrieve", "fwpkm_chunk_update", "fwpkm_forward_seq",
+           "fwpkm_stream_state_bytes", "fwpkm_stream_step", "fwpkm_stream_flush",
            "fwpkm_timing_enable", "fwpkm_timing_read")
 
 # kernel families of fwpkm_timing_read, in fwpkm_kernel order
 KERNELS = ("knorm", "score_select", "gather", "resid", "sort", "scatter", "pbar",
-           "score_stats", "score_rowstat", "kgrad", "fill", "select", "qt")
+           "score_stats", "score_rowstat", "kgrad", "fill", "select", "qt", "pend")
 
 
 class FwpkmError(RuntimeError):
@@ -46,6 +47,11 @@ class Cfg(ctypes.Structure):
         ("lookahead", ctypes.c_int32), ("znorm", ctypes.c_int32),
         ("znorm_eps", ctypes.c_float), ("use_addr", ctypes.c_int32),
     ]
+
+
+class StreamPos(ctypes.Structure):
+    """fwpkm_stream_pos: host-side position of a decode stream."""
+    _fields_ = [("pending", ctypes.c_int32), ("norms_valid", ctypes.c_int32)]
 
 
 def cfg_struct(c: FwpkmConfig) -> Cfg:
@@ -72,9 +78,14 @@ def load(path: str = LIB_PATH):
         lib.fwpkm_retrieve.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_chunk_update.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_forward_seq.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P]
+        SP = ctypes.POINTER(StreamPos)
+        lib.fwpkm_stream_state_bytes.argtypes = [C, i32, ctypes.POINTER(sz)]
+        lib.fwpkm_stream_step.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, SP, P, sz, P]
+        lib.fwpkm_stream_flush.argtypes = [C, i32, P, P, P, P, P, SP, P, sz, P]
         lib.fwpkm_timing_enable.argtypes = [i32]
         lib.fwpkm_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq,
+                  lib.fwpkm_stream_state_bytes, lib.fwpkm_stream_step, lib.fwpkm_stream_flush,
                   lib.fwpkm_timing_enable, lib.fwpkm_timing_read):
             f.restype = ctypes.c_int
         _lib = lib
@@ -222,3 +233,61 @@ def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_n
                                     _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat), _ptr(ws), wsb,
                                     _stream(stream)))
     return {"o": o, "vhat": vhat}
+
+
+def stream_state_bytes(cfg: FwpkmConfig, B: int) -> int:
+    out = ctypes.c_size_t(0)
+    c = cfg_struct(cfg)
+    _check(load().fwpkm_stream_state_bytes(ctypes.byref(c), int(B), ctypes.byref(out)))
+    return int(out.value)
+
+
+def stream_state(cfg: FwpkmConfig, B: int, device) -> tuple:
+    """A fresh (state, pos) pair for fwpkm_stream_step: device state of
+    stream_state_bytes() bytes and a StreamPos with nothing pending."""
+    state = torch.empty(max(stream_state_bytes(cfg, B), 256), dtype=torch.uint8, device=device)
+    return state, StreamPos(0, 0)
+
+
+def fwpkm_stream_step(cfg: FwpkmConfig, q, v, g, K1, K2, V, state, pos: StreamPos, o=None, vhat=None,
+                      ws=None, stream=None, want_vhat: bool = False):
+    """T new tokens of a decode stream; K1, K2, V updated by the chunk writes
+    the call triggers, pos advanced.  Returns dict(o, vhat)."""
+    sd = cfg.torch_dtype
+    B, T = g.shape
+    H, dq, dv = cfg.heads, cfg.d_q, cfg.d_v
+    dev = g.device
+    _dev(q, "q", sd, (B, T, H, dq)); _dev(v, "v", sd, (B, T, dv)); _dev(g, "g", torch.float32, (B, T))
+    _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
+    _dev(V, "V", sd, (B, cfg.N, dv))
+    _dev(state, "state", torch.uint8, (state.numel(),))
+    if state.numel() < stream_state_bytes(cfg, B):
+        raise ValueError("state is smaller than stream_state_bytes()")
+    o = torch.empty((B, T, dv), dtype=torch.float32, device=dev) if o is None else o
+    _dev(o, "o", torch.float32, (B, T, dv))
+    if vhat is None and want_vhat:
+        vhat = torch.empty((B, T, dv), dtype=torch.float32, device=dev)
+    if vhat is not None:
+        _dev(vhat, "vhat", torch.float32, (B, T, dv))
+    ws, wsb = _workspace(cfg, B, cfg.chunk, ws, dev)
+    c = cfg_struct(cfg)
+    _check(load().fwpkm_stream_step(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2), _ptr(V),
+                                    _ptr(o), _ptr(vhat), _ptr(state), ctypes.byref(pos), _ptr(ws), wsb,
+                                    _stream(stream)))
+    return {"o": o, "vhat": vhat}
+
+
+def fwpkm_stream_flush(cfg: FwpkmConfig, K1, K2, V, state, pos: StreamPos, v_next=None, ws=None, stream=None):
+    """End of the stream's sequences: writes the pending tokens."""
+    sd = cfg.torch_dtype
+    B = V.shape[0]
+    H, dq, dv = cfg.heads, cfg.d_q, cfg.d_v
+    _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
+    _dev(V, "V", sd, (B, cfg.N, dv))
+    _dev(state, "state", torch.uint8, (state.numel(),))
+    if v_next is not None:
+        _dev(v_next, "v_next", sd, (B, dv))
+    ws, wsb = _workspace(cfg, B, cfg.chunk, ws, V.device)
+    c = cfg_struct(cfg)
+    _check(load().fwpkm_stream_flush(ctypes.byref(c), B, _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(state),
+                                     ctypes.byref(pos), _ptr(ws), wsb, _stream(stream)))

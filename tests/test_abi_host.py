@@ -153,3 +153,52 @@ def test_empty_calls_are_noops():
                    None, None, None, 0, None) == fwpkm.OK
         assert _rc("fwpkm_forward_seq", ctypes.byref(c), B, T, 1, None, None, None, None, None, None, None, None,
                    None, None, 0, None) == fwpkm.OK
+
+
+def test_stream_state_bytes_cover_the_pending_chunk():
+    c = fwpkm.cfg_struct(GOOD)
+    out = ctypes.c_size_t(0)
+    assert _rc("fwpkm_stream_state_bytes", ctypes.byref(c), 3, ctypes.byref(out)) == fwpkm.OK
+    B, C, H, n, dq, dv, k = 3, GOOD.chunk, GOOD.heads, GOOD.n, GOOD.d_q, GOOD.d_v, GOOD.k
+    es = 4  # f32 storage
+    # norms, then q, g, targets, slot ids, weights and vhat of C tokens per sequence
+    floor = B * H * 2 * n * 4 + B * C * (H * dq * es + 4 + dv * es + 2 * H * k * 4 + dv * 4)
+    assert floor <= out.value <= floor + 7 * 256
+    assert _rc("fwpkm_stream_state_bytes", ctypes.byref(c), 0, ctypes.byref(out)) == fwpkm.OK
+    assert out.value == 0
+    assert _rc("fwpkm_stream_state_bytes", ctypes.byref(c), -1, ctypes.byref(out)) == fwpkm.EINVAL
+
+
+def test_stream_entry_points_reject_before_launch():
+    c = fwpkm.cfg_struct(GOOD)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    pos = fwpkm.StreamPos(0, 0)
+
+    def step(B, T, q, o, state, p, ws, wsb):
+        return _rc("fwpkm_stream_step", ctypes.byref(c), B, T, q, fake, fake, fake, fake, fake, o, None, state,
+                   p, ws, wsb, None)
+
+    assert step(1, 1, fake, fake, fake, None, fake, 1 << 30) == fwpkm.EINVAL          # pos NULL
+    assert step(1, 1, None, fake, fake, ctypes.byref(pos), fake, 1 << 30) == fwpkm.EINVAL  # q missing
+    assert step(1, 1, fake, None, fake, ctypes.byref(pos), fake, 1 << 30) == fwpkm.EINVAL  # o missing
+    assert step(1, 1, fake, fake, None, ctypes.byref(pos), fake, 1 << 30) == fwpkm.EINVAL  # state missing
+    assert step(1, 1, fake, fake, ctypes.c_void_p(0x1010), ctypes.byref(pos), fake, 1 << 30) == fwpkm.EINVAL
+    assert step(1, 1, fake, fake, fake, ctypes.byref(pos), fake, 16) == fwpkm.EWORKSPACE
+    assert step(1, -1, fake, fake, fake, ctypes.byref(pos), fake, 1 << 30) == fwpkm.EINVAL
+    for bad in (-1, GOOD.chunk + 1):
+        p = fwpkm.StreamPos(bad, 0)
+        assert step(1, 1, fake, fake, fake, ctypes.byref(p), fake, 1 << 30) == fwpkm.EINVAL
+        assert "pending" in fwpkm.load().fwpkm_last_error().decode()
+    # empty calls are no-ops and leave the position alone
+    p = fwpkm.StreamPos(5, 0)
+    assert step(0, 1, None, None, None, ctypes.byref(p), None, 0) == fwpkm.OK
+    assert step(2, 0, None, None, None, ctypes.byref(p), None, 0) == fwpkm.OK
+    assert (p.pending, p.norms_valid) == (5, 0)
+    # a flush with nothing pending launches nothing
+    p = fwpkm.StreamPos(0, 0)
+    assert _rc("fwpkm_stream_flush", ctypes.byref(c), 2, None, None, None, None, fake, ctypes.byref(p), None, 0,
+               None) == fwpkm.OK
+    p = fwpkm.StreamPos(3, 0)
+    assert _rc("fwpkm_stream_flush", ctypes.byref(c), 2, None, None, fake, fake, fake, ctypes.byref(p), fake,
+               1 << 30, None) == fwpkm.EINVAL  # K1 missing
+    assert p.pending == 3
