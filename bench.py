@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed steps (for profilers): no kernel timing pass, no CPU baseline")
+    ap.add_argument("--decode", action="store_true",
+                    help="time streaming decode (one token per call per sequence) instead of forward_seq")
+    ap.add_argument("--decode-tokens", type=int, default=1024, help="timed decode tokens per sequence")
     return ap.parse_args()
 
 
@@ -101,6 +104,89 @@ def traffic_from_profiles(kernel, workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def decode_bench(args, cfg, wl, B, q, v, g, K1, K2, V):
+    """Streaming decode: every call reads one new token of each of the B
+    sequences (fwpkm_stream_step with T = 1); a chunk write fires every C
+    tokens.  Prints one JSON line."""
+    import torch
+    from sparse_weight_memory_sub_amd import fwpkm
+
+    dev = q.device
+    stream = torch.cuda.current_stream()
+    st, pos = fwpkm.stream_state(cfg, B, dev)
+    ws = torch.empty(fwpkm.workspace_bytes(cfg, B, cfg.chunk), dtype=torch.uint8, device=dev)
+    T = q.shape[1]
+    o = torch.empty((B, 1, cfg.d_v), dtype=torch.float32, device=dev)
+    cursor = [0]
+
+    # per-token inputs made contiguous once, outside the timed region
+    q = torch.stack([q[:, t:t + 1].contiguous() for t in range(T)])  # [T][B][1][H][d_q]
+    v = torch.stack([v[:, t:t + 1].contiguous() for t in range(T)])
+    g = torch.stack([g[:, t:t + 1].contiguous() for t in range(T)])
+
+    def tokens(n):
+        for _ in range(n):
+            t = cursor[0] % T
+            cursor[0] += 1
+            fwpkm.fwpkm_stream_step(cfg, q[t], v[t], g[t], K1, K2, V, st, pos, o=o, ws=ws, stream=stream)
+
+    tokens(args.warmup * cfg.chunk // 4 + 1)
+    torch.cuda.synchronize()
+    K = args.decode_tokens
+
+    def timed(events):
+        fwpkm.timing_enable(events)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        start.record(stream)
+        tokens(K)
+        stop.record(stream)
+        enq = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - h0
+        fwpkm.timing_enable(False)
+        return start.elapsed_time(stop), wall * 1e3, enq * 1e3
+
+    ms, wall_ms, enq_ms = timed(False)
+    value = B * K / (ms / 1e3)
+    log(f"decode: {K} tokens x {B} sequences in {ms:.2f} ms ({ms / K * 1e3:.1f} us per call), "
+        f"{value:.4g} tokens/s; host wall {wall_ms:.2f} ms, of which enqueueing {enq_ms:.2f} ms")
+    ms_ev, _, _ = timed(True)
+    tk = fwpkm.timing_read()
+    es = 2 if cfg.store == "bf16" else 4
+    # algorithmic bytes of one read call: both codebooks once, the selected
+    # value rows, the token's q, v and the output row
+    kbytes = B * cfg.heads * 2 * cfg.n * cfg.d_h * es
+    gbytes = B * (cfg.heads * cfg.k * (cfg.d_v * es + 8) + cfg.d_v * (es + 8) + 4)
+    kernels = {}
+    for name, (t_ms, n) in tk.items():
+        if n:
+            kernels[name] = {"avg_ms": t_ms / n, "launches": n, "per_call_ms": t_ms / K}
+    sel = kernels.get("score_select")
+    roof = None
+    if sel:
+        ach = kbytes / (sel["avg_ms"] / 1e3) / 1e9
+        roof = {"kernel": "score_select", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": kbytes,
+                "avg_launch_ms": sel["avg_ms"]}
+    result = {
+        "metric": "FwPKM streaming decode tokens/s (one token per call per sequence, chunk writes included)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.store, "data": "synthetic",
+        "config": {"workload": f"{wl.name}-decode", "n_slots": cfg.N, "heads": cfg.heads, "d_q": cfg.d_q,
+                   "d_v": cfg.d_v, "k_half": cfg.k_half, "k": cfg.k, "chunk": cfg.chunk, "batch": B,
+                   "tokens_per_call": 1, "storage": cfg.store},
+        "host_wall_ms_per_step": wall_ms / K,
+        "host_enqueue_ms_per_step": enq_ms / K,
+        "ms_per_step_with_kernel_events": ms_ev / K,
+        "read_call_algorithmic_bytes": kbytes + gbytes,
+        "roofline": roof, "kernels": kernels,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -126,6 +212,10 @@ def main():
     q, v, g = q.to(dev), v.to(dev), g.to(dev)
     log(f"workload {wl.name}: B={B} T={T} N={cfg.N} H={cfg.heads} d_q={cfg.d_q} d_v={cfg.d_v} "
         f"k={cfg.k} C={cfg.chunk} {cfg.store}; inputs ready in {time.time() - t0:.1f}s")
+
+    if args.decode:
+        decode_bench(args, cfg, wl, B, q, v, g, K1, K2, V)
+        return
 
     want_cpu = not (args.no_cpu_baseline or args.profile_only)
     if want_cpu:

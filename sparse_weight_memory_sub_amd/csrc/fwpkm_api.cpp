@@ -201,7 +201,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, r, Z, m, part, lp, qT, k0, v0, k1, v1, counts, ph, pt, pts, phe;
+    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, m, part, lp, qT, k0, v0, k1, v1, counts, ph, pt, pts,
+        phe;
     size_t total;
 };
 
@@ -227,6 +228,7 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         }
         L.cand = take(Bs * p.H * 2 * T * static_cast<size_t>(score_cap(p.kh)) * 8);
         L.cnt = take(Bs * p.H * 2 * T * 4);
+        L.erow = take(Bs * p.H * 2 * std::min<size_t>(T, kRowTok) * p.n * 4);
     }
     if (with_update) {
         const size_t M = T * p.H * p.k;
@@ -296,7 +298,12 @@ ScoreArgs score_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstr
 int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
                 const void* K1, const void* K2, const float* knorm, int32_t* idx, float* w, int64_t iw_bstride,
                 bool stats, hipStream_t s) {
-    ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreSelect | (stats ? kScoreStats : 0));
+    // a handful of tokens (decode): whole rows of e and an exact top-k' of
+    // each; otherwise the two-pass sweep with candidate lists
+    const bool rows = !stats && Tc <= kRowTok;
+    ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm,
+                             rows ? kScoreRows : (kScoreSelect | (stats ? kScoreStats : 0)));
+    if (rows) a.erow = at<uint32_t>(ws, L.erow);
     a.cand = at<uint64_t>(ws, L.cand);
     a.cnt = at<int32_t>(ws, L.cnt);
     a.qn = at<float>(ws, L.qn);
@@ -313,6 +320,7 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     sa.q = q; sa.q_bstride = q_bstride; sa.K1 = K1; sa.K2 = K2;
     sa.B = B; sa.Tc = Tc; sa.n = p.n; sa.H = p.H; sa.dh = p.dh; sa.kh = p.kh; sa.k = p.k; sa.ncand = p.ncand;
     sa.eps = p.eps; sa.idx = idx; sa.w = w; sa.iw_bstride = iw_bstride; sa.cand_ab = p.cand;
+    sa.erow = a.erow;
     {
         TimedLaunch tl(FWPKM_K_SELECT, s);
         HIP_TRY(launch_select(sa, p.store, s));
@@ -512,22 +520,17 @@ int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T
     ga.vhat = vhat ? vhat + static_cast<size_t>(j) * p.dv : nullptr;
     ga.o_bstride = static_cast<int64_t>(T) * p.dv;
     ga.vhat2 = at<float>(st, S.vhat) + static_cast<size_t>(pend) * p.dv; ga.vhat2_bstride = C * p.dv;
+    // the token's q, g and (as a target) v into the pending chunk
+    ga.q = qb + j * qrow; ga.q_bstride = static_cast<int64_t>(T) * p.H * p.dq; ga.qrow = p.H * p.dq;
+    ga.pq = sq + pend * qrow; ga.pq_bstride = C * p.H * p.dq;
+    ga.pg = at<float>(st, S.g) + pend; ga.pg_bstride = C;
+    // v of token t is the target of pending slot pend + t, or with lookahead
+    // of the slot before it (none for the first token of a chunk)
+    ga.ptgt = stg; ga.ptgt_bstride = C * p.dv;
+    ga.ptgt_shift = p.look ? pend - 1 : pend;
     ga.B = B; ga.Tc = seg; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
-    {
-        TimedLaunch tl(FWPKM_K_GATHER, s);
-        HIP_TRY(launch_gather(ga, p.store, s));
-    }
-    TimedLaunch tl(FWPKM_K_PEND, s);
-    HIP_TRY(launch_copy2d(sq + pend * qrow, C * qrow, qb + j * qrow, T * qrow, seg * qrow, B, s));
-    HIP_TRY(launch_copy2d(at<float>(st, S.g) + pend, C * 4, g + j, T * 4, seg * 4, B, s));
-    if (!p.look) {
-        HIP_TRY(launch_copy2d(stg + pend * vrow, C * vrow, vb + j * vrow, T * vrow, seg * vrow, B, s));
-    } else if (pend > 0) {
-        // token j completes the pair of pending token pend-1
-        HIP_TRY(launch_copy2d(stg + (pend - 1) * vrow, C * vrow, vb + j * vrow, T * vrow, seg * vrow, B, s));
-    } else if (seg > 1) {
-        HIP_TRY(launch_copy2d(stg, C * vrow, vb + (j + 1) * vrow, T * vrow, (seg - 1) * vrow, B, s));
-    }
+    TimedLaunch tl(FWPKM_K_GATHER, s);
+    HIP_TRY(launch_gather(ga, p.store, s));
     return FWPKM_OK;
 }
 

@@ -179,10 +179,14 @@ enum ScoreMode : int {
     kScoreSelect = 1,   // candidate lists of the per-half top-k' -> cand, cnt
     kScoreStats = 2,    // per-tile partial sums of p over tokens -> part
     kScoreRowStat = 4,  // Z_t and m_t = sum_i p_ti log pbar_i -> Z, m
+    kScoreRows = 8,     // every e_ti written out -> erow (at most kRowTok tokens)
 };
+constexpr int kRowTok = 16;  // largest chunk scored by whole rows
 // Tokens per scoring workgroup, 16 per wavefront: 64, 128 or 256, chosen
 // per launch by score_tile().
 constexpr int kScoreTokMin = 64;
+constexpr int kGatherPart = 16;         // gather: entries summed per part (parts added in order)
+constexpr int kGatherSplitBelow = 1024; // gather: one wavefront per part below this many tokens
 constexpr int kScoreTokMax = 256;
 
 struct ScoreArgs {
@@ -202,6 +206,7 @@ struct ScoreArgs {
     const float* lp;      // [B][H][2][n]   log pbar
     float* Z;             // [B][H][2][Tc]
     float* m;             // [B][H][2][Tc]
+    uint32_t* erow;       // [B][H][2][Tc][n]  e bit patterns (rows mode)
     int tile;             // tokens per workgroup (set by launch_score)
 };
 
@@ -219,6 +224,7 @@ struct SelectArgs {
     float* w;
     int64_t iw_bstride;
     CandTable cand_ab;
+    const uint32_t* erow; // non-NULL: whole rows of e ([B][H][2][Tc][n]) instead of candidate lists
 };
 
 int score_keep(int kh);   // smallest e kept per lane in the first scoring pass
@@ -244,6 +250,17 @@ struct GatherArgs {
     float* r;             // nullable: residual [B][Tc][dv] when given
     float* vhat2;         // nullable: a second copy of vhat at vhat2 + b*vhat2_bstride + t*dv
     int64_t vhat2_bstride;
+    // stream: copies of the token's inputs into the pending chunk (pq nullable)
+    const void* q;        // q + (b*q_bstride + t*qrow) elements
+    int64_t q_bstride;
+    int qrow;             // H*d_q
+    void* pq;             // pq + (b*pq_bstride + t*qrow) elements
+    int64_t pq_bstride;
+    float* pg;            // pg + b*pg_bstride + t
+    int64_t pg_bstride;
+    void* ptgt;           // v of token t to ptgt + (b*ptgt_bstride + (t + ptgt_shift)*dv), if >= 0
+    int64_t ptgt_bstride;
+    int ptgt_shift;
     int B, Tc, H, k, dv;
     int64_t N;
     int znorm;

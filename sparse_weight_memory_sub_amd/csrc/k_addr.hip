@@ -125,7 +125,6 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     constexpr int CPRQ = DH * ES / 16;        // chunks per query row (wide image, 32 rows)
     constexpr int CPRT = 32 * ES / 16;        // chunks per transposed row (narrow image, DH rows)
     constexpr int QB = 32 * CPRQ * 16;        // bytes of one query tile
-    constexpr int TB = DH * CPRT * 16;        // bytes of one transposed tile
     constexpr int QBUF = QB + 3 * 32 * 4;     // a query tile + qn, 1/Z, m of its 32 tokens
     const int n = a.n, H = a.H, Tc = a.Tc;
 

@@ -7,10 +7,12 @@
 // paperlayer.ai A.1, A.3, A.5): r_t = g_t (v_hat_t - y_t) with y_t the
 // z-scored lookahead target.
 //
-// One wavefront per token; lane l owns elements [l*EPL, (l+1)*EPL) of every
-// d_v-row, so each row read is one coalesced d_v*elem_bytes transaction of
-// the wavefront.  Rows are fetched eight at a time to keep several HBM reads
-// in flight per wavefront.
+// Lane l owns elements [l*EPL, (l+1)*EPL) of every d_v-row, so each row read
+// is one coalesced d_v*elem_bytes transaction of a wavefront.  A token's H*k
+// rows are summed in parts of kGatherPart consecutive entries, each part in
+// entry order, and the parts are added in order: one wavefront per token
+// for large batches (k_gather), one wavefront per part when the tokens are
+// too few to fill the chip (k_gather_split, decode); both give the same bits.
 #include "fwpkm_internal.h"
 
 namespace fwpkm {
@@ -90,61 +92,56 @@ __device__ __forceinline__ void zscore(float (&y)[EPL], int dv, float eps) {
     for (int i = 0; i < EPL; ++i) y[i] = (y[i] - mean) * inv;
 }
 
+// Rows [e0, e0 + cnt) of the token's H*k (slot, weight) entries, summed in
+// entry order into acc (this lane's EPL columns).  Entry e0 + j is held by
+// lane `base + j` of the wavefront's (sl, wt) registers.  Rows are fetched
+// eight at a time so several HBM reads are in flight.
 template <int STORE, int EPL>
-__global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t tok = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (tok >= static_cast<int64_t>(a.B) * a.Tc) return;
-    const int b = static_cast<int>(tok / a.Tc), t = static_cast<int>(tok % a.Tc);
-    const int HK = a.H * a.k;
-    const size_t ib = static_cast<size_t>(b) * a.iw_bstride + static_cast<size_t>(t) * HK;
-    // up to 4*64 (slot, weight) entries, entry e held by lane e % 64, register e / 64
-    int32_t sl[4];
-    float wt[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int e = r * 64 + lane;
-        sl[r] = (e < HK) ? a.idx[ib + e] : 0;
-        wt[r] = (e < HK) ? a.w[ib + e] : 0.f;
-    }
-    const size_t vb = static_cast<size_t>(b) * static_cast<size_t>(a.N) * a.dv;
-    const size_t col = static_cast<size_t>(lane) * EPL;
-    float acc[EPL];
+__device__ __forceinline__ void gather_part(const GatherArgs& a, size_t vb, size_t col, int32_t sl, float wt, int base,
+                                            int cnt, float (&acc)[EPL]) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-
+    int j = 0;
+    for (; j + 8 <= cnt; j += 8) {
+        float x[8][EPL];
+        float ww[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int cnt = min(64, HK - r * 64);
-        if (cnt <= 0) break;
-        int j = 0;
-        for (; j + 8 <= cnt; j += 8) {
-            float x[8][EPL];
-            float ww[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int s = __builtin_amdgcn_readlane(sl[r], j + u);
-                ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt[r]), j + u));
-                ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww[u], x[u][i], acc[i]);
+        for (int u = 0; u < 8; ++u) {
+            const int s = __builtin_amdgcn_readlane(sl, base + j + u);
+            ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), base + j + u));
+            ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
         }
-        for (; j < cnt; ++j) {
-            float x[EPL];
-            const int s = __builtin_amdgcn_readlane(sl[r], j);
-            const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt[r]), j));
-            ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, x[i], acc[i]);
-        }
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww[u], x[u][i], acc[i]);
     }
+    for (; j < cnt; ++j) {
+        float x[EPL];
+        const int s = __builtin_amdgcn_readlane(sl, base + j);
+        const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), base + j));
+        ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, x[i], acc[i]);
+    }
+}
+
+// Row of `bytes` (a multiple of 16) from src to dst by the whole wavefront.
+__device__ __forceinline__ void copy_row16(void* dst, const void* src, int bytes, int lane) {
+    for (int w = lane; w < bytes / 16; w += 64)
+        reinterpret_cast<uint4*>(dst)[w] = reinterpret_cast<const uint4*>(src)[w];
+}
+
+// Everything after the weighted sum: v_hat, o, the residual and, for a
+// stream, the copies of the token's inputs into the pending chunk.
+template <int STORE, int EPL>
+__device__ __forceinline__ void gather_finish(const GatherArgs& a, int b, int t, int lane, const float (&tot)[EPL]) {
+    constexpr int ES = Store<STORE>::kBytes;
+    const size_t col = static_cast<size_t>(lane) * EPL;
     const float Hf = static_cast<float>(a.H);
     float vh[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) vh[i] = acc[i] / Hf;
+    for (int i = 0; i < EPL; ++i) vh[i] = tot[i] / Hf;
 
     const float gt = a.g[static_cast<size_t>(b) * a.g_bstride + t];
     if (a.o) {
@@ -170,6 +167,86 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
         for (int i = 0; i < EPL; ++i) rr[i] = gt * (vh[i] - y[i]);
         stf<EPL>(a.r + (static_cast<size_t>(b) * a.Tc + t) * a.dv + col, rr);
     }
+    if (a.pq) {
+        const int qbytes = a.qrow * ES;
+        copy_row16(static_cast<unsigned char*>(a.pq) + (static_cast<size_t>(b) * a.pq_bstride + static_cast<size_t>(t) * a.qrow) * ES,
+                   static_cast<const unsigned char*>(a.q) + (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(t) * a.qrow) * ES,
+                   qbytes, lane);
+        if (lane == 0) a.pg[static_cast<size_t>(b) * a.pg_bstride + t] = gt;
+        const int slot = t + a.ptgt_shift;
+        if (slot >= 0)
+            copy_row16(static_cast<unsigned char*>(a.ptgt) + (static_cast<size_t>(b) * a.ptgt_bstride + static_cast<size_t>(slot) * a.dv) * ES,
+                       static_cast<const unsigned char*>(a.v) + (static_cast<size_t>(b) * a.v_bstride + static_cast<size_t>(t) * a.dv) * ES,
+                       a.dv * ES, lane);
+    }
+}
+
+// One wavefront per token: the parts of kGatherPart entries are summed in
+// turn and folded into the total in part order.
+template <int STORE, int EPL>
+__global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t tok = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (tok >= static_cast<int64_t>(a.B) * a.Tc) return;
+    const int b = static_cast<int>(tok / a.Tc), t = static_cast<int>(tok % a.Tc);
+    const int HK = a.H * a.k;
+    const size_t ib = static_cast<size_t>(b) * a.iw_bstride + static_cast<size_t>(t) * HK;
+    // up to 4*64 (slot, weight) entries, entry e held by lane e % 64, register e / 64
+    int32_t sl[4];
+    float wt[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int e = r * 64 + lane;
+        sl[r] = (e < HK) ? a.idx[ib + e] : 0;
+        wt[r] = (e < HK) ? a.w[ib + e] : 0.f;
+    }
+    const size_t vb = static_cast<size_t>(b) * static_cast<size_t>(a.N) * a.dv;
+    const size_t col = static_cast<size_t>(lane) * EPL;
+    float tot[EPL];
+#pragma unroll
+    for (int p = 0; p < 256 / kGatherPart; ++p) {
+        const int e0 = p * kGatherPart;
+        if (e0 >= HK) break;
+        float acc[EPL];
+        gather_part<STORE, EPL>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64, min(kGatherPart, HK - e0), acc);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) tot[i] = (p == 0) ? acc[i] : tot[i] + acc[i];
+    }
+    gather_finish<STORE, EPL>(a, b, t, lane, tot);
+}
+
+// The same sums for few tokens: one workgroup per token, one wavefront per
+// part; the parts meet in LDS and the first wavefront folds them in part
+// order, so the result is bitwise that of k_gather.
+template <int STORE, int EPL>
+__global__ __launch_bounds__(64 * (256 / kGatherPart)) void k_gather_split(GatherArgs a) {
+    __shared__ float part[256 / kGatherPart][512];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t tok = blockIdx.x;
+    const int b = static_cast<int>(tok / a.Tc), t = static_cast<int>(tok % a.Tc);
+    const int HK = a.H * a.k;
+    const int nparts = (HK + kGatherPart - 1) / kGatherPart;
+    const size_t col = static_cast<size_t>(lane) * EPL;
+    if (wave < nparts) {
+        const int e0 = wave * kGatherPart;
+        const int cnt = min(kGatherPart, HK - e0);
+        const size_t ib = static_cast<size_t>(b) * a.iw_bstride + static_cast<size_t>(t) * HK + e0;
+        const int32_t sl = (lane < cnt) ? a.idx[ib + lane] : 0;
+        const float wt = (lane < cnt) ? a.w[ib + lane] : 0.f;
+        float acc[EPL];
+        gather_part<STORE, EPL>(a, static_cast<size_t>(b) * static_cast<size_t>(a.N) * a.dv, col, sl, wt, 0, cnt, acc);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) part[wave][col + i] = acc[i];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float tot[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) tot[i] = part[0][col + i];
+    for (int p = 1; p < nparts; ++p)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) tot[i] = tot[i] + part[p][col + i];
+    gather_finish<STORE, EPL>(a, b, t, lane, tot);
 }
 
 template <int STORE, int EPL>
@@ -193,8 +270,13 @@ __global__ __launch_bounds__(256) void k_resid(ResidArgs a) {
 template <int STORE, int EPL>
 hipError_t gather_t(const GatherArgs& a, hipStream_t s) {
     const int64_t toks = static_cast<int64_t>(a.B) * a.Tc;
-    const unsigned grid = static_cast<unsigned>((toks + 3) / 4);
-    hipLaunchKernelGGL((k_gather<STORE, EPL>), dim3(grid), dim3(256), 0, s, a);
+    if (toks < kGatherSplitBelow) {
+        const int nparts = (a.H * a.k + kGatherPart - 1) / kGatherPart;
+        hipLaunchKernelGGL((k_gather_split<STORE, EPL>), dim3(static_cast<unsigned>(toks)), dim3(64 * nparts), 0, s, a);
+    } else {
+        const unsigned grid = static_cast<unsigned>((toks + 3) / 4);
+        hipLaunchKernelGGL((k_gather<STORE, EPL>), dim3(grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

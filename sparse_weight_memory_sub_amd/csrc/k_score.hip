@@ -362,6 +362,63 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_rows
+// ---------------------------------------------------------------------------
+
+// Scoring of a chunk of at most 16 tokens (decode): every e_ti is written out
+// so the selection can take an exact top-k' of whole rows.  One wavefront per
+// (sequence, head, half, 16 sub-keys): the sub-key rows are the MFMA's B
+// operand, loaded straight from HBM, so the codebooks are read once with
+// every wavefront of the chip in flight.  The arithmetic (accumulators
+// seeded with ||K_i||^2, -2q, k-blocks in order, ||q||^2 + eps added last) is
+// that of k_score, so the e values are the same bits.
+template <int STORE, int DHS>
+__global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
+    constexpr int ES = Store<STORE>::kBytes;
+    const int n = a.n, H = a.H, Tc = a.Tc;
+    const int kblk = n / 16;
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (gw >= static_cast<int64_t>(a.B) * H * 2 * kblk) return;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int bhh = static_cast<int>(gw / kblk), key = static_cast<int>(gw % kblk) * 16 + r;
+    const int half = bhh & 1, bh = bhh >> 1;
+    const int h = bh % H, b = bh / H;
+    Frag<STORE> Bf[DHS];
+    load_row_frags<STORE, DHS>(Bf, static_cast<const unsigned char*>(half ? a.K2 : a.K1) +
+                                       (static_cast<size_t>(bh) * n + key) * (32 * DHS) * ES, g);
+    const float knv = a.knorm[static_cast<size_t>(bhh) * n + key];
+
+    Frag<STORE> A[DHS];
+    const bool tv = r < Tc;
+    load_row_frags<STORE, DHS>(A, static_cast<const unsigned char*>(a.q) +
+        (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(tv ? r : 0) * H * (64 * DHS) +
+         h * (64 * DHS) + half * (32 * DHS)) * ES, g);
+    float qsq = 0.f;
+#pragma unroll
+    for (int s = 0; s < DHS; ++s) {
+        if (!tv) frag_zero<STORE>(A[s]);
+        qsq += frag_sumsq<STORE>(A[s]);
+        frag_scale_m2(A[s]);
+    }
+    qsq += xor_lane(qsq, 16);
+    qsq += xor_lane(qsq, 32);
+    f32x4_t acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = knv;
+#pragma unroll
+    for (int s = 0; s < DHS; ++s) mma(A[s], Bf[s], acc);
+    const int eps_bits = __float_as_int(a.eps);
+    const size_t rowbase = static_cast<size_t>(bhh) * Tc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        const float qe = __shfl(qsq, t, 64) + a.eps;
+        const uint32_t eb = static_cast<uint32_t>(max(__float_as_int(qe + acc[i]), eps_bits));
+        if (t < Tc) a.erow[(rowbase + t) * n + key] = eb;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // k_select
 // ---------------------------------------------------------------------------
 
@@ -486,6 +543,59 @@ __device__ void half_topk(const SelectArgs& a, int b, int t, int h, int half, ui
     wave_sync();
 }
 
+// Sorted top-kh (value, sub-key) of one (token, head, half) from its whole
+// row of e bit patterns (rows mode), ties to the lower index.  Each lane
+// keeps its two smallest values; the kh-th smallest of those 128 is a bound
+// tau with at least kh values of the row <= tau, so every value <= tau is a
+// candidate (about kh of them) and one sort of the candidates finishes.
+// More than 64 candidates (many equal values) fall back to a radix select.
+__device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, uint64_t* buf, float* out_e,
+                              int* out_i) {
+    const int lane = lane_id();
+    const int n = a.n, npl = (n + 63) >> 6;
+    const uint32_t* e = a.erow + row * n;
+    uint32_t u[kNplMax];
+    uint32_t m0 = 0xffffffffu, m1 = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < kNplMax; ++j) {
+        const int i = j * 64 + lane;
+        u[j] = (j < npl && i < n) ? e[i] : 0x7f800000u;
+        const uint32_t lo = min(m0, u[j]), hi = max(m0, u[j]);
+        m0 = lo;
+        m1 = min(m1, hi);
+    }
+    uint32_t kept[2] = {m0, m1};
+    bitonic_sort<2, 64>(kept);
+    const uint32_t tau = static_cast<uint32_t>(__shfl(static_cast<int>(kept[0]), a.kh - 1, 64));  // kh <= 64
+    const uint64_t lt = lanemask_lt();
+    uint32_t total = 0u;
+#pragma unroll
+    for (int j = 0; j < kNplMax; ++j) {
+        if (j < npl) {
+            const bool c = u[j] <= tau;
+            const uint64_t bm = ballot(c);
+            const uint32_t pos = total + static_cast<uint32_t>(__popcll(bm & lt));
+            if (c && pos < 64u) buf[pos] = (static_cast<uint64_t>(u[j]) << 32) | static_cast<uint32_t>(j * 64 + lane);
+            total += static_cast<uint32_t>(__popcll(bm));
+        }
+    }
+    wave_sync();
+    uint64_t key[1];
+    if (total <= 64u) {
+        key[0] = (static_cast<uint32_t>(lane) < total) ? buf[lane] : ~0ull;
+    } else {
+        wave_sync();
+        radix_select(u, npl, a.kh, hist, buf);
+        key[0] = (lane < a.kh) ? buf[lane] : ~0ull;
+    }
+    bitonic_sort<1, 64>(key);
+    if (lane < a.kh) {
+        out_e[lane] = __uint_as_float(static_cast<uint32_t>(key[0] >> 32));
+        out_i[lane] = static_cast<int>(key[0] & 0xffffffffu);
+    }
+    wave_sync();
+}
+
 template <int R>
 __device__ void product_topk(const SelectArgs& a, const float* e1, const int* i1, const float* e2, const int* i2,
                              int32_t* idx_out, float* w_out) {
@@ -554,6 +664,33 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
 }
 
+// Selection from whole rows (rows mode, a few tokens): two wavefronts per
+// (token, head), one per half, then the first does the product top-k.
+__global__ __launch_bounds__(256) void k_select_rows(SelectArgs a) {
+    __shared__ uint64_t buf[4][64];
+    __shared__ uint32_t hist[4][256];
+    __shared__ float se[2][2][kMaxKHalf];
+    __shared__ int si[2][2][kMaxKHalf];
+    const int wave = threadIdx.x >> 6, slot = wave >> 1, half = wave & 1;
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 2 + slot;  // over B*Tc*H
+    const bool live = item < static_cast<int64_t>(a.B) * a.Tc * a.H;
+    int b = 0, t = 0, h = 0;
+    if (live) {
+        h = static_cast<int>(item % a.H);
+        const int64_t bt = item / a.H;
+        t = static_cast<int>(bt % a.Tc);
+        b = static_cast<int>(bt / a.Tc);
+        const size_t row = ((static_cast<size_t>(b * a.H + h) * 2) + half) * a.Tc + t;
+        half_topk_row(a, row, hist[wave], buf[wave], se[slot][half], si[slot][half]);
+    }
+    __syncthreads();
+    if (!live || half != 0) return;
+    const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
+    if (a.ncand <= 64) product_topk<1>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o);
+    else if (a.ncand <= 128) product_topk<2>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o);
+    else product_topk<4>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o);
+}
+
 template <int STORE, int DHS, int MK, int MODE, int NW>
 hipError_t score_w(const ScoreArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
@@ -596,6 +733,12 @@ hipError_t score_mode(const ScoreArgs& a, hipStream_t s) {
 
 template <int STORE, int DHS>
 hipError_t score_mk(const ScoreArgs& a, hipStream_t s) {
+    if (a.mode == kScoreRows) {
+        if (a.Tc > kRowTok) return hipErrorInvalidValue;
+        const int64_t waves = static_cast<int64_t>(a.B) * a.H * 2 * (a.n / 16);
+        hipLaunchKernelGGL((k_rows<STORE, DHS>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     // modes without selection do not keep per-lane minima
     if (a.mode == kScoreStats) return score_t<STORE, DHS, 1, kScoreStats>(a, s);
     if (a.mode == kScoreRowStat) return score_t<STORE, DHS, 1, kScoreRowStat>(a, s);
@@ -659,6 +802,10 @@ hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s) {
 
 hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s) {
     const int64_t items = static_cast<int64_t>(a.B) * a.Tc * a.H;
+    if (a.erow) {
+        hipLaunchKernelGGL(k_select_rows, dim3(static_cast<unsigned>((items + 1) / 2)), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     const unsigned grid = static_cast<unsigned>((items + 3) / 4);
     if (store == kBF16) hipLaunchKernelGGL(k_select<kBF16>, dim3(grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_select<kF32>, dim3(grid), dim3(256), 0, s, a);

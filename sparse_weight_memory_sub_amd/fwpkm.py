@@ -9,6 +9,7 @@ is missing, the call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -52,6 +53,12 @@ class Cfg(ctypes.Structure):
 class StreamPos(ctypes.Structure):
     """fwpkm_stream_pos: host-side position of a decode stream."""
     _fields_ = [("pending", ctypes.c_int32), ("norms_valid", ctypes.c_int32)]
+
+
+@functools.lru_cache(maxsize=256)
+def _cfg(c: FwpkmConfig) -> Cfg:
+    """A shared, never modified fwpkm_cfg of the configuration, for the calls."""
+    return cfg_struct(c)
 
 
 def cfg_struct(c: FwpkmConfig) -> Cfg:
@@ -116,9 +123,10 @@ def timing_read() -> dict:
     return out
 
 
+@functools.lru_cache(maxsize=256)
 def workspace_bytes(cfg: FwpkmConfig, B: int, T: int) -> int:
     out = ctypes.c_size_t(0)
-    c = cfg_struct(cfg)
+    c = _cfg(cfg)
     _check(load().fwpkm_workspace_bytes(ctypes.byref(c), int(B), int(T), ctypes.byref(out)))
     return int(out.value)
 
@@ -130,11 +138,11 @@ def _ptr(t):
 def _dev(t: torch.Tensor, name: str, dtype, shape):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -150,9 +158,9 @@ def _stream(stream):
 
 
 def _workspace(cfg, B, T, ws, device):
-    need = workspace_bytes(cfg, B, T)
+    """The caller's workspace (the library checks its size), or a new one."""
     if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(workspace_bytes(cfg, B, T), 256), dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -179,7 +187,7 @@ def fwpkm_retrieve(cfg: FwpkmConfig, q, v, g, K1, K2, V, o=None, vhat=None, idx=
     if idx is not None: _dev(idx, "idx", torch.int32, (B, T, H, k))
     if w is not None: _dev(w, "w", torch.float32, (B, T, H, k))
     ws, wsb = _workspace(cfg, B, T, ws, dev)
-    c = cfg_struct(cfg)
+    c = _cfg(cfg)
     _check(load().fwpkm_retrieve(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2), _ptr(V),
                                  _ptr(o), _ptr(vhat), _ptr(idx), _ptr(w), _ptr(ws), wsb, _stream(stream)))
     return {"o": o, "vhat": vhat, "idx": idx, "w": w}
@@ -201,7 +209,7 @@ def fwpkm_chunk_update(cfg: FwpkmConfig, q, g, tgt, n_tgt: int, idx, w, vhat, K1
     if n_read is not None:
         _dev(n_read, "n_read", torch.int32, (B, cfg.N))
     ws, wsb = _workspace(cfg, B, Tc, ws, g.device)
-    c = cfg_struct(cfg)
+    c = _cfg(cfg)
     _check(load().fwpkm_chunk_update(ctypes.byref(c), B, Tc, int(n_tgt), _ptr(q), _ptr(g),
                                      _ptr(tgt) if n_tgt > 0 else None, _ptr(idx), _ptr(w), _ptr(vhat),
                                      _ptr(K1), _ptr(K2), _ptr(V), _ptr(n_read), _ptr(ws), wsb, _stream(stream)))
@@ -228,16 +236,17 @@ def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_n
     if vhat is not None:
         _dev(vhat, "vhat", torch.float32, (B, T, dv))
     ws, wsb = _workspace(cfg, B, T, ws, dev)
-    c = cfg_struct(cfg)
+    c = _cfg(cfg)
     _check(load().fwpkm_forward_seq(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g), _ptr(v_next),
                                     _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat), _ptr(ws), wsb,
                                     _stream(stream)))
     return {"o": o, "vhat": vhat}
 
 
+@functools.lru_cache(maxsize=256)
 def stream_state_bytes(cfg: FwpkmConfig, B: int) -> int:
     out = ctypes.c_size_t(0)
-    c = cfg_struct(cfg)
+    c = _cfg(cfg)
     _check(load().fwpkm_stream_state_bytes(ctypes.byref(c), int(B), ctypes.byref(out)))
     return int(out.value)
 
@@ -270,7 +279,7 @@ def fwpkm_stream_step(cfg: FwpkmConfig, q, v, g, K1, K2, V, state, pos: StreamPo
     if vhat is not None:
         _dev(vhat, "vhat", torch.float32, (B, T, dv))
     ws, wsb = _workspace(cfg, B, cfg.chunk, ws, dev)
-    c = cfg_struct(cfg)
+    c = _cfg(cfg)
     _check(load().fwpkm_stream_step(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2), _ptr(V),
                                     _ptr(o), _ptr(vhat), _ptr(state), ctypes.byref(pos), _ptr(ws), wsb,
                                     _stream(stream)))
@@ -288,6 +297,6 @@ def fwpkm_stream_flush(cfg: FwpkmConfig, K1, K2, V, state, pos: StreamPos, v_nex
     if v_next is not None:
         _dev(v_next, "v_next", sd, (B, dv))
     ws, wsb = _workspace(cfg, B, cfg.chunk, ws, V.device)
-    c = cfg_struct(cfg)
+    c = _cfg(cfg)
     _check(load().fwpkm_stream_flush(ctypes.byref(c), B, _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(state),
                                      ctypes.byref(pos), _ptr(ws), wsb, _stream(stream)))

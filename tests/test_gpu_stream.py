@@ -165,3 +165,30 @@ def test_stream_million_layer_decode_bitwise():
     assert torch.equal(o, ref["o"]) and torch.equal(vh, ref["vhat"])
     for a, b in ((K1a, K1b), (K2a, K2b), (Va, Vb)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n,dup", [(64, 4), (256, 256)])
+def test_rows_mode_selection_equals_sweep_with_ties(n, dup):
+    """Chunks of at most 16 tokens select from whole rows of distances; with
+    exact ties (sub-keys repeated `dup` times, all equal for dup = n) both
+    selection paths keep the lower sub-key index."""
+    cfg = C(n, 2, 64, 64, 8, 8)
+    B, T = 2, 40
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=34)
+    K1 = K1.clone()
+    for i in range(n):
+        K1[:, :, i] = K1[:, :, (i // dup) * dup]
+    K1d, K2d, Vd = dev(K1, K2, V)
+    full = fwpkm.fwpkm_retrieve(cfg, *dev(q, v, g), K1d, K2d, Vd)  # one 40-token chunk: the sweep
+    for t0 in range(0, T, 8):
+        part = fwpkm.fwpkm_retrieve(cfg, *dev(q[:, t0:t0 + 8], v[:, t0:t0 + 8], g[:, t0:t0 + 8]), K1d, K2d, Vd)
+        assert torch.equal(part["idx"], full["idx"][:, t0:t0 + 8])
+        if dup < n:
+            assert torch.equal(part["w"], full["w"][:, t0:t0 + 8])
+            assert torch.equal(part["o"], full["o"][:, t0:t0 + 8])
+        else:
+            # the sweep's overflow path recomputes the equal distances another way
+            torch.testing.assert_close(part["w"], full["w"][:, t0:t0 + 8], rtol=1e-5, atol=1e-6)
+    # ties between equal sub-keys go to the lower index, as in the oracle
+    ora = oracle.retrieve(cfg, q, v, g, K1, K2, V)
+    assert np.array_equal(full["idx"].cpu().numpy(), ora["idx"])
