@@ -198,6 +198,36 @@ def pair_p(c, q, K1, K2, slots):
     return P
 
 
+def usage_counts(c, idx):
+    """Row contributions ([layer] D.3): the number of reads of every value
+    row, per sequence, from slot ids idx[B, T, H, k] -> [B, n*n] int64."""
+    idx = np.asarray(idx)
+    B = idx.shape[0]
+    out = np.zeros((B, c.n * c.n), np.int64)
+    for b in range(B):
+        np.add.at(out[b], idx[b].reshape(-1).astype(np.int64), 1)
+    return out
+
+
+def usage_metrics(counts):
+    """Addressing metrics ([layer] D.3) of row contributions counts[B, N]:
+    per sequence (coverage, collision, KLD, reads) as float64 [B, 4].
+    coverage = share of rows read at least once; collision = share of reads
+    that land on a row read more than once; KLD = KL(u || uniform) with
+    u = counts / reads, natural log.  No reads gives zeros."""
+    counts = np.asarray(counts, dtype=np.float64)
+    B, N = counts.shape
+    res = np.zeros((B, 4))
+    for b in range(B):
+        c = counts[b]
+        S = c.sum()
+        if S == 0:
+            continue
+        u = c[c > 0] / S
+        res[b] = [np.count_nonzero(c) / N, c[c > 1].sum() / S, float(np.sum(u * np.log(u * N))), S]
+    return res
+
+
 class Stream:
     """Streaming (inference) reading of the layer, token by token.
 

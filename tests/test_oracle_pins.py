@@ -495,6 +495,45 @@ def test_stream_carries_state_across_sequences():
     assert not np.array_equal(st.V, a["V"])
 
 
+# ---------------------------------------------------------------- addressing metrics
+def test_usage_metrics_closed_forms():
+    """[layer] D.3: coverage, collision and KLD of row contributions."""
+    N = 16
+    m = oracle.usage_metrics(np.ones((1, N), np.int64))        # every row read once
+    assert np.allclose(m[0], [1.0, 0.0, 0.0, N])
+    one = np.zeros((1, N), np.int64); one[0, 5] = 7             # all reads on one row
+    m = oracle.usage_metrics(one)
+    assert np.allclose(m[0], [1 / N, 1.0, math.log(N), 7])
+    hand = np.array([[3, 1, 0, 0]])                             # worked by hand
+    m = oracle.usage_metrics(hand)
+    assert np.allclose(m[0], [0.5, 0.75, 0.75 * math.log(3), 4])
+    assert np.array_equal(oracle.usage_metrics(np.zeros((2, N), np.int64)), np.zeros((2, 4)))
+
+
+def test_usage_kld_equals_library_relative_entropy():
+    from scipy.stats import entropy
+    rng = np.random.default_rng(3)
+    counts = rng.poisson(0.7, size=(3, 64))
+    m = oracle.usage_metrics(counts)
+    for b in range(3):
+        assert math.isclose(m[b, 2], entropy(counts[b] / counts[b].sum(), np.full(64, 1 / 64)), rel_tol=1e-12)
+
+
+def test_usage_counts_brute_force():
+    cfg, q, v, g, K1, K2, V = _seq_problem(T=20, C=8)
+    r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
+    counts = oracle.usage_counts(cfg, r["idx"])
+    B, T, H, k = r["idx"].shape
+    brute = np.zeros_like(counts)
+    for b in range(B):
+        for t in range(T):
+            for h in range(H):
+                for j in range(k):
+                    brute[b, r["idx"][b, t, h, j]] += 1
+    assert np.array_equal(counts, brute)
+    assert (counts.sum(1) == T * H * k).all()
+
+
 def test_near_tie_flag_on_duplicate_keys():
     cfg = FwpkmConfig(n=6, heads=1, d_q=4, d_v=2, k_half=2, k=2, chunk=4)
     q, v, g, K1, K2, V = _rand_problem(cfg, 1, 4, seed=6)
