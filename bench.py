@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time streaming decode (one token per call per sequence) instead of forward_seq")
     ap.add_argument("--decode-tokens", type=int, default=1024, help="timed decode tokens per sequence")
+    ap.add_argument("--usage", action="store_true",
+                    help="time forward_seq with row-contribution counting and the addressing metrics")
     return ap.parse_args()
 
 
@@ -187,6 +189,64 @@ def decode_bench(args, cfg, wl, B, q, v, g, K1, K2, V):
     print(json.dumps(result), flush=True)
 
 
+def usage_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V):
+    """forward_seq with row-contribution counts, and the addressing metrics
+    every 32K tokens of each sequence (paperlayer.ai D.3).  Prints one JSON
+    line."""
+    import torch
+    from sparse_weight_memory_sub_amd import fwpkm
+
+    dev = q.device
+    stream = torch.cuda.current_stream()
+    o = torch.empty((B, T, cfg.d_v), dtype=torch.float32, device=dev)
+    ws = torch.empty(fwpkm.workspace_bytes(cfg, B, T), dtype=torch.uint8, device=dev)
+    usage = torch.zeros((B, cfg.N), dtype=torch.int32, device=dev)
+    metrics = torch.empty((B, 4), dtype=torch.float64, device=dev)
+    mws = torch.empty(2048 * B, dtype=torch.uint8, device=dev)
+    interval = max(1, 32768 // T)  # steps per 32K tokens of a sequence
+
+    def run(n, count):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(n):
+            fwpkm.fwpkm_forward_seq(cfg, q, v, g, K1, K2, V, o=o, ws=ws, stream=stream,
+                                    usage=usage if count else None)
+            if count and (i + 1) % interval == 0:
+                fwpkm.fwpkm_usage_metrics(cfg, usage, reset=True, metrics=metrics, ws=mws, stream=stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / n
+
+    run(args.warmup, True)
+    usage.zero_()
+    steps = max(args.steps, interval)
+    ms_plain = run(steps, False)
+    ms_count = run(steps, True)
+    usage.zero_()  # the timing pass below is exactly one interval
+    fwpkm.timing_enable(True)
+    run(interval, True)
+    fwpkm.timing_enable(False)
+    ms_u, n_u = fwpkm.timing_read()["usage"]
+    m = metrics.cpu().numpy()
+    value = B * T / (ms_count / 1e3)
+    log(f"usage counting: {ms_count:.3f} ms/step against {ms_plain:.3f} without; metrics every {interval} steps")
+    result = {
+        "metric": "FwPKM layer tokens/s with row-contribution counting and addressing metrics every 32K tokens",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": ms_count, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.store, "data": "synthetic",
+        "config": {"workload": f"{wl.name}-usage", "n_slots": cfg.N, "heads": cfg.heads, "k": cfg.k,
+                   "batch": B, "seq_len": T, "interval_tokens": interval * T},
+        "ms_per_step_without_counting": ms_plain,
+        "usage_kernels_ms_per_step": ms_u / interval,
+        "usage_launches_per_step": n_u / interval,
+        "metrics_mean": {"coverage": float(m[:, 0].mean()), "collision": float(m[:, 1].mean()),
+                         "kld": float(m[:, 2].mean()), "reads": float(m[:, 3].mean())},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,6 +275,9 @@ def main():
 
     if args.decode:
         decode_bench(args, cfg, wl, B, q, v, g, K1, K2, V)
+        return
+    if args.usage:
+        usage_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V)
         return
 
     want_cpu = not (args.no_cpu_baseline or args.profile_only)

@@ -201,6 +201,35 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fwpkm_forward_seq that also counts row contributions for the addressing
+ * metrics ([layer] D.3): usage[B][n*n] int32 (nullable; caller-owned,
+ * zero it to start an interval) gets +1 per read (t, h, j) of its row, for
+ * every token of every pass.  Everything else is fwpkm_forward_seq.
+ */
+int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
+                            const void* q, const void* v, const float* g, const void* v_next,
+                            void* K1, void* K2, void* V,
+                            float* o, float* vhat, int32_t* usage,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Addressing metrics ([layer] D.3) of the row contributions c_i = usage[b][i]
+ * counted over an interval of tokens, per sequence b, into metrics[B][4]
+ * (double, device):
+ *   [0] coverage  = |{i : c_i > 0}| / N            (share of rows read)
+ *   [1] collision = sum_{c_i > 1} c_i / sum_i c_i   (share of reads that land
+ *                   on a row read more than once in the interval)
+ *   [2] KLD       = sum_i u_i ln(u_i N), u_i = c_i / sum_i c_i  (divergence of
+ *                   row use from uniform, natural log)
+ *   [3] sum_i c_i (reads counted).
+ * An interval with no reads gives zeros.  reset != 0 zeroes usage afterwards,
+ * starting the next interval.  Fixed reduction order: reproducible.
+ * ws: device scratch of at least 2048*B bytes, 256-byte aligned.
+ */
+int fwpkm_usage_metrics(const fwpkm_cfg* cfg, int32_t B, int32_t* usage, double* metrics, int32_t reset,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Streaming (inference) mode ([layer] A.1: lookahead pairs are collected
  * until a chunk is full, so a token's prediction never waits for its own
  * target; [layer] E.1: memory state carried across sequence boundaries).
@@ -239,12 +268,13 @@ int fwpkm_stream_state_bytes(const fwpkm_cfg* cfg, int32_t B, size_t* bytes);
  * T new tokens of B sequences: q[B][T][H][d_q], v[B][T][d_v] (store dtype),
  * g[B][T] float.  Outputs o[B][T][d_v] float (required), vhat[B][T][d_v]
  * float (nullable).  K1, K2, V are updated in place by every chunk write
- * the call triggers.
+ * the call triggers.  usage[B][n*n] int32 (nullable) counts the reads of
+ * the call's tokens, as in fwpkm_forward_seq_usage.
  */
 int fwpkm_stream_step(const fwpkm_cfg* cfg, int32_t B, int32_t T,
                       const void* q, const void* v, const float* g,
                       void* K1, void* K2, void* V,
-                      float* o, float* vhat,
+                      float* o, float* vhat, int32_t* usage,
                       void* state, fwpkm_stream_pos* pos,
                       void* ws, size_t ws_bytes, void* stream);
 
@@ -278,7 +308,8 @@ typedef enum {
     FWPKM_K_SELECT = 11,        /* per-half top-k', product top-k, weights         */
     FWPKM_K_QT = 12,            /* transposed query halves for the sub-key step    */
     FWPKM_K_PEND = 13,          /* copies into a stream's pending chunk            */
-    FWPKM_K_COUNT = 14
+    FWPKM_K_USAGE = 14,         /* row-contribution counts and addressing metrics  */
+    FWPKM_K_COUNT = 15
 } fwpkm_kernel;
 
 /*

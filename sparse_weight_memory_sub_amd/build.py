@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfwpkm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["fwpkm_api.cpp", "k_score.hip", "k_gather.hip", "k_sort.hip", "k_scatter.hip", "k_addr.hip"]
+SOURCES = ["fwpkm_api.cpp", "k_score.hip", "k_gather.hip", "k_sort.hip", "k_scatter.hip", "k_addr.hip",
+           "k_usage.hip"]
 
 ARCH = os.environ.get("FWPKM_OFFLOAD_ARCH", "gfx950")
 

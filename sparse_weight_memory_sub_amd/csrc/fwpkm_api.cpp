@@ -297,7 +297,7 @@ ScoreArgs score_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstr
 // head) top-k' of each half and the product top-k into idx / w.
 int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
                 const void* K1, const void* K2, const float* knorm, int32_t* idx, float* w, int64_t iw_bstride,
-                bool stats, hipStream_t s) {
+                bool stats, int32_t* usage, hipStream_t s) {
     // a handful of tokens (decode): whole rows of e and an exact top-k' of
     // each; otherwise the two-pass sweep with candidate lists
     const bool rows = !stats && Tc <= kRowTok;
@@ -321,6 +321,7 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     sa.B = B; sa.Tc = Tc; sa.n = p.n; sa.H = p.H; sa.dh = p.dh; sa.kh = p.kh; sa.k = p.k; sa.ncand = p.ncand;
     sa.eps = p.eps; sa.idx = idx; sa.w = w; sa.iw_bstride = iw_bstride; sa.cand_ab = p.cand;
     sa.erow = a.erow;
+    sa.usage = usage;
     {
         TimedLaunch tl(FWPKM_K_SELECT, s);
         HIP_TRY(launch_select(sa, p.store, s));
@@ -498,7 +499,7 @@ int stream_fire(const Plan& p, const StreamLayout& S, void* st, int B, int Tc, i
 // targets that the chunk's write will need.
 int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T, int j, int seg, int pend,
                     const void* q, const void* v, const float* g, const void* K1, const void* K2, const void* V,
-                    float* o, float* vhat, void* ws, hipStream_t s) {
+                    float* o, float* vhat, int32_t* usage, void* ws, hipStream_t s) {
     const Layout L = layout(p, B, seg, true, false);
     const int64_t C = p.C;
     const size_t qrow = static_cast<size_t>(p.H) * p.dq * p.es, vrow = static_cast<size_t>(p.dv) * p.es;
@@ -510,7 +511,7 @@ int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T
     int32_t* idx = at<int32_t>(st, S.idx) + static_cast<size_t>(pend) * p.H * p.k;
     float* w = at<float>(st, S.w) + static_cast<size_t>(pend) * p.H * p.k;
     int rc = select_topk(p, L, ws, B, seg, qb + j * qrow, static_cast<int64_t>(T) * p.H * p.dq, K1, K2,
-                         at<float>(st, S.knorm), idx, w, iwb, false, s);
+                         at<float>(st, S.knorm), idx, w, iwb, false, usage, s);
     if (rc) return rc;
     GatherArgs ga{};
     ga.V = V; ga.idx = idx; ga.w = w; ga.iw_bstride = iwb;
@@ -593,7 +594,7 @@ int fwpkm_retrieve(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, co
     float* ww = w ? w : at<float>(ws, L.w);
     const int64_t iwb = static_cast<int64_t>(T) * p.H * p.k;
     rc = select_topk(p, L, ws, B, T, q, static_cast<int64_t>(T) * p.H * p.dq, K1, K2, at<float>(ws, L.knorm), ii, ww,
-                     iwb, false, s);
+                     iwb, false, nullptr, s);
     if (rc) return rc;
     GatherArgs ga{};
     ga.V = V; ga.idx = ii; ga.w = ww; ga.iw_bstride = iwb;
@@ -646,6 +647,13 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
 int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q, const void* v,
                       const float* g, const void* v_next, void* K1, void* K2, void* V, float* o, float* vhat,
                       void* ws, size_t ws_bytes, void* stream) {
+    return fwpkm_forward_seq_usage(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, vhat, nullptr, ws, ws_bytes,
+                                   stream);
+}
+
+int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q,
+                            const void* v, const float* g, const void* v_next, void* K1, void* K2, void* V, float* o,
+                            float* vhat, int32_t* usage, void* ws, size_t ws_bytes, void* stream) {
     Plan p;
     int rc = make_plan(cfg, &p);
     if (rc) return rc;
@@ -698,9 +706,10 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
             // this buffer was last read by the value write two chunks ago
             if (step >= 2) HIP_TRY(hipStreamWaitEvent(s, ax->ev_write[buf], 0));
             // retrieval with the state left by the previous chunk
-            rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, at<float>(ws, L.knorm), idx, w, iwb, p.addr, s);
+            rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, at<float>(ws, L.knorm), idx, w, iwb, p.addr, usage, s);
             if (rc) return rc;
             HIP_TRY(hipEventRecord(ax->ev_sel, s));
+
             // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
             int n_tgt;
             const void* tgt;
@@ -776,8 +785,8 @@ int fwpkm_stream_state_bytes(const fwpkm_cfg* cfg, int32_t B, size_t* bytes) {
 }
 
 int fwpkm_stream_step(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, const void* v, const float* g,
-                      void* K1, void* K2, void* V, float* o, float* vhat, void* state, fwpkm_stream_pos* pos,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      void* K1, void* K2, void* V, float* o, float* vhat, int32_t* usage, void* state,
+                      fwpkm_stream_pos* pos, void* ws, size_t ws_bytes, void* stream) {
     Plan p;
     int rc = stream_args(cfg, B, state, pos, &p);
     if (rc) return rc;
@@ -799,18 +808,21 @@ int fwpkm_stream_step(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q,
     for (int j = 0; j < T;) {
         if (pend == p.C) {
             // a full chunk; with lookahead token j is its last token's target
-            if (p.look)
+            if (p.look) {
+                TimedLaunch tl(FWPKM_K_PEND, s);
                 HIP_TRY(launch_copy2d(at<unsigned char>(state, S.tgt) + (pend - 1) * vrow,
                                       static_cast<int64_t>(p.C) * vrow,
                                       static_cast<const unsigned char*>(v) + static_cast<size_t>(j) * vrow,
                                       static_cast<int64_t>(T) * vrow, vrow, B, s));
+            }
             rc = stream_fire(p, S, state, B, p.C, p.C, K1, K2, V, ws, s);
             if (rc) return rc;
             pend = 0;
         }
         const int seg = std::min(T - j, p.C - pend);
-        rc = stream_retrieve(p, S, state, B, T, j, seg, pend, q, v, g, K1, K2, V, o, vhat, ws, s);
+        rc = stream_retrieve(p, S, state, B, T, j, seg, pend, q, v, g, K1, K2, V, o, vhat, usage, ws, s);
         if (rc) return rc;
+
         pend += seg;
         j += seg;
         pos->pending = pend;
@@ -849,6 +861,7 @@ int fwpkm_stream_flush(const fwpkm_cfg* cfg, int32_t B, const void* v_next, void
     if (p.look) {
         if (v_next) {
             const size_t vrow = static_cast<size_t>(p.dv) * p.es;
+            TimedLaunch tl(FWPKM_K_PEND, s);
             HIP_TRY(launch_copy2d(at<unsigned char>(state, S.tgt) + (pend - 1) * vrow,
                                   static_cast<int64_t>(p.C) * vrow, v_next, static_cast<int64_t>(vrow), vrow, B, s));
         } else {
@@ -858,6 +871,22 @@ int fwpkm_stream_flush(const fwpkm_cfg* cfg, int32_t B, const void* v_next, void
     rc = stream_fire(p, S, state, B, pend, n_tgt, K1, K2, V, ws, s);
     if (rc) return rc;
     pos->pending = 0;
+    return ok();
+}
+
+int fwpkm_usage_metrics(const fwpkm_cfg* cfg, int32_t B, int32_t* usage, double* metrics, int32_t reset,
+                        void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int rc = make_plan(cfg, &p);
+    if (rc) return rc;
+    if (B < 0) return fail(FWPKM_EINVAL, "B must be >= 0");
+    if (B == 0) return ok();
+    if (!usage || !metrics) return fail(FWPKM_EINVAL, "usage and metrics are required");
+    rc = check_ws(ws, ws_bytes, static_cast<size_t>(B) * kUsageParts * 32);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TimedLaunch tl(FWPKM_K_USAGE, s);
+    HIP_TRY(launch_usage_metrics(usage, B, p.N, ws, metrics, reset ? 1 : 0, s));
     return ok();
 }
 

@@ -225,6 +225,7 @@ struct SelectArgs {
     int64_t iw_bstride;
     CandTable cand_ab;
     const uint32_t* erow; // non-NULL: whole rows of e ([B][H][2][Tc][n]) instead of candidate lists
+    int32_t* usage;       // nullable: usage[b*n*n + slot] += 1 per selected read
 };
 
 int score_keep(int kh);   // smallest e kept per lane in the first scoring pass
@@ -360,6 +361,11 @@ hipError_t launch_resid(const ResidArgs& a, int store, hipStream_t s);
 hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, int store, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t s);
+// metrics[b] = {coverage, collision, KLD, accesses} of usage[b][0..N); reset clears usage;
+// scratch holds B*kUsageParts partial sums of 32 bytes
+constexpr int kUsageParts = 64;
+hipError_t launch_usage_metrics(int32_t* usage, int B, int64_t N, void* scratch, double* metrics, int reset,
+                                hipStream_t s);
 // height rows of width_bytes (a multiple of 4) from src + y*spitch to dst + y*dpitch
 hipError_t launch_copy2d(void* dst, int64_t dpitch, const void* src, int64_t spitch, int64_t width_bytes,
                          int64_t height, hipStream_t s);

@@ -598,7 +598,7 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
 
 template <int R>
 __device__ void product_topk(const SelectArgs& a, const float* e1, const int* i1, const float* e2, const int* i2,
-                             int32_t* idx_out, float* w_out) {
+                             int32_t* idx_out, float* w_out, int32_t* usage) {
     const int lane = lane_id();
     uint64_t key[R];
 #pragma unroll
@@ -620,8 +620,11 @@ __device__ void product_topk(const SelectArgs& a, const float* e1, const int* i1
     const float ratio = (lane < a.k) ? (P0 / P) : 0.f;
     const float sum = wave_sum(ratio);
     if (lane < a.k) {
-        idx_out[lane] = static_cast<int32_t>(key[0] & 0xffffffffu);
+        const int32_t slot = static_cast<int32_t>(key[0] & 0xffffffffu);
+        idx_out[lane] = slot;
         w_out[lane] = ratio / sum;
+        // row contribution of this read (integer atomic: exact in any order)
+        if (usage && slot >= 0 && slot < a.n * a.n) atomicAdd(usage + slot, 1);
     }
 }
 
@@ -659,9 +662,10 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
             half_topk<STORE>(a, b, t, h, half, hist[wave], buf[wave], se[wave][half], si[wave][half]);
     }
     const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
-    if (a.ncand <= 64) product_topk<1>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
-    else if (a.ncand <= 128) product_topk<2>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
-    else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o);
+    int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
+    if (a.ncand <= 64) product_topk<1>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
+    else if (a.ncand <= 128) product_topk<2>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
+    else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
 }
 
 // Selection from whole rows (rows mode, a few tokens): two wavefronts per
@@ -686,9 +690,10 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs a) {
     __syncthreads();
     if (!live || half != 0) return;
     const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
-    if (a.ncand <= 64) product_topk<1>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o);
-    else if (a.ncand <= 128) product_topk<2>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o);
-    else product_topk<4>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o);
+    int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
+    if (a.ncand <= 64) product_topk<1>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
+    else if (a.ncand <= 128) product_topk<2>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
+    else product_topk<4>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
 }
 
 template <int STORE, int DHS, int MK, int MODE, int NW>

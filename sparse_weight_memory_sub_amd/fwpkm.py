@@ -25,12 +25,13 @@ _STATUS = {OK: "FWPKM_OK", EINVAL: "FWPKM_EINVAL", EUNSUPPORTED: "FWPKM_EUNSUPPO
 
 EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
            "fwpkm_retrieve", "fwpkm_chunk_update", "fwpkm_forward_seq",
+           "fwpkm_forward_seq_usage", "fwpkm_usage_metrics",
            "fwpkm_stream_state_bytes", "fwpkm_stream_step", "fwpkm_stream_flush",
            "fwpkm_timing_enable", "fwpkm_timing_read")
 
 # kernel families of fwpkm_timing_read, in fwpkm_kernel order
 KERNELS = ("knorm", "score_select", "gather", "resid", "sort", "scatter", "pbar",
-           "score_stats", "score_rowstat", "kgrad", "fill", "select", "qt", "pend")
+           "score_stats", "score_rowstat", "kgrad", "fill", "select", "qt", "pend", "usage")
 
 
 class FwpkmError(RuntimeError):
@@ -87,12 +88,15 @@ def load(path: str = LIB_PATH):
         lib.fwpkm_forward_seq.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P]
         SP = ctypes.POINTER(StreamPos)
         lib.fwpkm_stream_state_bytes.argtypes = [C, i32, ctypes.POINTER(sz)]
-        lib.fwpkm_stream_step.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, SP, P, sz, P]
+        lib.fwpkm_stream_step.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, SP, P, sz, P]
+        lib.fwpkm_forward_seq_usage.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        lib.fwpkm_usage_metrics.argtypes = [C, i32, P, P, i32, P, sz, P]
         lib.fwpkm_stream_flush.argtypes = [C, i32, P, P, P, P, P, SP, P, sz, P]
         lib.fwpkm_timing_enable.argtypes = [i32]
         lib.fwpkm_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq,
                   lib.fwpkm_stream_state_bytes, lib.fwpkm_stream_step, lib.fwpkm_stream_flush,
+                  lib.fwpkm_forward_seq_usage, lib.fwpkm_usage_metrics,
                   lib.fwpkm_timing_enable, lib.fwpkm_timing_read):
             f.restype = ctypes.c_int
         _lib = lib
@@ -217,9 +221,10 @@ def fwpkm_chunk_update(cfg: FwpkmConfig, q, g, tgt, n_tgt: int, idx, w, vhat, K1
 
 
 def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_next=None, o=None, vhat=None,
-                      ws=None, stream=None, want_vhat: bool = False):
+                      ws=None, stream=None, want_vhat: bool = False, usage=None):
     """Whole sequences, chunk-causal, `passes` times; K1, K2, V updated in place.
-    Returns dict(o, vhat) of the last pass."""
+    With `usage` ([B, N] int32) the reads are also counted
+    (fwpkm_forward_seq_usage).  Returns dict(o, vhat) of the last pass."""
     sd = cfg.torch_dtype
     B, T = g.shape
     H, dq, dv = cfg.heads, cfg.d_q, cfg.d_v
@@ -237,10 +242,32 @@ def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_n
         _dev(vhat, "vhat", torch.float32, (B, T, dv))
     ws, wsb = _workspace(cfg, B, T, ws, dev)
     c = _cfg(cfg)
-    _check(load().fwpkm_forward_seq(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g), _ptr(v_next),
-                                    _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat), _ptr(ws), wsb,
-                                    _stream(stream)))
+    if usage is None:
+        _check(load().fwpkm_forward_seq(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
+                                        _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat), _ptr(ws),
+                                        wsb, _stream(stream)))
+    else:
+        _dev(usage, "usage", torch.int32, (B, cfg.N))
+        _check(load().fwpkm_forward_seq_usage(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
+                                              _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat),
+                                              _ptr(usage), _ptr(ws), wsb, _stream(stream)))
     return {"o": o, "vhat": vhat}
+
+
+def fwpkm_usage_metrics(cfg: FwpkmConfig, usage, reset: bool = False, metrics=None, ws=None, stream=None):
+    """Addressing metrics of the counted interval: [B, 4] float64 tensor of
+    (coverage, collision, KLD, reads) per sequence; reset zeroes usage."""
+    B = usage.shape[0]
+    _dev(usage, "usage", torch.int32, (B, cfg.N))
+    if metrics is None:
+        metrics = torch.empty((B, 4), dtype=torch.float64, device=usage.device)
+    _dev(metrics, "metrics", torch.float64, (B, 4))
+    if ws is None:
+        ws = torch.empty(2048 * B, dtype=torch.uint8, device=usage.device)
+    c = _cfg(cfg)
+    _check(load().fwpkm_usage_metrics(ctypes.byref(c), B, _ptr(usage), _ptr(metrics), 1 if reset else 0, _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+    return metrics
 
 
 @functools.lru_cache(maxsize=256)
@@ -259,7 +286,7 @@ def stream_state(cfg: FwpkmConfig, B: int, device) -> tuple:
 
 
 def fwpkm_stream_step(cfg: FwpkmConfig, q, v, g, K1, K2, V, state, pos: StreamPos, o=None, vhat=None,
-                      ws=None, stream=None, want_vhat: bool = False):
+                      ws=None, stream=None, want_vhat: bool = False, usage=None):
     """T new tokens of a decode stream; K1, K2, V updated by the chunk writes
     the call triggers, pos advanced.  Returns dict(o, vhat)."""
     sd = cfg.torch_dtype
@@ -278,10 +305,12 @@ def fwpkm_stream_step(cfg: FwpkmConfig, q, v, g, K1, K2, V, state, pos: StreamPo
         vhat = torch.empty((B, T, dv), dtype=torch.float32, device=dev)
     if vhat is not None:
         _dev(vhat, "vhat", torch.float32, (B, T, dv))
+    if usage is not None:
+        _dev(usage, "usage", torch.int32, (B, cfg.N))
     ws, wsb = _workspace(cfg, B, cfg.chunk, ws, dev)
     c = _cfg(cfg)
     _check(load().fwpkm_stream_step(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2), _ptr(V),
-                                    _ptr(o), _ptr(vhat), _ptr(state), ctypes.byref(pos), _ptr(ws), wsb,
+                                    _ptr(o), _ptr(vhat), _ptr(usage), _ptr(state), ctypes.byref(pos), _ptr(ws), wsb,
                                     _stream(stream)))
     return {"o": o, "vhat": vhat}
 

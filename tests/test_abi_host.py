@@ -175,8 +175,8 @@ def test_stream_entry_points_reject_before_launch():
     pos = fwpkm.StreamPos(0, 0)
 
     def step(B, T, q, o, state, p, ws, wsb):
-        return _rc("fwpkm_stream_step", ctypes.byref(c), B, T, q, fake, fake, fake, fake, fake, o, None, state,
-                   p, ws, wsb, None)
+        return _rc("fwpkm_stream_step", ctypes.byref(c), B, T, q, fake, fake, fake, fake, fake, o, None, None,
+                   state, p, ws, wsb, None)
 
     assert step(1, 1, fake, fake, fake, None, fake, 1 << 30) == fwpkm.EINVAL          # pos NULL
     assert step(1, 1, None, fake, fake, ctypes.byref(pos), fake, 1 << 30) == fwpkm.EINVAL  # q missing
@@ -202,3 +202,16 @@ def test_stream_entry_points_reject_before_launch():
     assert _rc("fwpkm_stream_flush", ctypes.byref(c), 2, None, None, fake, fake, fake, ctypes.byref(p), fake,
                1 << 30, None) == fwpkm.EINVAL  # K1 missing
     assert p.pending == 3
+
+
+def test_usage_entry_points_reject_before_launch():
+    c = fwpkm.cfg_struct(GOOD)
+    fake = ctypes.c_void_p(0x1000)
+    assert _rc("fwpkm_usage_metrics", ctypes.byref(c), 2, None, fake, 1, fake, 4096, None) == fwpkm.EINVAL
+    assert _rc("fwpkm_usage_metrics", ctypes.byref(c), 2, fake, None, 0, fake, 4096, None) == fwpkm.EINVAL
+    assert _rc("fwpkm_usage_metrics", ctypes.byref(c), -1, fake, fake, 0, fake, 4096, None) == fwpkm.EINVAL
+    assert _rc("fwpkm_usage_metrics", ctypes.byref(c), 2, fake, fake, 0, fake, 4095, None) == fwpkm.EWORKSPACE
+    assert _rc("fwpkm_usage_metrics", ctypes.byref(c), 0, None, None, 0, None, 0, None) == fwpkm.OK
+    # forward_seq_usage validates like forward_seq (o missing)
+    assert _rc("fwpkm_forward_seq_usage", ctypes.byref(c), 1, 4, 1, fake, fake, fake, None, fake, fake, fake, None,
+               None, fake, fake, 1 << 30, None) == fwpkm.EINVAL
