@@ -198,6 +198,51 @@ def pair_p(c, q, K1, K2, slots):
     return P
 
 
+def _f64(c, x):
+    """Storage array (fp32, or bf16 bit patterns) -> float64 numpy, exactly."""
+    a = _np(x, _sdt(c))
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def retrieve_backward(c, q, v, g, K1, K2, V, idx, dO):
+    """Gradients of the retrieval output o w.r.t. q, v and g for the upstream
+    gradient dO[B,T,d_v], the slot selection idx[B,T,H,k] held fixed (top-k
+    is piecewise constant) and the state (K1, K2, V) as given.
+
+    The forward is written out in plain torch (CPU, float64) from the same
+    definitions as fwo_retrieve: per head and half d = ||q_half - K_i||^2,
+    pair score S = -log(eps + d1) - log(eps + d2) of each selected slot
+    i*n + j, w = softmax of the k scores, v_hat = (1/H) sum_h sum_j w V[slot],
+    o = g v_hat + (1 - g) v; torch autograd takes the gradient.
+    Returns dict(dq [B,T,H,d_q], dv [B,T,d_v], dg [B,T], o [B,T,d_v]) float64."""
+    import torch
+    n, H, dh = c.n, c.heads, c.d_q // 2
+    qt = torch.tensor(_f64(c, q), requires_grad=True)
+    vt = torch.tensor(_f64(c, v), requires_grad=True)
+    gt = torch.tensor(_np(g, np.float32).astype(np.float64), requires_grad=True)
+    K1t, K2t, Vt = (torch.tensor(_f64(c, x)) for x in (K1, K2, V))
+    it = torch.tensor(_np(idx, np.int32).astype(np.int64))
+    G = torch.tensor(np.asarray(dO, dtype=np.float64))
+    B, T = gt.shape
+    k = it.shape[-1]
+    bi = torch.arange(B).view(B, 1, 1, 1).expand(B, T, H, k)
+    hi = torch.arange(H).view(1, 1, H, 1).expand(B, T, H, k)
+    qh = qt.view(B, T, H, 2, dh)
+    k1 = K1t[bi, hi, it // n]  # [B,T,H,k,dh]
+    k2 = K2t[bi, hi, it % n]
+    d1 = ((qh[:, :, :, None, 0, :] - k1) ** 2).sum(-1)
+    d2 = ((qh[:, :, :, None, 1, :] - k2) ** 2).sum(-1)
+    S = -torch.log(c.idw_eps + d1) - torch.log(c.idw_eps + d2)
+    w = torch.softmax(S, dim=-1)
+    rows = Vt[bi, it]  # [B,T,H,k,d_v]
+    vhat = (w[..., None] * rows).sum(3).mean(2)
+    o = gt[..., None] * vhat + (1.0 - gt[..., None]) * vt
+    (o * G).sum().backward()
+    return {"dq": qt.grad.numpy(), "dv": vt.grad.numpy(), "dg": gt.grad.numpy(), "o": o.detach().numpy()}
+
+
 def usage_counts(c, idx):
     """Row contributions ([layer] D.3): the number of reads of every value
     row, per sequence, from slot ids idx[B, T, H, k] -> [B, n*n] int64."""

@@ -495,6 +495,64 @@ def test_stream_carries_state_across_sequences():
     assert not np.array_equal(st.V, a["V"])
 
 
+# ---------------------------------------------------------------- backward through retrieval
+def _bw_problem(seed=5, store="f32", k=4):
+    cfg = FwpkmConfig(n=6, heads=2, d_q=4, d_v=8, k_half=4, k=k, chunk=8, store=store)
+    q, v, g, K1, K2, V = _rand_problem(cfg, 2, 5, seed)
+    dO = np.random.default_rng(seed).standard_normal((2, 5, cfg.d_v))
+    return cfg, q, v, g, K1, K2, V, dO
+
+
+def test_backward_forward_matches_oracle_retrieve():
+    """The torch statement of the forward reproduces the C oracle's o."""
+    cfg, q, v, g, K1, K2, V, dO = _bw_problem()
+    r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
+    b = oracle.retrieve_backward(cfg, q, v, g, K1, K2, V, r["idx"], dO)
+    assert np.allclose(b["o"], r["o"], rtol=1e-12, atol=1e-12)
+
+
+def test_backward_equals_central_differences_of_the_c_oracle():
+    cfg, q, v, g, K1, K2, V, dO = _bw_problem()
+    r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
+    b = oracle.retrieve_backward(cfg, q, v, g, K1, K2, V, r["idx"], dO)
+    rng = np.random.default_rng(11)
+    # steps well above the fp32 rounding of the stored inputs; o is linear in v and g
+    hq, hv, hg = 1e-4, 1e-3, 1e-2
+
+    def L(qq, vv, gg):
+        rr = oracle.retrieve(cfg, qq, vv, gg, K1, K2, V)
+        assert np.array_equal(rr["idx"], r["idx"])  # the step keeps the selection
+        return float((rr["o"] * dO).sum())
+
+    for _ in range(3):
+        dq = torch.tensor(rng.standard_normal(q.shape), dtype=torch.float32)
+        num = (L(q + hq * dq, v, g) - L(q - hq * dq, v, g)) / (2 * hq)
+        assert math.isclose(num, float((b["dq"] * dq.double().numpy()).sum()), rel_tol=2e-3, abs_tol=1e-6)
+        dv = torch.tensor(rng.standard_normal(v.shape), dtype=torch.float32)
+        num = (L(q, v + hv * dv, g) - L(q, v - hv * dv, g)) / (2 * hv)
+        assert math.isclose(num, float((b["dv"] * dv.double().numpy()).sum()), rel_tol=1e-3, abs_tol=1e-6)
+        dg = torch.tensor(rng.standard_normal(g.shape), dtype=torch.float32) * 0.1
+        num = (L(q, v, g + hg * dg) - L(q, v, g - hg * dg)) / (2 * hg)
+        assert math.isclose(num, float((b["dg"] * dg.double().numpy()).sum()), rel_tol=1e-3, abs_tol=1e-6)
+
+
+def test_backward_special_cases():
+    cfg, q, v, g, K1, K2, V, dO = _bw_problem()
+    r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
+    # closed-gate tokens: o = v, so dq = 0, dv = dO, dg = dO . (vhat - v)
+    g0 = torch.zeros_like(g)
+    b = oracle.retrieve_backward(cfg, q, v, g0, K1, K2, V, r["idx"], dO)
+    assert np.array_equal(b["dq"], np.zeros_like(b["dq"]))
+    assert np.allclose(b["dv"], dO)
+    assert np.allclose(b["dg"], (dO * (r["vhat"] - v.double().numpy())).sum(-1))
+    # one slot per head: w = 1, no gradient reaches q
+    c1 = cfg.replace(k=1)
+    r1 = oracle.retrieve(c1, q, v, g, K1, K2, V)
+    b1 = oracle.retrieve_backward(c1, q, v, g, K1, K2, V, r1["idx"], dO)
+    assert np.abs(b1["dq"]).max() == 0.0
+    assert np.allclose(b1["dv"], (1 - g.double().numpy())[..., None] * dO)
+
+
 # ---------------------------------------------------------------- addressing metrics
 def test_usage_metrics_closed_forms():
     """[layer] D.3: coverage, collision and KLD of row contributions."""
