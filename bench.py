@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time streaming decode (one token per call per sequence) instead of forward_seq")
     ap.add_argument("--decode-tokens", type=int, default=1024, help="timed decode tokens per sequence")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fwpkm_forward_seq_backward (replayed pass with gradients w.r.t. q, v, g)")
     ap.add_argument("--usage", action="store_true",
                     help="time forward_seq with row-contribution counting and the addressing metrics")
     return ap.parse_args()
@@ -247,6 +249,68 @@ def usage_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V):
     print(json.dumps(result), flush=True)
 
 
+def backward_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V):
+    """fwpkm_forward_seq_backward: the pass replayed with each chunk's gradient
+    of o w.r.t. q, v and g.  Prints one JSON line."""
+    import torch
+    from sparse_weight_memory_sub_amd import fwpkm
+
+    dev = q.device
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(fwpkm.workspace_bytes(cfg, B, T), dtype=torch.uint8, device=dev)
+    dO = torch.randn((B, T, cfg.d_v), generator=torch.Generator().manual_seed(7)).to(dev)
+
+    def step():
+        fwpkm.fwpkm_forward_seq_backward(cfg, q, v, g, K1, K2, V, dO, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+
+    def timed(events):
+        fwpkm.timing_enable(events)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        fwpkm.timing_enable(False)
+        return start.elapsed_time(stop) / args.steps
+
+    ms = timed(False)
+    ms_ev = timed(True)
+    tk = fwpkm.timing_read()
+    es = 2 if cfg.store == "bf16" else 4
+    H, k, dv, dq, dh = cfg.heads, cfg.k, cfg.d_v, cfg.d_q, cfg.d_h
+    per_tok = (H * k * (dv * es + 8)          # selected value rows, slot ids and weights
+               + H * dq * es + dv * es + 4    # q, v, g
+               + 4 * dv                       # dO
+               + 4 * H * dq + 4 * dv + 4)     # dq, dv, dg written
+    Tc = min(cfg.chunk, T)
+    bwt, bwn = tk["backward"]
+    avg = bwt / bwn
+    # plus the codebooks once per launch (the selected sub-key rows are reread from L2)
+    nbytes = B * Tc * per_tok + B * H * 2 * cfg.n * dh * es
+    ach = nbytes / (avg / 1e3) / 1e9
+    kernels = {name: {"avg_ms": t / n, "launches": n} for name, (t, n) in tk.items() if n}
+    log(f"forward_seq_backward: {ms:.3f} ms/step; backward kernel {avg * 1e3:.1f} us per chunk, {ach:.0f} GB/s")
+    result = {
+        "metric": "FwPKM replayed pass with gradients w.r.t. q, v, g: tokens/s",
+        "value": B * T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.store, "data": "synthetic",
+        "config": {"workload": f"{wl.name}-backward", "n_slots": cfg.N, "heads": H, "d_q": dq, "d_v": dv,
+                   "k": k, "chunk": cfg.chunk, "batch": B, "seq_len": T},
+        "ms_per_step_with_kernel_events": ms_ev,
+        "roofline": {"kernel": "backward", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": nbytes,
+                     "avg_launch_ms": avg},
+        "kernels": kernels,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -278,6 +342,9 @@ def main():
         return
     if args.usage:
         usage_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V)
+        return
+    if args.backward:
+        backward_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V)
         return
 
     want_cpu = not (args.no_cpu_baseline or args.profile_only)

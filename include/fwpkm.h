@@ -174,6 +174,27 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Gradient of fwpkm_retrieve's output o with respect to q, v and g, for the
+ * upstream gradient dO[B][T][d_v] float, with the slot selection idx and the
+ * state (K1, K2, V) those outputs were retrieved with held fixed (the top-k
+ * selection is piecewise constant; the fast weights are given, not trained
+ * by this gradient).  With G = dO_t, per token:
+ *   dg_t = G . (vhat_t - v_t),  dv_t = (1 - g_t) G,
+ *   a_j = (g_t/H) G . V[idx_j],  dS_j = w_j (a_j - sum_{l in head} w_l a_l),
+ *   dq_half = sum_j dS_j * (-2) (q_half - K_half[sub_j]) / (eps + ||q_half - K_half[sub_j]||^2)
+ * (S_j = -log(eps + d1) - log(eps + d2) is the pair score of [layer] A.2,
+ * w = softmax(S) over the head's k slots).
+ * Inputs:  q, v, g, K1, K2, V as for fwpkm_retrieve; idx[B][T][H][k] int32
+ *          and w[B][T][H][k] float as returned by it for this state.
+ * Outputs: dq[B][T][H][d_q], dv[B][T][d_v], dg[B][T], all float.
+ */
+int fwpkm_retrieve_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T,
+                            const void* q, const void* v, const float* g,
+                            const void* K1, const void* K2, const void* V,
+                            const int32_t* idx, const float* w, const float* dO,
+                            float* dq, float* dv, float* dg, void* stream);
+
+/*
  * Whole sequences: chunks of C tokens in causal order, each read with the
  * state left by the previous chunk and then written ([layer] 3, 3.1), the
  * whole input repeated `passes` times with state carried (iterative
@@ -199,6 +220,25 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
                       void* K1, void* K2, void* V,
                       float* o, float* vhat,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gradients of fwpkm_forward_seq's output o (of its last pass) with respect to
+ * q, v and g, for the upstream gradient dO[B][T][d_v] float, by replay: call
+ * it with the state (K1, K2, V) that fwpkm_forward_seq started from.  It runs
+ * the same chunks in the same order (one kernel at a time on `stream`), so it
+ * rewrites the state exactly as the forward did and, when o is given,
+ * reproduces o bit for bit; each chunk of the last pass also gets
+ * fwpkm_retrieve_backward's gradient against the state that chunk was read
+ * with, before that chunk's write.  The fast-weight writes themselves are not
+ * differentiated (each chunk's state is taken as given).
+ * Outputs: dq[B][T][H][d_q], dv[B][T][d_v], dg[B][T] float (required);
+ *          o[B][T][d_v] float (nullable).
+ */
+int fwpkm_forward_seq_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
+                               const void* q, const void* v, const float* g, const void* v_next,
+                               void* K1, void* K2, void* V,
+                               const float* dO, float* dq, float* dv, float* dg, float* o,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /*
  * fwpkm_forward_seq that also counts row contributions for the addressing
@@ -309,7 +349,8 @@ typedef enum {
     FWPKM_K_QT = 12,            /* transposed query halves for the sub-key step    */
     FWPKM_K_PEND = 13,          /* copies into a stream's pending chunk            */
     FWPKM_K_USAGE = 14,         /* row-contribution counts and addressing metrics  */
-    FWPKM_K_COUNT = 15
+    FWPKM_K_BACKWARD = 15,      /* gradient of the retrieval output                */
+    FWPKM_K_COUNT = 16
 } fwpkm_kernel;
 
 /*

@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libfwpkm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["fwpkm_api.cpp", "k_score.hip", "k_gather.hip", "k_sort.hip", "k_scatter.hip", "k_addr.hip",
-           "k_usage.hip"]
+           "k_usage.hip", "k_backward.hip"]
 
 ARCH = os.environ.get("FWPKM_OFFLOAD_ARCH", "gfx950")
 

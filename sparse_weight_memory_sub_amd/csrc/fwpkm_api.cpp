@@ -644,23 +644,31 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
     return ok();
 }
 
-int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q, const void* v,
-                      const float* g, const void* v_next, void* K1, void* K2, void* V, float* o, float* vhat,
-                      void* ws, size_t ws_bytes, void* stream) {
-    return fwpkm_forward_seq_usage(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, vhat, nullptr, ws, ws_bytes,
-                                   stream);
-}
+}  // extern "C"
 
-int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q,
-                            const void* v, const float* g, const void* v_next, void* K1, void* K2, void* V, float* o,
-                            float* vhat, int32_t* usage, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Gradient outputs of a replayed pass (fwpkm_forward_seq_backward).
+struct SeqGrad {
+    const float* dO;
+    float* dq;
+    float* dv;
+    float* dg;
+};
+
+int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q, const void* v,
+                     const float* g, const void* v_next, void* K1, void* K2, void* V, float* o, float* vhat,
+                     int32_t* usage, const SeqGrad* grad, void* ws, size_t ws_bytes, void* stream) {
     Plan p;
     int rc = make_plan(cfg, &p);
     if (rc) return rc;
     if (B < 0 || T < 0) return fail(FWPKM_EINVAL, "B and T must be >= 0");
     if (passes < 1) return fail(FWPKM_EINVAL, "passes must be >= 1 (got %d)", passes);
     if (B == 0 || T == 0) return ok();
-    if (!q || !v || !g || !K1 || !K2 || !V || !o) return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V and o are required");
+    if (!q || !v || !g || !K1 || !K2 || !V || (!o && !grad))
+        return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V and o are required");
+    if (grad && (!grad->dO || !grad->dq || !grad->dv || !grad->dg))
+        return fail(FWPKM_EINVAL, "dO, dq, dv and dg are required");
     const int Cm = std::min(T, p.C);
     if (static_cast<int64_t>(B) * Cm * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*C*heads*k too large");
     const Layout L = layout(p, B, Cm, true, true, 2);
@@ -677,7 +685,9 @@ int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t 
     Aux* ax = nullptr;
     HIP_TRY(aux_streams(&ax));
     const char* env_single = std::getenv("FWPKM_SINGLE_STREAM");
-    const bool single = timing().on || (env_single && env_single[0] == '1');
+    // the replay for gradients keeps every kernel in order on one stream:
+    // a chunk's gradient reads V and K before that chunk's write
+    const bool single = timing().on || (env_single && env_single[0] == '1') || grad != nullptr;
     hipStream_t sv = single ? s : ax->sv;
     // With two streams the value path of a chunk runs as two half-batch
     // launches of gather + write: between them the key path's kernels find
@@ -747,7 +757,7 @@ int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t 
                 ga.n_tgt = n_tgt;
                 ga.tgt_last = tgt_last ? static_cast<const unsigned char*>(tgt_last) + bo * p.dv * p.es : nullptr;
                 ga.tgt_last_bstride = p.dv;
-                ga.o = last_pass ? o + bo * vbs + static_cast<size_t>(t0) * p.dv : nullptr;
+                ga.o = (last_pass && o) ? o + bo * vbs + static_cast<size_t>(t0) * p.dv : nullptr;
                 ga.vhat = (last_pass && vhat) ? vhat + bo * vbs + static_cast<size_t>(t0) * p.dv : nullptr;
                 ga.o_bstride = vbs;
                 ga.r = at<float>(ws, L.r) + bo * Tc * p.dv;
@@ -756,6 +766,26 @@ int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t 
                 {
                     TimedLaunch tl(FWPKM_K_GATHER, sv);
                     HIP_TRY(launch_gather(ga, p.store, sv));
+                }
+                if (grad && last_pass) {
+                    // gradient of this chunk's o against the state it was read from
+                    const size_t t0s = static_cast<size_t>(t0);
+                    BackwardArgs ba{};
+                    ba.q = qc + bo * qb * p.es; ba.q_bstride = qb;
+                    ba.v = ga.v; ba.v_bstride = vbs;
+                    ba.g = ga.g; ba.g_bstride = T;
+                    ba.idx = ga.idx; ba.w = ga.w; ba.iw_bstride = iwb;
+                    ba.K1 = static_cast<const unsigned char*>(K1) + bo * p.H * p.n * p.dh * p.es;
+                    ba.K2 = static_cast<const unsigned char*>(K2) + bo * p.H * p.n * p.dh * p.es;
+                    ba.V = ga.V;
+                    ba.dO = grad->dO + bo * vbs + t0s * p.dv;
+                    ba.dq = grad->dq + bo * qb + t0s * p.H * p.dq;
+                    ba.dv_out = grad->dv + bo * vbs + t0s * p.dv;
+                    ba.dg = grad->dg + bo * T + t0s;
+                    ba.B = nb; ba.T = Tc; ba.n = p.n; ba.H = p.H; ba.dh = p.dh; ba.dv = p.dv; ba.k = p.k;
+                    ba.N = p.N; ba.eps = p.eps;
+                    TimedLaunch tl(FWPKM_K_BACKWARD, sv);
+                    HIP_TRY(launch_backward(ba, p.store, sv));
                 }
                 rc = write_rows(p, L, ws, b0, nb, Tc, n_tgt, w, iwb, V, nullptr, sorted, sv);
                 if (rc) return rc;
@@ -772,6 +802,33 @@ int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t 
     HIP_TRY(hipEventRecord(ax->ev_end, sv));
     HIP_TRY(hipStreamWaitEvent(s, ax->ev_end, 0));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q, const void* v,
+                      const float* g, const void* v_next, void* K1, void* K2, void* V, float* o, float* vhat,
+                      void* ws, size_t ws_bytes, void* stream) {
+    return forward_seq_impl(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, vhat, nullptr, nullptr, ws, ws_bytes,
+                            stream);
+}
+
+int fwpkm_forward_seq_usage(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q,
+                            const void* v, const float* g, const void* v_next, void* K1, void* K2, void* V, float* o,
+                            float* vhat, int32_t* usage, void* ws, size_t ws_bytes, void* stream) {
+    return forward_seq_impl(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, vhat, usage, nullptr, ws, ws_bytes,
+                            stream);
+}
+
+int fwpkm_forward_seq_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q,
+                               const void* v, const float* g, const void* v_next, void* K1, void* K2, void* V,
+                               const float* dO, float* dq, float* dv, float* dg, float* o, void* ws, size_t ws_bytes,
+                               void* stream) {
+    const SeqGrad grad{dO, dq, dv, dg};
+    return forward_seq_impl(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, nullptr, nullptr, &grad, ws, ws_bytes,
+                            stream);
 }
 
 int fwpkm_stream_state_bytes(const fwpkm_cfg* cfg, int32_t B, size_t* bytes) {
@@ -871,6 +928,26 @@ int fwpkm_stream_flush(const fwpkm_cfg* cfg, int32_t B, const void* v_next, void
     rc = stream_fire(p, S, state, B, pend, n_tgt, K1, K2, V, ws, s);
     if (rc) return rc;
     pos->pending = 0;
+    return ok();
+}
+
+int fwpkm_retrieve_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q, const void* v, const float* g,
+                            const void* K1, const void* K2, const void* V, const int32_t* idx, const float* w,
+                            const float* dO, float* dq, float* dv, float* dg, void* stream) {
+    Plan p;
+    int rc = make_plan(cfg, &p);
+    if (rc) return rc;
+    if (B < 0 || T < 0) return fail(FWPKM_EINVAL, "B and T must be >= 0");
+    if (static_cast<int64_t>(B) * T * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*T*heads*k too large");
+    if (B == 0 || T == 0) return ok();
+    if (!q || !v || !g || !K1 || !K2 || !V || !idx || !w || !dO || !dq || !dv || !dg)
+        return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V, idx, w, dO, dq, dv and dg are required");
+    BackwardArgs a{q, static_cast<int64_t>(T) * p.H * p.dq, v, static_cast<int64_t>(T) * p.dv, g, T, idx, w,
+                   static_cast<int64_t>(T) * p.H * p.k, K1, K2, V, dO, dq, dv, dg, B, T, p.n, p.H, p.dh, p.dv, p.k,
+                   p.N, p.eps};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TimedLaunch tl(FWPKM_K_BACKWARD, s);
+    HIP_TRY(launch_backward(a, p.store, s));
     return ok();
 }
 

@@ -134,7 +134,7 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    for (int o = 32; o >= 1; o >>= 1) x += xor_lane(x, o);
     return x;
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
@@ -354,6 +354,35 @@ hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s);
 // the current device: the largest tile whose grid still covers every
 // compute unit, else the smallest.
 int score_tile(int B, int H, int Tc);
+// Gradient of the retrieval output w.r.t. q, v and g for T tokens of B
+// sequences; per-sequence strides in elements:
+//   q, dq (f32):         + b*q_bstride + (t*H + h)*2*dh
+//   v, dO, dv_out (f32): + b*v_bstride + t*dv
+//   g, dg:               + b*g_bstride + t
+//   idx, w:              + b*iw_bstride + (t*H + h)*k
+struct BackwardArgs {
+    const void* q;
+    int64_t q_bstride;
+    const void* v;
+    int64_t v_bstride;
+    const float* g;
+    int64_t g_bstride;
+    const int32_t* idx;
+    const float* w;
+    int64_t iw_bstride;
+    const void* K1;
+    const void* K2;
+    const void* V;
+    const float* dO;
+    float* dq;
+    float* dv_out;
+    float* dg;
+    int B, T, n, H, dh, dv, k;
+    int64_t N;
+    float eps;
+};
+hipError_t launch_backward(const BackwardArgs& a, int store, hipStream_t s);
+
 hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int store, hipStream_t s);

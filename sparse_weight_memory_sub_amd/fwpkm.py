@@ -25,13 +25,14 @@ _STATUS = {OK: "FWPKM_OK", EINVAL: "FWPKM_EINVAL", EUNSUPPORTED: "FWPKM_EUNSUPPO
 
 EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
            "fwpkm_retrieve", "fwpkm_chunk_update", "fwpkm_forward_seq",
-           "fwpkm_forward_seq_usage", "fwpkm_usage_metrics",
+           "fwpkm_retrieve_backward", "fwpkm_forward_seq_backward", "fwpkm_forward_seq_usage",
+           "fwpkm_usage_metrics",
            "fwpkm_stream_state_bytes", "fwpkm_stream_step", "fwpkm_stream_flush",
            "fwpkm_timing_enable", "fwpkm_timing_read")
 
 # kernel families of fwpkm_timing_read, in fwpkm_kernel order
 KERNELS = ("knorm", "score_select", "gather", "resid", "sort", "scatter", "pbar",
-           "score_stats", "score_rowstat", "kgrad", "fill", "select", "qt", "pend", "usage")
+           "score_stats", "score_rowstat", "kgrad", "fill", "select", "qt", "pend", "usage", "backward")
 
 
 class FwpkmError(RuntimeError):
@@ -91,12 +92,15 @@ def load(path: str = LIB_PATH):
         lib.fwpkm_stream_step.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, SP, P, sz, P]
         lib.fwpkm_forward_seq_usage.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_usage_metrics.argtypes = [C, i32, P, P, i32, P, sz, P]
+        lib.fwpkm_retrieve_backward.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.fwpkm_forward_seq_backward.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_stream_flush.argtypes = [C, i32, P, P, P, P, P, SP, P, sz, P]
         lib.fwpkm_timing_enable.argtypes = [i32]
         lib.fwpkm_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq,
                   lib.fwpkm_stream_state_bytes, lib.fwpkm_stream_step, lib.fwpkm_stream_flush,
-                  lib.fwpkm_forward_seq_usage, lib.fwpkm_usage_metrics,
+                  lib.fwpkm_forward_seq_usage, lib.fwpkm_usage_metrics, lib.fwpkm_retrieve_backward,
+                  lib.fwpkm_forward_seq_backward,
                   lib.fwpkm_timing_enable, lib.fwpkm_timing_read):
             f.restype = ctypes.c_int
         _lib = lib
@@ -197,6 +201,31 @@ def fwpkm_retrieve(cfg: FwpkmConfig, q, v, g, K1, K2, V, o=None, vhat=None, idx=
     return {"o": o, "vhat": vhat, "idx": idx, "w": w}
 
 
+def fwpkm_retrieve_backward(cfg: FwpkmConfig, q, v, g, K1, K2, V, idx, w, dO, dq=None, dv=None, dg=None,
+                            stream=None):
+    """Gradient of fwpkm_retrieve's o w.r.t. q, v and g for upstream dO, the
+    selection idx / w and the state held fixed.  Returns dict(dq, dv, dg)."""
+    sd = cfg.torch_dtype
+    B, T = g.shape
+    H, dqd, dvd, k = cfg.heads, cfg.d_q, cfg.d_v, cfg.k
+    dev = g.device
+    _dev(q, "q", sd, (B, T, H, dqd)); _dev(v, "v", sd, (B, T, dvd)); _dev(g, "g", torch.float32, (B, T))
+    _dev(K1, "K1", sd, (B, H, cfg.n, dqd // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dqd // 2))
+    _dev(V, "V", sd, (B, cfg.N, dvd))
+    _dev(idx, "idx", torch.int32, (B, T, H, k)); _dev(w, "w", torch.float32, (B, T, H, k))
+    _dev(dO, "dO", torch.float32, (B, T, dvd))
+    dq = torch.empty((B, T, H, dqd), dtype=torch.float32, device=dev) if dq is None else dq
+    dv = torch.empty((B, T, dvd), dtype=torch.float32, device=dev) if dv is None else dv
+    dg = torch.empty((B, T), dtype=torch.float32, device=dev) if dg is None else dg
+    _dev(dq, "dq", torch.float32, (B, T, H, dqd)); _dev(dv, "dv", torch.float32, (B, T, dvd))
+    _dev(dg, "dg", torch.float32, (B, T))
+    c = _cfg(cfg)
+    _check(load().fwpkm_retrieve_backward(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2),
+                                          _ptr(V), _ptr(idx), _ptr(w), _ptr(dO), _ptr(dq), _ptr(dv), _ptr(dg),
+                                          _stream(stream)))
+    return {"dq": dq, "dv": dv, "dg": dg}
+
+
 def fwpkm_chunk_update(cfg: FwpkmConfig, q, g, tgt, n_tgt: int, idx, w, vhat, K1, K2, V, n_read=None,
                        ws=None, stream=None):
     """One chunk's write; K1, K2, V are updated in place.  Returns n_read (or None)."""
@@ -252,6 +281,33 @@ def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_n
                                               _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat),
                                               _ptr(usage), _ptr(ws), wsb, _stream(stream)))
     return {"o": o, "vhat": vhat}
+
+
+def fwpkm_forward_seq_backward(cfg: FwpkmConfig, q, v, g, K1, K2, V, dO, passes: int = 1, v_next=None,
+                               want_o: bool = False, ws=None, stream=None):
+    """Gradients of forward_seq's o w.r.t. q, v, g by replay from the state
+    forward_seq started with (K1, K2, V are rewritten as the forward did).
+    Returns dict(dq, dv, dg, o)."""
+    sd = cfg.torch_dtype
+    B, T = g.shape
+    H, dqd, dvd = cfg.heads, cfg.d_q, cfg.d_v
+    dev = g.device
+    _dev(q, "q", sd, (B, T, H, dqd)); _dev(v, "v", sd, (B, T, dvd)); _dev(g, "g", torch.float32, (B, T))
+    if v_next is not None:
+        _dev(v_next, "v_next", sd, (B, dvd))
+    _dev(K1, "K1", sd, (B, H, cfg.n, dqd // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dqd // 2))
+    _dev(V, "V", sd, (B, cfg.N, dvd))
+    _dev(dO, "dO", torch.float32, (B, T, dvd))
+    dq = torch.empty((B, T, H, dqd), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, T, dvd), dtype=torch.float32, device=dev)
+    dg = torch.empty((B, T), dtype=torch.float32, device=dev)
+    o = torch.empty((B, T, dvd), dtype=torch.float32, device=dev) if want_o else None
+    ws, wsb = _workspace(cfg, B, T, ws, dev)
+    c = _cfg(cfg)
+    _check(load().fwpkm_forward_seq_backward(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
+                                             _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(dO), _ptr(dq),
+                                             _ptr(dv), _ptr(dg), _ptr(o), _ptr(ws), wsb, _stream(stream)))
+    return {"dq": dq, "dv": dv, "dg": dg, "o": o}
 
 
 def fwpkm_usage_metrics(cfg: FwpkmConfig, usage, reset: bool = False, metrics=None, ws=None, stream=None):

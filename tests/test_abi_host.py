@@ -215,3 +215,22 @@ def test_usage_entry_points_reject_before_launch():
     # forward_seq_usage validates like forward_seq (o missing)
     assert _rc("fwpkm_forward_seq_usage", ctypes.byref(c), 1, 4, 1, fake, fake, fake, None, fake, fake, fake, None,
                None, fake, fake, 1 << 30, None) == fwpkm.EINVAL
+
+
+def test_retrieve_backward_rejects_before_launch():
+    c = fwpkm.cfg_struct(GOOD)
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake] * 12
+    assert _rc("fwpkm_retrieve_backward", ctypes.byref(c), 1, 4, *args[:11], None, None) == fwpkm.EINVAL  # dg missing
+    assert _rc("fwpkm_retrieve_backward", ctypes.byref(c), -1, 4, *args, None) == fwpkm.EINVAL
+    assert _rc("fwpkm_retrieve_backward", ctypes.byref(c), 0, 4, *([None] * 12), None) == fwpkm.OK
+
+
+def test_forward_seq_backward_rejects_before_launch():
+    c = fwpkm.cfg_struct(GOOD)
+    fake = ctypes.c_void_p(0x1000)
+    # dq missing
+    assert _rc("fwpkm_forward_seq_backward", ctypes.byref(c), 1, 4, 1, fake, fake, fake, None, fake, fake, fake,
+               fake, None, fake, fake, None, fake, 1 << 30, None) == fwpkm.EINVAL
+    assert _rc("fwpkm_forward_seq_backward", ctypes.byref(c), 1, 4, 0, fake, fake, fake, None, fake, fake, fake,
+               fake, fake, fake, fake, None, fake, 1 << 30, None) == fwpkm.EINVAL  # passes = 0
