@@ -9,7 +9,8 @@ ctypes.
 
 Configuration objects are duck-typed: anything with the attributes ``n,
 heads, d_q, d_v, k_half, k, chunk, store ('f32'|'bf16'), idw_eps, lr_v, lr_k,
-lookahead, znorm, znorm_eps, use_addr`` works.
+lookahead, znorm, znorm_eps, use_addr`` works (optionally ``gate_weight`` and
+``score`` ('idw' | 'dot'), default True and 'idw').
 
 Storage-typed arrays (q, v, targets, K1, K2, V) are float32 arrays for
 ``store='f32'`` and uint16 arrays holding bf16 bit patterns for
@@ -48,6 +49,7 @@ class _Cfg(ctypes.Structure):
         ("idw_eps", ctypes.c_double), ("lr_v", ctypes.c_double), ("lr_k", ctypes.c_double),
         ("lookahead", ctypes.c_int32), ("znorm", ctypes.c_int32),
         ("znorm_eps", ctypes.c_double), ("use_addr", ctypes.c_int32),
+        ("gate_weight", ctypes.c_int32), ("score", ctypes.c_int32),
     ]
 
 
@@ -83,7 +85,8 @@ def _cfg(c) -> _Cfg:
     return _Cfg(int(c.n), int(c.heads), int(c.d_q), int(c.d_v), int(c.k_half), int(c.k),
                 int(c.chunk), store, float(c.idw_eps), float(c.lr_v), float(c.lr_k),
                 int(bool(c.lookahead)), int(bool(c.znorm)), float(c.znorm_eps),
-                int(bool(c.use_addr)))
+                int(bool(c.use_addr)), int(bool(getattr(c, "gate_weight", True))),
+                {"idw": 0, "dot": 1}[getattr(c, "score", "idw")])
 
 
 def _np(x, dtype):
@@ -213,7 +216,8 @@ def retrieve_backward(c, q, v, g, K1, K2, V, idx, dO):
 
     The forward is written out in plain torch (CPU, float64) from the same
     definitions as fwo_retrieve: per head and half d = ||q_half - K_i||^2,
-    pair score S = -log(eps + d1) - log(eps + d2) of each selected slot
+    pair score S = -log(eps + d1) - log(eps + d2) (with dot scoring
+    S = q1 . K1_i + q2 . K2_j) of each selected slot
     i*n + j, w = softmax of the k scores, v_hat = (1/H) sum_h sum_j w V[slot],
     o = g v_hat + (1 - g) v; torch autograd takes the gradient.
     Returns dict(dq [B,T,H,d_q], dv [B,T,d_v], dg [B,T], o [B,T,d_v]) float64."""
@@ -232,9 +236,12 @@ def retrieve_backward(c, q, v, g, K1, K2, V, idx, dO):
     qh = qt.view(B, T, H, 2, dh)
     k1 = K1t[bi, hi, it // n]  # [B,T,H,k,dh]
     k2 = K2t[bi, hi, it % n]
-    d1 = ((qh[:, :, :, None, 0, :] - k1) ** 2).sum(-1)
-    d2 = ((qh[:, :, :, None, 1, :] - k2) ** 2).sum(-1)
-    S = -torch.log(c.idw_eps + d1) - torch.log(c.idw_eps + d2)
+    if getattr(c, "score", "idw") == "dot":
+        S = (qh[:, :, :, None, 0, :] * k1).sum(-1) + (qh[:, :, :, None, 1, :] * k2).sum(-1)
+    else:
+        d1 = ((qh[:, :, :, None, 0, :] - k1) ** 2).sum(-1)
+        d2 = ((qh[:, :, :, None, 1, :] - k2) ** 2).sum(-1)
+        S = -torch.log(c.idw_eps + d1) - torch.log(c.idw_eps + d2)
     w = torch.softmax(S, dim=-1)
     rows = Vt[bi, it]  # [B,T,H,k,d_v]
     vhat = (w[..., None] * rows).sum(3).mean(2)

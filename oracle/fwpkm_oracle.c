@@ -84,6 +84,7 @@ static int cfg_ok(const fwo_cfg* c) {
     if (c->chunk < 1) return 0;
     if (c->store != FWO_F32 && c->store != FWO_BF16) return 0;
     if (!(c->idw_eps > 0.0)) return 0;
+    if (c->score != FWO_SCORE_IDW && c->score != FWO_SCORE_DOT) return 0;
     return 1;
 }
 
@@ -105,6 +106,14 @@ static int cmp_scored(const void* a, const void* b) {
     return (x->id > y->id) - (x->id < y->id);
 }
 
+/* Dot product of a query half and one sub-key (product-key memory's own
+ * scoring, paperlayer.ai 2.2; the ablation of A.2 / D.1). */
+static double dot_qk(const void* q, size_t qoff, const void* K, size_t koff, int dh, int store) {
+    double acc = 0.0;
+    for (int u = 0; u < dh; ++u) acc += ld(q, qoff + u, store) * ld(K, koff + u, store);
+    return acc;
+}
+
 /* Squared Euclidean distance between a query half and one sub-key, taken
  * directly as a sum of squared differences (IDW scoring, paperlayer.ai
  * A.2: Euclidean distance replaces the dot product). */
@@ -122,9 +131,9 @@ static double sq_dist(const void* q, size_t qoff, const void* K, size_t koff,
 typedef struct {
     int32_t* slot;  /* [k] */
     double* w;      /* [k] */
-    double* P;      /* [k] (eps+d1)(eps+d2) */
-    double* d1;     /* [n] squared distances of half 1 (kept for addressing) */
-    double* d2;     /* [n] squared distances of half 2 */
+    double* P;      /* [k] (eps+d1)(eps+d2); dot scoring: exp(-(s1+s2)) */
+    double* d1;     /* [n] half 1, kept for addressing: squared distances (IDW) or dot products */
+    double* d2;     /* [n] half 2 */
     uint8_t tie;
 } pk_result;
 
@@ -150,12 +159,18 @@ static void pk_search(const fwo_cfg* c, const void* qtok, const void* K1h,
     scored* h2 = scratch + n;
     scored* pr = scratch + 2 * n;
 
+    const int dot = c->score == FWO_SCORE_DOT;
     for (int i = 0; i < n; ++i) {
-        R->d1[i] = sq_dist(qtok, 0, K1h, (size_t)i * dh, dh, c->store);
-        R->d2[i] = sq_dist(qtok, dh, K2h, (size_t)i * dh, dh, c->store);
-        h1[i].s = -log(eps + R->d1[i]);
+        if (dot) {
+            R->d1[i] = dot_qk(qtok, 0, K1h, (size_t)i * dh, dh, c->store);
+            R->d2[i] = dot_qk(qtok, dh, K2h, (size_t)i * dh, dh, c->store);
+        } else {
+            R->d1[i] = sq_dist(qtok, 0, K1h, (size_t)i * dh, dh, c->store);
+            R->d2[i] = sq_dist(qtok, dh, K2h, (size_t)i * dh, dh, c->store);
+        }
+        h1[i].s = dot ? R->d1[i] : -log(eps + R->d1[i]);
         h1[i].id = i;
-        h2[i].s = -log(eps + R->d2[i]);
+        h2[i].s = dot ? R->d2[i] : -log(eps + R->d2[i]);
         h2[i].id = i;
     }
     qsort(h1, (size_t)n, sizeof(scored), cmp_scored);
@@ -176,7 +191,7 @@ static void pk_search(const fwo_cfg* c, const void* qtok, const void* K1h,
         R->slot[j] = pr[j].id;
         R->w[j] = exp(pr[j].s - smax) / z;
         int i1 = pr[j].id / n, i2 = pr[j].id % n;
-        R->P[j] = (eps + R->d1[i1]) * (eps + R->d2[i2]);
+        R->P[j] = dot ? exp(-pr[j].s) : (eps + R->d1[i1]) * (eps + R->d2[i2]);
     }
 
     /* Near-tie flag: a decision whose two alternatives differ by less than
@@ -184,19 +199,31 @@ static void pk_search(const fwo_cfg* c, const void* qtok, const void* K1h,
     R->tie = 0;
     if (tie_rel > 0.0) {
         /* (a) which k' sub-keys of each half are kept */
-        if (kh < n) {
-            double in1 = eps + R->d1[h1[kh - 1].id], out1 = eps + R->d1[h1[kh].id];
-            double in2 = eps + R->d2[h2[kh - 1].id], out2 = eps + R->d2[h2[kh].id];
-            if (out1 - in1 <= tie_rel * out1 || out2 - in2 <= tie_rel * out2) R->tie = 1;
-        }
-        /* (b) which k pairs are kept and (c) their order */
-        int last = (k < m) ? k : k - 1;
-        for (int j = 0; j < last; ++j) {
-            int a1 = pr[j].id / n, a2 = pr[j].id % n;
-            int b1 = pr[j + 1].id / n, b2 = pr[j + 1].id % n;
-            double pa = (eps + R->d1[a1]) * (eps + R->d2[a2]);
-            double pb = (eps + R->d1[b1]) * (eps + R->d2[b2]);
-            if (pb - pa <= tie_rel * pb) R->tie = 1;
+        if (dot) {
+            /* dot scores: a gap below tie_rel of the scores' size */
+            if (kh < n) {
+                if (h1[kh - 1].s - h1[kh].s <= tie_rel * (fabs(h1[kh - 1].s) + fabs(h1[kh].s)) ||
+                    h2[kh - 1].s - h2[kh].s <= tie_rel * (fabs(h2[kh - 1].s) + fabs(h2[kh].s)))
+                    R->tie = 1;
+            }
+            int last = (k < m) ? k : k - 1;
+            for (int j = 0; j < last; ++j)
+                if (pr[j].s - pr[j + 1].s <= tie_rel * (fabs(pr[j].s) + fabs(pr[j + 1].s))) R->tie = 1;
+        } else {
+            if (kh < n) {
+                double in1 = eps + R->d1[h1[kh - 1].id], out1 = eps + R->d1[h1[kh].id];
+                double in2 = eps + R->d2[h2[kh - 1].id], out2 = eps + R->d2[h2[kh].id];
+                if (out1 - in1 <= tie_rel * out1 || out2 - in2 <= tie_rel * out2) R->tie = 1;
+            }
+            /* (b) which k pairs are kept and (c) their order */
+            int last = (k < m) ? k : k - 1;
+            for (int j = 0; j < last; ++j) {
+                int a1 = pr[j].id / n, a2 = pr[j].id % n;
+                int b1 = pr[j + 1].id / n, b2 = pr[j + 1].id % n;
+                double pa = (eps + R->d1[a1]) * (eps + R->d2[a2]);
+                double pb = (eps + R->d1[b1]) * (eps + R->d2[b2]);
+                if (pb - pa <= tie_rel * pb) R->tie = 1;
+            }
         }
     }
 }
@@ -218,6 +245,12 @@ int fwo_pair_p(const fwo_cfg* c, int32_t B, int32_t T, int32_t m,
                     int32_t s = slots[o];
                     if (s < 0 || s >= N) { P[o] = NAN; continue; }
                     int i1 = s / n, i2 = s % n;
+                    if (c->score == FWO_SCORE_DOT) {
+                        /* exp(-(s1 + s2)): decreasing in the pair score, like the IDW product */
+                        P[o] = exp(-(dot_qk(q, qoff, K1, koff + (size_t)i1 * dh, dh, c->store) +
+                                     dot_qk(q, qoff + dh, K2, koff + (size_t)i2 * dh, dh, c->store)));
+                        continue;
+                    }
                     double d1 = 0.0, d2 = 0.0;
                     for (int u = 0; u < dh; ++u) {
                         double x = ld(q, qoff + u, c->store) - ld(K1, koff + (size_t)i1 * dh + u, c->store);
@@ -346,7 +379,8 @@ static void memorise_one(const fwo_cfg* c, int32_t Tc, int32_t n_tgt,
             const double inv = 1.0 / sqrt(var + c->znorm_eps);
             for (int e = 0; e < dv; ++e) y[e] = (y[e] - mean) * inv;
         }
-        const double gt = (double)g_b[t];
+        /* the gate weights the token's reconstruction error (A.5), unless disabled */
+        const double gt = c->gate_weight ? (double)g_b[t] : 1.0;
         for (int e = 0; e < dv; ++e) r[e] = gt * (vhat_b[(size_t)t * dv + e] - y[e]);
         for (int h = 0; h < H; ++h)
             for (int j = 0; j < k; ++j) {
@@ -386,7 +420,9 @@ static void memorise_one(const fwo_cfg* c, int32_t Tc, int32_t n_tgt,
 /*
  * K step of one codebook (one sequence, head and half) for one chunk
  * (rainbus digest method step 5; paperlayer.ai 3.4):
- *   p_t = softmax(s_t) over all n sub-keys, s_{t,i} = -log(eps + d_{t,i});
+ *   p_t = softmax(s_t) over all n sub-keys, s_{t,i} = -log(eps + d_{t,i})
+ *   (or s_{t,i} = q_t . K_i with dot-product scoring, where dist holds the
+ *   dot products and ds/dK_i = q_t);
  *   pbar = (1/Tc) sum_t p_t;  L = -H(pbar) = sum_i pbar_i ln pbar_i.
  * Gradient by the chain rule through the softmax and the IDW score:
  *   dL/ds_{t,i} = (1/Tc) p_{t,i} (ln pbar_i - m_t), m_t = sum_l p_{t,l} ln pbar_l;
@@ -399,16 +435,17 @@ static void address_one(const fwo_cfg* c, int32_t Tc, const double* dist, size_t
                         void* Kh, double* p, double* lp, double* m, double* grad) {
     const int n = c->n, dh = c->d_q / 2;
     const double eps = c->idw_eps;
+    const int dot = c->score == FWO_SCORE_DOT;
     for (int t = 0; t < Tc; ++t) {
         const double* d = dist + (size_t)t * dist_stride;
         double smax = -INFINITY;
         for (int i = 0; i < n; ++i) {
-            double s = -log(eps + d[i]);
+            double s = dot ? d[i] : -log(eps + d[i]);
             if (s > smax) smax = s;
         }
         double z = 0.0;
-        for (int i = 0; i < n; ++i) z += exp(-log(eps + d[i]) - smax);
-        for (int i = 0; i < n; ++i) p[(size_t)t * n + i] = exp(-log(eps + d[i]) - smax) / z;
+        for (int i = 0; i < n; ++i) z += exp((dot ? d[i] : -log(eps + d[i])) - smax);
+        for (int i = 0; i < n; ++i) p[(size_t)t * n + i] = exp((dot ? d[i] : -log(eps + d[i])) - smax) / z;
     }
     for (int i = 0; i < n; ++i) {
         double s = 0.0;
@@ -424,10 +461,11 @@ static void address_one(const fwo_cfg* c, int32_t Tc, const double* dist, size_t
         for (int u = 0; u < dh; ++u) grad[u] = 0.0;
         for (int t = 0; t < Tc; ++t) {
             const double dLds = p[(size_t)t * n + i] * (lp[i] - m[t]) / Tc;
-            const double scale = 2.0 / (eps + dist[(size_t)t * dist_stride + i]);
+            /* ds/dK_i: 2 (q - K_i) / (eps + d) for IDW, q for the dot product */
+            const double scale = dot ? 1.0 : 2.0 / (eps + dist[(size_t)t * dist_stride + i]);
             for (int u = 0; u < dh; ++u) {
                 const double qu = ld(q_b, (size_t)t * q_stride_tok + q_off + u, c->store);
-                const double ku = ld(Kh, (size_t)i * dh + u, c->store);
+                const double ku = dot ? 0.0 : ld(Kh, (size_t)i * dh + u, c->store);
                 grad[u] += dLds * scale * (qu - ku);
             }
         }
@@ -524,7 +562,8 @@ int fwo_chunk_update(const fwo_cfg* c, int32_t B, int32_t Tc, int32_t n_tgt,
     const int64_t N = (int64_t)n * n;
     if (n_read) memset(n_read, 0, sizeof(int32_t) * (size_t)B * (size_t)N);
 
-    /* distances with the chunk's (pre-update) keys */
+    /* distances (or dot products) with the chunk's (pre-update) keys */
+    const int dot = c->score == FWO_SCORE_DOT;
     double* dist1 = (double*)malloc(sizeof(double) * (size_t)B * Tc * H * n);
     double* dist2 = (double*)malloc(sizeof(double) * (size_t)B * Tc * H * n);
     if (!dist1 || !dist2) { free(dist1); free(dist2); return -1; }
@@ -536,8 +575,13 @@ int fwo_chunk_update(const fwo_cfg* c, int32_t B, int32_t Tc, int32_t n_tgt,
                 const size_t koff = ((size_t)b * H + h) * n * dh;
                 const size_t doff = (((size_t)b * Tc + t) * H + h) * n;
                 for (int i = 0; i < n; ++i) {
-                    dist1[doff + i] = sq_dist(q, qoff, K1, koff + (size_t)i * dh, dh, c->store);
-                    dist2[doff + i] = sq_dist(q, qoff + dh, K2, koff + (size_t)i * dh, dh, c->store);
+                    if (dot) {
+                        dist1[doff + i] = dot_qk(q, qoff, K1, koff + (size_t)i * dh, dh, c->store);
+                        dist2[doff + i] = dot_qk(q, qoff + dh, K2, koff + (size_t)i * dh, dh, c->store);
+                    } else {
+                        dist1[doff + i] = sq_dist(q, qoff, K1, koff + (size_t)i * dh, dh, c->store);
+                        dist2[doff + i] = sq_dist(q, qoff + dh, K2, koff + (size_t)i * dh, dh, c->store);
+                    }
                 }
             }
     mem_ws mw = {NULL, NULL, NULL, NULL};

@@ -26,6 +26,10 @@
  *   mean; z-score per token over d_v with population variance; addressing
  *   distribution p_t = softmax(s_t) over all n sub-keys; chunk average over
  *   the chunk's actual token count; plain SGD steps lr_v, lr_k.
+ * Variants (paperlayer.ai D, the ablation axes): gate_weight = 0 drops the
+ *   gate from the memorisation error (A.5 switched off); score = dot uses
+ *   PKM's dot product s = q . k in place of the IDW score for the selection,
+ *   the weights and the addressing p, with ds/dk = q in the key step.
  *
  * Parity pins: see tests/test_oracle_pins.py.  The readings listed above
  * that the pages do not fix (IDW form and eps, head mean, z-score axis,
@@ -60,7 +64,14 @@ typedef struct {
     int32_t znorm;    /* 1: z-score each target over d_v */
     double znorm_eps; /* variance epsilon of the z-score */
     int32_t use_addr; /* 1: apply the addressing step to K1, K2 */
+    int32_t gate_weight; /* 1: memorisation MSE weighted by the gate g_t; 0: unweighted */
+    int32_t score;    /* FWO_SCORE_IDW or FWO_SCORE_DOT */
 } fwo_cfg;
+
+/* Sub-key scoring: inverse distance s = -log(eps + ||q - k||^2) (the method),
+ * or the plain dot product s = q . k of product-key memory (its ablation). */
+#define FWO_SCORE_IDW 0
+#define FWO_SCORE_DOT 1
 
 /* Layouts (row-major, all per sequence b of the batch):
  *   q[B][T][H][d_q], v[B][T][d_v], tgt[B][n_tgt][d_v] (store dtype)
@@ -104,7 +115,8 @@ int fwo_forward_seq(const fwo_cfg* c, int32_t B, int32_t T, int32_t passes,
                     double* o, double* vhat, int32_t chunk_limit);
 
 /* (eps+d1)(eps+d2) in double for arbitrary slots slots[B][T][H][m]
- * against frozen K1, K2 (used to judge near-tie alternatives). */
+ * against frozen K1, K2 (used to judge near-tie alternatives); with dot
+ * scoring exp(-(s1 + s2)), which orders pairs the same way. */
 int fwo_pair_p(const fwo_cfg* c, int32_t B, int32_t T, int32_t m,
                const void* q, const void* K1, const void* K2,
                const int32_t* slots, double* P);

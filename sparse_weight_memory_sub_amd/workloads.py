@@ -44,6 +44,8 @@ class FwpkmConfig:
     znorm: bool = True
     znorm_eps: float = 1e-5
     use_addr: bool = True
+    gate_weight: bool = True  # memorisation MSE weighted by the gate (paperlayer.ai A.5)
+    score: str = "idw"        # sub-key scoring: 'idw' (paperlayer.ai A.2) or 'dot' (PKM's product)
 
     @property
     def N(self) -> int:

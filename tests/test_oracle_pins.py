@@ -127,6 +127,10 @@ def _full_scores(cfg, q, K1, K2):
     """Scores of all N slots, computed without the product-key restriction."""
     q = np.asarray(q, np.float64); K1 = np.asarray(K1, np.float64); K2 = np.asarray(K2, np.float64)
     dh = cfg.d_q // 2
+    if cfg.score == "dot":
+        s1 = (q[:, :, :, None, :dh].astype(np.float64) * K1[:, None, :, :, :]).sum(-1)  # [B,T,H,n]
+        s2 = (q[:, :, :, None, dh:].astype(np.float64) * K2[:, None, :, :, :]).sum(-1)
+        return (s1[..., :, None] + s2[..., None, :]).reshape(*s1.shape[:-1], -1)
     d1 = ((q[:, :, :, None, :dh] - K1[:, None, :, :, :]) ** 2).sum(-1)  # [B,T,H,n]
     d2 = ((q[:, :, :, None, dh:] - K2[:, None, :, :, :]) ** 2).sum(-1)
     s1 = -np.log(cfg.idw_eps + d1)
@@ -134,9 +138,10 @@ def _full_scores(cfg, q, K1, K2):
     return (s1[..., :, None] + s2[..., None, :]).reshape(*s1.shape[:-1], -1)  # slot = i*n + j
 
 
+@pytest.mark.parametrize("score", ["idw", "dot"])
 @pytest.mark.parametrize("n,kh,k,H", [(4, 4, 4, 1), (8, 5, 5, 2), (12, 6, 3, 1), (16, 8, 8, 3), (16, 16, 16, 1)])
-def test_topk_equals_brute_force_over_all_slots(n, kh, k, H):
-    cfg = FwpkmConfig(n=n, heads=H, d_q=6, d_v=5, k_half=kh, k=k, chunk=8)
+def test_topk_equals_brute_force_over_all_slots(n, kh, k, H, score):
+    cfg = FwpkmConfig(n=n, heads=H, d_q=6, d_v=5, k_half=kh, k=k, chunk=8, score=score)
     q, v, g, K1, K2, V = _rand_problem(cfg, 2, 9, seed=11 + n + k)
     r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
     S = _full_scores(cfg, q.numpy(), K1.numpy(), K2.numpy())
@@ -173,9 +178,11 @@ def _targets(cfg, v):
     return y
 
 
-@pytest.mark.parametrize("H,k,znorm", [(1, 4, False), (2, 3, True), (3, 6, True)])
-def test_value_write_equals_dense_matmul_over_read_counts(H, k, znorm):
-    cfg = FwpkmConfig(n=7, heads=H, d_q=4, d_v=6, k_half=k, k=k, chunk=16, znorm=znorm, use_addr=False)
+@pytest.mark.parametrize("H,k,znorm,gate", [(1, 4, False, True), (2, 3, True, True), (3, 6, True, True),
+                                            (2, 3, True, False)])
+def test_value_write_equals_dense_matmul_over_read_counts(H, k, znorm, gate):
+    cfg = FwpkmConfig(n=7, heads=H, d_q=4, d_v=6, k_half=k, k=k, chunk=16, znorm=znorm, use_addr=False,
+                      gate_weight=gate)
     B, Tc = 2, 16
     q, v, g, K1, K2, V = _rand_problem(cfg, B, Tc, seed=21 + H)
     # many repeated queries so rows are read many times
@@ -192,7 +199,8 @@ def test_value_write_equals_dense_matmul_over_read_counts(H, k, znorm):
                 for j in range(k):
                     S[t, r["idx"][b, t, h, j]] += r["w"][b, t, h, j] / H
                     cnt[r["idx"][b, t, h, j]] += 1
-        R = g.numpy()[b, :n_tgt, None].astype(np.float64) * (r["vhat"][b, :n_tgt] - _targets(cfg, tgt.numpy()[b]))
+        gw = g.numpy()[b, :n_tgt, None].astype(np.float64) if gate else 1.0  # paperlayer.ai A.5 and its ablation
+        R = gw * (r["vhat"][b, :n_tgt] - _targets(cfg, tgt.numpy()[b]))
         G = S.T @ R
         Vb = V.numpy()[b].astype(np.float64)
         want = Vb.copy()
@@ -278,17 +286,20 @@ def _addr_loss(cfg, q, K1, K2):
     L = 0.0
     for half, K in ((0, K1), (1, K2)):
         qh = q[..., half * dh:(half + 1) * dh]  # [B,T,H,dh]
-        d = ((qh[:, :, :, None, :] - K[:, None, :, :, :]) ** 2).sum(-1)  # [B,T,H,n]
-        p = torch.softmax(-torch.log(cfg.idw_eps + d), dim=-1)
+        if cfg.score == "dot":
+            p = torch.softmax((qh[:, :, :, None, :] * K[:, None, :, :, :]).sum(-1), dim=-1)
+        else:
+            d = ((qh[:, :, :, None, :] - K[:, None, :, :, :]) ** 2).sum(-1)  # [B,T,H,n]
+            p = torch.softmax(-torch.log(cfg.idw_eps + d), dim=-1)
         pbar = p.mean(1)  # [B,H,n]
         L = L + (pbar * torch.log(pbar)).sum()
     return L
 
 
-@pytest.mark.parametrize("store", ["f32"])
-def test_key_step_equals_autograd_of_entropy_loss(store):
+@pytest.mark.parametrize("store,score", [("f32", "idw"), ("f32", "dot")])
+def test_key_step_equals_autograd_of_entropy_loss(store, score):
     cfg = FwpkmConfig(n=7, heads=2, d_q=6, d_v=3, k_half=3, k=3, chunk=10, use_addr=True, lr_k=0.7,
-                      store=store)
+                      store=store, score=score)
     B, Tc = 2, 10
     q, v, g, K1, K2, V = _rand_problem(cfg, B, Tc, seed=8)
     r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
@@ -496,23 +507,25 @@ def test_stream_carries_state_across_sequences():
 
 
 # ---------------------------------------------------------------- backward through retrieval
-def _bw_problem(seed=5, store="f32", k=4):
-    cfg = FwpkmConfig(n=6, heads=2, d_q=4, d_v=8, k_half=4, k=k, chunk=8, store=store)
+def _bw_problem(seed=5, store="f32", k=4, score="idw"):
+    cfg = FwpkmConfig(n=6, heads=2, d_q=4, d_v=8, k_half=4, k=k, chunk=8, store=store, score=score)
     q, v, g, K1, K2, V = _rand_problem(cfg, 2, 5, seed)
     dO = np.random.default_rng(seed).standard_normal((2, 5, cfg.d_v))
     return cfg, q, v, g, K1, K2, V, dO
 
 
-def test_backward_forward_matches_oracle_retrieve():
+@pytest.mark.parametrize("score", ["idw", "dot"])
+def test_backward_forward_matches_oracle_retrieve(score):
     """The torch statement of the forward reproduces the C oracle's o."""
-    cfg, q, v, g, K1, K2, V, dO = _bw_problem()
+    cfg, q, v, g, K1, K2, V, dO = _bw_problem(score=score)
     r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
     b = oracle.retrieve_backward(cfg, q, v, g, K1, K2, V, r["idx"], dO)
     assert np.allclose(b["o"], r["o"], rtol=1e-12, atol=1e-12)
 
 
-def test_backward_equals_central_differences_of_the_c_oracle():
-    cfg, q, v, g, K1, K2, V, dO = _bw_problem()
+@pytest.mark.parametrize("score", ["idw", "dot"])
+def test_backward_equals_central_differences_of_the_c_oracle(score):
+    cfg, q, v, g, K1, K2, V, dO = _bw_problem(score=score)
     r = oracle.retrieve(cfg, q, v, g, K1, K2, V)
     b = oracle.retrieve_backward(cfg, q, v, g, K1, K2, V, r["idx"], dO)
     rng = np.random.default_rng(11)
