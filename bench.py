@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time streaming decode (one token per call per sequence) instead of forward_seq")
     ap.add_argument("--decode-tokens", type=int, default=1024, help="timed decode tokens per sequence")
+    ap.add_argument("--score", choices=("idw", "dot"), default=None,
+                    help="sub-key scoring variant (default: the workload's, IDW)")
+    ap.add_argument("--no-gate-weight", action="store_true",
+                    help="memorisation error without the gate weighting (an ablation)")
     ap.add_argument("--backward", action="store_true",
                     help="time fwpkm_forward_seq_backward (replayed pass with gradients w.r.t. q, v, g)")
     ap.add_argument("--usage", action="store_true",
@@ -326,6 +330,11 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     wl = WORKLOADS[args.workload]
     cfg, B, T = wl.cfg, wl.B, wl.T
+    if args.score or args.no_gate_weight:
+        cfg = cfg.replace(score=args.score or cfg.score, gate_weight=not args.no_gate_weight and cfg.gate_weight)
+        wl = wl.__class__(**{**wl.__dict__, "cfg": cfg,
+                             "name": wl.name + ("-dot" if cfg.score == "dot" else "")
+                             + ("-nogate" if not cfg.gate_weight else "")})
     passes = args.passes or wl.passes
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -401,6 +410,7 @@ def main():
         "dtype": cfg.store, "data": "synthetic",
         "config": {"workload": wl.name, "n_slots": cfg.N, "heads": cfg.heads, "d_q": cfg.d_q, "d_v": cfg.d_v,
                    "k_half": cfg.k_half, "k": cfg.k, "chunk": cfg.chunk, "batch": B, "seq_len": T,
+                   "score": cfg.score, "gate_weight": cfg.gate_weight,
                    "passes": passes, "storage": cfg.store, "accumulate": "f32", "state": "carried across steps"},
     }
     if args.profile_only:

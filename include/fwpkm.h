@@ -42,9 +42,12 @@
 extern "C" {
 #endif
 
-#define FWPKM_ABI_VERSION 1
+#define FWPKM_ABI_VERSION 2
 
 typedef enum { FWPKM_F32 = 0, FWPKM_BF16 = 1 } fwpkm_dtype;
+
+/* Sub-key scoring (fwpkm_cfg.score). */
+typedef enum { FWPKM_SCORE_IDW = 0, FWPKM_SCORE_DOT = 1 } fwpkm_score;
 
 typedef enum {
     FWPKM_OK = 0,
@@ -83,6 +86,14 @@ typedef enum {
  *   znorm    1: z-score each target over d_v ([layer] A.3).
  *   znorm_eps variance epsilon of the z-score.
  *   use_addr 1: apply the addressing step to K1, K2 ([digest] step 5).
+ *   gate_weight 1: the memorisation error of token t is weighted by its gate
+ *            g_t ([layer] A.5); 0: unweighted (the ablation of [layer] D).
+ *   score    FWPKM_SCORE_IDW: s = -log(eps + ||q_half - K_i||^2) ([layer] A.2);
+ *            FWPKM_SCORE_DOT: s = q_half . K_i, product-key memory's own
+ *            scoring ([layer] 2.2; the ablation of A.2 and D.1).  The score
+ *            drives the top-k' and top-k (pair score s1 + s2), the weights
+ *            (softmax of the k pair scores) and the addressing distribution
+ *            p_t = softmax(s_t); the key step uses ds/dK_i = q_t.
  */
 typedef struct {
     int32_t n;
@@ -100,6 +111,8 @@ typedef struct {
     int32_t znorm;
     float znorm_eps;
     int32_t use_addr;
+    int32_t gate_weight;
+    int32_t score;
 } fwpkm_cfg;
 
 /* FWPKM_ABI_VERSION of the loaded library. */

@@ -141,7 +141,7 @@ struct Plan {
     int n, H, dq, dh, dv, kh, k, C, store, es;
     int64_t N;
     float eps, lr_v, lr_k, zeps;
-    int look, znorm, addr;
+    int look, znorm, addr, gate, dot;
     CandTable cand;
     int ncand;
     int sort_passes;
@@ -159,6 +159,8 @@ int make_plan(const fwpkm_cfg* c, Plan* p) {
         return fail(FWPKM_EINVAL, "k must be in [1, k_half^2] (got %d)", c->k);
     if (c->chunk < 1) return fail(FWPKM_EINVAL, "chunk must be >= 1 (got %d)", c->chunk);
     if (c->store != FWPKM_F32 && c->store != FWPKM_BF16) return fail(FWPKM_EINVAL, "store must be FWPKM_F32 or FWPKM_BF16");
+    if (c->score != FWPKM_SCORE_IDW && c->score != FWPKM_SCORE_DOT)
+        return fail(FWPKM_EINVAL, "score must be FWPKM_SCORE_IDW or FWPKM_SCORE_DOT");
     if (!(c->idw_eps > 0.f) || !std::isfinite(c->idw_eps)) return fail(FWPKM_EINVAL, "idw_eps must be finite and > 0");
     if (!std::isfinite(c->lr_v) || !std::isfinite(c->lr_k)) return fail(FWPKM_EINVAL, "lr_v and lr_k must be finite");
     if (!(c->znorm_eps >= 0.f) || !std::isfinite(c->znorm_eps)) return fail(FWPKM_EINVAL, "znorm_eps must be finite and >= 0");
@@ -180,6 +182,7 @@ int make_plan(const fwpkm_cfg* c, Plan* p) {
     p->N = static_cast<int64_t>(c->n) * c->n;
     p->eps = c->idw_eps; p->lr_v = c->lr_v; p->lr_k = c->lr_k; p->zeps = c->znorm_eps;
     p->look = c->lookahead != 0; p->znorm = c->znorm != 0; p->addr = c->use_addr != 0;
+    p->gate = c->gate_weight != 0; p->dot = c->score == FWPKM_SCORE_DOT;
     // product candidates: ranks (a, b) of the two sorted lists with (a+1)(b+1) <= k
     int m = 0;
     std::memset(&p->cand, 0, sizeof p->cand);
@@ -201,8 +204,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, m, part, lp, qT, k0, v0, k1, v1, counts, ph, pt, pts,
-        phe;
+    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, M, m, part, lp, qT, k0, v0, k1, v1, counts, ph, pt,
+        pts, phe;
     size_t total;
 };
 
@@ -236,6 +239,7 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         const size_t pieces = (M + kPiece - 1) / kPiece;
         L.r = take(Bs * T * p.dv * 4);
         L.Z = take(Bs * p.H * 2 * T * 4);
+        L.M = take(Bs * p.H * 2 * T * 4);
         L.m = take(Bs * p.H * 2 * T * 4);
         L.part = take(Bs * p.H * 2 * ntiles * p.n * 4);
         L.lp = take(Bs * p.H * 2 * p.n * 4);
@@ -289,7 +293,7 @@ ScoreArgs score_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstr
     ScoreArgs a{};
     a.q = q; a.q_bstride = q_bstride; a.K1 = K1; a.K2 = K2; a.knorm = knorm;
     a.B = B; a.Tc = Tc; a.n = p.n; a.H = p.H; a.dh = p.dh; a.kh = p.kh;
-    a.eps = p.eps; a.mode = mode; a.cap = score_cap(p.kh);
+    a.eps = p.eps; a.mode = mode; a.cap = score_cap(p.kh); a.dot = p.dot;
     return a;
 }
 
@@ -310,6 +314,7 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     if (stats) {
         a.part = at<float>(ws, L.part);
         a.Z = at<float>(ws, L.Z);
+        a.M = at<float>(ws, L.M);
     }
     {
         TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
@@ -322,6 +327,7 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     sa.eps = p.eps; sa.idx = idx; sa.w = w; sa.iw_bstride = iw_bstride; sa.cand_ab = p.cand;
     sa.erow = a.erow;
     sa.usage = usage;
+    sa.dot = p.dot;
     {
         TimedLaunch tl(FWPKM_K_SELECT, s);
         HIP_TRY(launch_select(sa, p.store, s));
@@ -404,12 +410,13 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
         a.qn = at<float>(ws, L.qn);
         a.part = at<float>(ws, L.part);
         a.Z = at<float>(ws, L.Z);
+        a.M = at<float>(ws, L.M);
         TimedLaunch tl(FWPKM_K_SWEEP_STATS, s);
         HIP_TRY(launch_score(a, p.store, s));
     }
     PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, 0, Tc};
     {
-        const int tile = score_tile(B, p.H, Tc);
+        const int tile = score_tile(B, p.H, Tc, p.dot != 0);
         pa.ntiles = (Tc + tile - 1) / tile;
     }
     {
@@ -419,6 +426,7 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     ScoreArgs ra = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreRowStat);
     ra.lp = at<float>(ws, L.lp);
     ra.Z = at<float>(ws, L.Z);
+    ra.M = at<float>(ws, L.M);
     ra.m = at<float>(ws, L.m);
     {
         TimedLaunch tl(FWPKM_K_SWEEP_ROWSTAT, s);
@@ -434,6 +442,7 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     ka.q = q; ka.q_bstride = q_bstride; ka.qT = at<void>(ws, L.qT); ka.Tp = Tp;
     ka.K1 = K1; ka.K2 = K2; ka.knorm = knorm;
     ka.qn = at<float>(ws, L.qn); ka.Z = at<float>(ws, L.Z); ka.m = at<float>(ws, L.m); ka.lp = at<float>(ws, L.lp);
+    ka.M = at<float>(ws, L.M); ka.dot = p.dot;
     ka.B = B; ka.Tc = Tc; ka.n = p.n; ka.H = p.H; ka.dh = p.dh; ka.eps = p.eps; ka.lr = p.lr_k;
     {
         TimedLaunch tl(FWPKM_K_KGRAD, s);
@@ -481,7 +490,7 @@ int stream_fire(const Plan& p, const StreamLayout& S, void* st, int B, int Tc, i
     const int64_t C = p.C;
     if (n_tgt > 0) {
         ResidArgs ra{at<float>(st, S.vhat), at<float>(st, S.g), at<void>(st, S.tgt), at<float>(ws, L.r),
-                     C * p.dv, C, C * p.dv, B, Tc, n_tgt, p.dv, p.znorm, p.zeps};
+                     C * p.dv, C, C * p.dv, B, Tc, n_tgt, p.dv, p.znorm, p.zeps, p.gate};
         TimedLaunch tl(FWPKM_K_RESID, s);
         HIP_TRY(launch_resid(ra, p.store, s));
     }
@@ -629,7 +638,7 @@ int fwpkm_chunk_update(const fwpkm_cfg* cfg, int32_t B, int32_t Tc, int32_t n_tg
     HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     if (n_tgt > 0) {
         ResidArgs ra{vhat, g, tgt, at<float>(ws, L.r), static_cast<int64_t>(Tc) * p.dv, Tc,
-                     static_cast<int64_t>(n_tgt) * p.dv, B, Tc, n_tgt, p.dv, p.znorm, p.zeps};
+                     static_cast<int64_t>(n_tgt) * p.dv, B, Tc, n_tgt, p.dv, p.znorm, p.zeps, p.gate};
         TimedLaunch tl(FWPKM_K_RESID, s);
         HIP_TRY(launch_resid(ra, p.store, s));
     }
@@ -762,7 +771,7 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                 ga.o_bstride = vbs;
                 ga.r = at<float>(ws, L.r) + bo * Tc * p.dv;
                 ga.B = nb; ga.Tc = Tc; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
-                ga.znorm = p.znorm; ga.znorm_eps = p.zeps;
+                ga.znorm = p.znorm; ga.znorm_eps = p.zeps; ga.gate_w = p.gate;
                 {
                     TimedLaunch tl(FWPKM_K_GATHER, sv);
                     HIP_TRY(launch_gather(ga, p.store, sv));
@@ -783,7 +792,7 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                     ba.dv_out = grad->dv + bo * vbs + t0s * p.dv;
                     ba.dg = grad->dg + bo * T + t0s;
                     ba.B = nb; ba.T = Tc; ba.n = p.n; ba.H = p.H; ba.dh = p.dh; ba.dv = p.dv; ba.k = p.k;
-                    ba.N = p.N; ba.eps = p.eps;
+                    ba.N = p.N; ba.eps = p.eps; ba.dot = p.dot;
                     TimedLaunch tl(FWPKM_K_BACKWARD, sv);
                     HIP_TRY(launch_backward(ba, p.store, sv));
                 }
@@ -944,7 +953,7 @@ int fwpkm_retrieve_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T, const vo
         return fail(FWPKM_EINVAL, "q, v, g, K1, K2, V, idx, w, dO, dq, dv and dg are required");
     BackwardArgs a{q, static_cast<int64_t>(T) * p.H * p.dq, v, static_cast<int64_t>(T) * p.dv, g, T, idx, w,
                    static_cast<int64_t>(T) * p.H * p.k, K1, K2, V, dO, dq, dv, dg, B, T, p.n, p.H, p.dh, p.dv, p.k,
-                   p.N, p.eps};
+                   p.N, p.eps, p.dot};
     hipStream_t s = static_cast<hipStream_t>(stream);
     TimedLaunch tl(FWPKM_K_BACKWARD, s);
     HIP_TRY(launch_backward(a, p.store, s));

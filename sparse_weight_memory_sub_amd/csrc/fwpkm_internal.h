@@ -132,6 +132,16 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// Order-preserving map of floats to unsigned ints (ascending float ->
+// ascending uint) and its inverse: dot scores select on ord(-s).
+__device__ __forceinline__ uint32_t ord_f32(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += xor_lane(x, o);
@@ -207,6 +217,8 @@ struct ScoreArgs {
     float* Z;             // [B][H][2][Tc]
     float* m;             // [B][H][2][Tc]
     uint32_t* erow;       // [B][H][2][Tc][n]  e bit patterns (rows mode)
+    float* M;             // [B][H][2][Tc]  row maximum of s (dot scoring's softmax)
+    int dot;              // dot-product scoring: keys are ord(-s), p = exp(s - M) / Z
     int tile;             // tokens per workgroup (set by launch_score)
 };
 
@@ -226,6 +238,7 @@ struct SelectArgs {
     CandTable cand_ab;
     const uint32_t* erow; // non-NULL: whole rows of e ([B][H][2][Tc][n]) instead of candidate lists
     int32_t* usage;       // nullable: usage[b*n*n + slot] += 1 per selected read
+    int dot;              // dot-product scoring: keys are ord(-s), pair value -(s1 + s2)
 };
 
 int score_keep(int kh);   // smallest e kept per lane in the first scoring pass
@@ -266,6 +279,7 @@ struct GatherArgs {
     int64_t N;
     int znorm;
     float znorm_eps;
+    int gate_w;           // 1: r = g (vhat - y); 0: r = vhat - y
 };
 
 struct ResidArgs {        // r = g (vhat - z(tgt)) for t < n_tgt
@@ -276,6 +290,7 @@ struct ResidArgs {        // r = g (vhat - z(tgt)) for t < n_tgt
     int64_t vhat_bstride, g_bstride, tgt_bstride;
     int B, Tc, n_tgt, dv, znorm;
     float znorm_eps;
+    int gate_w;
 };
 
 struct SortArgs {
@@ -337,6 +352,8 @@ struct KgradArgs {
     const float* lp;      // [B][H][2][n]
     int B, Tc, n, H, dh;
     float eps, lr;
+    const float* M;       // [B][H][2][Tc] row maximum of s (dot scoring)
+    int dot;
 };
 
 struct KnormArgs {
@@ -353,7 +370,7 @@ hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s);
 // Tokens per scoring workgroup for B sequences of H heads and Tc tokens on
 // the current device: the largest tile whose grid still covers every
 // compute unit, else the smallest.
-int score_tile(int B, int H, int Tc);
+int score_tile(int B, int H, int Tc, bool dot);
 // Gradient of the retrieval output w.r.t. q, v and g for T tokens of B
 // sequences; per-sequence strides in elements:
 //   q, dq (f32):         + b*q_bstride + (t*H + h)*2*dh
@@ -380,6 +397,7 @@ struct BackwardArgs {
     int B, T, n, H, dh, dv, k;
     int64_t N;
     float eps;
+    int dot;
 };
 hipError_t launch_backward(const BackwardArgs& a, int store, hipStream_t s);
 

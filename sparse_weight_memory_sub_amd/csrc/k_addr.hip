@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_qt(QtArgs a) {
 // row layout of the MFMA distance tiles.
 __device__ __forceinline__ int tok_of(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4); }
 
-template <int STORE, int DHS>
+template <int STORE, int DHS, bool DOT>
 __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int ES = Store<STORE>::kBytes;
@@ -151,9 +151,11 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     float kn = 0.f, lpv = 0.f;
     if (active) {
         load_row_frags<STORE, DHS>(Bk, Kb + static_cast<size_t>(key) * DH * ES, g);
+        if constexpr (!DOT) {
 #pragma unroll
-        for (int s = 0; s < DHS; ++s) frag_scale_m2(Bk[s]);
-        kn = a.knorm[static_cast<size_t>(bhh) * n + key];
+            for (int s = 0; s < DHS; ++s) frag_scale_m2(Bk[s]);
+            kn = a.knorm[static_cast<size_t>(bhh) * n + key];
+        }
         lpv = a.lp[static_cast<size_t>(bhh) * n + key];
     }
     const int eps_bits = __float_as_int(a.eps);
@@ -178,7 +180,8 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
 #pragma unroll
     for (int c = 0; c < NCT; ++c) gacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float colsum = 0.f;
-    const float inv_tc2 = 2.f / static_cast<float>(Tc);
+    // a_ti = (2/C)(ln pbar_i - m_t)/(Z_t e^2) for IDW, (1/C)(ln pbar_i - m_t) e^(s - M_t)/Z_t for dot
+    const float inv_tc2 = (DOT ? 1.f : 2.f) / static_cast<float>(Tc);
 
     // Token blocks of 32.  Key blocks of one (sequence, head, half) run side by
     // side and read the same query rows: each starts at a different block
@@ -201,7 +204,8 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
             const int which = threadIdx.x >> 5, t = tb + (threadIdx.x & 31);
             if (t < Tc) {
                 const size_t o = static_cast<size_t>(bhh) * Tc + t;
-                x = which == 0 ? a.qn[o] : (which == 1 ? __builtin_amdgcn_rcpf(a.Z[o]) : a.m[o]);
+                // first row: ||q||^2 (IDW) or the row maximum M_t of s (dot)
+                x = which == 0 ? (DOT ? a.M[o] : a.qn[o]) : (which == 1 ? __builtin_amdgcn_rcpf(a.Z[o]) : a.m[o]);
             }
         }
         return x;
@@ -247,11 +251,16 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = sub * 16 + 4 * g + i;
-                    const float e = __int_as_float(max(__float_as_int((tq[row] + a.eps) + acc[i]), eps_bits));
-                    const float ie = __builtin_amdgcn_rcpf(e);
+                    float val;
+                    if constexpr (DOT) {
+                        val = inv_tc2 * (lpv - tq[64 + row]) * tq[32 + row] * __expf(acc[i] - tq[row]);
+                    } else {
+                        const float e = __int_as_float(max(__float_as_int((tq[row] + a.eps) + acc[i]), eps_bits));
+                        const float ie = __builtin_amdgcn_rcpf(e);
+                        val = inv_tc2 * (lpv - tq[64 + row]) * tq[32 + row] * ie * ie;
+                    }
                     // tokens past the chunk have 1/Z = 0; the select also drops
                     // whatever their (unfilled) query rows produced
-                    const float val = inv_tc2 * (lpv - tq[64 + row]) * tq[32 + row] * ie * ie;
                     av[sub * 4 + i] = (tb + row < Tc) ? val : 0.f;
                     colsum += av[sub * 4 + i];
                 }
@@ -319,7 +328,8 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
             const int k = key0 + 4 * g + i;
             const size_t off = static_cast<size_t>(k) * DH + col;
             const float kv = ld_elem<STORE>(Kb, off);
-            const float grad = gacc[c][i] - cs[i] * kv;
+            // IDW: sum_t a (q_t - K_i); dot: sum_t a q_t
+            const float grad = DOT ? gacc[c][i] : gacc[c][i] - cs[i] * kv;
             float kn2 = kv - a.lr * grad;
             if constexpr (STORE == kBF16) kn2 = bf16_to_f32(f32_to_bf16(kn2));
             st_elem<STORE>(Kb, off, kn2);
@@ -337,31 +347,31 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     }
 }
 
-template <int STORE, int DHS>
+template <int STORE, int DHS, bool DOT>
 hipError_t kgrad_t(const KgradArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int DH = 32 * DHS;
     constexpr size_t LDS = 2 * (static_cast<size_t>(32) * DH * ES + 3 * 32 * 4) + static_cast<size_t>(DH) * 32 * ES;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_kgrad<STORE, DHS>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_kgrad<STORE, DHS, DOT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int nkb = (a.n + 63) / 64;
     const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * nkb;
-    hipLaunchKernelGGL((k_kgrad<STORE, DHS>), dim3(grid), dim3(256), LDS, s, a);
+    hipLaunchKernelGGL((k_kgrad<STORE, DHS, DOT>), dim3(grid), dim3(256), LDS, s, a);
     return hipGetLastError();
 }
 
 template <int STORE>
 hipError_t kgrad_s(const KgradArgs& a, hipStream_t s) {
     switch (a.dh / 32) {
-        case 1: return kgrad_t<STORE, 1>(a, s);
-        case 2: return kgrad_t<STORE, 2>(a, s);
-        case 4: return kgrad_t<STORE, 4>(a, s);
-        case 8: return kgrad_t<STORE, 8>(a, s);
+        case 1: return a.dot ? kgrad_t<STORE, 1, true>(a, s) : kgrad_t<STORE, 1, false>(a, s);
+        case 2: return a.dot ? kgrad_t<STORE, 2, true>(a, s) : kgrad_t<STORE, 2, false>(a, s);
+        case 4: return a.dot ? kgrad_t<STORE, 4, true>(a, s) : kgrad_t<STORE, 4, false>(a, s);
+        case 8: return a.dot ? kgrad_t<STORE, 8, true>(a, s) : kgrad_t<STORE, 8, false>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -9,7 +9,9 @@
 // fixed, for an upstream gradient G = dL/do:
 //   dL/dg = G . (v_hat - v),  dL/dv = (1 - g) G,
 //   a_j = (g/H) G . V[slot_j],  dL/dS_j = w_j (a_j - sum_l w_l a_l),
-//   dL/dq_half = sum_j dL/dS_j * (-2) (q_half - K_half[sub_j]) / (eps + d_j).
+//   dL/dq_half = sum_j dL/dS_j * (-2) (q_half - K_half[sub_j]) / (eps + d_j),
+// or with dot-product scores (S_j = q1 . K1[a_j] + q2 . K2[b_j])
+//   dL/dq_half = sum_j dL/dS_j K_half[sub_j].
 // The distances are recomputed by direct differences.
 //
 // One wavefront per token.  The value rows are read as in the gather (lane l
@@ -63,7 +65,7 @@ __device__ __forceinline__ void ld_seg(const void* base, size_t off, float (&x)[
     }
 }
 
-template <int STORE, int EPL, int DHS>
+template <int STORE, int EPL, int DHS, bool DOT>
 __global__ __launch_bounds__(256) void k_backward(BackwardArgs a) {
     constexpr int DH = 32 * DHS;
     constexpr int EPQ = DH / 16;  // elements of a half row per lane of a 16-lane group
@@ -186,19 +188,26 @@ __global__ __launch_bounds__(256) void k_backward(BackwardArgs a) {
                 const int sub = ok ? (hf ? slot % n : slot / n) : 0;
                 float kx[EPQ], diff[EPQ];
                 ld_seg<STORE, EPQ>(Kh, kb + static_cast<size_t>(sub) * DH, kx);
-                float part = 0.f;
+                if constexpr (DOT) {
+                    // dS/dq_half = K_half[sub]
+                    const float coef = ok ? lds_ds[wave][e] : 0.f;
 #pragma unroll
-                for (int i = 0; i < EPQ; ++i) {
-                    diff[i] = qv[i] - kx[i];
-                    part = fmaf(diff[i], diff[i], part);
+                    for (int i = 0; i < EPQ; ++i) acc[i] = fmaf(coef, kx[i], acc[i]);
+                } else {
+                    float part = 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPQ; ++i) {
+                        diff[i] = qv[i] - kx[i];
+                        part = fmaf(diff[i], diff[i], part);
+                    }
+                    part += xor_lane(part, 1);
+                    part += xor_lane(part, 2);
+                    part += xor_lane(part, 4);
+                    part += xor_lane(part, 8);
+                    const float coef = ok ? lds_ds[wave][e] * (-2.f) / (a.eps + part) : 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPQ; ++i) acc[i] = fmaf(coef, diff[i], acc[i]);
                 }
-                part += xor_lane(part, 1);
-                part += xor_lane(part, 2);
-                part += xor_lane(part, 4);
-                part += xor_lane(part, 8);
-                const float coef = ok ? lds_ds[wave][e] * (-2.f) / (a.eps + part) : 0.f;
-#pragma unroll
-                for (int i = 0; i < EPQ; ++i) acc[i] = fmaf(coef, diff[i], acc[i]);
             }
 #pragma unroll
             for (int i = 0; i < EPQ; ++i) {
@@ -220,13 +229,20 @@ __global__ __launch_bounds__(256) void k_backward(BackwardArgs a) {
     }
 }
 
+template <int STORE, int EPL, int DHS>
+hipError_t backward_k(const BackwardArgs& a, unsigned grid, hipStream_t s) {
+    if (a.dot) hipLaunchKernelGGL((k_backward<STORE, EPL, DHS, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_backward<STORE, EPL, DHS, false>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int STORE, int EPL>
 hipError_t backward_d(const BackwardArgs& a, unsigned grid, hipStream_t s) {
     switch (a.dh / 32) {
-        case 1: hipLaunchKernelGGL((k_backward<STORE, EPL, 1>), dim3(grid), dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_backward<STORE, EPL, 2>), dim3(grid), dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_backward<STORE, EPL, 4>), dim3(grid), dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((k_backward<STORE, EPL, 8>), dim3(grid), dim3(256), 0, s, a); break;
+        case 1: return backward_k<STORE, EPL, 1>(a, grid, s);
+        case 2: return backward_k<STORE, EPL, 2>(a, grid, s);
+        case 4: return backward_k<STORE, EPL, 4>(a, grid, s);
+        case 8: return backward_k<STORE, EPL, 8>(a, grid, s);
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

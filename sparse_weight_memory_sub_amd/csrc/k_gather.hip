@@ -5,7 +5,7 @@
 // steps 2-3): v_hat_t = (1/H) sum_h sum_j w V[idx], o_t = g_t v_hat_t +
 // (1 - g_t) v_t.  Residual of the gated reconstruction loss (digest step 4;
 // paperlayer.ai A.1, A.3, A.5): r_t = g_t (v_hat_t - y_t) with y_t the
-// z-scored lookahead target.
+// z-scored lookahead target (r_t = v_hat_t - y_t with the gate weighting off).
 //
 // Lane l owns elements [l*EPL, (l+1)*EPL) of every d_v-row, so each row read
 // is one coalesced d_v*elem_bytes transaction of a wavefront.  A token's H*k
@@ -110,8 +110,9 @@ __device__ __forceinline__ void gather_finish(const GatherArgs& a, int b, int t,
             ldrow<STORE, EPL>(a.tgt, static_cast<size_t>(b) * a.tgt_bstride + static_cast<size_t>(t) * a.dv + col, y);
         if (a.znorm) zscore<EPL>(y, a.dv, a.znorm_eps);
         float rr[EPL];
+        const float gw = a.gate_w ? gt : 1.f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) rr[i] = gt * (vh[i] - y[i]);
+        for (int i = 0; i < EPL; ++i) rr[i] = gw * (vh[i] - y[i]);
         stf<EPL>(a.r + (static_cast<size_t>(b) * a.Tc + t) * a.dv + col, rr);
     }
     if (a.pq) {
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(256) void k_resid(ResidArgs a) {
     ldrow<STORE, EPL>(a.tgt, static_cast<size_t>(b) * a.tgt_bstride + static_cast<size_t>(t) * a.dv + col, y);
     if (a.znorm) zscore<EPL>(y, a.dv, a.znorm_eps);
     ldrow<kF32, EPL>(a.vhat, static_cast<size_t>(b) * a.vhat_bstride + static_cast<size_t>(t) * a.dv + col, vh);
-    const float gt = a.g[static_cast<size_t>(b) * a.g_bstride + t];
+    const float gt = a.gate_w ? a.g[static_cast<size_t>(b) * a.g_bstride + t] : 1.f;
     float rr[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) rr[i] = gt * (vh[i] - y[i]);

@@ -129,7 +129,7 @@ __device__ __forceinline__ void bitonic_sort_lists(uint64_t (&x)[L]) {
 // One sweep of a.tile tokens of one (sequence, head, half) against all n
 // sub-keys of that half.  MODE is a combination of kScoreSelect,
 // kScoreStats and kScoreRowStat (the latter alone).
-template <int STORE, int DHS, int MK, int MODE, int NW>
+template <int STORE, int DHS, int MK, int MODE, int NW, bool DOT>
 __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int KB = kKB<STORE>;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
     for (int s = 0; s < DHS; ++s) {
         if (!tv) frag_zero<STORE>(A[s]);
         qsq += frag_sumsq<STORE>(A[s]);
-        frag_scale_m2(A[s]);
+        if constexpr (!DOT) frag_scale_m2(A[s]);  // dot scores use q itself
     }
     qsq += xor_lane(qsq, 16);
     qsq += xor_lane(qsq, 32);
@@ -196,17 +196,23 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
 
     float zinv[4] = {0.f, 0.f, 0.f, 0.f};  // 1/Z_t of the selection pass (0 past the chunk)
     float zrow[4] = {1.f, 1.f, 1.f, 1.f};  // Z_t from the workspace (row statistic)
+    float mrow[4] = {0.f, 0.f, 0.f, 0.f};  // dot scoring: the row maximum M_t of s
     uint32_t tau[4] = {0u, 0u, 0u, 0u};
     if constexpr (ROW) {
         for (int i = threadIdx.x; i < n; i += 64 * NW) lps[i] = a.lp[static_cast<size_t>(bhh) * n + i];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (rv[i]) zrow[i] = a.Z[rowbase + tw0 + 4 * g + i];
+            if (rv[i]) {
+                zrow[i] = a.Z[rowbase + tw0 + 4 * g + i];
+                if constexpr (DOT) mrow[i] = a.M[rowbase + tw0 + 4 * g + i];
+            }
     }
 
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         float zacc[4] = {0.f, 0.f, 0.f, 0.f}, macc[4] = {0.f, 0.f, 0.f, 0.f};
+        // dot scoring's Z: a running maximum and the sum of exp(s - max) per lane
+        float zmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         uint32_t keep[4][MK];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
                 colv[ct] = 0.f;
                 if (blk * KB + ct * 16 >= n) continue;  // partial last block (n % 16 == 0)
                 const int key = blk * KB + ct * 16 + r;
-                const float knv = kns[key];
+                const float knv = DOT ? 0.f : kns[key];
                 f32x4_t acc;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] = knv;
@@ -258,11 +264,21 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
                     // e = max(eps + d, eps): the large ||q||^2 enters with one
                     // rounding at the end; a signed-integer max of the bit
                     // patterns orders these floats exactly (eps > 0)
-                    const uint32_t eb = static_cast<uint32_t>(max(__float_as_int(qe[i] + acc[i]), eps_bits));
+                    // dot scoring: smaller ord(-s) is better, p ~ exp(s - M)
+                    const uint32_t eb = DOT ? ord_f32(-acc[i])
+                                            : static_cast<uint32_t>(max(__float_as_int(qe[i] + acc[i]), eps_bits));
                     const float e = __uint_as_float(eb);
                     if (pass == 0) {
-                        if constexpr (STATS) zacc[i] += fast_rcp(e);
-                        if constexpr (ROW) macc[i] = fmaf(fast_rcp(e), lpk, macc[i]);
+                        if constexpr (STATS) {
+                            if constexpr (DOT) {
+                                const float mx = fmaxf(zmax[i], acc[i]);
+                                zacc[i] = zacc[i] * __expf(zmax[i] - mx) + __expf(acc[i] - mx);
+                                zmax[i] = mx;
+                            } else {
+                                zacc[i] += fast_rcp(e);
+                            }
+                        }
+                        if constexpr (ROW) macc[i] = fmaf(DOT ? __expf(acc[i] - mrow[i]) : fast_rcp(e), lpk, macc[i]);
                         if constexpr (SEL) {
                             // keep the MK smallest of this lane, ascending
                             uint32_t x = eb;
@@ -274,7 +290,7 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
                             }
                         }
                     } else {
-                        if constexpr (STATS) cs = fmaf(fast_rcp(e), zinv[i], cs);
+                        if constexpr (STATS) cs = fmaf(DOT ? __expf(acc[i] - mrow[i]) : fast_rcp(e), zinv[i], cs);
                         if constexpr (SEL) {
                             if (eb <= tau[i]) {
                                 const uint32_t pos = atomicAdd(&ccnt[wave * 16 + 4 * g + i], 1u);
@@ -315,10 +331,24 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = zacc[i];
-                    x += xor_lane(x, 1);
-                    x += xor_lane(x, 2);
-                    x += xor_lane(x, 4);
-                    x += xor_lane(x, 8);
+                    if constexpr (DOT) {
+                        // merge (max, sum) pairs: sum' = sum e^(max - M) + sum2 e^(max2 - M)
+                        float mx = zmax[i];
+#pragma unroll
+                        for (int o = 1; o <= 8; o <<= 1) {
+                            const float m2 = xor_lane(mx, o), x2 = xor_lane(x, o);
+                            const float M = fmaxf(mx, m2);
+                            x = x * __expf(mx - M) + x2 * __expf(m2 - M);
+                            mx = M;
+                        }
+                        mrow[i] = mx;
+                        if (r == 0 && rv[i]) a.M[rowbase + tw0 + 4 * g + i] = mx;
+                    } else {
+                        x += xor_lane(x, 1);
+                        x += xor_lane(x, 2);
+                        x += xor_lane(x, 4);
+                        x += xor_lane(x, 8);
+                    }
                     zinv[i] = rv[i] ? fast_rcp(x) : 0.f;
                     if (r == 0 && rv[i]) a.Z[rowbase + tw0 + 4 * g + i] = x;
                 }
@@ -372,7 +402,7 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
 // every wavefront of the chip in flight.  The arithmetic (accumulators
 // seeded with ||K_i||^2, -2q, k-blocks in order, ||q||^2 + eps added last) is
 // that of k_score, so the e values are the same bits.
-template <int STORE, int DHS>
+template <int STORE, int DHS, bool DOT>
 __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     constexpr int ES = Store<STORE>::kBytes;
     const int n = a.n, H = a.H, Tc = a.Tc;
@@ -386,7 +416,7 @@ __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     Frag<STORE> Bf[DHS];
     load_row_frags<STORE, DHS>(Bf, static_cast<const unsigned char*>(half ? a.K2 : a.K1) +
                                        (static_cast<size_t>(bh) * n + key) * (32 * DHS) * ES, g);
-    const float knv = a.knorm[static_cast<size_t>(bhh) * n + key];
+    const float knv = DOT ? 0.f : a.knorm[static_cast<size_t>(bhh) * n + key];
 
     Frag<STORE> A[DHS];
     const bool tv = r < Tc;
@@ -398,7 +428,7 @@ __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     for (int s = 0; s < DHS; ++s) {
         if (!tv) frag_zero<STORE>(A[s]);
         qsq += frag_sumsq<STORE>(A[s]);
-        frag_scale_m2(A[s]);
+        if constexpr (!DOT) frag_scale_m2(A[s]);
     }
     qsq += xor_lane(qsq, 16);
     qsq += xor_lane(qsq, 32);
@@ -413,7 +443,7 @@ __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     for (int i = 0; i < 4; ++i) {
         const int t = 4 * g + i;
         const float qe = __shfl(qsq, t, 64) + a.eps;
-        const uint32_t eb = static_cast<uint32_t>(max(__float_as_int(qe + acc[i]), eps_bits));
+        const uint32_t eb = DOT ? ord_f32(-acc[i]) : static_cast<uint32_t>(max(__float_as_int(qe + acc[i]), eps_bits));
         if (t < Tc) a.erow[(rowbase + t) * n + key] = eb;
     }
 }
@@ -510,14 +540,19 @@ __device__ void half_topk(const SelectArgs& a, int b, int t, int h, int half, ui
 #pragma unroll
         for (int j = 0; j < kNplMax; ++j) {
             const int i = j * 64 + lane;
-            u[j] = 0x7f800000u;
+            u[j] = 0xffffffffu;
             if (j < npl && i < n) {
                 float d = 0.f;
                 for (int x = 0; x < dh; ++x) {
-                    const float diff = ld_elem<STORE>(q, x) - ld_elem<STORE>(K, kb + static_cast<size_t>(i) * dh + x);
-                    d = fmaf(diff, diff, d);
+                    const float qx = ld_elem<STORE>(q, x), kx = ld_elem<STORE>(K, kb + static_cast<size_t>(i) * dh + x);
+                    if (a.dot) {
+                        d = fmaf(qx, kx, d);
+                    } else {
+                        const float diff = qx - kx;
+                        d = fmaf(diff, diff, d);
+                    }
                 }
-                u[j] = __float_as_uint(a.eps + d);
+                u[j] = a.dot ? ord_f32(-d) : __float_as_uint(a.eps + d);
             }
         }
         radix_select(u, npl, a.kh, hist, buf);
@@ -537,7 +572,8 @@ __device__ void half_topk(const SelectArgs& a, int b, int t, int h, int half, ui
         bitonic_sort<4, 64>(key);
     }
     if (lane < a.kh) {
-        out_e[lane] = __uint_as_float(static_cast<uint32_t>(key[0] >> 32));
+        const uint32_t kbits = static_cast<uint32_t>(key[0] >> 32);
+        out_e[lane] = a.dot ? unord_f32(kbits) : __uint_as_float(kbits);
         out_i[lane] = static_cast<int>(key[0] & 0xffffffffu);
     }
     wave_sync();
@@ -559,7 +595,7 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
 #pragma unroll
     for (int j = 0; j < kNplMax; ++j) {
         const int i = j * 64 + lane;
-        u[j] = (j < npl && i < n) ? e[i] : 0x7f800000u;
+        u[j] = (j < npl && i < n) ? e[i] : 0xffffffffu;
         const uint32_t lo = min(m0, u[j]), hi = max(m0, u[j]);
         m0 = lo;
         m1 = min(m1, hi);
@@ -590,7 +626,8 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
     }
     bitonic_sort<1, 64>(key);
     if (lane < a.kh) {
-        out_e[lane] = __uint_as_float(static_cast<uint32_t>(key[0] >> 32));
+        const uint32_t kbits = static_cast<uint32_t>(key[0] >> 32);
+        out_e[lane] = a.dot ? unord_f32(kbits) : __uint_as_float(kbits);
         out_i[lane] = static_cast<int>(key[0] & 0xffffffffu);
     }
     wave_sync();
@@ -607,17 +644,20 @@ __device__ void product_topk(const SelectArgs& a, const float* e1, const int* i1
         if (c < a.ncand) {
             const uint32_t ab = a.cand_ab.ab[c];
             const int ia = static_cast<int>(ab >> 6), ib = static_cast<int>(ab & 63u);
-            const float P = e1[ia] * e2[ib];
+            // IDW: P = (eps + d1)(eps + d2); dot: v = -(s1 + s2); smaller is better
+            const float P = a.dot ? e1[ia] + e2[ib] : e1[ia] * e2[ib];
             const uint32_t slot = static_cast<uint32_t>(i1[ia] * a.n + i2[ib]);
-            key[r] = (static_cast<uint64_t>(__float_as_uint(P)) << 32) | slot;
+            key[r] = (static_cast<uint64_t>(a.dot ? ord_f32(P) : __float_as_uint(P)) << 32) | slot;
         } else {
             key[r] = ~0ull;
         }
     }
     bitonic_sort<R, 64>(key);
-    const float P = __uint_as_float(static_cast<uint32_t>(key[0] >> 32));
+    const uint32_t pbits = static_cast<uint32_t>(key[0] >> 32);
+    const float P = a.dot ? unord_f32(pbits) : __uint_as_float(pbits);
     const float P0 = __shfl(P, 0, 64);
-    const float ratio = (lane < a.k) ? (P0 / P) : 0.f;
+    // w = softmax of the k pair scores: (1/P)/sum(1/P) for IDW, exp(-v)/sum for dot
+    const float ratio = (lane < a.k) ? (a.dot ? __expf(P0 - P) : (P0 / P)) : 0.f;
     const float sum = wave_sum(ratio);
     if (lane < a.k) {
         const int32_t slot = static_cast<int32_t>(key[0] & 0xffffffffu);
@@ -652,7 +692,8 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
         if (lane < a.kh) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                se[wave][half][lane] = __uint_as_float(static_cast<uint32_t>(key[half] >> 32));
+                const uint32_t kbits = static_cast<uint32_t>(key[half] >> 32);
+                se[wave][half][lane] = a.dot ? unord_f32(kbits) : __uint_as_float(kbits);
                 si[wave][half][lane] = static_cast<int>(key[half] & 0xffffffffu);
             }
         }
@@ -696,7 +737,7 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs a) {
     else product_topk<4>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
 }
 
-template <int STORE, int DHS, int MK, int MODE, int NW>
+template <int STORE, int DHS, int MK, int MODE, int NW, bool DOT>
 hipError_t score_w(const ScoreArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int KB = kKB<STORE>;
@@ -706,23 +747,25 @@ hipError_t score_w(const ScoreArgs& a, hipStream_t s) {
                        ((MODE & kScoreRowStat) ? static_cast<size_t>(a.n) * 4 : 0);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK, MODE, NW>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK, MODE, NW, DOT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int ntiles = (a.Tc + 16 * NW - 1) / (16 * NW);
     const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * ntiles;
-    hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE, NW>), dim3(grid), dim3(64 * NW), lds, s, a);
+    hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE, NW, DOT>), dim3(grid), dim3(64 * NW), lds, s, a);
     return hipGetLastError();
 }
 
 template <int STORE, int DHS, int MK, int MODE>
 hipError_t score_t(const ScoreArgs& a, hipStream_t s) {
+    // dot-product scoring (an ablation) is built for 64-token tiles only
+    if (a.dot) return score_w<STORE, DHS, MK, MODE, 4, true>(a, s);
     switch (a.tile) {
-        case 64: return score_w<STORE, DHS, MK, MODE, 4>(a, s);
-        case 128: return score_w<STORE, DHS, MK, MODE, 8>(a, s);
-        case 256: return score_w<STORE, DHS, MK, MODE, 16>(a, s);
+        case 64: return score_w<STORE, DHS, MK, MODE, 4, false>(a, s);
+        case 128: return score_w<STORE, DHS, MK, MODE, 8, false>(a, s);
+        case 256: return score_w<STORE, DHS, MK, MODE, 16, false>(a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -741,7 +784,10 @@ hipError_t score_mk(const ScoreArgs& a, hipStream_t s) {
     if (a.mode == kScoreRows) {
         if (a.Tc > kRowTok) return hipErrorInvalidValue;
         const int64_t waves = static_cast<int64_t>(a.B) * a.H * 2 * (a.n / 16);
-        hipLaunchKernelGGL((k_rows<STORE, DHS>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
+        if (a.dot)
+            hipLaunchKernelGGL((k_rows<STORE, DHS, true>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_rows<STORE, DHS, false>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
         return hipGetLastError();
     }
     // modes without selection do not keep per-lane minima
@@ -775,7 +821,8 @@ int score_keep(int kh) {
 
 int score_cap(int kh) { return kh <= 32 ? 128 : 256; }
 
-int score_tile(int B, int H, int Tc) {
+int score_tile(int B, int H, int Tc, bool dot) {
+    if (dot) return kScoreTokMin;  // the dot-product variant is built for 64-token tiles
     // compute units of the current device, looked up once per device
     static int cus[64] = {};
     int dev = 0;
@@ -801,7 +848,7 @@ int score_tile(int B, int H, int Tc) {
 
 hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s) {
     ScoreArgs b = a;
-    b.tile = score_tile(a.B, a.H, a.Tc);
+    b.tile = score_tile(a.B, a.H, a.Tc, a.dot != 0);
     return store == kBF16 ? score_s<kBF16>(b, s) : score_s<kF32>(b, s);
 }
 

@@ -49,6 +49,7 @@ class Cfg(ctypes.Structure):
         ("idw_eps", ctypes.c_float), ("lr_v", ctypes.c_float), ("lr_k", ctypes.c_float),
         ("lookahead", ctypes.c_int32), ("znorm", ctypes.c_int32),
         ("znorm_eps", ctypes.c_float), ("use_addr", ctypes.c_int32),
+        ("gate_weight", ctypes.c_int32), ("score", ctypes.c_int32),
     ]
 
 
@@ -66,7 +67,8 @@ def _cfg(c: FwpkmConfig) -> Cfg:
 def cfg_struct(c: FwpkmConfig) -> Cfg:
     return Cfg(int(c.n), int(c.heads), int(c.d_q), int(c.d_v), int(c.k_half), int(c.k), int(c.chunk),
                {"f32": 0, "bf16": 1}[c.store], float(c.idw_eps), float(c.lr_v), float(c.lr_k),
-               int(bool(c.lookahead)), int(bool(c.znorm)), float(c.znorm_eps), int(bool(c.use_addr)))
+               int(bool(c.lookahead)), int(bool(c.znorm)), float(c.znorm_eps), int(bool(c.use_addr)),
+               int(bool(c.gate_weight)), {"idw": 0, "dot": 1}[c.score])
 
 
 _lib = None

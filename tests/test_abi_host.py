@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_empty_error():
-    assert fwpkm.abi_version() == 1
+    assert fwpkm.abi_version() == 2
     assert fwpkm.load().fwpkm_last_error() is not None
 
 

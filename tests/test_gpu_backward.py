@@ -23,8 +23,8 @@ def _need_gpu(request):
     torch.cuda.synchronize()
 
 
-def C(n, H, dq, dv, kh, k, store="f32"):
-    return FwpkmConfig(n=n, heads=H, d_q=dq, d_v=dv, k_half=kh, k=k, chunk=64, store=store)
+def C(n, H, dq, dv, kh, k, store="f32", **kw):
+    return FwpkmConfig(n=n, heads=H, d_q=dq, d_v=dv, k_half=kh, k=k, chunk=64, store=store, **kw)
 
 
 CASES = [
@@ -33,6 +33,8 @@ CASES = [
     ("f32_k_gt_khalf", C(32, 1, 64, 64, 4, 10), 1, 20, 0.5),
     ("bf16_n128_h4", C(128, 4, 256, 256, 16, 16, store="bf16"), 2, 30, 0.3),
     ("bf16_million_layer", C(1024, 4, 512, 512, 32, 32, store="bf16"), 2, 24, 0.02),
+    ("dot_f32_n64_h2", C(64, 2, 64, 64, 8, 8, score="dot"), 2, 30, 0.5),
+    ("dot_bf16_n128_h4", C(128, 4, 256, 256, 16, 16, store="bf16", score="dot"), 2, 20, 0.3),
 ]
 
 

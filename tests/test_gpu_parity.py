@@ -59,6 +59,10 @@ RETRIEVE_CASES = [
     ("bf16_n256_h2_d512", C(256, 2, 512, 512, 32, 32, store="bf16"), 1, 33, 0.02),
     ("bf16_n1024_h1", C(1024, 1, 512, 512, 32, 32, store="bf16"), 1, 24, 0.02),
     ("bf16_n64_h3_kstd", C(64, 3, 64, 128, 12, 20, store="bf16"), 2, 19, 0.5),
+    # the pages' ablation: product-key memory's dot-product scoring
+    ("dot_f32_n64_h2", C(64, 2, 64, 64, 8, 8, score="dot"), 2, 37, 0.5),
+    ("dot_f32_k_gt_khalf", C(32, 1, 64, 64, 4, 10, score="dot"), 1, 20, 0.5),
+    ("dot_bf16_n256_h2_d512", C(256, 2, 512, 512, 32, 32, store="bf16", score="dot"), 1, 33, 0.02),
 ]
 
 
@@ -103,6 +107,10 @@ UPDATE_CASES = [
     ("bf16_n128_h4", C(128, 4, 256, 256, 16, 16, store="bf16"), 2, 40, 0.02, "gauss"),
     ("bf16_n256_d512", C(256, 2, 512, 512, 32, 32, store="bf16", lr_k=1e3), 1, 64, 0.5, "gauss"),
     ("bf16_zipf", C(128, 4, 256, 256, 16, 16, store="bf16"), 2, 200, 0.02, "zipf"),
+    # ablation variants: memorisation error without the gate, dot-product scoring
+    ("f32_nogate", C(64, 2, 64, 64, 8, 8, lr_k=50.0, gate_weight=False), 2, 37, 0.5, "gauss"),
+    ("dot_f32_n64", C(64, 1, 64, 64, 8, 8, lr_k=50.0, score="dot"), 2, 37, 0.5, "gauss"),
+    ("dot_bf16_n128_h4", C(128, 4, 256, 256, 16, 16, store="bf16", lr_k=20.0, score="dot"), 2, 40, 0.02, "gauss"),
 ]
 
 
@@ -247,6 +255,32 @@ def test_forward_seq_equals_chunked_calls_bitwise(store, v_next):
     assert torch.equal(out["vhat"], vh_chunked)
     for a, b in ((K1a, K1b), (K2a, K2b), (Va, Vb)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("store,variant", [("f32", "dot"), ("bf16", "dot"), ("f32", "nogate")])
+def test_variant_forward_seq_equals_chunked_calls_bitwise(store, variant):
+    kw = {"score": "dot"} if variant == "dot" else {"gate_weight": False}
+    cfg = C(64, 2, 64, 128, 8, 8, chunk=24, store=store, lr_k=20.0, **kw)
+    B, T = 2, 100
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=22, kstd=0.5)
+    qd, vd, gd, K1a, K2a, Va = dev(q, v, g, K1, K2, V)
+    out = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1a, K2a, Va, want_vhat=True)
+    K1b, K2b, Vb = dev(K1, K2, V)
+    outs = _chunked_gpu(cfg, q, v, g, K1b, K2b, Vb)
+    torch.cuda.synchronize()
+    assert torch.equal(out["o"], torch.cat([r["o"] for r in outs], 1))
+    for a, b in ((K1a, K1b), (K2a, K2b), (Va, Vb)):
+        assert torch.equal(a, b)
+    assert not torch.equal(K1a.cpu(), K1)  # the key step moved the codebook
+
+
+def test_tiny_workload_dot_scoring_resync_parity():
+    wl = WORKLOADS["tiny"]
+    cfg = wl.cfg.replace(score="dot")
+    q, v, g, extra = make_tokens(cfg, wl.B, 512, wl.seed, wl.kind)
+    K1, K2, V = make_state(cfg, wl.B, wl.seed)
+    near = _resync_parity(cfg, q, v, g, K1, K2, V)
+    print(f"  near-tie tokens over the run: {near}")
 
 
 def test_forward_seq_passes_carry_state():

@@ -70,10 +70,11 @@ def cuts_mixed(T, single=30):
     return cuts
 
 
-@pytest.mark.parametrize("store,look,v_next", [("f32", True, False), ("bf16", True, False),
-                                               ("f32", False, False), ("bf16", True, True)])
-def test_stream_equals_forward_seq_bitwise(store, look, v_next):
-    cfg = C(64, 2, 64, 128, 8, 8, chunk=24, store=store, lr_k=20.0, lookahead=look)
+@pytest.mark.parametrize("store,look,v_next,score", [("f32", True, False, "idw"), ("bf16", True, False, "idw"),
+                                                     ("f32", False, False, "idw"), ("bf16", True, True, "idw"),
+                                                     ("bf16", True, False, "dot")])
+def test_stream_equals_forward_seq_bitwise(store, look, v_next, score):
+    cfg = C(64, 2, 64, 128, 8, 8, chunk=24, store=store, lr_k=20.0, lookahead=look, score=score)
     B, T = 2, 100
     q, v, g, K1, K2, V = problem(cfg, B, T, seed=31)
     vn = torch.randn((B, cfg.d_v), generator=torch.Generator().manual_seed(6)).to(cfg.torch_dtype) if v_next else None
