@@ -92,9 +92,11 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SRC = {"gather": ("k_gather.hip",), "scatter": ("k_scatter.hip",),
-              "score_select": ("k_score.hip", "mfma_frag.h"), "score_rowstat": ("k_score.hip", "mfma_frag.h"),
-              "kgrad": ("k_addr.hip", "mfma_frag.h")}
+KERNEL_SRC = {"gather": ("k_gather.hip", "rows.h", "fwpkm_internal.h"),
+              "scatter": ("k_scatter.hip", "fwpkm_internal.h"),
+              "score_select": ("k_score.hip", "mfma_frag.h", "fwpkm_internal.h"),
+              "score_rowstat": ("k_score.hip", "mfma_frag.h", "fwpkm_internal.h"),
+              "kgrad": ("k_addr.hip", "mfma_frag.h", "fwpkm_internal.h")}
 
 
 def traffic_from_profiles(kernel, workload):
