@@ -193,3 +193,20 @@ def test_rows_mode_selection_equals_sweep_with_ties(n, dup):
     # ties between equal sub-keys go to the lower index, as in the oracle
     ora = oracle.retrieve(cfg, q, v, g, K1, K2, V)
     assert np.array_equal(full["idx"].cpu().numpy(), ora["idx"])
+
+
+@pytest.mark.parametrize("chunk,cuts", [(24, [0, 100]),            # one call over four chunk writes
+                                        (1, [0, 1, 2, 5, 9, 10]),  # a write after every token
+                                        (7, [0, 7, 14, 15, 30])])  # calls ending exactly on chunk ends
+def test_stream_edge_splits_equal_forward_seq(chunk, cuts):
+    cfg = C(64, 2, 64, 64, 8, 8, chunk=chunk, lr_k=10.0)
+    B, T = 2, cuts[-1]
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=35)
+    qd, vd, gd, K1a, K2a, Va = dev(q, v, g, K1, K2, V)
+    ref = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1a, K2a, Va, want_vhat=True)
+    K1b, K2b, Vb = dev(K1, K2, V)
+    o, vh, _ = stream_gpu(cfg, q, v, g, K1b, K2b, Vb, cuts)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref["o"]) and torch.equal(vh, ref["vhat"])
+    for a, b in ((K1a, K1b), (K2a, K2b), (Va, Vb)):
+        assert torch.equal(a, b)
