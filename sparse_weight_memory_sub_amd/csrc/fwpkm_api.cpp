@@ -199,6 +199,51 @@ int make_plan(const fwpkm_cfg* c, Plan* p) {
     return FWPKM_OK;
 }
 
+// Whole-row scoring (k_rows + reductions over the stored rows) for chunks
+// whose 64-token tiles cannot give every compute unit a workgroup (decode,
+// a single long sequence), as long as the rows fit kRowBytesCap.
+constexpr size_t kRowBytesCap = static_cast<size_t>(512) << 20;
+
+size_t row_bytes(const Plan& p, int B, int Tc) {
+    return static_cast<size_t>(B) * p.H * 2 * static_cast<size_t>(Tc) * p.n * 4;
+}
+
+// FWPKM_SCORE_PATH = "sweep" or "rows" overrides the choice (both compute
+// the same selection; the statistics differ only in summation order).
+int score_path_override() {
+    const char* e = std::getenv("FWPKM_SCORE_PATH");
+    if (!e) return 0;
+    if (std::strcmp(e, "sweep") == 0) return 1;
+    if (std::strcmp(e, "rows") == 0) return 2;
+    return 0;
+}
+
+bool use_rows(const Plan& p, int B, int Tc) {
+    const int ov = score_path_override();
+    if (ov == 1) return false;
+    if (ov == 2) return row_bytes(p, B, Tc) <= kRowBytesCap || Tc <= kRowTok;
+    if (Tc <= kRowTok) return true;
+    const long long wgs = static_cast<long long>(B) * p.H * 2 * ((Tc + kScoreTokMin - 1) / kScoreTokMin);
+    return wgs < device_cus() && row_bytes(p, B, Tc) <= kRowBytesCap;
+}
+
+// Longest chunk of at most T tokens scored by whole rows: both conditions of
+// use_rows are monotone in Tc, so the chunks that use rows are 1..rows_max.
+int rows_max(const Plan& p, int B, int T) {
+    const long long m = static_cast<long long>(B) * p.H * 2;
+    const int ov = score_path_override();
+    if (ov == 1) return 0;
+    const long long by_tiles = ov == 2 ? T : 64 * ((device_cus() - 1) / m);  // m * ceil(Tc/64) < CUs
+    const long long by_bytes = static_cast<long long>(kRowBytesCap / (static_cast<size_t>(m) * p.n * 4));
+    const long long tmax = std::min<long long>(T, std::min(by_tiles, by_bytes));
+    return static_cast<int>(std::max<long long>(tmax, std::min(T, kRowTok)));
+}
+
+// Token tile of the usage partials for a chunk.
+int stat_tile(const Plan& p, int B, int Tc) {
+    return use_rows(p, B, Tc) ? kScoreTokMin : score_tile(B, p.H, Tc, p.dot != 0);
+}
+
 constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -231,8 +276,8 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         }
         L.cand = take(Bs * p.H * 2 * T * static_cast<size_t>(score_cap(p.kh)) * 8);
         L.cnt = take(Bs * p.H * 2 * T * 4);
-        L.erow = take(Bs * p.H * 2 * std::min<size_t>(T, kRowTok) * p.n * 4);
     }
+    L.erow = take(row_bytes(p, B, rows_max(p, B, Tt)));
     if (with_update) {
         const size_t M = T * p.H * p.k;
         const size_t tiles = (M + kSortTile - 1) / kSortTile;
@@ -302,9 +347,10 @@ ScoreArgs score_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstr
 int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
                 const void* K1, const void* K2, const float* knorm, int32_t* idx, float* w, int64_t iw_bstride,
                 bool stats, int32_t* usage, hipStream_t s) {
-    // a handful of tokens (decode): whole rows of e and an exact top-k' of
-    // each; otherwise the two-pass sweep with candidate lists
-    const bool rows = !stats && Tc <= kRowTok;
+    // short chunks (decode, one long sequence): whole rows of e, an exact
+    // top-k' of each and statistics by reductions over the rows; otherwise
+    // the two-pass sweep with candidate lists
+    const bool rows = use_rows(p, B, Tc);
     ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm,
                              rows ? kScoreRows : (kScoreSelect | (stats ? kScoreStats : 0)));
     if (rows) a.erow = at<uint32_t>(ws, L.erow);
@@ -319,6 +365,7 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     {
         TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
         HIP_TRY(launch_score(a, p.store, s));
+        if (rows && stats) HIP_TRY(launch_row_stats(a, 0, s));
     }
     SelectArgs sa{};
     sa.cand = a.cand; sa.cnt = a.cnt; sa.cap = a.cap;
@@ -405,18 +452,21 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
 // knorm holds ||K_i||^2 of the current codebooks; the key step rewrites it.
 int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
             void* K1, void* K2, bool have_stats, float* knorm, hipStream_t s) {
+    const bool rows = use_rows(p, B, Tc);
     if (!have_stats) {
-        ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreStats);
+        ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, rows ? kScoreRows : kScoreStats);
         a.qn = at<float>(ws, L.qn);
         a.part = at<float>(ws, L.part);
         a.Z = at<float>(ws, L.Z);
         a.M = at<float>(ws, L.M);
+        if (rows) a.erow = at<uint32_t>(ws, L.erow);
         TimedLaunch tl(FWPKM_K_SWEEP_STATS, s);
         HIP_TRY(launch_score(a, p.store, s));
+        if (rows) HIP_TRY(launch_row_stats(a, 0, s));
     }
     PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, 0, Tc};
     {
-        const int tile = score_tile(B, p.H, Tc, p.dot != 0);
+        const int tile = stat_tile(p, B, Tc);
         pa.ntiles = (Tc + tile - 1) / tile;
     }
     {
@@ -430,7 +480,12 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     ra.m = at<float>(ws, L.m);
     {
         TimedLaunch tl(FWPKM_K_SWEEP_ROWSTAT, s);
-        HIP_TRY(launch_score(ra, p.store, s));
+        if (rows) {
+            ra.erow = at<uint32_t>(ws, L.erow);
+            HIP_TRY(launch_row_stats(ra, 1, s));
+        } else {
+            HIP_TRY(launch_score(ra, p.store, s));
+        }
     }
     const int Tp = (Tc + 31) / 32 * 32;
     {

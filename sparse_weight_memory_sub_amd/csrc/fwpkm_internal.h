@@ -189,9 +189,9 @@ enum ScoreMode : int {
     kScoreSelect = 1,   // candidate lists of the per-half top-k' -> cand, cnt
     kScoreStats = 2,    // per-tile partial sums of p over tokens -> part
     kScoreRowStat = 4,  // Z_t and m_t = sum_i p_ti log pbar_i -> Z, m
-    kScoreRows = 8,     // every e_ti written out -> erow (at most kRowTok tokens)
+    kScoreRows = 8,     // every e_ti written out -> erow
 };
-constexpr int kRowTok = 16;  // largest chunk scored by whole rows
+constexpr int kRowTok = 16;  // chunks this short are always scored by whole rows
 // Tokens per scoring workgroup, 16 per wavefront: 64, 128 or 256, chosen
 // per launch by score_tile().
 constexpr int kScoreTokMin = 64;
@@ -371,6 +371,12 @@ hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s);
 // the current device: the largest tile whose grid still covers every
 // compute unit, else the smallest.
 int score_tile(int B, int H, int Tc, bool dot);
+// compute units of the current device (cached per device)
+int device_cus();
+// Statistics of stored rows (rows mode): what = 0 writes Z (and M for dot
+// scoring) and the per-64-token usage partials into part; what = 1 writes m
+// (needs lp).
+hipError_t launch_row_stats(const ScoreArgs& a, int what, hipStream_t s);
 // Gradient of the retrieval output w.r.t. q, v and g for T tokens of B
 // sequences; per-sequence strides in elements:
 //   q, dq (f32):         + b*q_bstride + (t*H + h)*2*dh

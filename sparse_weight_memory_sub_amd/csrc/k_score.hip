@@ -395,22 +395,29 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
 // k_rows
 // ---------------------------------------------------------------------------
 
-// Scoring of a chunk of at most 16 tokens (decode): every e_ti is written out
-// so the selection can take an exact top-k' of whole rows.  One wavefront per
-// (sequence, head, half, 16 sub-keys): the sub-key rows are the MFMA's B
-// operand, loaded straight from HBM, so the codebooks are read once with
-// every wavefront of the chip in flight.  The arithmetic (accumulators
-// seeded with ||K_i||^2, -2q, k-blocks in order, ||q||^2 + eps added last) is
-// that of k_score, so the e values are the same bits.
+// Scoring by whole rows, for chunks whose token tiles cannot fill the chip
+// (decode; a single long sequence): every e_ti is written out so the
+// selection takes an exact top-k' of whole rows and the addressing
+// statistics are reductions over the stored rows.  One wavefront per
+// (sequence, head, half, 16 sub-keys, 16 tokens): the sub-key rows are the
+// MFMA's B operand, loaded straight from memory (wavefronts of the same
+// sub-keys are adjacent, so the rereads hit L2).  The arithmetic
+// (accumulators seeded with ||K_i||^2, -2q, k-blocks in order, ||q||^2 + eps
+// added last) is that of k_score, so the e values are the same bits.
+// Dot scoring writes ord(-s).  With a.qn the first sub-key block's
+// wavefronts also write ||q_half||^2 of their tokens.
 template <int STORE, int DHS, bool DOT>
 __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     constexpr int ES = Store<STORE>::kBytes;
     const int n = a.n, H = a.H, Tc = a.Tc;
-    const int kblk = n / 16;
+    const int kblk = n / 16, ttiles = (Tc + 15) / 16;
     const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (gw >= static_cast<int64_t>(a.B) * H * 2 * kblk) return;
+    if (gw >= static_cast<int64_t>(a.B) * H * 2 * kblk * ttiles) return;
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    const int bhh = static_cast<int>(gw / kblk), key = static_cast<int>(gw % kblk) * 16 + r;
+    const int tt = static_cast<int>(gw % ttiles);
+    const int64_t rest = gw / ttiles;
+    const int kb = static_cast<int>(rest % kblk), bhh = static_cast<int>(rest / kblk);
+    const int key = kb * 16 + r, t0 = tt * 16;
     const int half = bhh & 1, bh = bhh >> 1;
     const int h = bh % H, b = bh / H;
     Frag<STORE> Bf[DHS];
@@ -419,9 +426,10 @@ __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     const float knv = DOT ? 0.f : a.knorm[static_cast<size_t>(bhh) * n + key];
 
     Frag<STORE> A[DHS];
-    const bool tv = r < Tc;
+    const int tok = t0 + r;
+    const bool tv = tok < Tc;
     load_row_frags<STORE, DHS>(A, static_cast<const unsigned char*>(a.q) +
-        (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(tv ? r : 0) * H * (64 * DHS) +
+        (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(tv ? tok : 0) * H * (64 * DHS) +
          h * (64 * DHS) + half * (32 * DHS)) * ES, g);
     float qsq = 0.f;
 #pragma unroll
@@ -432,20 +440,101 @@ __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     }
     qsq += xor_lane(qsq, 16);
     qsq += xor_lane(qsq, 32);
+    const size_t rowbase = static_cast<size_t>(bhh) * Tc;
+    if (a.qn && kb == 0 && g == 0 && tv) a.qn[rowbase + tok] = qsq;
     f32x4_t acc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = knv;
 #pragma unroll
     for (int s = 0; s < DHS; ++s) mma(A[s], Bf[s], acc);
     const int eps_bits = __float_as_int(a.eps);
-    const size_t rowbase = static_cast<size_t>(bhh) * Tc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int t = 4 * g + i;
-        const float qe = __shfl(qsq, t, 64) + a.eps;
+        const int t = t0 + 4 * g + i;
+        const float qe = __shfl(qsq, 4 * g + i, 64) + a.eps;
         const uint32_t eb = DOT ? ord_f32(-acc[i]) : static_cast<uint32_t>(max(__float_as_int(qe + acc[i]), eps_bits));
         if (t < Tc) a.erow[(rowbase + t) * n + key] = eb;
     }
+}
+
+// p_ti (without 1/Z_t) from a stored row entry: 1/e for IDW, exp(s - M_t) for dot.
+template <bool DOT>
+__device__ __forceinline__ float row_weight(uint32_t u, float M) {
+    if constexpr (DOT) return __expf(-unord_f32(u) - M);
+    else return fast_rcp(__uint_as_float(u));
+}
+
+// Row statistics of stored rows: Z_t = sum_i 1/e_ti (IDW), or M_t = max_i s_ti
+// and Z_t = sum_i exp(s_ti - M_t) (dot).  One wavefront per row; each lane
+// sums its sub-keys j*64 + lane in order, then an xor butterfly.
+template <bool DOT>
+__global__ __launch_bounds__(256) void k_row_z(ScoreArgs a) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // bhh*Tc + t
+    if (row >= static_cast<int64_t>(a.B) * a.H * 2 * a.Tc) return;
+    const int lane = threadIdx.x & 63, n = a.n;
+    const uint32_t* e = a.erow + static_cast<size_t>(row) * n;
+    float M = 0.f;
+    if constexpr (DOT) {
+        float mx = -INFINITY;
+        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, -unord_f32(e[i]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, xor_lane(mx, o));
+        M = mx;
+    }
+    float z = 0.f;
+    for (int i = lane; i < n; i += 64) z += row_weight<DOT>(e[i], M);
+    z = wave_sum(z);
+    if (lane == 0) {
+        a.Z[row] = z;
+        if constexpr (DOT) a.M[row] = M;
+    }
+}
+
+// Per-tile partial sums over tokens of p_ti for every sub-key (the pieces of
+// the chunk's usage pbar), tiles of kScoreTokMin tokens.  One workgroup per
+// (sequence, head, half, tile, 64 sub-keys): lane = sub-key, wavefront w sums
+// tokens [16w, 16w + 16) of the tile in order, and the four wavefront sums
+// are added in order.
+template <bool DOT>
+__global__ __launch_bounds__(256) void k_row_colsum(ScoreArgs a) {
+    __shared__ float wsum[4][64];
+    const int ntiles = (a.Tc + kScoreTokMin - 1) / kScoreTokMin;
+    const int kblk = (a.n + 63) / 64;
+    const int kb = blockIdx.x % kblk;
+    const int tile = (blockIdx.x / kblk) % ntiles;
+    const int bhh = blockIdx.x / (kblk * ntiles);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = a.n, i = kb * 64 + lane;
+    const int t0 = tile * kScoreTokMin + wave * 16, t1 = min(a.Tc, t0 + 16);
+    const size_t rowbase = static_cast<size_t>(bhh) * a.Tc;
+    float s = 0.f;
+    if (i < n)
+        for (int t = t0; t < t1; ++t) {
+            const size_t row = rowbase + t;
+            const float M = DOT ? a.M[row] : 0.f;
+            s = fmaf(row_weight<DOT>(a.erow[row * n + i], M), fast_rcp(a.Z[row]), s);
+        }
+    wsum[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && i < n)
+        a.part[(static_cast<size_t>(bhh) * ntiles + tile) * n + i] =
+            ((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane];
+}
+
+// Row statistic m_t = sum_i p_ti ln pbar_i from stored rows.
+template <bool DOT>
+__global__ __launch_bounds__(256) void k_row_m(ScoreArgs a) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= static_cast<int64_t>(a.B) * a.H * 2 * a.Tc) return;
+    const int lane = threadIdx.x & 63, n = a.n;
+    const int bhh = static_cast<int>(row / a.Tc);
+    const uint32_t* e = a.erow + static_cast<size_t>(row) * n;
+    const float* lp = a.lp + static_cast<size_t>(bhh) * n;
+    const float M = DOT ? a.M[row] : 0.f;
+    float x = 0.f;
+    for (int i = lane; i < n; i += 64) x = fmaf(row_weight<DOT>(e[i], M), lp[i], x);
+    x = wave_sum(x);
+    if (lane == 0) a.m[row] = x / a.Z[row];
 }
 
 // ---------------------------------------------------------------------------
@@ -782,8 +871,7 @@ hipError_t score_mode(const ScoreArgs& a, hipStream_t s) {
 template <int STORE, int DHS>
 hipError_t score_mk(const ScoreArgs& a, hipStream_t s) {
     if (a.mode == kScoreRows) {
-        if (a.Tc > kRowTok) return hipErrorInvalidValue;
-        const int64_t waves = static_cast<int64_t>(a.B) * a.H * 2 * (a.n / 16);
+        const int64_t waves = static_cast<int64_t>(a.B) * a.H * 2 * (a.n / 16) * ((a.Tc + 15) / 16);
         if (a.dot)
             hipLaunchKernelGGL((k_rows<STORE, DHS, true>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
         else
@@ -823,20 +911,7 @@ int score_cap(int kh) { return kh <= 32 ? 128 : 256; }
 
 int score_tile(int B, int H, int Tc, bool dot) {
     if (dot) return kScoreTokMin;  // the dot-product variant is built for 64-token tiles
-    // compute units of the current device, looked up once per device
-    static int cus[64] = {};
-    int dev = 0;
-    int ncu = 256;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-        if (cus[dev] == 0) {
-            int v = 0;
-            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-                cus[dev] = v;
-            else
-                cus[dev] = ncu;
-        }
-        ncu = cus[dev];
-    }
+    const int ncu = device_cus();
     const int span = (Tc + 15) / 16 * 16;  // no wider than the chunk
     for (int tile = kScoreTokMax; tile > kScoreTokMin; tile >>= 1) {
         if (tile > span) continue;
@@ -844,6 +919,38 @@ int score_tile(int B, int H, int Tc, bool dot) {
         if (wgs >= ncu) return tile;
     }
     return kScoreTokMin;
+}
+
+hipError_t launch_row_stats(const ScoreArgs& a, int what, hipStream_t s) {
+    const int64_t rows = static_cast<int64_t>(a.B) * a.H * 2 * a.Tc;
+    const unsigned rgrid = static_cast<unsigned>((rows + 3) / 4);
+    if (what == 0) {  // Z (and M), then the usage partials
+        const int ntiles = (a.Tc + kScoreTokMin - 1) / kScoreTokMin;
+        const unsigned cgrid = static_cast<unsigned>(a.B * a.H * 2 * ntiles * ((a.n + 63) / 64));
+        if (a.dot) {
+            hipLaunchKernelGGL(k_row_z<true>, dim3(rgrid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(k_row_colsum<true>, dim3(cgrid), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL(k_row_z<false>, dim3(rgrid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(k_row_colsum<false>, dim3(cgrid), dim3(256), 0, s, a);
+        }
+    } else {  // the row statistic m
+        if (a.dot) hipLaunchKernelGGL(k_row_m<true>, dim3(rgrid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_row_m<false>, dim3(rgrid), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        cus[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+                       ? v : 256;
+    }
+    return cus[dev];
 }
 
 hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s) {

@@ -133,8 +133,13 @@ def timing_read() -> dict:
     return out
 
 
-@functools.lru_cache(maxsize=256)
 def workspace_bytes(cfg: FwpkmConfig, B: int, T: int) -> int:
+    # the size follows the scoring path, which FWPKM_SCORE_PATH can override
+    return _workspace_bytes(cfg, int(B), int(T), os.environ.get("FWPKM_SCORE_PATH", ""))
+
+
+@functools.lru_cache(maxsize=256)
+def _workspace_bytes(cfg: FwpkmConfig, B: int, T: int, path: str) -> int:
     out = ctypes.c_size_t(0)
     c = _cfg(cfg)
     _check(load().fwpkm_workspace_bytes(ctypes.byref(c), int(B), int(T), ctypes.byref(out)))

@@ -5,6 +5,8 @@ fwpkm_forward_seq does over the same tokens, whatever the split into calls
 (checked bit for bit), and agree with the oracle's token-by-token reading
 (oracle.Stream, pinned to the oracle's chunked pass on the CPU).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -180,7 +182,11 @@ def test_rows_mode_selection_equals_sweep_with_ties(n, dup):
     for i in range(n):
         K1[:, :, i] = K1[:, :, (i // dup) * dup]
     K1d, K2d, Vd = dev(K1, K2, V)
-    full = fwpkm.fwpkm_retrieve(cfg, *dev(q, v, g), K1d, K2d, Vd)  # one 40-token chunk: the sweep
+    os.environ["FWPKM_SCORE_PATH"] = "sweep"
+    try:
+        full = fwpkm.fwpkm_retrieve(cfg, *dev(q, v, g), K1d, K2d, Vd)  # one 40-token chunk: the sweep
+    finally:
+        del os.environ["FWPKM_SCORE_PATH"]
     for t0 in range(0, T, 8):
         part = fwpkm.fwpkm_retrieve(cfg, *dev(q[:, t0:t0 + 8], v[:, t0:t0 + 8], g[:, t0:t0 + 8]), K1d, K2d, Vd)
         assert torch.equal(part["idx"], full["idx"][:, t0:t0 + 8])
