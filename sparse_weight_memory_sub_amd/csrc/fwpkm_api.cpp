@@ -281,7 +281,13 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
     if (with_update) {
         const size_t M = T * p.H * p.k;
         const size_t tiles = (M + kSortTile - 1) / kSortTile;
-        const size_t pieces = (M + kPiece - 1) / kPiece;
+        // the most pieces any chunk of up to T tokens with targets can need
+        // (smaller chunks may use smaller pieces)
+        size_t pieces = 1;
+        for (int nt = 1; nt <= Tt; ++nt) {
+            const int Mn = nt * p.H * p.k, pc = scatter_piece(Mn);
+            pieces = std::max(pieces, static_cast<size_t>((Mn + pc - 1) / pc));
+        }
         L.r = take(Bs * T * p.dv * 4);
         L.Z = take(Bs * p.H * 2 * T * 4);
         L.M = take(Bs * p.H * 2 * T * 4);
@@ -416,7 +422,8 @@ int write_rows(const Plan& p, const Layout& L, void* ws, int b0, int nb, int Tc,
                int64_t iw_bstride, void* V, int32_t* n_read, int sorted, hipStream_t s) {
     const int M = n_tgt * p.H * p.k;
     if (M == 0) return FWPKM_OK;
-    const int pieces = (M + kPiece - 1) / kPiece;
+    const int piece = scatter_piece(M);
+    const int pieces = (M + piece - 1) / piece;
     const size_t kb = static_cast<size_t>(b0);
     ScatterArgs sa{};
     sa.keys = at<uint32_t>(ws, sorted ? L.k1 : L.k0) + kb * M;
@@ -427,7 +434,7 @@ int write_rows(const Plan& p, const Layout& L, void* ws, int b0, int nb, int Tc,
     sa.n_read = n_read ? n_read + kb * static_cast<size_t>(p.N) : nullptr;
     sa.ph = at<float>(ws, L.ph) + kb * pieces * p.dv; sa.pt = at<float>(ws, L.pt) + kb * pieces * p.dv;
     sa.pt_start = at<int32_t>(ws, L.pts) + kb * pieces; sa.ph_end = at<int32_t>(ws, L.phe) + kb * pieces;
-    sa.B = nb; sa.M = M; sa.pieces = pieces; sa.H = p.H; sa.k = p.k; sa.dv = p.dv; sa.Tc = Tc;
+    sa.B = nb; sa.M = M; sa.pieces = pieces; sa.piece = piece; sa.H = p.H; sa.k = p.k; sa.dv = p.dv; sa.Tc = Tc;
     sa.N = static_cast<uint32_t>(p.N); sa.lr = p.lr_v; sa.inv_h = 1.f / static_cast<float>(p.H);
     TimedLaunch tl(FWPKM_K_SCATTER, s);
     HIP_TRY(launch_scatter(sa, p.store, s));

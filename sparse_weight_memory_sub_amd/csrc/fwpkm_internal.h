@@ -321,6 +321,7 @@ struct ScatterArgs {
     int32_t* pt_start;    // [B][pieces] start position of the leaving run, or -1
     int32_t* ph_end;      // [B][pieces] end position (exclusive) of the entering run, or -1
     int B, M, pieces, H, k, dv, Tc;
+    int piece;            // sorted positions per piece (wavefront), <= 64
     uint32_t N;
     float lr, inv_h;
 };
@@ -428,6 +429,16 @@ hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s);
 
 constexpr int kSortItems = 8;                  // entries per thread
 constexpr int kSortTile = 256 * kSortItems;    // entries per sort workgroup
-constexpr int kPiece = 64;                     // sorted positions per scatter wavefront
+constexpr int kPiece = 64;                     // sorted positions per scatter wavefront (at most)
+// Positions per scatter piece for a sequence of M sorted reads: 64, or 32 /
+// 16 when 64-position pieces would give a sequence fewer than kPieceWaves
+// wavefronts.  It depends on M only, so a sequence's write sums in the same
+// order whatever the batch around it.
+constexpr int kPieceWaves = 1024;
+inline int scatter_piece(int M) {
+    int piece = kPiece;
+    while (piece > 16 && (M + piece - 1) / piece < kPieceWaves) piece >>= 1;
+    return piece;
+}
 
 }  // namespace fwpkm

@@ -8,7 +8,8 @@
 // 3.3: read-count consensus; A.3: no clipping; A.4: sum reduction).  Rows
 // that nobody read are never touched.
 //
-// The sorted list is cut into pieces of 64 positions, one wavefront each;
+// The sorted list is cut into pieces of up to 64 positions (fewer when a
+// small batch would leave the chip idle), one wavefront each;
 // lane l owns elements [l*EPL, (l+1)*EPL) of a d_v row.  A wavefront sums
 // each run of its piece in list order.  Runs inside the piece are written
 // straight away; a run that crosses a piece boundary leaves per-piece
@@ -192,9 +193,9 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
     const int64_t wid = static_cast<int64_t>(blk) * 4 + wave;
     if (wid >= static_cast<int64_t>(a.B) * a.pieces) return;
     const int b = static_cast<int>(wid / a.pieces), p = static_cast<int>(wid % a.pieces);
-    const int p0 = p * kPiece;
+    const int p0 = p * a.piece;
     const int pos = p0 + lane;
-    const bool valid = pos < a.M;
+    const bool valid = lane < a.piece && pos < a.M;
     const uint32_t* keys = a.keys + static_cast<size_t>(b) * a.M;
     const uint32_t* vals = a.vals + static_cast<size_t>(b) * a.M;
     const uint32_t key = valid ? keys[pos] : 0xffffffffu;
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
     uint32_t prev = __shfl_up(key, 1, 64);
     uint32_t next = __shfl_down(key, 1, 64);
     if (lane == 0) prev = (p0 > 0) ? keys[p0 - 1] : 0xfffffffeu;
-    if (lane == 63) next = (pos + 1 < a.M) ? keys[pos + 1] : 0xfffffffeu;
+    if (lane == a.piece - 1) next = (pos + 1 < a.M) ? keys[pos + 1] : 0xfffffffeu;
     const bool head = valid && (pos == 0 || prev != key);
     const bool tail = valid && (pos == a.M - 1 || next != key);
     const int HK = a.H * a.k;
