@@ -239,6 +239,13 @@ int rows_max(const Plan& p, int B, int T) {
     return static_cast<int>(std::max<long long>(tmax, std::min(T, kRowTok)));
 }
 
+// FWPKM_KGRAD_SPLIT = <s> fixes the key step's token split at s (capped by
+// the chunk's 32-token blocks) in place of the per-sequence rule.
+int kgrad_split_override() {
+    const char* e = std::getenv("FWPKM_KGRAD_SPLIT");
+    return e ? std::max(0, std::atoi(e)) : 0;
+}
+
 // Token tile of the usage partials for a chunk.
 int stat_tile(const Plan& p, int B, int Tc) {
     return use_rows(p, B, Tc) ? kScoreTokMin : score_tile(B, p.H, Tc, p.dot != 0);
@@ -249,8 +256,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, M, m, part, lp, qT, k0, v0, k1, v1, counts, ph, pt,
-        pts, phe;
+    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, M, m, part, lp, qT, kpart, k0, v0, k1, v1, counts,
+        ph, pt, pts, phe;
     size_t total;
 };
 
@@ -295,6 +302,9 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         L.part = take(Bs * p.H * 2 * ntiles * p.n * 4);
         L.lp = take(Bs * p.H * 2 * p.n * 4);
         L.qT = take(Bs * p.H * 2 * p.dh * ((T + 31) / 32 * 32) * p.es);
+        int ksplit = 1;
+        for (int nt = 1; nt <= Tt; nt += 32) ksplit = std::max(ksplit, kgrad_split(p.H, p.n, nt, kgrad_split_override(), nullptr));
+        L.kpart = ksplit > 1 ? take(kgrad_part_floats(B, p.H, p.n, p.dh, ksplit) * 4) : 0;
         L.k0 = take(Bs * M * 4);
         L.v0 = take(Bs * M * 4);
         L.k1 = take(Bs * M * 4);
@@ -506,6 +516,8 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     ka.qn = at<float>(ws, L.qn); ka.Z = at<float>(ws, L.Z); ka.m = at<float>(ws, L.m); ka.lp = at<float>(ws, L.lp);
     ka.M = at<float>(ws, L.M); ka.dot = p.dot;
     ka.B = B; ka.Tc = Tc; ka.n = p.n; ka.H = p.H; ka.dh = p.dh; ka.eps = p.eps; ka.lr = p.lr_k;
+    ka.split = kgrad_split(p.H, p.n, Tc, kgrad_split_override(), &ka.per);
+    ka.part = ka.split > 1 ? at<float>(ws, L.kpart) : nullptr;
     {
         TimedLaunch tl(FWPKM_K_KGRAD, s);
         HIP_TRY(launch_kgrad(ka, p.store, s));

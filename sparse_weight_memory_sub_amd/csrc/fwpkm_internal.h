@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace fwpkm {
 
 // ---------------------------------------------------------------------------
@@ -355,7 +357,45 @@ struct KgradArgs {
     float eps, lr;
     const float* M;       // [B][H][2][Tc] row maximum of s (dot scoring)
     int dot;
+    // Token split: split > 1 runs each 64-key block as `split` workgroups over
+    // `per` consecutive 32-token blocks each, which leave their sums in `part`
+    // (kgrad_part_floats floats) for k_kgrad_finish to add in split order.
+    int split, per;
+    float* part;
 };
+
+// Token split of the key step for one sequence.  Only a sequence with fewer
+// than kKgradSplitBelow 64-key workgroups (H * 2 * ceil(n/64)) is split: a
+// power of two <= 8 that brings them up to kKgradWgs, with at least
+// kKgradMinBlocks 32-token blocks per split.  Wider sequences already give
+// the chip enough workgroups at modest batch sizes, and the partials' round
+// trip through memory would cost more than the split gains.  The rule reads
+// per-sequence sizes only, so a sequence's keys sum in the same order
+// whatever the batch around it.  `override` > 0 replaces the power of two
+// (still capped by the block count).  Returns the split and sets *per
+// (blocks per split) so that no split is empty.
+constexpr int kKgradSplitBelow = 64;
+constexpr int kKgradWgs = 256;
+constexpr int kKgradMinBlocks = 2;
+inline int kgrad_split(int H, int n, int Tc, int override, int* per) {
+    const int nblk = (Tc + 31) / 32;
+    const int P = H * 2 * ((n + 63) / 64);
+    int s = 1;
+    if (override > 0) {
+        s = std::min(override, nblk);
+    } else if (P < kKgradSplitBelow) {
+        while (s < 8 && P * 2 * s <= kKgradWgs && 2 * s * kKgradMinBlocks <= nblk) s *= 2;
+    }
+    s = std::max(s, 1);
+    const int pb = (nblk + s - 1) / s;
+    if (per) *per = pb;
+    return (nblk + pb - 1) / pb;
+}
+// Floats of the split partials: per (sequence, head, half, split, key), a
+// row of dh gradient sums and one column sum.
+inline size_t kgrad_part_floats(int B, int H, int n, int dh, int split) {
+    return static_cast<size_t>(B) * H * 2 * split * n * (static_cast<size_t>(dh) + 1);
+}
 
 struct KnormArgs {
     const void* K1;

@@ -117,7 +117,55 @@ __global__ __launch_bounds__(256) void k_qt(QtArgs a) {
 // row layout of the MFMA distance tiles.
 __device__ __forceinline__ int tok_of(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4); }
 
+// Split partials: [B*H*2][split][n][dh] sums over the split's tokens of
+// a_ti q_t, then [B*H*2][split][n] sums of a_ti.
+__device__ __forceinline__ float* part_colsum(const KgradArgs& a, int dh) {
+    return a.part + static_cast<size_t>(a.B) * a.H * 2 * a.split * a.n * dh;
+}
+
+// Key update of one wave's 16 keys from the summed tiles: gacc[c][i] holds
+// sum_t a_ti q_t[16c + r] of key key0 + 4g + i, colsum (lanes r) sum_t a_ti
+// of key key0 + r.  IDW: K -= lr * (sum a q - (sum a) K); dot: K -= lr * sum a q.
+// Rewrites ||K||^2 of the new keys.
 template <int STORE, int DHS, bool DOT>
+__device__ __forceinline__ void kgrad_apply(const KgradArgs& a, unsigned char* Kb, int bhh, int key0, int r, int g,
+                                            const f32x4_t* gacc, float colsum) {
+    constexpr int DH = 32 * DHS;
+    constexpr int NCT = DHS * 2;
+    const int n = a.n;
+    float cs[4], ksq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        cs[i] = __shfl(colsum, 4 * g + i, 64);
+        ksq[i] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const int col = c * 16 + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = key0 + 4 * g + i;
+            const size_t off = static_cast<size_t>(k) * DH + col;
+            const float kv = ld_elem<STORE>(Kb, off);
+            const float grad = DOT ? gacc[c][i] : gacc[c][i] - cs[i] * kv;
+            float kn2 = kv - a.lr * grad;
+            if constexpr (STORE == kBF16) kn2 = bf16_to_f32(f32_to_bf16(kn2));
+            st_elem<STORE>(Kb, off, kn2);
+            ksq[i] = fmaf(kn2, kn2, ksq[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float x = ksq[i];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        if (r == 0) a.knorm[static_cast<size_t>(bhh) * n + key0 + 4 * g + i] = x;
+    }
+}
+
+template <int STORE, int DHS, bool DOT, bool SPLIT>
 __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int ES = Store<STORE>::kBytes;
@@ -131,7 +179,9 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     const int nkb = (n + 63) / 64;
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int kb = static_cast<int>(lid % nkb);
-    const int bhh = static_cast<int>(lid / nkb);  // (b*H + h)*2 + half
+    const int split = SPLIT ? a.split : 1;
+    const int sp = static_cast<int>((lid / nkb) % split);
+    const int bhh = static_cast<int>(lid / nkb / split);  // (b*H + h)*2 + half
     const int half = bhh & 1, bh = bhh >> 1;
     const int h = bh % H, b = bh / H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -183,11 +233,14 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     // a_ti = (2/C)(ln pbar_i - m_t)/(Z_t e^2) for IDW, (1/C)(ln pbar_i - m_t) e^(s - M_t)/Z_t for dot
     const float inv_tc2 = (DOT ? 1.f : 2.f) / static_cast<float>(Tc);
 
-    // Token blocks of 32.  Key blocks of one (sequence, head, half) run side by
-    // side and read the same query rows: each starts at a different block
-    // (fixed order per key block, so the sums stay reproducible).
-    const int nblk = (Tc + 31) / 32;
-    auto tok_block = [&](int bi) { return ((bi + kb) % nblk) * 32; };
+    // Token blocks of 32; this workgroup takes blocks b0 .. b0+nblk-1 of the
+    // chunk (all of them without a split).  Key blocks of one (sequence, head,
+    // half) run side by side and read the same query rows: each starts at a
+    // different block (fixed order per key block, so the sums stay
+    // reproducible).
+    const int b0 = SPLIT ? sp * a.per : 0;
+    const int nblk = SPLIT ? min(a.per, (Tc + 31) / 32 - b0) : (Tc + 31) / 32;
+    auto tok_block = [&](int bi) { return (b0 + (bi + kb) % nblk) * 32; };
     // LDS: two query tiles (with their token statistics), used in turn, and
     // one transposed tile
     unsigned char* tbuf = smem + 2 * QBUF;
@@ -314,38 +367,116 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     // colsum over the four lane groups: lanes with the same r hold the same key
     colsum += __shfl_xor(colsum, 16, 64);
     colsum += __shfl_xor(colsum, 32, 64);
-    float cs[4], ksq[4];
+    if constexpr (SPLIT) {
+        // leave this split's sums for k_kgrad_finish, one row of d_h per key
+        const size_t rows = static_cast<size_t>(bhh) * a.split + sp;
+        float* pg = a.part + rows * n * DH;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        cs[i] = __shfl(colsum, 4 * g + i, 64);
-        ksq[i] = 0.f;
-    }
+        for (int c = 0; c < NCT; ++c) {
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-        const int col = c * 16 + r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = key0 + 4 * g + i;
-            const size_t off = static_cast<size_t>(k) * DH + col;
-            const float kv = ld_elem<STORE>(Kb, off);
-            // IDW: sum_t a (q_t - K_i); dot: sum_t a q_t
-            const float grad = DOT ? gacc[c][i] : gacc[c][i] - cs[i] * kv;
-            float kn2 = kv - a.lr * grad;
-            if constexpr (STORE == kBF16) kn2 = bf16_to_f32(f32_to_bf16(kn2));
-            st_elem<STORE>(Kb, off, kn2);
-            ksq[i] = fmaf(kn2, kn2, ksq[i]);
+            for (int i = 0; i < 4; ++i) pg[static_cast<size_t>(key0 + 4 * g + i) * DH + 16 * c + r] = gacc[c][i];
         }
+        if (g == 0) part_colsum(a, DH)[rows * n + key0 + r] = colsum;
+    } else {
+        kgrad_apply<STORE, DHS, DOT>(a, Kb, bhh, key0, r, g, gacc, colsum);
+    }
+}
+
+// Split sums and key update of 8 columns (8j .. 8j+7) of key kg (bhh*n + key);
+// the new values also go to out[0..7].
+template <int STORE, int DHS, bool DOT>
+__device__ __forceinline__ void update_row(const KgradArgs& a, size_t kg, int j, float* out) {
+    constexpr int ES = Store<STORE>::kBytes;
+    constexpr int DH = 32 * DHS;
+    const int n = a.n;
+    const int bhh = static_cast<int>(kg / n), k = static_cast<int>(kg % n);
+    const int bh = bhh >> 1, half = bhh & 1;
+    const float* pg = a.part + (static_cast<size_t>(bhh) * a.split * n + k) * DH + 8 * j;
+    const float* pc = part_colsum(a, DH) + static_cast<size_t>(bhh) * a.split * n + k;
+    const size_t sstride = static_cast<size_t>(n) * DH;
+    float4 s0 = *reinterpret_cast<const float4*>(pg), s1 = *reinterpret_cast<const float4*>(pg + 4);
+    float cs = pc[0];
+    for (int sp = 1; sp < a.split; ++sp) {
+        const float4 x0 = *reinterpret_cast<const float4*>(pg + sp * sstride);
+        const float4 x1 = *reinterpret_cast<const float4*>(pg + sp * sstride + 4);
+        s0.x += x0.x; s0.y += x0.y; s0.z += x0.z; s0.w += x0.w;
+        s1.x += x1.x; s1.y += x1.y; s1.z += x1.z; s1.w += x1.w;
+        cs += pc[static_cast<size_t>(sp) * n];
+    }
+    const float gs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    unsigned char* Kb = static_cast<unsigned char*>(half ? a.K2 : a.K1) +
+        (static_cast<size_t>(bh) * n * DH + static_cast<size_t>(k) * DH + 8 * j) * ES;
+    float kv[8], kn[8];
+    if constexpr (STORE == kBF16) {
+        const uint4 x = *reinterpret_cast<const uint4*>(Kb);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kv[2 * e] = __uint_as_float(w[e] << 16);
+            kv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    } else {
+        const float4 x0 = reinterpret_cast<const float4*>(Kb)[0], x1 = reinterpret_cast<const float4*>(Kb)[1];
+        kv[0] = x0.x; kv[1] = x0.y; kv[2] = x0.z; kv[3] = x0.w;
+        kv[4] = x1.x; kv[5] = x1.y; kv[6] = x1.z; kv[7] = x1.w;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float x = ksq[i];
+    for (int e = 0; e < 8; ++e) {
+        // IDW: sum_t a (q_t - K_i); dot: sum_t a q_t
+        const float grad = DOT ? gs[e] : gs[e] - cs * kv[e];
+        float x = kv[e] - a.lr * grad;
+        if constexpr (STORE == kBF16) x = bf16_to_f32(f32_to_bf16(x));
+        kn[e] = x;
+        out[e] = x;
+    }
+    if constexpr (STORE == kBF16) {
+        uint4 y;
+        y.x = pack_bf16x2(kn[0], kn[1]);
+        y.y = pack_bf16x2(kn[2], kn[3]);
+        y.z = pack_bf16x2(kn[4], kn[5]);
+        y.w = pack_bf16x2(kn[6], kn[7]);
+        *reinterpret_cast<uint4*>(Kb) = y;
+    } else {
+        reinterpret_cast<float4*>(Kb)[0] = make_float4(kn[0], kn[1], kn[2], kn[3]);
+        reinterpret_cast<float4*>(Kb)[1] = make_float4(kn[4], kn[5], kn[6], kn[7]);
+    }
+}
+
+// Sum over the token splits of k_kgrad, in split order, then the key update:
+// one thread per 8 columns of a key, DH/8 adjacent threads per key.  The new
+// norms are summed in k_knorm's order (lane r over columns r + 16c, then
+// across the 16 lanes), so a run that recomputes them from the keys agrees
+// bit for bit with one that carries them.
+template <int STORE, int DHS, bool DOT>
+__global__ __launch_bounds__(256) void k_kgrad_finish(KgradArgs a) {
+    constexpr int DH = 32 * DHS;
+    constexpr int TPK = DH / 8;   // threads per key: 4 .. 32
+    constexpr int KPW = 256 / TPK;  // keys per workgroup
+    __shared__ float rows[256 * 8];  // the workgroup's new keys, row-major
+    const int n = a.n;
+    const size_t total = static_cast<size_t>(a.B) * a.H * 2 * n;
+    const size_t t = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    const size_t kg = t / TPK;  // (bhh * n) + key
+    const int j = static_cast<int>(t % TPK);
+    if (kg < total) update_row<STORE, DHS, DOT>(a, kg, j, rows + threadIdx.x * 8);
+    __syncthreads();
+    for (int pr = threadIdx.x; pr < KPW * 16; pr += 256) {  // uniform per wave
+        const int kl = pr >> 4, r = pr & 15;
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < DH / 16; ++c) {
+            const float v = rows[kl * DH + 16 * c + r];
+            x = fmaf(v, v, x);
+        }
         x += __shfl_xor(x, 1, 64);
         x += __shfl_xor(x, 2, 64);
         x += __shfl_xor(x, 4, 64);
         x += __shfl_xor(x, 8, 64);
-        if (r == 0) a.knorm[static_cast<size_t>(bhh) * n + key0 + 4 * g + i] = x;
+        const size_t key = static_cast<size_t>(blockIdx.x) * KPW + kl;
+        if (r == 0 && key < total) a.knorm[key] = x;
     }
 }
+
 
 template <int STORE, int DHS, bool DOT>
 hipError_t kgrad_t(const KgradArgs& a, hipStream_t s) {
@@ -354,14 +485,25 @@ hipError_t kgrad_t(const KgradArgs& a, hipStream_t s) {
     constexpr size_t LDS = 2 * (static_cast<size_t>(32) * DH * ES + 3 * 32 * 4) + static_cast<size_t>(DH) * 32 * ES;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_kgrad<STORE, DHS, DOT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
+        for (const void* f : {reinterpret_cast<const void*>(&k_kgrad<STORE, DHS, DOT, false>),
+                              reinterpret_cast<const void*>(&k_kgrad<STORE, DHS, DOT, true>)}) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
     const int nkb = (a.n + 63) / 64;
     const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * nkb;
-    hipLaunchKernelGGL((k_kgrad<STORE, DHS, DOT>), dim3(grid), dim3(256), LDS, s, a);
+    if (a.split <= 1) {
+        hipLaunchKernelGGL((k_kgrad<STORE, DHS, DOT, false>), dim3(grid), dim3(256), LDS, s, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_kgrad<STORE, DHS, DOT, true>), dim3(grid * a.split), dim3(256), LDS, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t threads = static_cast<size_t>(a.B) * a.H * 2 * a.n * (DH / 8);
+    hipLaunchKernelGGL((k_kgrad_finish<STORE, DHS, DOT>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -134,12 +134,14 @@ def timing_read() -> dict:
 
 
 def workspace_bytes(cfg: FwpkmConfig, B: int, T: int) -> int:
-    # the size follows the scoring path, which FWPKM_SCORE_PATH can override
-    return _workspace_bytes(cfg, int(B), int(T), os.environ.get("FWPKM_SCORE_PATH", ""))
+    # the size follows the scoring path and the key step's token split, which
+    # FWPKM_SCORE_PATH and FWPKM_KGRAD_SPLIT can override
+    return _workspace_bytes(cfg, int(B), int(T), os.environ.get("FWPKM_SCORE_PATH", ""),
+                            os.environ.get("FWPKM_KGRAD_SPLIT", ""))
 
 
 @functools.lru_cache(maxsize=256)
-def _workspace_bytes(cfg: FwpkmConfig, B: int, T: int, path: str) -> int:
+def _workspace_bytes(cfg: FwpkmConfig, B: int, T: int, path: str, ksplit: str) -> int:
     out = ctypes.c_size_t(0)
     c = _cfg(cfg)
     _check(load().fwpkm_workspace_bytes(ctypes.byref(c), int(B), int(T), ctypes.byref(out)))
