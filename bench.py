@@ -488,10 +488,20 @@ def main():
         oracle.forward_seq(cfg, qs, vs, gs, *pristine, passes=1, chunk_limit=nc)
         dt = time.perf_counter() - t1
         tok = ns * min(T, nc * cfg.chunk)
+        # the same oracle on one thread, over one sequence's first chunk
+        oracle.set_threads(1)
+        t1 = time.perf_counter()
+        oracle.forward_seq(cfg, qs[:1], vs[:1], gs[:1], *(x[:1] for x in pristine), passes=1, chunk_limit=1)
+        dt1 = time.perf_counter() - t1
+        oracle.set_threads(threads)
+        tok1 = min(T, cfg.chunk)
         result["cpu_baseline"] = {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                   "sample": f"{ns} sequence(s) x first {nc} chunk(s) of pass 1 "
-                                            f"({tok} tokens, {dt:.1f} s, fp64 C oracle, OpenMP)"}
-        log(f"cpu oracle: {tok / dt:.4g} tokens/s on {threads} threads ({dt:.1f} s)")
+                                            f"({tok} tokens, {dt:.1f} s, fp64 C oracle, OpenMP)",
+                                  "value_1thread": tok1 / dt1,
+                                  "sample_1thread": f"1 sequence x first chunk ({tok1} tokens, {dt1:.1f} s)"}
+        log(f"cpu oracle: {tok / dt:.4g} tokens/s on {threads} threads ({dt:.1f} s); "
+            f"{tok1 / dt1:.4g} tokens/s on 1 thread ({dt1:.1f} s)")
     print(json.dumps(result), flush=True)
 
 

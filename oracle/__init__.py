@@ -74,6 +74,8 @@ def _load():
         lib.fwo_double_to_bf16.argtypes = [ctypes.c_double]
         lib.fwo_double_to_bf16.restype = ctypes.c_uint16
         lib.fwo_num_threads.restype = ctypes.c_int
+        lib.fwo_set_threads.argtypes = [ctypes.c_int]
+        lib.fwo_set_threads.restype = None
         for f in (lib.fwo_retrieve, lib.fwo_chunk_update, lib.fwo_forward_seq, lib.fwo_pair_p):
             f.restype = ctypes.c_int
         _lib = lib
@@ -119,6 +121,11 @@ def _p(a):
 
 def num_threads() -> int:
     return int(_load().fwo_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Thread count of later oracle calls (the OpenMP default is every core)."""
+    _load().fwo_set_threads(int(n))
 
 
 def double_to_bf16(x: float) -> int:

@@ -71,6 +71,14 @@ int fwo_num_threads(void) {
 #endif
 }
 
+void fwo_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ */
 /* argument checks                                                      */
 /* ------------------------------------------------------------------ */

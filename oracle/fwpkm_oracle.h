@@ -127,6 +127,9 @@ uint16_t fwo_double_to_bf16(double x);
 /* Number of OpenMP threads the oracle runs with. */
 int fwo_num_threads(void);
 
+/* Sets the OpenMP thread count of later calls (n > 0). */
+void fwo_set_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif
