@@ -365,6 +365,8 @@ int fwo_retrieve(const fwo_cfg* c, int32_t B, int32_t T,
  *   grad_{V_i} L_mem = sum over reads (t,h,j) of row i of (w/H) g_t (v_hat_t - y_t);
  *   grad_agg V_i = grad_{V_i} L_mem / N_read,i;  V_i <- V_i - lr_v grad_agg V_i.
  * tgt_row(t) gives the raw target of token t (t < n_tgt).
+ * A slot id outside [0, N) names no row: the read is skipped (the library's
+ * boundary takes such ids as a caller error and skips them the same way).
  */
 static void memorise_one(const fwo_cfg* c, int32_t Tc, int32_t n_tgt,
                          const float* g_b, const void* tgt_b, size_t tgt_stride_tok,
@@ -394,6 +396,7 @@ static void memorise_one(const fwo_cfg* c, int32_t Tc, int32_t n_tgt,
             for (int j = 0; j < k; ++j) {
                 const size_t ent = ((size_t)t * H + h) * k + j;
                 const int32_t s = idx_b[ent];
+                if (s < 0 || (int64_t)s >= (int64_t)c->n * c->n) continue;
                 int32_t row = rowmap[s];
                 if (row < 0) {
                     row = nrows++;

@@ -287,7 +287,7 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
     L.erow = take(row_bytes(p, B, rows_max(p, B, Tt)));
     if (with_update) {
         const size_t M = T * p.H * p.k;
-        const size_t tiles = (M + kSortTile - 1) / kSortTile;
+        const size_t tiles = (M + kSortTileSmall - 1) / kSortTileSmall;  // the most any tile size gives
         // the most pieces any chunk of up to T tokens with targets can need
         // (smaller chunks may use smaller pieces)
         size_t pieces = 1;
@@ -408,7 +408,8 @@ int sort_reads(const Plan& p, const Layout& L, void* ws, int B, int n_tgt, const
     const int M = n_tgt * p.H * p.k;
     *sorted = 0;
     if (M == 0) return FWPKM_OK;
-    const int tiles = (M + kSortTile - 1) / kSortTile;
+    const int items = sort_items(B, M);
+    const int tiles = (M + 256 * items - 1) / (256 * items);
     uint32_t* kb[2] = {at<uint32_t>(ws, L.k0), at<uint32_t>(ws, L.k1)};
     uint32_t* vb[2] = {at<uint32_t>(ws, L.v0), at<uint32_t>(ws, L.v1)};
     int cur = 0;
@@ -421,6 +422,7 @@ int sort_reads(const Plan& p, const Layout& L, void* ws, int B, int n_tgt, const
         a.counts = at<uint32_t>(ws, L.counts);
         a.B = B; a.M = M; a.tiles = tiles; a.shift = 8 * pass; a.first = pass == 0;
         a.N = static_cast<uint32_t>(p.N);
+        a.items = items;
         HIP_TRY(launch_sort_pass(a, s));
         cur ^= 1;
     }

@@ -308,6 +308,7 @@ struct SortArgs {
     int shift;
     int first;
     uint32_t N;           // slot ids >= N (or < 0) become the sentinel key N
+    int items;            // entries per thread: kSortItems or kSortItemsSmall
 };
 
 struct ScatterArgs {
@@ -469,6 +470,15 @@ hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s);
 
 constexpr int kSortItems = 8;                  // entries per thread
 constexpr int kSortTile = 256 * kSortItems;    // entries per sort workgroup
+// Sorts whose 2048-entry tiles give fewer than kSortMinTiles workgroups
+// (a single long sequence, a small batch) use 512-entry tiles instead.
+constexpr int kSortItemsSmall = 2;
+constexpr int kSortTileSmall = 256 * kSortItemsSmall;
+constexpr int kSortMinTiles = 64;
+inline int sort_items(int B, int M) {
+    return static_cast<long long>(B) * ((M + kSortTile - 1) / kSortTile) < kSortMinTiles ? kSortItemsSmall
+                                                                                          : kSortItems;
+}
 constexpr int kPiece = 64;                     // sorted positions per scatter wavefront (at most)
 // Positions per scatter piece for a sequence of M sorted reads: 64, or 32 /
 // 16 when 64-position pieces would give a sequence fewer than kPieceWaves

@@ -29,14 +29,15 @@ __device__ __forceinline__ uint32_t load_key(const SortArgs& a, int b, int pos) 
     return a.kin[static_cast<size_t>(b) * a.M + pos];
 }
 
+template <int ITEMS>
 __global__ __launch_bounds__(256) void k_sort_count(SortArgs a) {
     __shared__ uint32_t hist[256];
     const int tile = blockIdx.x, b = blockIdx.y;
     hist[threadIdx.x] = 0u;
     __syncthreads();
-    const int base = tile * kSortTile;
+    const int base = tile * 256 * ITEMS;
 #pragma unroll
-    for (int it = 0; it < kSortItems; ++it) {
+    for (int it = 0; it < ITEMS; ++it) {
         const int pos = base + it * 256 + threadIdx.x;
         if (pos < a.M) atomicAdd(&hist[(load_key(a, b, pos) >> a.shift) & 255u], 1u);
     }
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(256) void k_sort_count(SortArgs a) {
     a.counts[(static_cast<size_t>(b) * a.tiles + tile) * 256 + threadIdx.x] = hist[threadIdx.x];
 }
 
+template <int ITEMS>
 __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
     __shared__ uint32_t cnt[4][256];
     __shared__ uint32_t toff[256];
@@ -82,12 +84,12 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
     }
     __syncthreads();
 
-    constexpr int kPerWave = kSortTile / 4;
-    const int wbase = tile * kSortTile + wave * kPerWave;
+    constexpr int kPerWave = 64 * ITEMS;
+    const int wbase = tile * 256 * ITEMS + wave * kPerWave;
     const uint64_t lt = lanemask_lt();
-    uint32_t key[kSortItems], val[kSortItems], loc[kSortItems];
+    uint32_t key[ITEMS], val[ITEMS], loc[ITEMS];
 #pragma unroll
-    for (int r = 0; r < kSortItems; ++r) {
+    for (int r = 0; r < ITEMS; ++r) {
         const int pos = wbase + r * 64 + lane;
         const bool valid = pos < a.M;
         key[r] = valid ? load_key(a, b, pos) : 0u;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kSortItems; ++r) {
+    for (int r = 0; r < ITEMS; ++r) {
         const int pos = wbase + r * 64 + lane;
         if (pos < a.M) {
             const uint32_t d = (key[r] >> a.shift) & 255u;
@@ -133,8 +135,15 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
 
 hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.tiles), static_cast<unsigned>(a.B));
-    hipLaunchKernelGGL(k_sort_count, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_sort_scatter, grid, dim3(256), 0, s, a);
+    if (a.items == kSortItemsSmall) {
+        hipLaunchKernelGGL(k_sort_count<kSortItemsSmall>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_sort_scatter<kSortItemsSmall>, grid, dim3(256), 0, s, a);
+    } else if (a.items == kSortItems) {
+        hipLaunchKernelGGL(k_sort_count<kSortItems>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_sort_scatter<kSortItems>, grid, dim3(256), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

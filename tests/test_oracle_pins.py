@@ -213,6 +213,44 @@ def test_value_write_equals_dense_matmul_over_read_counts(H, k, znorm, gate):
         assert nr[b].sum() == n_tgt * H * k
 
 
+def test_value_write_skips_out_of_range_ids():
+    """Slot ids outside [0, N) (a caller error the boundary skips) name no
+    row: the write equals the dense formula over the valid reads alone."""
+    cfg = FwpkmConfig(n=5, heads=2, d_q=4, d_v=3, k_half=3, k=3, chunk=10, use_addr=False)
+    B, Tc = 1, 10
+    q, v, g, K1, K2, V = _rand_problem(cfg, B, Tc, seed=31)
+    gen = np.random.default_rng(31)
+    idx = gen.integers(0, cfg.N, size=(B, Tc, 2, 3)).astype(np.int32)
+    idx[0, :, 0, 0] = -1
+    idx[0, ::3, 1, 2] = cfg.N
+    idx[0, 4, 1, :] = cfg.N + 7
+    w = gen.random((B, Tc, 2, 3))
+    vhat = gen.standard_normal((B, Tc, 3))
+    tgt, n_tgt = v[:, 1:].contiguous(), Tc - 1
+    _, _, Vn, nr = oracle.chunk_update(cfg, q, g, tgt, n_tgt, idx, w, vhat, K1, K2, V)
+    N = cfg.N
+    S = np.zeros((n_tgt, N))
+    cnt = np.zeros(N, np.int64)
+    for t in range(n_tgt):
+        for h in range(2):
+            for j in range(3):
+                s_ = int(idx[0, t, h, j])
+                if 0 <= s_ < N:
+                    S[t, s_] += w[0, t, h, j] / 2
+                    cnt[s_] += 1
+    R = g.numpy()[0, :n_tgt, None].astype(np.float64) * (vhat[0, :n_tgt] - _targets(cfg, tgt.numpy()[0]))
+    G = S.T @ R
+    Vb = V.numpy()[0].astype(np.float64)
+    want = Vb.copy()
+    rd = cnt > 0
+    want[rd] = Vb[rd] - G[rd] / cnt[rd, None]
+    np.testing.assert_array_equal(nr[0], cnt)
+    np.testing.assert_allclose(Vn[0], want.astype(np.float32), rtol=2e-6, atol=1e-7)
+    # every read out of range: nothing is written
+    _, _, Vn, nr = oracle.chunk_update(cfg, q, g, tgt, n_tgt, np.full_like(idx, -1), w, vhat, K1, K2, V)
+    assert np.array_equal(Vn, V.numpy()) and not nr.any()
+
+
 def test_value_write_equals_autograd_of_literal_loss():
     cfg = FwpkmConfig(n=4, heads=2, d_q=4, d_v=5, k_half=3, k=3, chunk=12, use_addr=False)
     B, Tc = 1, 12
