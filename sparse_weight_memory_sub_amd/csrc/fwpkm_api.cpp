@@ -381,7 +381,6 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     {
         TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
         HIP_TRY(launch_score(a, p.store, s));
-        if (rows && stats) HIP_TRY(launch_row_stats(a, 0, s));
     }
     SelectArgs sa{};
     sa.cand = a.cand; sa.cnt = a.cnt; sa.cap = a.cap;
@@ -391,6 +390,12 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
     sa.erow = a.erow;
     sa.usage = usage;
     sa.dot = p.dot;
+    if (rows && stats) {
+        // whole-row selection also leaves Z (and M); the usage partials
+        // follow in the addressing step
+        sa.Z = a.Z;
+        sa.M = a.M;
+    }
     {
         TimedLaunch tl(FWPKM_K_SELECT, s);
         HIP_TRY(launch_select(sa, p.store, s));
@@ -465,9 +470,10 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
     return write_rows(p, L, ws, 0, B, Tc, n_tgt, w, iw_bstride, V, n_read, sorted, s);
 }
 
-// Addressing step of one chunk.  With `have_stats` the chunk's usage
-// partial sums (and ||q||^2) are already in the workspace from the
-// retrieval's scoring; otherwise a stats scoring pass computes them first.
+// Addressing step of one chunk.  With `have_stats` the retrieval already left
+// ||q||^2 and Z (and M) in the workspace, and on the sweep path the usage
+// partial sums too (on the rows path they are taken here from the stored
+// rows); otherwise a stats scoring pass computes all of them first.
 // knorm holds ||K_i||^2 of the current codebooks; the key step rewrites it.
 int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
             void* K1, void* K2, bool have_stats, float* knorm, hipStream_t s) {
@@ -490,6 +496,15 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     }
     {
         TimedLaunch tl(FWPKM_K_PBAR, s);
+        if (have_stats && rows) {
+            // the selection left Z (and M): the per-tile usage partials, then pbar
+            ScoreArgs ca = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreRows);
+            ca.erow = at<uint32_t>(ws, L.erow);
+            ca.part = at<float>(ws, L.part);
+            ca.Z = at<float>(ws, L.Z);
+            ca.M = at<float>(ws, L.M);
+            HIP_TRY(launch_row_stats(ca, 2, s));
+        }
         HIP_TRY(launch_pbar(pa, s));
     }
     ScoreArgs ra = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreRowStat);

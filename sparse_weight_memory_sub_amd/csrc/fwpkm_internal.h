@@ -241,6 +241,8 @@ struct SelectArgs {
     const uint32_t* erow; // non-NULL: whole rows of e ([B][H][2][Tc][n]) instead of candidate lists
     int32_t* usage;       // nullable: usage[b*n*n + slot] += 1 per selected read
     int dot;              // dot-product scoring: keys are ord(-s), pair value -(s1 + s2)
+    float* Z;             // whole rows only, nullable: Z_t (and M_t for dot) of every
+    float* M;             //   row, computed as k_row_z computes them
 };
 
 int score_keep(int kh);   // smallest e kept per lane in the first scoring pass

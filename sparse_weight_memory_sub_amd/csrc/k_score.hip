@@ -689,6 +689,28 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
         m0 = lo;
         m1 = min(m1, hi);
     }
+    if (a.Z) {
+        // the row statistics from the loaded row, in k_row_z's order
+        float M = 0.f;
+        if (a.dot) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < kNplMax; ++j)
+                if (j < npl && j * 64 + lane < n) mx = fmaxf(mx, -unord_f32(u[j]));
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, xor_lane(mx, o));
+            M = mx;
+        }
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < kNplMax; ++j)
+            if (j < npl && j * 64 + lane < n) z += a.dot ? row_weight<true>(u[j], M) : row_weight<false>(u[j], 0.f);
+        z = wave_sum(z);
+        if (lane == 0) {
+            a.Z[row] = z;
+            if (a.dot) a.M[row] = M;
+        }
+    }
     uint32_t kept[2] = {m0, m1};
     bitonic_sort<2, 64>(kept);
     const uint32_t tau = static_cast<uint32_t>(__shfl(static_cast<int>(kept[0]), a.kh - 1, 64));  // kh <= 64
@@ -924,14 +946,14 @@ int score_tile(int B, int H, int Tc, bool dot) {
 hipError_t launch_row_stats(const ScoreArgs& a, int what, hipStream_t s) {
     const int64_t rows = static_cast<int64_t>(a.B) * a.H * 2 * a.Tc;
     const unsigned rgrid = static_cast<unsigned>((rows + 3) / 4);
-    if (what == 0) {  // Z (and M), then the usage partials
+    if (what == 0 || what == 2) {  // Z (and M) unless the selection left them, then the usage partials
         const int ntiles = (a.Tc + kScoreTokMin - 1) / kScoreTokMin;
         const unsigned cgrid = static_cast<unsigned>(a.B * a.H * 2 * ntiles * ((a.n + 63) / 64));
         if (a.dot) {
-            hipLaunchKernelGGL(k_row_z<true>, dim3(rgrid), dim3(256), 0, s, a);
+            if (what == 0) hipLaunchKernelGGL(k_row_z<true>, dim3(rgrid), dim3(256), 0, s, a);
             hipLaunchKernelGGL(k_row_colsum<true>, dim3(cgrid), dim3(256), 0, s, a);
         } else {
-            hipLaunchKernelGGL(k_row_z<false>, dim3(rgrid), dim3(256), 0, s, a);
+            if (what == 0) hipLaunchKernelGGL(k_row_z<false>, dim3(rgrid), dim3(256), 0, s, a);
             hipLaunchKernelGGL(k_row_colsum<false>, dim3(cgrid), dim3(256), 0, s, a);
         }
     } else {  // the row statistic m
