@@ -476,7 +476,7 @@ constexpr int kSortTile = 256 * kSortItems;    // entries per sort workgroup
 // (a single long sequence, a small batch) use 512-entry tiles instead.
 constexpr int kSortItemsSmall = 2;
 constexpr int kSortTileSmall = 256 * kSortItemsSmall;
-constexpr int kSortMinTiles = 64;
+constexpr int kSortMinTiles = 128;
 inline int sort_items(int B, int M) {
     return static_cast<long long>(B) * ((M + kSortTile - 1) / kSortTile) < kSortMinTiles ? kSortItemsSmall
                                                                                           : kSortItems;
