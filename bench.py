@@ -40,8 +40,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="million")
-    ap.add_argument("--passes", type=int, default=None)
+    ap.add_argument("--workload", default="million", choices=("million", "mid", "collision", "long", "tiny"),
+                    help="workload shape (default: the million-slot layer)")
+    ap.add_argument("--passes", type=int, default=None, help="passes over each sequence (default: the workload's)")
     ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences of the oracle sample (default 5)")
     ap.add_argument("--cpu-chunks", type=int, default=None, help="chunks per sequence of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
