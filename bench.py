@@ -321,7 +321,7 @@ def backward_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the FwPKM layer benchmark runs on one GPU; --gpus must be 1",
                           "requested_gpus": args.gpus}))
         sys.exit(2)
 

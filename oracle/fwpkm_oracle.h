@@ -115,7 +115,7 @@ int fwo_forward_seq(const fwo_cfg* c, int32_t B, int32_t T, int32_t passes,
                     double* o, double* vhat, int32_t chunk_limit);
 
 /* (eps+d1)(eps+d2) in double for arbitrary slots slots[B][T][H][m]
- * against frozen K1, K2 (used to judge near-tie alternatives); with dot
+ * against frozen K1, K2 (used to assess near-tie alternatives); with dot
  * scoring exp(-(s1 + s2)), which orders pairs the same way. */
 int fwo_pair_p(const fwo_cfg* c, int32_t B, int32_t T, int32_t m,
                const void* q, const void* K1, const void* K2,
