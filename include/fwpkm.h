@@ -73,8 +73,9 @@ typedef enum {
  *   k_half   k': sub-keys kept per half, 1 <= k' <= min(n, 64).
  *   k        final top-k, 1 <= k <= min(k'*k', 64), and the number of
  *            candidate pairs (a, b) with (a+1)(b+1) <= k must be <= 256
- *            (true for every k <= 48).  k <= k' makes the search exact over
- *            all N slots.
+ *            (true for every k <= 59; k = 64 with k' = 64 needs about 300
+ *            and is refused with FWPKM_EUNSUPPORTED).  heads * k <= 256.
+ *            k <= k' makes the search exact over all N slots.
  *   chunk    C: tokens per fast-weight write (fwpkm_forward_seq only).
  *   store    fwpkm_dtype of q, v, targets, K1, K2, V.
  *   idw_eps  eps of the inverse-distance score s = -log(eps + ||q-k||^2)
