@@ -93,7 +93,7 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SRC = {"gather": ("k_gather.hip", "rows.h", "fwpkm_internal.h"),
+KERNEL_SRC = {"gather": ("k_gather.hip", "gather.h", "rows.h", "fwpkm_internal.h"),
               "scatter": ("k_scatter.hip", "fwpkm_internal.h"),
               "score_select": ("k_score.hip", "mfma_frag.h", "fwpkm_internal.h"),
               "score_rowstat": ("k_score.hip", "mfma_frag.h", "fwpkm_internal.h"),

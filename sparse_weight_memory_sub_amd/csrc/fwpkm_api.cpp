@@ -358,6 +358,20 @@ ScoreArgs score_args(const Plan& p, int B, int Tc, const void* q, int64_t q_bstr
     return a;
 }
 
+// Selection arguments for the scoring `a` just launched.
+SelectArgs select_args(const Plan& p, const ScoreArgs& a, const void* q, int64_t q_bstride, const void* K1,
+                       const void* K2, int32_t* idx, float* w, int64_t iw_bstride, int32_t* usage) {
+    SelectArgs sa{};
+    sa.cand = a.cand; sa.cnt = a.cnt; sa.cap = a.cap;
+    sa.q = q; sa.q_bstride = q_bstride; sa.K1 = K1; sa.K2 = K2;
+    sa.B = a.B; sa.Tc = a.Tc; sa.n = p.n; sa.H = p.H; sa.dh = p.dh; sa.kh = p.kh; sa.k = p.k; sa.ncand = p.ncand;
+    sa.eps = p.eps; sa.idx = idx; sa.w = w; sa.iw_bstride = iw_bstride; sa.cand_ab = p.cand;
+    sa.erow = a.erow;
+    sa.usage = usage;
+    sa.dot = p.dot;
+    return sa;
+}
+
 // Retrieval's selection of Tc tokens: candidate scoring, then per (token,
 // head) top-k' of each half and the product top-k into idx / w.
 int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
@@ -382,14 +396,7 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
         TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
         HIP_TRY(launch_score(a, p.store, s));
     }
-    SelectArgs sa{};
-    sa.cand = a.cand; sa.cnt = a.cnt; sa.cap = a.cap;
-    sa.q = q; sa.q_bstride = q_bstride; sa.K1 = K1; sa.K2 = K2;
-    sa.B = B; sa.Tc = Tc; sa.n = p.n; sa.H = p.H; sa.dh = p.dh; sa.kh = p.kh; sa.k = p.k; sa.ncand = p.ncand;
-    sa.eps = p.eps; sa.idx = idx; sa.w = w; sa.iw_bstride = iw_bstride; sa.cand_ab = p.cand;
-    sa.erow = a.erow;
-    sa.usage = usage;
-    sa.dot = p.dot;
+    SelectArgs sa = select_args(p, a, q, q_bstride, K1, K2, idx, w, iw_bstride, usage);
     if (rows && stats) {
         // whole-row selection also leaves Z (and M); the usage partials
         // follow in the addressing step
@@ -597,6 +604,13 @@ int stream_fire(const Plan& p, const StreamLayout& S, void* st, int B, int Tc, i
 // Retrieval of tokens [j, j + seg) of this call (T tokens per sequence)
 // into the pending slots [pend, pend + seg), with the copies of q, g and the
 // targets that the chunk's write will need.
+// FWPKM_DECODE=unfused keeps decode's selection and read as two launches (the
+// tests compare the two forms).
+bool fused_decode_off() {
+    const char* e = std::getenv("FWPKM_DECODE");
+    return e && std::strcmp(e, "unfused") == 0;
+}
+
 int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T, int j, int seg, int pend,
                     const void* q, const void* v, const float* g, const void* K1, const void* K2, const void* V,
                     float* o, float* vhat, int32_t* usage, void* ws, hipStream_t s) {
@@ -610,9 +624,27 @@ int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T
     const int64_t iwb = C * p.H * p.k;
     int32_t* idx = at<int32_t>(st, S.idx) + static_cast<size_t>(pend) * p.H * p.k;
     float* w = at<float>(st, S.w) + static_cast<size_t>(pend) * p.H * p.k;
-    int rc = select_topk(p, L, ws, B, seg, qb + j * qrow, static_cast<int64_t>(T) * p.H * p.dq, K1, K2,
-                         at<float>(st, S.knorm), idx, w, iwb, false, usage, s);
-    if (rc) return rc;
+    const void* qj = qb + j * qrow;
+    const int64_t qbs = static_cast<int64_t>(T) * p.H * p.dq;
+    // few tokens scored by whole rows: selection and read fused per token
+    const bool fused = use_rows(p, B, seg) && select_gather_fits(p.H, p.k) &&
+                       static_cast<int64_t>(B) * seg < kGatherSplitBelow && !fused_decode_off();
+    SelectArgs sa{};
+    if (fused) {
+        ScoreArgs a = score_args(p, B, seg, qj, qbs, K1, K2, at<float>(st, S.knorm), kScoreRows);
+        a.erow = at<uint32_t>(ws, L.erow);
+        a.cand = at<uint64_t>(ws, L.cand);
+        a.cnt = at<int32_t>(ws, L.cnt);
+        a.qn = at<float>(ws, L.qn);
+        {
+            TimedLaunch tl(FWPKM_K_SWEEP_SELECT, s);
+            HIP_TRY(launch_score(a, p.store, s));
+        }
+        sa = select_args(p, a, qj, qbs, K1, K2, idx, w, iwb, usage);
+    } else {
+        int rc = select_topk(p, L, ws, B, seg, qj, qbs, K1, K2, at<float>(st, S.knorm), idx, w, iwb, false, usage, s);
+        if (rc) return rc;
+    }
     GatherArgs ga{};
     ga.V = V; ga.idx = idx; ga.w = w; ga.iw_bstride = iwb;
     ga.v = vb + j * vrow; ga.v_bstride = static_cast<int64_t>(T) * p.dv;
@@ -630,8 +662,13 @@ int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T
     ga.ptgt = stg; ga.ptgt_bstride = C * p.dv;
     ga.ptgt_shift = p.look ? pend - 1 : pend;
     ga.B = B; ga.Tc = seg; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
-    TimedLaunch tl(FWPKM_K_GATHER, s);
-    HIP_TRY(launch_gather(ga, p.store, s));
+    if (fused) {
+        TimedLaunch tl(FWPKM_K_SELECT, s);
+        HIP_TRY(launch_select_gather(sa, ga, p.store, s));
+    } else {
+        TimedLaunch tl(FWPKM_K_GATHER, s);
+        HIP_TRY(launch_gather(ga, p.store, s));
+    }
     return FWPKM_OK;
 }
 

@@ -453,6 +453,13 @@ hipError_t launch_backward(const BackwardArgs& a, int store, hipStream_t s);
 
 hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s);
+// Whole-row selection and the value read of the same few tokens fused in one
+// workgroup per token (decode), for 2*H and the read's parts within kSgWaves
+// wavefronts (select_gather_fits); the same results as launch_select
+// followed by launch_gather.
+constexpr int kSgWaves = 16;
+bool select_gather_fits(int H, int k);
+hipError_t launch_select_gather(const SelectArgs& a, const GatherArgs& ga, int store, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int store, hipStream_t s);
 hipError_t launch_resid(const ResidArgs& a, int store, hipStream_t s);
 hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s);

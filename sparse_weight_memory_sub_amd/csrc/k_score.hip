@@ -40,6 +40,7 @@
 // i*n + j) and the weights (1/P)/sum(1/P) = softmax of s1 + s2.  A token
 // whose candidate list overflowed recomputes its distances exactly and
 // selects by radix select.
+#include "gather.h"
 #include "mfma_frag.h"
 
 namespace fwpkm {
@@ -848,6 +849,45 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs a) {
     else product_topk<4>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
 }
 
+// Decode: one token's selection and read in one workgroup.  Wavefront 2h+half
+// takes the top-k' of row (h, half); wavefront h < H then the product top-k
+// of head h, written to idx / w; then one wavefront per part of the H*k
+// entries reads the value rows (gather_token_split).  The same device code in
+// the same order as k_select_rows followed by k_gather_split, so the same bits,
+// with one launch fewer on a path where a launch is a large part of a token.
+// The selection's scratch and the read's parts are never live together.
+constexpr int kSgScratch = (kSgWaves * 64 * 8 + kSgWaves * 256 * 4) > (kSgWaves * 512 * 4)
+                               ? (kSgWaves * 64 * 8 + kSgWaves * 256 * 4) : (kSgWaves * 512 * 4);
+
+template <int STORE, int EPL>
+__global__ __launch_bounds__(64 * kSgWaves) void k_select_gather(SelectArgs a, GatherArgs ga) {
+    __shared__ __align__(16) unsigned char scratch[kSgScratch];
+    __shared__ float se[kSgWaves / 2][2][kMaxKHalf];
+    __shared__ int si[kSgWaves / 2][2][kMaxKHalf];
+    uint64_t (*buf)[64] = reinterpret_cast<uint64_t (*)[64]>(scratch);
+    uint32_t (*hist)[256] = reinterpret_cast<uint32_t (*)[256]>(scratch + kSgWaves * 64 * 8);
+    float (*part)[512] = reinterpret_cast<float (*)[512]>(scratch);
+    const int wave = threadIdx.x >> 6;
+    const int64_t tok = blockIdx.x;  // b*Tc + t
+    const int t = static_cast<int>(tok % a.Tc), b = static_cast<int>(tok / a.Tc);
+    if (wave < 2 * a.H) {
+        const int h = wave >> 1, half = wave & 1;
+        const size_t row = ((static_cast<size_t>(b * a.H + h) * 2) + half) * a.Tc + t;
+        half_topk_row(a, row, hist[wave], buf[wave], se[h][half], si[h][half]);
+    }
+    __syncthreads();
+    if (wave < a.H) {
+        const int h = wave;
+        const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
+        int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
+        if (a.ncand <= 64) product_topk<1>(a, se[h][0], si[h][0], se[h][1], si[h][1], a.idx + o, a.w + o, u);
+        else if (a.ncand <= 128) product_topk<2>(a, se[h][0], si[h][0], se[h][1], si[h][1], a.idx + o, a.w + o, u);
+        else product_topk<4>(a, se[h][0], si[h][0], se[h][1], si[h][1], a.idx + o, a.w + o, u);
+    }
+    __syncthreads();  // the slot lists are visible to the workgroup; the scratch is free
+    gather_token_split<STORE, EPL>(ga, tok, part);
+}
+
 template <int STORE, int DHS, int MK, int MODE, int NW, bool DOT>
 hipError_t score_w(const ScoreArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
@@ -979,6 +1019,30 @@ hipError_t launch_score(const ScoreArgs& a, int store, hipStream_t s) {
     ScoreArgs b = a;
     b.tile = score_tile(a.B, a.H, a.Tc, a.dot != 0);
     return store == kBF16 ? score_s<kBF16>(b, s) : score_s<kF32>(b, s);
+}
+
+bool select_gather_fits(int H, int k) {
+    return 2 * H <= kSgWaves && (H * k + kGatherPart - 1) / kGatherPart <= kSgWaves;
+}
+
+template <int STORE>
+hipError_t select_gather_s(const SelectArgs& a, const GatherArgs& ga, hipStream_t s) {
+    const int nparts = (a.H * a.k + kGatherPart - 1) / kGatherPart;
+    const int nw = max(2 * a.H, nparts);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Tc)), block(64 * nw);
+    switch (ga.dv / 64) {
+        case 1: hipLaunchKernelGGL((k_select_gather<STORE, 1>), grid, block, 0, s, a, ga); break;
+        case 2: hipLaunchKernelGGL((k_select_gather<STORE, 2>), grid, block, 0, s, a, ga); break;
+        case 4: hipLaunchKernelGGL((k_select_gather<STORE, 4>), grid, block, 0, s, a, ga); break;
+        case 8: hipLaunchKernelGGL((k_select_gather<STORE, 8>), grid, block, 0, s, a, ga); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_select_gather(const SelectArgs& a, const GatherArgs& ga, int store, hipStream_t s) {
+    if (!a.erow || !select_gather_fits(a.H, a.k) || a.B != ga.B || a.Tc != ga.Tc) return hipErrorInvalidValue;
+    return store == kBF16 ? select_gather_s<kBF16>(a, ga, s) : select_gather_s<kF32>(a, ga, s);
 }
 
 hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s) {

@@ -216,3 +216,42 @@ def test_stream_edge_splits_equal_forward_seq(chunk, cuts):
     assert torch.equal(o, ref["o"]) and torch.equal(vh, ref["vhat"])
     for a, b in ((K1a, K1b), (K2a, K2b), (Va, Vb)):
         assert torch.equal(a, b)
+
+
+FUSED_CASES = [
+    ("f32_idw_h2", C(64, 2, 64, 64, 8, 8, chunk=24)),
+    ("bf16_dot_h3", C(128, 3, 128, 128, 16, 16, chunk=24, store="bf16", score="dot")),
+    ("f32_h8_k32", C(64, 8, 64, 64, 32, 32, chunk=24)),    # 16 wavefronts: the most the fused kernel takes
+    ("f32_h9_k8", C(64, 9, 64, 64, 8, 8, chunk=24)),       # 18 selection wavefronts: two launches
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_decode_fused_selection_and_read_equal_two_launches(case):
+    """Decode (one token per call) with its selection and value read fused in
+    one workgroup per token against the two-launch form (FWPKM_DECODE=
+    unfused): outputs, slot counts and state bit for bit."""
+    name, cfg = case
+    B, T = 3, 60
+    q, v, g, K1, K2, V = problem(cfg, B, T, seed=44)
+    res = []
+    for form in ("fused", "unfused"):
+        if form == "unfused":
+            os.environ["FWPKM_DECODE"] = "unfused"
+        try:
+            K1d, K2d, Vd = dev(K1, K2, V)
+            st, pos = fwpkm.stream_state(cfg, B, DEV)
+            usage = torch.zeros((B, cfg.N), dtype=torch.int32, device=DEV)
+            outs = []
+            for t in range(T):
+                qd, vd, gd = dev(q[:, t:t + 1], v[:, t:t + 1], g[:, t:t + 1])
+                r = fwpkm.fwpkm_stream_step(cfg, qd, vd, gd, K1d, K2d, Vd, st, pos, want_vhat=True, usage=usage)
+                outs.append(torch.cat([r["o"], r["vhat"]], -1))
+            fwpkm.fwpkm_stream_flush(cfg, K1d, K2d, Vd, st, pos)
+            torch.cuda.synchronize()
+            res.append((torch.cat(outs, 1), usage, K1d, K2d, Vd))
+        finally:
+            os.environ.pop("FWPKM_DECODE", None)
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    assert int(res[0][1].sum()) == B * T * cfg.heads * cfg.k
