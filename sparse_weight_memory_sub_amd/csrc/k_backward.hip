@@ -107,19 +107,25 @@ __global__ __launch_bounds__(256) void k_backward(BackwardArgs a) {
         const int cnt = min(64, HK - r * 64);
         if (cnt <= 0) break;
         for (int j0 = 0; j0 < cnt; j0 += 8) {
-            float dot[8];
+            // the eight rows' loads all in flight before their use; an id
+            // outside [0, N) reads row 0 in its place and contributes nothing
+            float dot[8], x[8][EPL], ww[8];
+            bool ok[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = (j0 + u < cnt) ? __builtin_amdgcn_readlane(sl[r], j0 + u) : -1;
+                ok[u] = s >= 0 && s < a.N;
+                ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt[r]), min(j0 + u, 63)));
+                ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(ok[u] ? s : 0) * dv + col, x[u]);
+            }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 dot[u] = 0.f;
-                const int s = (j0 + u < cnt) ? __builtin_amdgcn_readlane(sl[r], j0 + u) : -1;
-                if (s >= 0 && s < a.N) {  // ids outside [0, N) are skipped, never dereferenced
-                    const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt[r]), j0 + u));
-                    float x[EPL];
-                    ldrow<STORE, EPL, true>(a.V, vb + static_cast<size_t>(s) * dv + col, x);
+                if (ok[u]) {
 #pragma unroll
                     for (int i = 0; i < EPL; ++i) {
-                        vh[i] = fmaf(ww, x[i], vh[i]);
-                        dot[u] = fmaf(G[i], x[i], dot[u]);
+                        vh[i] = fmaf(ww[u], x[u][i], vh[i]);
+                        dot[u] = fmaf(G[i], x[u][i], dot[u]);
                     }
                 }
             }
@@ -180,33 +186,44 @@ __global__ __launch_bounds__(256) void k_backward(BackwardArgs a) {
             ld_seg<STORE, EPQ>(a.q, qoff, qv);
 #pragma unroll
             for (int i = 0; i < EPQ; ++i) acc[i] = 0.f;
-            for (int j0 = 0; j0 < k; j0 += 4) {
-                const int j = j0 + grp;
-                const int e = h * k + j;
-                const int32_t slot = (j < k) ? lsl[wave][e] : -1;
-                const bool ok = slot >= 0 && slot < a.N;
-                const int sub = ok ? (hf ? slot % n : slot / n) : 0;
-                float kx[EPQ], diff[EPQ];
-                ld_seg<STORE, EPQ>(Kh, kb + static_cast<size_t>(sub) * DH, kx);
-                if constexpr (DOT) {
-                    // dS/dq_half = K_half[sub]
-                    const float coef = ok ? lds_ds[wave][e] : 0.f;
+            // a group's slots j = grp, grp + 4, ... in order, KQ sub-key rows
+            // requested before the first is used
+            constexpr int KQ = 4;
+            for (int j0 = 0; j0 < k; j0 += 4 * KQ) {
+                float kx[KQ][EPQ];
+                int e[KQ];
+                bool ok[KQ];
 #pragma unroll
-                    for (int i = 0; i < EPQ; ++i) acc[i] = fmaf(coef, kx[i], acc[i]);
-                } else {
-                    float part = 0.f;
+                for (int c = 0; c < KQ; ++c) {
+                    const int j = j0 + 4 * c + grp;
+                    e[c] = h * k + j;
+                    const int32_t slot = (j < k) ? lsl[wave][e[c]] : -1;
+                    ok[c] = slot >= 0 && slot < a.N;
+                    const int sub = ok[c] ? (hf ? slot % n : slot / n) : 0;
+                    ld_seg<STORE, EPQ>(Kh, kb + static_cast<size_t>(sub) * DH, kx[c]);
+                }
 #pragma unroll
-                    for (int i = 0; i < EPQ; ++i) {
-                        diff[i] = qv[i] - kx[i];
-                        part = fmaf(diff[i], diff[i], part);
+                for (int c = 0; c < KQ; ++c) {
+                    if constexpr (DOT) {
+                        // dS/dq_half = K_half[sub]
+                        const float coef = ok[c] ? lds_ds[wave][e[c]] : 0.f;
+#pragma unroll
+                        for (int i = 0; i < EPQ; ++i) acc[i] = fmaf(coef, kx[c][i], acc[i]);
+                    } else {
+                        float diff[EPQ], part = 0.f;
+#pragma unroll
+                        for (int i = 0; i < EPQ; ++i) {
+                            diff[i] = qv[i] - kx[c][i];
+                            part = fmaf(diff[i], diff[i], part);
+                        }
+                        part += xor_lane(part, 1);
+                        part += xor_lane(part, 2);
+                        part += xor_lane(part, 4);
+                        part += xor_lane(part, 8);
+                        const float coef = ok[c] ? lds_ds[wave][e[c]] * (-2.f) / (a.eps + part) : 0.f;
+#pragma unroll
+                        for (int i = 0; i < EPQ; ++i) acc[i] = fmaf(coef, diff[i], acc[i]);
                     }
-                    part += xor_lane(part, 1);
-                    part += xor_lane(part, 2);
-                    part += xor_lane(part, 4);
-                    part += xor_lane(part, 8);
-                    const float coef = ok ? lds_ds[wave][e] * (-2.f) / (a.eps + part) : 0.f;
-#pragma unroll
-                    for (int i = 0; i < EPQ; ++i) acc[i] = fmaf(coef, diff[i], acc[i]);
                 }
             }
 #pragma unroll
