@@ -474,16 +474,23 @@ __global__ __launch_bounds__(256) void k_row_z(ScoreArgs a) {
     if (row >= static_cast<int64_t>(a.B) * a.H * 2 * a.Tc) return;
     const int lane = threadIdx.x & 63, n = a.n;
     const uint32_t* e = a.erow + static_cast<size_t>(row) * n;
+    uint32_t ev[kNplMax];
+#pragma unroll
+    for (int j = 0; j < kNplMax; ++j) ev[j] = (j * 64 + lane < n) ? e[j * 64 + lane] : 0u;
     float M = 0.f;
     if constexpr (DOT) {
         float mx = -INFINITY;
-        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, -unord_f32(e[i]));
+#pragma unroll
+        for (int j = 0; j < kNplMax; ++j)
+            if (j * 64 + lane < n) mx = fmaxf(mx, -unord_f32(ev[j]));
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, xor_lane(mx, o));
         M = mx;
     }
     float z = 0.f;
-    for (int i = lane; i < n; i += 64) z += row_weight<DOT>(e[i], M);
+#pragma unroll
+    for (int j = 0; j < kNplMax; ++j)
+        if (j * 64 + lane < n) z += row_weight<DOT>(ev[j], M);
     z = wave_sum(z);
     if (lane == 0) {
         a.Z[row] = z;
@@ -509,12 +516,21 @@ __global__ __launch_bounds__(256) void k_row_colsum(ScoreArgs a) {
     const int t0 = tile * kScoreTokMin + wave * 16, t1 = min(a.Tc, t0 + 16);
     const size_t rowbase = static_cast<size_t>(bhh) * a.Tc;
     float s = 0.f;
-    if (i < n)
-        for (int t = t0; t < t1; ++t) {
-            const size_t row = rowbase + t;
-            const float M = DOT ? a.M[row] : 0.f;
-            s = fmaf(row_weight<DOT>(a.erow[row * n + i], M), fast_rcp(a.Z[row]), s);
+    if (i < n) {
+        // the wavefront's 16 tokens: every load in flight first, then the sum in token order
+        uint32_t ev[16];
+        float zv[16], mv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const size_t row = rowbase + min(t0 + u, a.Tc - 1);  // in the chunk; only t < t1 is summed
+            ev[u] = a.erow[row * n + i];
+            zv[u] = a.Z[row];
+            mv[u] = DOT ? a.M[row] : 0.f;
         }
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (t0 + u < t1) s = fmaf(row_weight<DOT>(ev[u], mv[u]), fast_rcp(zv[u]), s);
+    }
     wsum[wave][lane] = s;
     __syncthreads();
     if (wave == 0 && i < n)
@@ -532,8 +548,19 @@ __global__ __launch_bounds__(256) void k_row_m(ScoreArgs a) {
     const uint32_t* e = a.erow + static_cast<size_t>(row) * n;
     const float* lp = a.lp + static_cast<size_t>(bhh) * n;
     const float M = DOT ? a.M[row] : 0.f;
+    // every load in flight first, then the sum over sub-keys lane, lane+64, ... in order
+    uint32_t ev[kNplMax];
+    float lv[kNplMax];
+#pragma unroll
+    for (int j = 0; j < kNplMax; ++j) {
+        const bool in = j * 64 + lane < n;
+        ev[j] = in ? e[j * 64 + lane] : 0u;
+        lv[j] = in ? lp[j * 64 + lane] : 0.f;
+    }
     float x = 0.f;
-    for (int i = lane; i < n; i += 64) x = fmaf(row_weight<DOT>(e[i], M), lp[i], x);
+#pragma unroll
+    for (int j = 0; j < kNplMax; ++j)
+        if (j * 64 + lane < n) x = fmaf(row_weight<DOT>(ev[j], M), lv[j], x);
     x = wave_sum(x);
     if (lane == 0) a.m[row] = x / a.Z[row];
 }
