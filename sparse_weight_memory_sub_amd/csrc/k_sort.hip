@@ -88,12 +88,19 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
     const int wbase = tile * 256 * ITEMS + wave * kPerWave;
     const uint64_t lt = lanemask_lt();
     uint32_t key[ITEMS], val[ITEMS], loc[ITEMS];
+    // every round's key and value requested before the first ranking (the
+    // ranking's LDS fences would otherwise hold each load behind the last)
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
         const int pos = wbase + r * 64 + lane;
         const bool valid = pos < a.M;
         key[r] = valid ? load_key(a, b, pos) : 0u;
         val[r] = valid ? (a.first ? static_cast<uint32_t>(pos) : a.vin[static_cast<size_t>(b) * a.M + pos]) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int pos = wbase + r * 64 + lane;
+        const bool valid = pos < a.M;
         const uint32_t d = (key[r] >> a.shift) & 255u;
         uint64_t peers = ballot(valid);
 #pragma unroll
