@@ -369,15 +369,17 @@ struct KgradArgs {
 
 // Token split of the key step for one sequence.  Only a sequence with fewer
 // than kKgradSplitBelow 64-key workgroups (H * 2 * ceil(n/64)) is split: a
-// power of two <= 8 that brings them up to kKgradWgs, with at least
+// power of two <= kKgradMaxSplit that brings them up to kKgradWgs, with at least
 // kKgradMinBlocks 32-token blocks per split.  Wider sequences already give
 // the chip enough workgroups at modest batch sizes, and the partials' round
 // trip through memory would cost more than the split gains.  The rule reads
 // per-sequence sizes only, so a sequence's keys sum in the same order
 // whatever the batch around it.  `override` > 0 replaces the power of two
-// (still capped by the block count).  Returns the split and sets *per
+// (still capped by kKgradMaxSplit, which k_kgrad_finish holds in registers,
+// and by the block count).  Returns the split and sets *per
 // (blocks per split) so that no split is empty.
 constexpr int kKgradSplitBelow = 64;
+constexpr int kKgradMaxSplit = 8;
 constexpr int kKgradWgs = 256;
 constexpr int kKgradMinBlocks = 2;
 inline int kgrad_split(int H, int n, int Tc, int override, int* per) {
@@ -385,9 +387,9 @@ inline int kgrad_split(int H, int n, int Tc, int override, int* per) {
     const int P = H * 2 * ((n + 63) / 64);
     int s = 1;
     if (override > 0) {
-        s = std::min(override, nblk);
+        s = std::min(std::min(override, kKgradMaxSplit), nblk);
     } else if (P < kKgradSplitBelow) {
-        while (s < 8 && P * 2 * s <= kKgradWgs && 2 * s * kKgradMinBlocks <= nblk) s *= 2;
+        while (s < kKgradMaxSplit && P * 2 * s <= kKgradWgs && 2 * s * kKgradMinBlocks <= nblk) s *= 2;
     }
     s = std::max(s, 1);
     const int pb = (nblk + s - 1) / s;

@@ -394,14 +394,26 @@ __device__ __forceinline__ void update_row(const KgradArgs& a, size_t kg, int j,
     const float* pg = a.part + (static_cast<size_t>(bhh) * a.split * n + k) * DH + 8 * j;
     const float* pc = part_colsum(a, DH) + static_cast<size_t>(bhh) * a.split * n + k;
     const size_t sstride = static_cast<size_t>(n) * DH;
-    float4 s0 = *reinterpret_cast<const float4*>(pg), s1 = *reinterpret_cast<const float4*>(pg + 4);
-    float cs = pc[0];
-    for (int sp = 1; sp < a.split; ++sp) {
-        const float4 x0 = *reinterpret_cast<const float4*>(pg + sp * sstride);
-        const float4 x1 = *reinterpret_cast<const float4*>(pg + sp * sstride + 4);
-        s0.x += x0.x; s0.y += x0.y; s0.z += x0.z; s0.w += x0.w;
-        s1.x += x1.x; s1.y += x1.y; s1.z += x1.z; s1.w += x1.w;
-        cs += pc[static_cast<size_t>(sp) * n];
+    // every split's partials requested first (at most kKgradMaxSplit), then
+    // added in split order
+    float4 x0[kKgradMaxSplit], x1[kKgradMaxSplit];
+    float xc[kKgradMaxSplit];
+#pragma unroll
+    for (int sp = 0; sp < kKgradMaxSplit; ++sp) {
+        const int q = sp < a.split ? sp : 0;
+        x0[sp] = *reinterpret_cast<const float4*>(pg + q * sstride);
+        x1[sp] = *reinterpret_cast<const float4*>(pg + q * sstride + 4);
+        xc[sp] = pc[static_cast<size_t>(q) * n];
+    }
+    float4 s0 = x0[0], s1 = x1[0];
+    float cs = xc[0];
+#pragma unroll
+    for (int sp = 1; sp < kKgradMaxSplit; ++sp) {
+        if (sp < a.split) {
+            s0.x += x0[sp].x; s0.y += x0[sp].y; s0.z += x0[sp].z; s0.w += x0[sp].w;
+            s1.x += x1[sp].x; s1.y += x1[sp].y; s1.z += x1[sp].z; s1.w += x1[sp].w;
+            cs += xc[sp];
+        }
     }
     const float gs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     unsigned char* Kb = static_cast<unsigned char*>(half ? a.K2 : a.K1) +
