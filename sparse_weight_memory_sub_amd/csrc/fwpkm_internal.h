@@ -367,12 +367,14 @@ struct KgradArgs {
     float* part;
 };
 
-// Token split of the key step for one sequence.  Only a sequence with fewer
-// than kKgradSplitBelow 64-key workgroups (H * 2 * ceil(n/64)) is split: a
-// power of two <= kKgradMaxSplit that brings them up to kKgradWgs, with at least
-// kKgradMinBlocks 32-token blocks per split.  Wider sequences already give
+// Token split of the key step for one sequence.  A sequence with fewer than
+// kKgradSplitBelow 64-key workgroups (H * 2 * ceil(n/64)) is split by a power
+// of two <= kKgradMaxSplit that brings them up to kKgradWgs, with at least
+// kKgradMinBlocks 32-token blocks per split.  A wider sequence already gives
 // the chip enough workgroups at modest batch sizes, and the partials' round
-// trip through memory would cost more than the split gains.  The rule reads
+// trip through memory costs more than the split gains -- unless its chunk is
+// long: then each split keeps at least kKgradLongBlocks blocks (a 1024-token
+// chunk splits in two; 512 and fewer tokens do not).  The rule reads
 // per-sequence sizes only, so a sequence's keys sum in the same order
 // whatever the batch around it.  `override` > 0 replaces the power of two
 // (still capped by kKgradMaxSplit, which k_kgrad_finish holds in registers,
@@ -382,6 +384,7 @@ constexpr int kKgradSplitBelow = 64;
 constexpr int kKgradMaxSplit = 8;
 constexpr int kKgradWgs = 256;
 constexpr int kKgradMinBlocks = 2;
+constexpr int kKgradLongBlocks = 16;
 inline int kgrad_split(int H, int n, int Tc, int override, int* per) {
     const int nblk = (Tc + 31) / 32;
     const int P = H * 2 * ((n + 63) / 64);
@@ -390,6 +393,8 @@ inline int kgrad_split(int H, int n, int Tc, int override, int* per) {
         s = std::min(std::min(override, kKgradMaxSplit), nblk);
     } else if (P < kKgradSplitBelow) {
         while (s < kKgradMaxSplit && P * 2 * s <= kKgradWgs && 2 * s * kKgradMinBlocks <= nblk) s *= 2;
+    } else {
+        while (s < kKgradMaxSplit && 2 * s * kKgradLongBlocks <= nblk) s *= 2;
     }
     s = std::max(s, 1);
     const int pb = (nblk + s - 1) / s;
