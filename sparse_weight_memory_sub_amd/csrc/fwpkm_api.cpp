@@ -672,7 +672,7 @@ int stream_retrieve(const Plan& p, const StreamLayout& S, void* st, int B, int T
     return FWPKM_OK;
 }
 
-int stream_args(const fwpkm_cfg* cfg, int32_t B, void* state, fwpkm_stream_pos* pos, Plan* p) {
+int stream_args(const fwpkm_cfg* cfg, int32_t B, fwpkm_stream_pos* pos, Plan* p) {
     int rc = make_plan(cfg, p);
     if (rc) return rc;
     if (B < 0) return fail(FWPKM_EINVAL, "B must be >= 0");
@@ -982,7 +982,7 @@ int fwpkm_stream_step(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q,
                       void* K1, void* K2, void* V, float* o, float* vhat, int32_t* usage, void* state,
                       fwpkm_stream_pos* pos, void* ws, size_t ws_bytes, void* stream) {
     Plan p;
-    int rc = stream_args(cfg, B, state, pos, &p);
+    int rc = stream_args(cfg, B, pos, &p);
     if (rc) return rc;
     if (T < 0) return fail(FWPKM_EINVAL, "T must be >= 0");
     if (B == 0 || T == 0) return ok();
@@ -1033,7 +1033,7 @@ int fwpkm_stream_step(const fwpkm_cfg* cfg, int32_t B, int32_t T, const void* q,
 int fwpkm_stream_flush(const fwpkm_cfg* cfg, int32_t B, const void* v_next, void* K1, void* K2, void* V,
                        void* state, fwpkm_stream_pos* pos, void* ws, size_t ws_bytes, void* stream) {
     Plan p;
-    int rc = stream_args(cfg, B, state, pos, &p);
+    int rc = stream_args(cfg, B, pos, &p);
     if (rc) return rc;
     if (B == 0 || pos->pending == 0) {
         pos->pending = 0;

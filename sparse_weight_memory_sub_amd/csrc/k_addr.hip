@@ -112,11 +112,6 @@ __global__ __launch_bounds__(256) void k_qt(QtArgs a) {
     }
 }
 
-// token of element j of lane group g in the 32-token block: the first four
-// from the 16-token sub-tile 0, the last four from sub-tile 1, matching the
-// row layout of the MFMA distance tiles.
-__device__ __forceinline__ int tok_of(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4); }
-
 // Split partials: [B*H*2][split][n][dh] sums over the split's tokens of
 // a_ti q_t, then [B*H*2][split][n] sums of a_ti.
 __device__ __forceinline__ float* part_colsum(const KgradArgs& a, int dh) {
