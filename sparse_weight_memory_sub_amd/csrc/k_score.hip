@@ -425,6 +425,12 @@ __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     load_row_frags<STORE, DHS>(Bf, static_cast<const unsigned char*>(half ? a.K2 : a.K1) +
                                        (static_cast<size_t>(bh) * n + key) * (32 * DHS) * ES, g);
     const float knv = DOT ? 0.f : a.knorm[static_cast<size_t>(bhh) * n + key];
+    if constexpr (!DOT) {
+        // -2 K rather than -2 q: the same exact products as the sweep's,
+        // without a scaled copy of the query fragments beside the ones ||q||^2 reads
+#pragma unroll
+        for (int s = 0; s < DHS; ++s) frag_scale_m2(Bf[s]);
+    }
 
     Frag<STORE> A[DHS];
     const int tok = t0 + r;
@@ -437,7 +443,6 @@ __global__ __launch_bounds__(256) void k_rows(ScoreArgs a) {
     for (int s = 0; s < DHS; ++s) {
         if (!tv) frag_zero<STORE>(A[s]);
         qsq += frag_sumsq<STORE>(A[s]);
-        if constexpr (!DOT) frag_scale_m2(A[s]);
     }
     qsq += xor_lane(qsq, 16);
     qsq += xor_lane(qsq, 32);
