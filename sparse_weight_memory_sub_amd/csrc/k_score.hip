@@ -812,10 +812,65 @@ __device__ void product_topk(const SelectArgs& a, const float* e1, const int* i1
     }
 }
 
+// Items (token, head) of a launch from which the rare-path items get a
+// launch of their own (measured: 32768 items, the million batch, gain 1.2%;
+// 16384, collision, and 8192, mid, lose about as much to the extra launch).
+constexpr int64_t kSelectSplitItems = 32768;
+
+// Both candidate lists of an item fit one 64-wide register (the usual case).
+__device__ __forceinline__ bool lists_fit(const SelectArgs& a, int c0, int c1) {
+    return c0 <= 64 && c1 <= 64 && a.cap >= 64;
+}
+
+// The items whose candidate lists do not fit one register (a list over 64
+// entries, or over its capacity): exact top-k' of each half by recompute and
+// radix select, then the product top-k, as k_select would.  A separate
+// kernel so that k_select, which nearly every item takes, does not carry this
+// path's registers.  Each wavefront checks 64 consecutive items and takes
+// the ones that did not fit, in order; it usually finds none.
 template <int STORE>
-__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
+__global__ __launch_bounds__(256) void k_select_ovf(SelectArgs a) {
     __shared__ uint64_t buf[4][64];
     __shared__ uint32_t hist[4][256];
+    __shared__ float se[4][2][kMaxKHalf];
+    __shared__ int si[4][2][kMaxKHalf];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t items = static_cast<int64_t>(a.B) * a.Tc * a.H;
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 64;
+    bool ovf = false;
+    if (i0 + lane < items) {
+        const int64_t item = i0 + lane;
+        const int h = static_cast<int>(item % a.H);
+        const int64_t bt = item / a.H;
+        const int t = static_cast<int>(bt % a.Tc), b = static_cast<int>(bt / a.Tc);
+        const size_t row0 = (static_cast<size_t>(b * a.H + h) * 2) * a.Tc + t;
+        ovf = !lists_fit(a, a.cnt[row0], a.cnt[row0 + a.Tc]);
+    }
+    uint64_t todo = ballot(ovf);
+    while (todo) {
+        const int l = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+        todo &= todo - 1;
+        const int64_t item = i0 + l;
+        const int h = static_cast<int>(item % a.H);
+        const int64_t bt = item / a.H;
+        const int t = static_cast<int>(bt % a.Tc), b = static_cast<int>(bt / a.Tc);
+        for (int half = 0; half < 2; ++half)
+            half_topk<STORE>(a, b, t, h, half, hist[wave], buf[wave], se[wave][half], si[wave][half]);
+        const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
+        int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
+        if (a.ncand <= 64) product_topk<1>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
+        else if (a.ncand <= 128) product_topk<2>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
+        else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
+        wave_sync();
+    }
+}
+
+// INLINE: the items whose lists do not fit are taken here too; otherwise
+// they are left to k_select_ovf (chosen per launch by the item count).
+template <int STORE, bool INLINE>
+__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
+    __shared__ uint64_t buf[INLINE ? 4 : 1][64];
+    __shared__ uint32_t hist[INLINE ? 4 : 1][256];
     __shared__ float se[4][2][kMaxKHalf];
     __shared__ int si[4][2][kMaxKHalf];
     const int wave = threadIdx.x >> 6;
@@ -826,7 +881,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     const int t = static_cast<int>(bt % a.Tc), b = static_cast<int>(bt / a.Tc);
     const size_t row0 = (static_cast<size_t>(b * a.H + h) * 2) * a.Tc + t;  // half 0; half 1 is Tc further
     const int c0 = a.cnt[row0], c1 = a.cnt[row0 + a.Tc];
-    if (c0 <= 64 && c1 <= 64 && a.cap >= 64) {
+    if (lists_fit(a, c0, c1)) {
         // the usual case: both lists fit one register; sort them together
         const int lane = threadIdx.x & 63;
         uint64_t key[2];
@@ -843,8 +898,10 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
         }
         wave_sync();
     } else {
+        if constexpr (!INLINE) return;  // k_select_ovf takes this item
         for (int half = 0; half < 2; ++half)
-            half_topk<STORE>(a, b, t, h, half, hist[wave], buf[wave], se[wave][half], si[wave][half]);
+            half_topk<STORE>(a, b, t, h, half, hist[INLINE ? wave : 0], buf[INLINE ? wave : 0], se[wave][half],
+                             si[wave][half]);
     }
     const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
     int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
@@ -1084,8 +1141,27 @@ hipError_t launch_select(const SelectArgs& a, int store, hipStream_t s) {
         return hipGetLastError();
     }
     const unsigned grid = static_cast<unsigned>((items + 3) / 4);
-    if (store == kBF16) hipLaunchKernelGGL(k_select<kBF16>, dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_select<kF32>, dim3(grid), dim3(256), 0, s, a);
+    const unsigned ogrid = static_cast<unsigned>((items + 255) / 256);  // 64 items per wavefront
+    // Many items: the usual path alone (27 registers instead of over 100)
+    // and the rare one in a launch of its own, which leaves the value path
+    // more of the chip (million: 8.08 -> 7.98 ms per step).  Fewer items: the
+    // extra launch costs about what it gives back (mid: 2.29 -> 2.31 ms).
+    const bool split = items >= kSelectSplitItems;
+    if (store == kBF16) {
+        if (split) {
+            hipLaunchKernelGGL((k_select<kBF16, false>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(k_select_ovf<kBF16>, dim3(ogrid), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((k_select<kBF16, true>), dim3(grid), dim3(256), 0, s, a);
+        }
+    } else {
+        if (split) {
+            hipLaunchKernelGGL((k_select<kF32, false>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(k_select_ovf<kF32>, dim3(ogrid), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((k_select<kF32, true>), dim3(grid), dim3(256), 0, s, a);
+        }
+    }
     return hipGetLastError();
 }
 
