@@ -220,14 +220,18 @@ int fwpkm_retrieve_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T,
  * Outputs: o[B][T][d_v] float (required), vhat[B][T][d_v] float
  *          (nullable), both from the last pass.
  * passes >= 1.
- * Streams: the key path of each chunk is enqueued on `stream`, its value
- * path (sort of the reads, then gather and value write as two half-batch
- * launches each) on a second stream the library creates
- * once per host thread and device (default priority); events fork it from
- * and join it back to `stream`, so when `stream` reaches the end of this
- * call everything is done.  While kernel timing is on (fwpkm_timing_enable),
- * or when the environment variable FWPKM_SINGLE_STREAM is "1", both paths
- * stay on `stream`: the same kernels in the same order, one at a time.
+ * Streams: the key path of each chunk (scoring, selection, usage
+ * statistics, key step) is enqueued on `stream`, the value path (sort of
+ * the reads, then gather and value write as two half-batch launches each)
+ * on a value stream.  On the sweep scoring path, a chunk with fewer than
+ * 2^19 reads (B * tokens * heads * k) runs its selection and sort on a
+ * third, selection stream instead.  The library creates both streams once
+ * per host thread and device (default priority); events fork them from
+ * and join them back to `stream`, so when `stream` reaches the end of this
+ * call everything is done.  While kernel
+ * timing is on (fwpkm_timing_enable), or when the environment variable
+ * FWPKM_SINGLE_STREAM is "1", everything stays on `stream`: the same
+ * kernels, one at a time.  The results are the same bits either way.
  */
 int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                       const void* q, const void* v, const float* g, const void* v_next,

@@ -111,11 +111,12 @@ class TimedLaunch {
     hipEvent_t start_ = nullptr, stop_ = nullptr;
 };
 
-// Second stream and fork/join events of fwpkm_forward_seq, one set per
-// (host thread, device), created on first use and never released.
+// The value stream and the selection stream of fwpkm_forward_seq with their
+// fork/join events, one set per (host thread, device), created on first use
+// and never released.
 struct Aux {
-    hipStream_t sv = nullptr;
-    hipEvent_t ev_start = nullptr, ev_sel = nullptr, ev_end = nullptr;
+    hipStream_t sv = nullptr, sx = nullptr;
+    hipEvent_t ev_start = nullptr, ev_sel = nullptr, ev_end = nullptr, ev_scored = nullptr, ev_sorted = nullptr;
     hipEvent_t ev_write[2] = {nullptr, nullptr};
 };
 
@@ -128,7 +129,9 @@ hipError_t aux_streams(Aux** out) {
     if (!per_dev[dev]) {
         Aux* a = new Aux();
         if ((e = hipStreamCreateWithFlags(&a->sv, hipStreamNonBlocking)) != hipSuccess) return e;
-        hipEvent_t* evs[5] = {&a->ev_start, &a->ev_sel, &a->ev_end, &a->ev_write[0], &a->ev_write[1]};
+        if ((e = hipStreamCreateWithFlags(&a->sx, hipStreamNonBlocking)) != hipSuccess) return e;
+        hipEvent_t* evs[7] = {&a->ev_start, &a->ev_sel,      &a->ev_end,     &a->ev_scored,
+                              &a->ev_sorted, &a->ev_write[0], &a->ev_write[1]};
         for (hipEvent_t* ev : evs)
             if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
         per_dev[dev] = a;
@@ -136,6 +139,10 @@ hipError_t aux_streams(Aux** out) {
     *out = per_dev[dev];
     return hipSuccess;
 }
+
+// Chunks with fewer reads (sequences x tokens x heads x k) than this run
+// their selection and sort on forward_seq's selection stream.
+constexpr int64_t kApartReads = int64_t{1} << 19;
 
 struct Plan {
     int n, H, dq, dh, dv, kh, k, C, store, es;
@@ -256,8 +263,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, M, m, part, lp, qT, kpart, k0, v0, k1, v1, counts,
-        ph, pt, pts, phe;
+    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, M, m, part, lp, qT, kpart, counts, ph, pt, pts, phe;
+    size_t k0[2], v0[2], k1[2], v1[2];  // radix sort ping-pong buffers, [1] only with iw_copies = 2
     size_t total;
 };
 
@@ -305,10 +312,14 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         int ksplit = 1;
         for (int nt = 1; nt <= Tt; nt += 32) ksplit = std::max(ksplit, kgrad_split(p.H, p.n, nt, kgrad_split_override(), nullptr));
         L.kpart = ksplit > 1 ? take(kgrad_part_floats(B, p.H, p.n, p.dh, ksplit) * 4) : 0;
-        L.k0 = take(Bs * M * 4);
-        L.v0 = take(Bs * M * 4);
-        L.k1 = take(Bs * M * 4);
-        L.v1 = take(Bs * M * 4);
+        // forward_seq sorts chunk c+1 while chunk c's write still reads its
+        // sorted reads: a second set of sort buffers, by chunk parity
+        for (int set = 0; set < std::min(iw_copies, 2); ++set) {
+            L.k0[set] = take(Bs * M * 4);
+            L.v0[set] = take(Bs * M * 4);
+            L.k1[set] = take(Bs * M * 4);
+            L.v1[set] = take(Bs * M * 4);
+        }
         L.counts = take(Bs * 256 * std::max<size_t>(tiles, 1) * 4);
         L.ph = take(Bs * pieces * p.dv * 4);
         L.pt = take(Bs * pieces * p.dv * 4);
@@ -376,10 +387,11 @@ SelectArgs select_args(const Plan& p, const ScoreArgs& a, const void* q, int64_t
 // head) top-k' of each half and the product top-k into idx / w.
 int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
                 const void* K1, const void* K2, const float* knorm, int32_t* idx, float* w, int64_t iw_bstride,
-                bool stats, int32_t* usage, hipStream_t s) {
+                bool stats, int32_t* usage, hipStream_t s, hipStream_t s_sel = nullptr, hipEvent_t ev_scored = nullptr) {
     // short chunks (decode, one long sequence): whole rows of e, an exact
     // top-k' of each and statistics by reductions over the rows; otherwise
-    // the two-pass sweep with candidate lists
+    // the two-pass sweep with candidate lists.  With `s_sel` (sweep path
+    // only) the selection runs there, after the scoring on `s`.
     const bool rows = use_rows(p, B, Tc);
     ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm,
                              rows ? kScoreRows : (kScoreSelect | (stats ? kScoreStats : 0)));
@@ -403,9 +415,15 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
         sa.Z = a.Z;
         sa.M = a.M;
     }
+    hipStream_t ss = s;
+    if (s_sel && s_sel != s && !rows) {
+        HIP_TRY(hipEventRecord(ev_scored, s));
+        HIP_TRY(hipStreamWaitEvent(s_sel, ev_scored, 0));
+        ss = s_sel;
+    }
     {
-        TimedLaunch tl(FWPKM_K_SELECT, s);
-        HIP_TRY(launch_select(sa, p.store, s));
+        TimedLaunch tl(FWPKM_K_SELECT, ss);
+        HIP_TRY(launch_select(sa, p.store, ss));
     }
     return FWPKM_OK;
 }
@@ -415,15 +433,17 @@ int select_topk(const Plan& p, const Layout& L, void* ws, int B, int Tc, const v
 // of every sequence's reads by slot (sort_reads, which returns the buffer
 // holding the result), then the value write of sequences [b0, b0 + nb)
 // (write_rows).
+// `set` picks the buffer set (1 exists only in forward_seq's layout); the
+// result is reported as 2 * set + the ping-pong side that holds it.
 int sort_reads(const Plan& p, const Layout& L, void* ws, int B, int n_tgt, const int32_t* idx, int64_t iw_bstride,
-               int* sorted, hipStream_t s) {
+               int* sorted, hipStream_t s, int set = 0) {
     const int M = n_tgt * p.H * p.k;
-    *sorted = 0;
+    *sorted = 2 * set;
     if (M == 0) return FWPKM_OK;
     const int items = sort_items(B, M);
     const int tiles = (M + 256 * items - 1) / (256 * items);
-    uint32_t* kb[2] = {at<uint32_t>(ws, L.k0), at<uint32_t>(ws, L.k1)};
-    uint32_t* vb[2] = {at<uint32_t>(ws, L.v0), at<uint32_t>(ws, L.v1)};
+    uint32_t* kb[2] = {at<uint32_t>(ws, L.k0[set]), at<uint32_t>(ws, L.k1[set])};
+    uint32_t* vb[2] = {at<uint32_t>(ws, L.v0[set]), at<uint32_t>(ws, L.v1[set])};
     int cur = 0;
     TimedLaunch tl(FWPKM_K_SORT, s);
     for (int pass = 0; pass < p.sort_passes; ++pass) {
@@ -438,7 +458,7 @@ int sort_reads(const Plan& p, const Layout& L, void* ws, int B, int n_tgt, const
         HIP_TRY(launch_sort_pass(a, s));
         cur ^= 1;
     }
-    *sorted = cur;
+    *sorted = 2 * set + cur;
     return FWPKM_OK;
 }
 
@@ -450,8 +470,9 @@ int write_rows(const Plan& p, const Layout& L, void* ws, int b0, int nb, int Tc,
     const int pieces = (M + piece - 1) / piece;
     const size_t kb = static_cast<size_t>(b0);
     ScatterArgs sa{};
-    sa.keys = at<uint32_t>(ws, sorted ? L.k1 : L.k0) + kb * M;
-    sa.vals = at<uint32_t>(ws, sorted ? L.v1 : L.v0) + kb * M;
+    const int set = sorted >> 1;
+    sa.keys = at<uint32_t>(ws, (sorted & 1) ? L.k1[set] : L.k0[set]) + kb * M;
+    sa.vals = at<uint32_t>(ws, (sorted & 1) ? L.v1[set] : L.v0[set]) + kb * M;
     sa.w = w + kb * iw_bstride; sa.w_bstride = iw_bstride;
     sa.r = at<float>(ws, L.r) + kb * Tc * p.dv;
     sa.V = static_cast<unsigned char*>(V) + kb * static_cast<size_t>(p.N) * p.dv * p.es;
@@ -483,7 +504,7 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
 // rows); otherwise a stats scoring pass computes all of them first.
 // knorm holds ||K_i||^2 of the current codebooks; the key step rewrites it.
 int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
-            void* K1, void* K2, bool have_stats, float* knorm, hipStream_t s) {
+            void* K1, void* K2, bool have_stats, float* knorm, hipStream_t s, hipEvent_t before_kstep = nullptr) {
     const bool rows = use_rows(p, B, Tc);
     if (!have_stats) {
         ScoreArgs a = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, rows ? kScoreRows : kScoreStats);
@@ -542,6 +563,8 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     ka.B = B; ka.Tc = Tc; ka.n = p.n; ka.H = p.H; ka.dh = p.dh; ka.eps = p.eps; ka.lr = p.lr_k;
     ka.split = kgrad_split(p.H, p.n, Tc, kgrad_split_override(), &ka.per);
     ka.part = ka.split > 1 ? at<float>(ws, L.kpart) : nullptr;
+    // the key step rewrites K1/K2, which a selection on another stream may still read
+    if (before_kstep) HIP_TRY(hipStreamWaitEvent(s, before_kstep, 0));
     {
         TimedLaunch tl(FWPKM_K_KGRAD, s);
         HIP_TRY(launch_kgrad(ka, p.store, s));
@@ -813,11 +836,21 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // The key path (scoring, selection, usage statistics, key step) stays on
-    // the caller's stream; the value path (gather, sort, value write) of the
-    // same chunk runs on a second stream of the library.  They meet at the
-    // selection of each chunk, and the slot/weight lists alternate between
-    // two buffers so chunk c+1's selection only waits for chunk c-1's write.
-    // With kernel timing on, or FWPKM_SINGLE_STREAM=1, both paths stay on
+    // the caller's stream; the value path (sort, gather, value write) of the
+    // same chunk runs on a value stream of the library.  They meet at the
+    // selection of each chunk.  On the sweep path, chunks of fewer than
+    // kApartReads reads move the selection and the sort to a third,
+    // selection stream: the selection waits for the scoring, the key step
+    // for the selection (which reads K1/K2), so the usage statistics overlap
+    // the selection, and the sort leaves the value path.  (On the rows path
+    // the statistics use what the selection leaves, so it stays on the key
+    // path.)  Measured: 131K-read chunks (B = 8, 4 heads, k = 16, 256
+    // tokens) 2.31 -> 2.22 ms per step; at 1M reads (B = 16, 4 heads,
+    // k = 32, 512 tokens) the value path already fills HBM and the extra
+    // concurrency slows it, 7.99 -> 8.15 ms, so there they stay.  The
+    // slot/weight lists and the sort buffers alternate between two sets, so
+    // chunk c+1's selection and sort only wait for chunk c-1's write.  With
+    // kernel timing on, or FWPKM_SINGLE_STREAM=1, everything stays on
     // `stream` (same work, one kernel at a time).
     Aux* ax = nullptr;
     HIP_TRY(aux_streams(&ax));
@@ -826,12 +859,14 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     // a chunk's gradient reads V and K before that chunk's write
     const bool single = timing().on || (env_single && env_single[0] == '1') || grad != nullptr;
     hipStream_t sv = single ? s : ax->sv;
+    hipStream_t sx = single ? s : ax->sx;
     // With two streams the value path of a chunk runs as two half-batch
     // launches of gather + write: between them the key path's kernels find
     // room on the chip (measured: 9.30 -> 8.83 ms per step at B=16).
     const int group = single ? B : std::max(1, (B + 1) / 2);
     HIP_TRY(hipEventRecord(ax->ev_start, s));
     HIP_TRY(hipStreamWaitEvent(sv, ax->ev_start, 0));
+    HIP_TRY(hipStreamWaitEvent(sx, ax->ev_start, 0));
     HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     const int64_t qb = static_cast<int64_t>(T) * p.H * p.dq;
     const int64_t vbs = static_cast<int64_t>(T) * p.dv;
@@ -850,12 +885,19 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
             const int buf = static_cast<int>(step & 1);
             int32_t* idx = idxs[buf];
             float* w = ws_w[buf];
-            // this buffer was last read by the value write two chunks ago
-            if (step >= 2) HIP_TRY(hipStreamWaitEvent(s, ax->ev_write[buf], 0));
+            // where this chunk's selection and sort run: apart from the key and
+            // value paths on the sweep path of chunks with fewer than
+            // kApartReads reads; bigger chunks keep them on those paths
+            const int64_t reads = static_cast<int64_t>(B) * Tc * p.H * p.k;
+            const bool sel_apart = sx != s && !use_rows(p, B, Tc) && reads < kApartReads;
+            hipStream_t ss = sel_apart ? sx : s;
+            // these lists and sort buffers were last read by the value write two chunks ago
+            if (step >= 2) HIP_TRY(hipStreamWaitEvent(ss, ax->ev_write[buf], 0));
             // retrieval with the state left by the previous chunk
-            rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, at<float>(ws, L.knorm), idx, w, iwb, p.addr, usage, s);
+            rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, at<float>(ws, L.knorm), idx, w, iwb, p.addr, usage, s,
+                             sel_apart ? sx : nullptr, ax->ev_scored);
             if (rc) return rc;
-            HIP_TRY(hipEventRecord(ax->ev_sel, s));
+            HIP_TRY(hipEventRecord(ax->ev_sel, ss));
 
             // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
             int n_tgt;
@@ -876,12 +918,20 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                     n_tgt = Tc - 1;
                 }
             }
-            // value path of this chunk: the sort of all reads, then gather and
-            // value write by groups of `group` sequences
-            HIP_TRY(hipStreamWaitEvent(sv, ax->ev_sel, 0));
+            // the sort of all reads, then the value path: gather and value
+            // write by groups of `group` sequences
+            const bool sort_apart = sel_apart;
+            hipStream_t so = sort_apart ? sx : sv;
+            if (ss != so) HIP_TRY(hipStreamWaitEvent(so, ax->ev_sel, 0));
             int sorted = 0;
-            rc = sort_reads(p, L, ws, B, n_tgt, idx, iwb, &sorted, sv);
+            // on the value stream the write that reads the sorted buffers is in
+            // order behind the sort; apart, chunks alternate between two sets
+            rc = sort_reads(p, L, ws, B, n_tgt, idx, iwb, &sorted, so, sort_apart ? buf : 0);
             if (rc) return rc;
+            if (so != sv) {
+                HIP_TRY(hipEventRecord(ax->ev_sorted, so));
+                HIP_TRY(hipStreamWaitEvent(sv, ax->ev_sorted, 0));
+            }
             for (int b0 = 0; b0 < B; b0 += group) {
                 const int nb = std::min(group, B - b0);
                 const size_t bo = static_cast<size_t>(b0);
@@ -928,10 +978,14 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                 if (rc) return rc;
             }
             HIP_TRY(hipEventRecord(ax->ev_write[buf], sv));
-            // key path: addressing step of this chunk
+            // key path: addressing step of this chunk; the next chunk's
+            // scoring rewrites the candidate lists this selection reads
             if (p.addr) {
-                rc = address(p, L, ws, B, Tc, qc, qb, K1, K2, true, at<float>(ws, L.knorm), s);
+                rc = address(p, L, ws, B, Tc, qc, qb, K1, K2, true, at<float>(ws, L.knorm), s,
+                             sel_apart ? ax->ev_sel : nullptr);
                 if (rc) return rc;
+            } else if (sel_apart) {
+                HIP_TRY(hipStreamWaitEvent(s, ax->ev_sel, 0));
             }
         }
     }

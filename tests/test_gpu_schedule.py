@@ -1,0 +1,79 @@
+"""GPU: fwpkm_forward_seq's multi-stream schedule (key path on the caller's
+stream; gather and value write on a value stream; for chunks under 2^19
+reads on the sweep path, selection and sort on a selection stream; lists
+and sort buffers alternating by chunk) gives the same bits as the same call
+with every kernel on one stream, along both scoring paths, on both sides
+of the read threshold, with and without the addressing step, over a
+partial last chunk and two passes, and with read counting."""
+import os
+
+import pytest
+import torch
+
+from sparse_weight_memory_sub_amd import fwpkm
+from sparse_weight_memory_sub_amd.workloads import FwpkmConfig, make_state, make_tokens
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] {request.node.name}", flush=True)
+    yield
+    torch.cuda.synchronize()
+    for k in ("FWPKM_SCORE_PATH", "FWPKM_SINGLE_STREAM"):
+        os.environ.pop(k, None)
+
+
+def C(**kw):
+    base = dict(n=256, heads=2, d_q=128, d_v=64, k_half=16, k=16, chunk=256, store="bf16", lr_k=5.0)
+    base.update(kw)
+    return FwpkmConfig(**base)
+
+
+def run(cfg, B, T, passes, seed, single, usage):
+    if single:
+        os.environ["FWPKM_SINGLE_STREAM"] = "1"
+    else:
+        os.environ.pop("FWPKM_SINGLE_STREAM", None)
+    q, v, g, _ = make_tokens(cfg, B, T, seed, "gauss")
+    K1, K2, V = (x.to(DEV).contiguous() for x in make_state(cfg, B, seed, std=0.5))
+    qd, vd, gd = (x.to(DEV).contiguous() for x in (q, v, g))
+    u = torch.zeros((B, cfg.N), dtype=torch.int32, device=DEV) if usage else None
+    out = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1, K2, V, passes=passes, want_vhat=True, usage=u)
+    torch.cuda.synchronize()
+    res = {"o": out["o"], "vhat": out["vhat"], "K1": K1, "K2": K2, "V": V}
+    if usage:
+        res["usage"] = u
+    return {k: x.cpu() for k, x in res.items()}
+
+
+CASES = [
+    # (name, cfg, B, T, passes, scoring path, count reads)
+    ("sweep_addr", C(), 4, 1024, 1, "sweep", False),
+    ("sweep_no_addr", C(use_addr=False), 4, 1024, 1, "sweep", False),
+    ("sweep_ragged_two_passes", C(), 3, 1000, 2, "sweep", False),
+    ("sweep_usage", C(store="f32"), 2, 768, 1, "sweep", True),
+    ("rows_addr", C(), 2, 1000, 2, "rows", False),
+    ("chosen_path", C(chunk=128), 4, 640, 1, None, False),
+    # 4 x 1024 x 4 x 32 = 2^19 reads per chunk: selection stays on the key path
+    ("sweep_big_chunks", C(heads=4, d_q=64, k_half=32, k=32, chunk=1024), 4, 2048, 1, "sweep", False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_multi_stream_schedule_equals_one_stream(case):
+    name, cfg, B, T, passes, path, usage = case
+    if path:
+        os.environ["FWPKM_SCORE_PATH"] = path
+    one = run(cfg, B, T, passes, 61, True, usage)
+    many = run(cfg, B, T, passes, 61, False, usage)
+    # a second multi-stream call on the same (cached) workspace and streams
+    again = run(cfg, B, T, passes, 61, False, usage)
+    for k in one:
+        assert torch.equal(one[k].view(-1).view(torch.uint8), many[k].view(-1).view(torch.uint8)), f"{name} {k}"
+        assert torch.equal(many[k].view(-1).view(torch.uint8), again[k].view(-1).view(torch.uint8)), f"{name} {k}"
