@@ -924,9 +924,10 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
             hipStream_t so = sort_apart ? sx : sv;
             if (ss != so) HIP_TRY(hipStreamWaitEvent(so, ax->ev_sel, 0));
             int sorted = 0;
-            // on the value stream the write that reads the sorted buffers is in
-            // order behind the sort; apart, chunks alternate between two sets
-            rc = sort_reads(p, L, ws, B, n_tgt, idx, iwb, &sorted, so, sort_apart ? buf : 0);
+            // chunks alternate between two sets of sort buffers wherever their
+            // sort runs: a pass's short last chunk may sort apart while the
+            // chunk before it is still being written from the value stream
+            rc = sort_reads(p, L, ws, B, n_tgt, idx, iwb, &sorted, so, buf);
             if (rc) return rc;
             if (so != sv) {
                 HIP_TRY(hipEventRecord(ax->ev_sorted, so));

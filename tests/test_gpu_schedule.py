@@ -62,6 +62,9 @@ CASES = [
     ("chosen_path", C(chunk=128), 4, 640, 1, None, False),
     # 4 x 1024 x 4 x 32 = 2^19 reads per chunk: selection stays on the key path
     ("sweep_big_chunks", C(heads=4, d_q=64, k_half=32, k=32, chunk=1024), 4, 2048, 1, "sweep", False),
+    # two full chunks at 2^19 reads, then a 512-token chunk under it, twice:
+    # the schedule changes at the last chunk and again at the next pass
+    ("threshold_crossing", C(heads=4, d_q=64, k_half=32, k=32, chunk=1024), 4, 2560, 2, "sweep", False),
 ]
 
 
