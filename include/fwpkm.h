@@ -225,7 +225,8 @@ int fwpkm_retrieve_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T,
  * the reads, then gather and value write as two half-batch launches each)
  * on a value stream.  On the sweep scoring path, a chunk with fewer than
  * 2^19 reads (B * tokens * heads * k) runs its selection and sort on a
- * third, selection stream instead.  The library creates both streams once
+ * third, selection stream instead, and when half a batch is under 4
+ * sequences its gather and write are one launch each.  The library creates both streams once
  * per host thread and device (default priority); events fork them from
  * and join them back to `stream`, so when `stream` reaches the end of this
  * call everything is done.  While kernel

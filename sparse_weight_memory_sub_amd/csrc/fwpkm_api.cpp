@@ -862,7 +862,8 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     hipStream_t sx = single ? s : ax->sx;
     // With two streams the value path of a chunk runs as two half-batch
     // launches of gather + write: between them the key path's kernels find
-    // room on the chip (measured: 9.30 -> 8.83 ms per step at B=16).
+    // room on the chip (measured: 9.30 -> 8.83 ms per step at B=16); see
+    // below for the one exception.
     const int group = single ? B : std::max(1, (B + 1) / 2);
     HIP_TRY(hipEventRecord(ax->ev_start, s));
     HIP_TRY(hipStreamWaitEvent(sv, ax->ev_start, 0));
@@ -933,8 +934,13 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                 HIP_TRY(hipEventRecord(ax->ev_sorted, so));
                 HIP_TRY(hipStreamWaitEvent(sv, ax->ev_sorted, 0));
             }
-            for (int b0 = 0; b0 < B; b0 += group) {
-                const int nb = std::min(group, B - b0);
+            // with the selection apart, a half batch of under 4 sequences is
+            // too few wavefronts for the write: one launch (measured, 4
+            // sequences, 1024 tokens: 1.38 -> 1.36 ms per step; 8 sequences
+            // of 256 tokens lose 2.21 -> 2.33 ms the same way)
+            const int grp = (sel_apart && group < 4) ? B : group;
+            for (int b0 = 0; b0 < B; b0 += grp) {
+                const int nb = std::min(grp, B - b0);
                 const size_t bo = static_cast<size_t>(b0);
                 GatherArgs ga{};
                 ga.V = static_cast<unsigned char*>(V) + bo * static_cast<size_t>(p.N) * p.dv * p.es;
