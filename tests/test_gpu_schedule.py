@@ -80,3 +80,29 @@ def test_multi_stream_schedule_equals_one_stream(case):
     for k in one:
         assert torch.equal(one[k].view(-1).view(torch.uint8), many[k].view(-1).view(torch.uint8)), f"{name} {k}"
         assert torch.equal(many[k].view(-1).view(torch.uint8), again[k].view(-1).view(torch.uint8)), f"{name} {k}"
+
+
+@pytest.mark.parametrize("path", ["sweep", "rows"])
+def test_caller_side_stream(path):
+    """Enqueued on a side stream of the caller (default priority): the
+    library's streams fork from and join back to that stream, so work the
+    caller orders after it sees the finished state, the same bits as a call
+    on the current stream."""
+    os.environ["FWPKM_SCORE_PATH"] = path
+    cfg, B, T = C(), 3, 1000
+    ref = run(cfg, B, T, 1, 62, False, False)
+    q, v, g, _ = make_tokens(cfg, B, T, 62, "gauss")
+    K1, K2, V = (x.to(DEV).contiguous() for x in make_state(cfg, B, 62, std=0.5))
+    qd, vd, gd = (x.to(DEV).contiguous() for x in (q, v, g))
+    o = torch.empty((B, T, cfg.d_v), dtype=torch.float32, device=DEV)
+    vh = torch.empty_like(o)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1, K2, V, o=o, vhat=vh, stream=side)
+    # ordered after the call on the side stream only
+    with torch.cuda.stream(side):
+        got = {"o": o.clone(), "vhat": vh.clone(), "K1": K1.clone(), "K2": K2.clone(), "V": V.clone()}
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for k, x in got.items():
+        assert torch.equal(x.cpu().view(-1).view(torch.uint8), ref[k].view(-1).view(torch.uint8)), k
