@@ -31,6 +31,36 @@
  *   - B == 0 or a token count of 0 is a successful no-op.
  *   - Calls on one stream are ordered; concurrent calls that share state
  *     buffers or a workspace on different streams race.
+ *
+ * Limits of this GPU path (the method itself allows any size; a call
+ * outside them returns FWPKM_EUNSUPPORTED before anything is enqueued):
+ *
+ *   quantity          method              this GPU path
+ *   n (N = n*n)       n >= 1, n*n < 2^31  16 <= n <= 1024, n % 16 == 0
+ *   d_q / 2           >= 1                32, 64, 128 or 256
+ *   d_v               >= 1                64, 128, 256 or 512
+ *   k' (k_half)       1 <= k' <= n        k' <= 64
+ *   k                 1 <= k <= k'^2      k <= 64; at most 256 pairs (a+1)(b+1) <= k
+ *   heads * k         any                 <= 256
+ *   B * tokens * heads * k of one call    < 2^31
+ *
+ * A caller with another d_q can zero-pad: query halves and sub-keys padded
+ * with zeros to the next supported d_q / 2 leave every distance ||q - K||^2
+ * and every dot product unchanged, and the key step leaves the padded
+ * sub-key columns at zero, so the padded layer computes the same values.
+ * Value columns can be padded the same way only with znorm = 0 (the
+ * z-score's mean and variance run over all d_v columns).
+ *
+ * Debug overrides (tests, sweeps and profiling).  Read at every call, and
+ * only while the environment variable FWPKM_DEBUG is "1"; none changes a
+ * result beyond the order of a float sum, and none is needed in use:
+ *   FWPKM_SINGLE_STREAM=1        fwpkm_forward_seq keeps every kernel on the
+ *                                caller's stream (the same bits);
+ *   FWPKM_SCORE_PATH=sweep|rows  pins the scoring path (the same selection;
+ *                                usage statistics summed in another order);
+ *   FWPKM_KGRAD_SPLIT=<s>        fixes the key step's token split (at most 8);
+ *   FWPKM_DECODE=unfused         decode's selection and value read as two
+ *                                launches (the same bits).
  */
 #ifndef FWPKM_H
 #define FWPKM_H
@@ -42,7 +72,7 @@
 extern "C" {
 #endif
 
-#define FWPKM_ABI_VERSION 2
+#define FWPKM_ABI_VERSION 3
 
 typedef enum { FWPKM_F32 = 0, FWPKM_BF16 = 1 } fwpkm_dtype;
 
@@ -226,13 +256,16 @@ int fwpkm_retrieve_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T,
  * on a value stream.  On the sweep scoring path, a chunk with fewer than
  * 2^19 reads (B * tokens * heads * k) runs its selection and sort on a
  * third, selection stream instead, and when half a batch is under 4
- * sequences its gather and write are one launch each.  The library creates both streams once
- * per host thread and device (default priority); events fork them from
- * and join them back to `stream`, so when `stream` reaches the end of this
- * call everything is done.  While kernel
- * timing is on (fwpkm_timing_enable), or when the environment variable
- * FWPKM_SINGLE_STREAM is "1", everything stays on `stream`: the same
- * kernels, one at a time.  The results are the same bits either way.
+ * sequences its gather and write are one launch each.  The library creates
+ * both streams (default priority) and seven events on the first such call
+ * per host thread and device of `stream`, on that device, and keeps them
+ * until fwpkm_release_streams() on that thread (or the end of the
+ * process); events fork them from and join them back to `stream`, so when
+ * `stream` reaches the end of this call everything is done.  While kernel
+ * timing is on (fwpkm_timing_enable), or under the debug override
+ * FWPKM_SINGLE_STREAM, everything stays on `stream`: the same kernels, one
+ * at a time, and no stream or event of the library is used.  The results
+ * are the same bits either way.
  */
 int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                       const void* q, const void* v, const float* g, const void* v_next,
@@ -347,6 +380,16 @@ int fwpkm_stream_flush(const fwpkm_cfg* cfg, int32_t B, const void* v_next,
                        void* K1, void* K2, void* V,
                        void* state, fwpkm_stream_pos* pos,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Destroys the value and selection streams and events that
+ * fwpkm_forward_seq created for the calling host thread (on every device),
+ * after waiting for the work enqueued on them; the next multi-stream call
+ * on the thread creates new ones.  For hosts that run the layer from
+ * short-lived threads.  Returns FWPKM_OK (also when there is nothing to
+ * release) or FWPKM_EHIP.
+ */
+int fwpkm_release_streams(void);
 
 /*
  * Kernel timing (observability; not part of the method).  Kernel families

@@ -112,32 +112,81 @@ class TimedLaunch {
 };
 
 // The value stream and the selection stream of fwpkm_forward_seq with their
-// fork/join events, one set per (host thread, device), created on first use
-// and never released.
+// fork/join events, one set per (host thread, device of the caller's
+// stream), created on the first multi-stream call and kept until
+// fwpkm_release_streams() on that thread (or the end of the process).
 struct Aux {
     hipStream_t sv = nullptr, sx = nullptr;
     hipEvent_t ev_start = nullptr, ev_sel = nullptr, ev_end = nullptr, ev_scored = nullptr, ev_sorted = nullptr;
     hipEvent_t ev_write[2] = {nullptr, nullptr};
 };
 
-hipError_t aux_streams(Aux** out) {
-    thread_local std::vector<Aux*> per_dev;
+thread_local std::vector<Aux*> t_aux;  // indexed by device
+
+// Destroys one set (its streams first wait for their work).
+hipError_t aux_destroy(Aux* a) {
+    hipError_t first = hipSuccess;
+    auto keep = [&](hipError_t e) {
+        if (first == hipSuccess) first = e;
+    };
+    for (hipStream_t st : {a->sv, a->sx})
+        if (st) {
+            keep(hipStreamSynchronize(st));
+            keep(hipStreamDestroy(st));
+        }
+    for (hipEvent_t ev : {a->ev_start, a->ev_sel, a->ev_end, a->ev_scored, a->ev_sorted, a->ev_write[0],
+                          a->ev_write[1]})
+        if (ev) keep(hipEventDestroy(ev));
+    delete a;
+    return first;
+}
+
+// Device that work enqueued on `s` runs on (the current device for the
+// null stream).
+hipError_t stream_device(hipStream_t s, int* dev) {
+    if (!s) return hipGetDevice(dev);
+    return hipStreamGetDevice(s, dev);
+}
+
+hipError_t aux_streams(hipStream_t caller, Aux** out) {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    hipError_t e = stream_device(caller, &dev);
     if (e != hipSuccess) return e;
-    if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1, nullptr);
-    if (!per_dev[dev]) {
+    if (dev < 0) return hipErrorInvalidDevice;
+    if (static_cast<int>(t_aux.size()) <= dev) t_aux.resize(dev + 1, nullptr);
+    if (!t_aux[dev]) {
+        // create them on the caller's device, then restore the current one
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
         Aux* a = new Aux();
-        if ((e = hipStreamCreateWithFlags(&a->sv, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipStreamCreateWithFlags(&a->sx, hipStreamNonBlocking)) != hipSuccess) return e;
+        e = hipStreamCreateWithFlags(&a->sv, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->sx, hipStreamNonBlocking);
         hipEvent_t* evs[7] = {&a->ev_start, &a->ev_sel,      &a->ev_end,     &a->ev_scored,
                               &a->ev_sorted, &a->ev_write[0], &a->ev_write[1]};
         for (hipEvent_t* ev : evs)
-            if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
-        per_dev[dev] = a;
+            if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) {
+            (void)aux_destroy(a);  // the creation error is the one reported
+            return e;
+        }
+        t_aux[dev] = a;
     }
-    *out = per_dev[dev];
+    *out = t_aux[dev];
     return hipSuccess;
+}
+
+// Environment overrides for tests, sweeps and profiling, read only while
+// FWPKM_DEBUG=1 (otherwise NULL): FWPKM_SINGLE_STREAM, FWPKM_SCORE_PATH,
+// FWPKM_KGRAD_SPLIT, FWPKM_DECODE.
+const char* debug_env(const char* name) {
+    const char* on = std::getenv("FWPKM_DEBUG");
+    if (!on || std::strcmp(on, "1") != 0) return nullptr;
+    return std::getenv(name);
 }
 
 // Chunks with fewer reads (sequences x tokens x heads x k) than this run
@@ -218,7 +267,7 @@ size_t row_bytes(const Plan& p, int B, int Tc) {
 // FWPKM_SCORE_PATH = "sweep" or "rows" overrides the choice (both compute
 // the same selection; the statistics differ only in summation order).
 int score_path_override() {
-    const char* e = std::getenv("FWPKM_SCORE_PATH");
+    const char* e = debug_env("FWPKM_SCORE_PATH");
     if (!e) return 0;
     if (std::strcmp(e, "sweep") == 0) return 1;
     if (std::strcmp(e, "rows") == 0) return 2;
@@ -249,7 +298,7 @@ int rows_max(const Plan& p, int B, int T) {
 // FWPKM_KGRAD_SPLIT = <s> fixes the key step's token split at s (capped by
 // the chunk's 32-token blocks) in place of the per-sequence rule.
 int kgrad_split_override() {
-    const char* e = std::getenv("FWPKM_KGRAD_SPLIT");
+    const char* e = debug_env("FWPKM_KGRAD_SPLIT");
     return e ? std::max(0, std::atoi(e)) : 0;
 }
 
@@ -263,8 +312,9 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for B sequences of Tt tokens per step.
 struct Layout {
-    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, M, m, part, lp, qT, kpart, counts, ph, pt, pts, phe;
-    size_t k0[2], v0[2], k1[2], v1[2];  // radix sort ping-pong buffers, [1] only with iw_copies = 2
+    size_t idx, w, idx2, w2, knorm, qn, cand, cnt, erow, r, Z, M, m, part, lp, qT, kpart, ph, pt, pts, phe;
+    // radix sort ping-pong buffers and per-tile digit counts, [1] only with iw_copies = 2
+    size_t k0[2], v0[2], k1[2], v1[2], counts[2];
     size_t total;
 };
 
@@ -313,14 +363,15 @@ Layout layout(const Plan& p, int B, int Tt, bool with_iw, bool with_update, int 
         for (int nt = 1; nt <= Tt; nt += 32) ksplit = std::max(ksplit, kgrad_split(p.H, p.n, nt, kgrad_split_override(), nullptr));
         L.kpart = ksplit > 1 ? take(kgrad_part_floats(B, p.H, p.n, p.dh, ksplit) * 4) : 0;
         // forward_seq sorts chunk c+1 while chunk c's write still reads its
-        // sorted reads: a second set of sort buffers, by chunk parity
+        // sorted reads, and two chunks' sorts may run at once on different
+        // streams: a second set of sort buffers and digit counts, by chunk parity
         for (int set = 0; set < std::min(iw_copies, 2); ++set) {
             L.k0[set] = take(Bs * M * 4);
             L.v0[set] = take(Bs * M * 4);
             L.k1[set] = take(Bs * M * 4);
             L.v1[set] = take(Bs * M * 4);
+            L.counts[set] = take(Bs * 256 * std::max<size_t>(tiles, 1) * 4);
         }
-        L.counts = take(Bs * 256 * std::max<size_t>(tiles, 1) * 4);
         L.ph = take(Bs * pieces * p.dv * 4);
         L.pt = take(Bs * pieces * p.dv * 4);
         L.pts = take(Bs * pieces * 4);
@@ -451,7 +502,7 @@ int sort_reads(const Plan& p, const Layout& L, void* ws, int B, int n_tgt, const
         a.idx = idx; a.idx_bstride = iw_bstride;
         a.kin = kb[cur]; a.vin = vb[cur];
         a.kout = kb[cur ^ 1]; a.vout = vb[cur ^ 1];
-        a.counts = at<uint32_t>(ws, L.counts);
+        a.counts = at<uint32_t>(ws, L.counts[set]);
         a.B = B; a.M = M; a.tiles = tiles; a.shift = 8 * pass; a.first = pass == 0;
         a.N = static_cast<uint32_t>(p.N);
         a.items = items;
@@ -630,7 +681,7 @@ int stream_fire(const Plan& p, const StreamLayout& S, void* st, int B, int Tc, i
 // FWPKM_DECODE=unfused keeps decode's selection and read as two launches (the
 // tests compare the two forms).
 bool fused_decode_off() {
-    const char* e = std::getenv("FWPKM_DECODE");
+    const char* e = debug_env("FWPKM_DECODE");
     return e && std::strcmp(e, "unfused") == 0;
 }
 
@@ -832,9 +883,9 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     const int Cm = std::min(T, p.C);
     if (static_cast<int64_t>(B) * Cm * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*C*heads*k too large");
     const Layout L = layout(p, B, Cm, true, true, 2);
+    hipStream_t s = static_cast<hipStream_t>(stream);
     rc = check_ws(ws, ws_bytes, L.total);
     if (rc) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     // The key path (scoring, selection, usage statistics, key step) stays on
     // the caller's stream; the value path (sort, gather, value write) of the
     // same chunk runs on a value stream of the library.  They meet at the
@@ -850,14 +901,19 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     // concurrency slows it, 7.99 -> 8.15 ms, so there they stay.  The
     // slot/weight lists and the sort buffers alternate between two sets, so
     // chunk c+1's selection and sort only wait for chunk c-1's write.  With
-    // kernel timing on, or FWPKM_SINGLE_STREAM=1, everything stays on
-    // `stream` (same work, one kernel at a time).
-    Aux* ax = nullptr;
-    HIP_TRY(aux_streams(&ax));
-    const char* env_single = std::getenv("FWPKM_SINGLE_STREAM");
+    // kernel timing on, or with the debug
+    // override FWPKM_SINGLE_STREAM=1, everything stays on `stream` (same
+    // work, one kernel at a time) and no stream or event of the library is
+    // used.
+    const char* env_single = debug_env("FWPKM_SINGLE_STREAM");
     // the replay for gradients keeps every kernel in order on one stream:
     // a chunk's gradient reads V and K before that chunk's write
     const bool single = timing().on || (env_single && env_single[0] == '1') || grad != nullptr;
+    Aux none;  // no events: every record and wait below is skipped when single
+    Aux* ax = &none;
+    if (!single) HIP_TRY(aux_streams(s, &ax));
+    auto record = [&](hipEvent_t ev, hipStream_t st) { return single ? hipSuccess : hipEventRecord(ev, st); };
+    auto wait = [&](hipStream_t st, hipEvent_t ev) { return single ? hipSuccess : hipStreamWaitEvent(st, ev, 0); };
     hipStream_t sv = single ? s : ax->sv;
     hipStream_t sx = single ? s : ax->sx;
     // With two streams the value path of a chunk runs as two half-batch
@@ -865,9 +921,9 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     // room on the chip (measured: 9.30 -> 8.83 ms per step at B=16); see
     // below for the one exception.
     const int group = single ? B : std::max(1, (B + 1) / 2);
-    HIP_TRY(hipEventRecord(ax->ev_start, s));
-    HIP_TRY(hipStreamWaitEvent(sv, ax->ev_start, 0));
-    HIP_TRY(hipStreamWaitEvent(sx, ax->ev_start, 0));
+    HIP_TRY(record(ax->ev_start, s));
+    HIP_TRY(wait(sv, ax->ev_start));
+    HIP_TRY(wait(sx, ax->ev_start));
     HIP_TRY(knorm_launch(p, B, K1, K2, at<float>(ws, L.knorm), s));
     const int64_t qb = static_cast<int64_t>(T) * p.H * p.dq;
     const int64_t vbs = static_cast<int64_t>(T) * p.dv;
@@ -893,12 +949,12 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
             const bool sel_apart = sx != s && !use_rows(p, B, Tc) && reads < kApartReads;
             hipStream_t ss = sel_apart ? sx : s;
             // these lists and sort buffers were last read by the value write two chunks ago
-            if (step >= 2) HIP_TRY(hipStreamWaitEvent(ss, ax->ev_write[buf], 0));
+            if (step >= 2) HIP_TRY(wait(ss, ax->ev_write[buf]));
             // retrieval with the state left by the previous chunk
             rc = select_topk(p, L, ws, B, Tc, qc, qb, K1, K2, at<float>(ws, L.knorm), idx, w, iwb, p.addr, usage, s,
                              sel_apart ? sx : nullptr, ax->ev_scored);
             if (rc) return rc;
-            HIP_TRY(hipEventRecord(ax->ev_sel, ss));
+            HIP_TRY(record(ax->ev_sel, ss));
 
             // targets: lookahead pairs t with t+1; the sequence's last token uses v_next or has none
             int n_tgt;
@@ -923,16 +979,20 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
             // write by groups of `group` sequences
             const bool sort_apart = sel_apart;
             hipStream_t so = sort_apart ? sx : sv;
-            if (ss != so) HIP_TRY(hipStreamWaitEvent(so, ax->ev_sel, 0));
+            if (ss != so) HIP_TRY(wait(so, ax->ev_sel));
             int sorted = 0;
-            // chunks alternate between two sets of sort buffers wherever their
-            // sort runs: a pass's short last chunk may sort apart while the
-            // chunk before it is still being written from the value stream
+            // chunks alternate between two sets of sort buffers (keys, values
+            // and digit counts) wherever their sort runs.  A chunk's sort and
+            // write touch only its own set, last used by the chunk two before,
+            // whose write ev_write[buf] orders first.  Nothing orders the sorts
+            // of neighbouring chunks against each other: a pass's short last
+            // chunk may sort apart while the chunk before it still sorts or is
+            // written on the value stream, so the two must share no buffer.
             rc = sort_reads(p, L, ws, B, n_tgt, idx, iwb, &sorted, so, buf);
             if (rc) return rc;
             if (so != sv) {
-                HIP_TRY(hipEventRecord(ax->ev_sorted, so));
-                HIP_TRY(hipStreamWaitEvent(sv, ax->ev_sorted, 0));
+                HIP_TRY(record(ax->ev_sorted, so));
+                HIP_TRY(wait(sv, ax->ev_sorted));
             }
             // with the selection apart, a half batch of under 4 sequences is
             // too few wavefronts for the write: one launch (measured, 4
@@ -984,7 +1044,7 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                 rc = write_rows(p, L, ws, b0, nb, Tc, n_tgt, w, iwb, V, nullptr, sorted, sv);
                 if (rc) return rc;
             }
-            HIP_TRY(hipEventRecord(ax->ev_write[buf], sv));
+            HIP_TRY(record(ax->ev_write[buf], sv));
             // key path: addressing step of this chunk; the next chunk's
             // scoring rewrites the candidate lists this selection reads
             if (p.addr) {
@@ -992,13 +1052,13 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                              sel_apart ? ax->ev_sel : nullptr);
                 if (rc) return rc;
             } else if (sel_apart) {
-                HIP_TRY(hipStreamWaitEvent(s, ax->ev_sel, 0));
+                HIP_TRY(wait(s, ax->ev_sel));
             }
         }
     }
     // join: the caller's stream sees every write
-    HIP_TRY(hipEventRecord(ax->ev_end, sv));
-    HIP_TRY(hipStreamWaitEvent(s, ax->ev_end, 0));
+    HIP_TRY(record(ax->ev_end, sv));
+    HIP_TRY(wait(s, ax->ev_end));
     return ok();
 }
 
@@ -1027,6 +1087,19 @@ int fwpkm_forward_seq_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32
     const SeqGrad grad{dO, dq, dv, dg};
     return forward_seq_impl(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, nullptr, nullptr, &grad, ws, ws_bytes,
                             stream);
+}
+
+int fwpkm_release_streams(void) {
+    hipError_t first = hipSuccess;
+    for (Aux*& a : t_aux)
+        if (a) {
+            const hipError_t e = aux_destroy(a);
+            if (first == hipSuccess) first = e;
+            a = nullptr;
+        }
+    t_aux.clear();
+    if (first != hipSuccess) return fail(FWPKM_EHIP, "releasing the library's streams: %s", hipGetErrorString(first));
+    return ok();
 }
 
 int fwpkm_stream_state_bytes(const fwpkm_cfg* cfg, int32_t B, size_t* bytes) {

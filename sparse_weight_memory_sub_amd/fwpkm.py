@@ -28,7 +28,7 @@ EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
            "fwpkm_retrieve_backward", "fwpkm_forward_seq_backward", "fwpkm_forward_seq_usage",
            "fwpkm_usage_metrics",
            "fwpkm_stream_state_bytes", "fwpkm_stream_step", "fwpkm_stream_flush",
-           "fwpkm_timing_enable", "fwpkm_timing_read")
+           "fwpkm_release_streams", "fwpkm_timing_enable", "fwpkm_timing_read")
 
 # kernel families of fwpkm_timing_read, in fwpkm_kernel order
 KERNELS = ("knorm", "score_select", "gather", "resid", "sort", "scatter", "pbar",
@@ -97,12 +97,13 @@ def load(path: str = LIB_PATH):
         lib.fwpkm_retrieve_backward.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.fwpkm_forward_seq_backward.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_stream_flush.argtypes = [C, i32, P, P, P, P, P, SP, P, sz, P]
+        lib.fwpkm_release_streams.argtypes = []
         lib.fwpkm_timing_enable.argtypes = [i32]
         lib.fwpkm_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq,
                   lib.fwpkm_stream_state_bytes, lib.fwpkm_stream_step, lib.fwpkm_stream_flush,
                   lib.fwpkm_forward_seq_usage, lib.fwpkm_usage_metrics, lib.fwpkm_retrieve_backward,
-                  lib.fwpkm_forward_seq_backward,
+                  lib.fwpkm_forward_seq_backward, lib.fwpkm_release_streams,
                   lib.fwpkm_timing_enable, lib.fwpkm_timing_read):
             f.restype = ctypes.c_int
         _lib = lib
@@ -116,6 +117,11 @@ def _check(rc: int):
 
 def abi_version() -> int:
     return int(load().fwpkm_abi_version())
+
+
+def release_streams() -> None:
+    """Destroy the streams and events fwpkm_forward_seq made for this thread."""
+    _check(load().fwpkm_release_streams())
 
 
 def timing_enable(on: bool = True) -> None:
@@ -174,10 +180,33 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _workspace(cfg, B, T, ws, device):
-    """The caller's workspace (the library checks its size), or a new one."""
+def _new(fresh, shape, dtype, device):
+    """A tensor this binding allocates for a call (listed in `fresh`)."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    fresh.append(t)
+    return t
+
+
+def _mine(stream, fresh):
+    """Tensors this binding allocated (on torch's current stream) for a call
+    enqueued on another `stream`: tell the caching allocator that `stream`
+    uses them, so a block freed when the call returns (the workspace) or
+    later (an output) is not handed to new work before `stream` is done
+    with it."""
+    if stream is None or not fresh:
+        return
+    ts = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if ts.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in fresh:
+        t.record_stream(ts)
+
+
+def _workspace(cfg, B, T, ws, device, fresh):
+    """The caller's workspace (the library checks its size), or a new one
+    (listed in `fresh`)."""
     if ws is None:
-        ws = torch.empty(max(workspace_bytes(cfg, B, T), 256), dtype=torch.uint8, device=device)
+        ws = _new(fresh, (max(workspace_bytes(cfg, B, T), 256),), torch.uint8, device)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -192,21 +221,23 @@ def fwpkm_retrieve(cfg: FwpkmConfig, q, v, g, K1, K2, V, o=None, vhat=None, idx=
     _dev(q, "q", sd, (B, T, H, dq)); _dev(v, "v", sd, (B, T, dv)); _dev(g, "g", torch.float32, (B, T))
     _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
     _dev(V, "V", sd, (B, cfg.N, dv))
-    o = torch.empty((B, T, dv), dtype=torch.float32, device=dev) if o is None else o
+    fresh = []
+    o = _new(fresh, (B, T, dv), torch.float32, dev) if o is None else o
     if vhat is None and "vhat" in want:
-        vhat = torch.empty((B, T, dv), dtype=torch.float32, device=dev)
+        vhat = _new(fresh, (B, T, dv), torch.float32, dev)
     if idx is None and "idx" in want:
-        idx = torch.empty((B, T, H, k), dtype=torch.int32, device=dev)
+        idx = _new(fresh, (B, T, H, k), torch.int32, dev)
     if w is None and "w" in want:
-        w = torch.empty((B, T, H, k), dtype=torch.float32, device=dev)
+        w = _new(fresh, (B, T, H, k), torch.float32, dev)
     _dev(o, "o", torch.float32, (B, T, dv))
     if vhat is not None: _dev(vhat, "vhat", torch.float32, (B, T, dv))
     if idx is not None: _dev(idx, "idx", torch.int32, (B, T, H, k))
     if w is not None: _dev(w, "w", torch.float32, (B, T, H, k))
-    ws, wsb = _workspace(cfg, B, T, ws, dev)
+    ws, wsb = _workspace(cfg, B, T, ws, dev, fresh)
     c = _cfg(cfg)
     _check(load().fwpkm_retrieve(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2), _ptr(V),
                                  _ptr(o), _ptr(vhat), _ptr(idx), _ptr(w), _ptr(ws), wsb, _stream(stream)))
+    _mine(stream, fresh)
     return {"o": o, "vhat": vhat, "idx": idx, "w": w}
 
 
@@ -223,15 +254,17 @@ def fwpkm_retrieve_backward(cfg: FwpkmConfig, q, v, g, K1, K2, V, idx, w, dO, dq
     _dev(V, "V", sd, (B, cfg.N, dvd))
     _dev(idx, "idx", torch.int32, (B, T, H, k)); _dev(w, "w", torch.float32, (B, T, H, k))
     _dev(dO, "dO", torch.float32, (B, T, dvd))
-    dq = torch.empty((B, T, H, dqd), dtype=torch.float32, device=dev) if dq is None else dq
-    dv = torch.empty((B, T, dvd), dtype=torch.float32, device=dev) if dv is None else dv
-    dg = torch.empty((B, T), dtype=torch.float32, device=dev) if dg is None else dg
+    fresh = []
+    dq = _new(fresh, (B, T, H, dqd), torch.float32, dev) if dq is None else dq
+    dv = _new(fresh, (B, T, dvd), torch.float32, dev) if dv is None else dv
+    dg = _new(fresh, (B, T), torch.float32, dev) if dg is None else dg
     _dev(dq, "dq", torch.float32, (B, T, H, dqd)); _dev(dv, "dv", torch.float32, (B, T, dvd))
     _dev(dg, "dg", torch.float32, (B, T))
     c = _cfg(cfg)
     _check(load().fwpkm_retrieve_backward(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2),
                                           _ptr(V), _ptr(idx), _ptr(w), _ptr(dO), _ptr(dq), _ptr(dv), _ptr(dg),
                                           _stream(stream)))
+    _mine(stream, fresh)
     return {"dq": dq, "dv": dv, "dg": dg}
 
 
@@ -250,11 +283,13 @@ def fwpkm_chunk_update(cfg: FwpkmConfig, q, g, tgt, n_tgt: int, idx, w, vhat, K1
     _dev(V, "V", sd, (B, cfg.N, dv))
     if n_read is not None:
         _dev(n_read, "n_read", torch.int32, (B, cfg.N))
-    ws, wsb = _workspace(cfg, B, Tc, ws, g.device)
+    fresh = []
+    ws, wsb = _workspace(cfg, B, Tc, ws, g.device, fresh)
     c = _cfg(cfg)
     _check(load().fwpkm_chunk_update(ctypes.byref(c), B, Tc, int(n_tgt), _ptr(q), _ptr(g),
                                      _ptr(tgt) if n_tgt > 0 else None, _ptr(idx), _ptr(w), _ptr(vhat),
                                      _ptr(K1), _ptr(K2), _ptr(V), _ptr(n_read), _ptr(ws), wsb, _stream(stream)))
+    _mine(stream, fresh)
     return n_read
 
 
@@ -272,13 +307,14 @@ def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_n
         _dev(v_next, "v_next", sd, (B, dv))
     _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
     _dev(V, "V", sd, (B, cfg.N, dv))
-    o = torch.empty((B, T, dv), dtype=torch.float32, device=dev) if o is None else o
+    fresh = []
+    o = _new(fresh, (B, T, dv), torch.float32, dev) if o is None else o
     _dev(o, "o", torch.float32, (B, T, dv))
     if vhat is None and want_vhat:
-        vhat = torch.empty((B, T, dv), dtype=torch.float32, device=dev)
+        vhat = _new(fresh, (B, T, dv), torch.float32, dev)
     if vhat is not None:
         _dev(vhat, "vhat", torch.float32, (B, T, dv))
-    ws, wsb = _workspace(cfg, B, T, ws, dev)
+    ws, wsb = _workspace(cfg, B, T, ws, dev, fresh)
     c = _cfg(cfg)
     if usage is None:
         _check(load().fwpkm_forward_seq(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
@@ -289,6 +325,7 @@ def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_n
         _check(load().fwpkm_forward_seq_usage(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
                                               _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat),
                                               _ptr(usage), _ptr(ws), wsb, _stream(stream)))
+    _mine(stream, fresh)
     return {"o": o, "vhat": vhat}
 
 
@@ -307,15 +344,17 @@ def fwpkm_forward_seq_backward(cfg: FwpkmConfig, q, v, g, K1, K2, V, dO, passes:
     _dev(K1, "K1", sd, (B, H, cfg.n, dqd // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dqd // 2))
     _dev(V, "V", sd, (B, cfg.N, dvd))
     _dev(dO, "dO", torch.float32, (B, T, dvd))
-    dq = torch.empty((B, T, H, dqd), dtype=torch.float32, device=dev)
-    dv = torch.empty((B, T, dvd), dtype=torch.float32, device=dev)
-    dg = torch.empty((B, T), dtype=torch.float32, device=dev)
-    o = torch.empty((B, T, dvd), dtype=torch.float32, device=dev) if want_o else None
-    ws, wsb = _workspace(cfg, B, T, ws, dev)
+    fresh = []
+    dq = _new(fresh, (B, T, H, dqd), torch.float32, dev)
+    dv = _new(fresh, (B, T, dvd), torch.float32, dev)
+    dg = _new(fresh, (B, T), torch.float32, dev)
+    o = _new(fresh, (B, T, dvd), torch.float32, dev) if want_o else None
+    ws, wsb = _workspace(cfg, B, T, ws, dev, fresh)
     c = _cfg(cfg)
     _check(load().fwpkm_forward_seq_backward(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
                                              _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(dO), _ptr(dq),
                                              _ptr(dv), _ptr(dg), _ptr(o), _ptr(ws), wsb, _stream(stream)))
+    _mine(stream, fresh)
     return {"dq": dq, "dv": dv, "dg": dg, "o": o}
 
 
@@ -324,14 +363,16 @@ def fwpkm_usage_metrics(cfg: FwpkmConfig, usage, reset: bool = False, metrics=No
     (coverage, collision, KLD, reads) per sequence; reset zeroes usage."""
     B = usage.shape[0]
     _dev(usage, "usage", torch.int32, (B, cfg.N))
+    fresh = []
     if metrics is None:
-        metrics = torch.empty((B, 4), dtype=torch.float64, device=usage.device)
+        metrics = _new(fresh, (B, 4), torch.float64, usage.device)
     _dev(metrics, "metrics", torch.float64, (B, 4))
     if ws is None:
-        ws = torch.empty(2048 * B, dtype=torch.uint8, device=usage.device)
+        ws = _new(fresh, (2048 * B,), torch.uint8, usage.device)
     c = _cfg(cfg)
     _check(load().fwpkm_usage_metrics(ctypes.byref(c), B, _ptr(usage), _ptr(metrics), 1 if reset else 0, _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)))
+    _mine(stream, fresh)
     return metrics
 
 
@@ -364,19 +405,21 @@ def fwpkm_stream_step(cfg: FwpkmConfig, q, v, g, K1, K2, V, state, pos: StreamPo
     _dev(state, "state", torch.uint8, (state.numel(),))
     if state.numel() < stream_state_bytes(cfg, B):
         raise ValueError("state is smaller than stream_state_bytes()")
-    o = torch.empty((B, T, dv), dtype=torch.float32, device=dev) if o is None else o
+    fresh = []
+    o = _new(fresh, (B, T, dv), torch.float32, dev) if o is None else o
     _dev(o, "o", torch.float32, (B, T, dv))
     if vhat is None and want_vhat:
-        vhat = torch.empty((B, T, dv), dtype=torch.float32, device=dev)
+        vhat = _new(fresh, (B, T, dv), torch.float32, dev)
     if vhat is not None:
         _dev(vhat, "vhat", torch.float32, (B, T, dv))
     if usage is not None:
         _dev(usage, "usage", torch.int32, (B, cfg.N))
-    ws, wsb = _workspace(cfg, B, cfg.chunk, ws, dev)
+    ws, wsb = _workspace(cfg, B, cfg.chunk, ws, dev, fresh)
     c = _cfg(cfg)
     _check(load().fwpkm_stream_step(ctypes.byref(c), B, T, _ptr(q), _ptr(v), _ptr(g), _ptr(K1), _ptr(K2), _ptr(V),
                                     _ptr(o), _ptr(vhat), _ptr(usage), _ptr(state), ctypes.byref(pos), _ptr(ws), wsb,
                                     _stream(stream)))
+    _mine(stream, fresh)
     return {"o": o, "vhat": vhat}
 
 
@@ -390,7 +433,9 @@ def fwpkm_stream_flush(cfg: FwpkmConfig, K1, K2, V, state, pos: StreamPos, v_nex
     _dev(state, "state", torch.uint8, (state.numel(),))
     if v_next is not None:
         _dev(v_next, "v_next", sd, (B, dv))
-    ws, wsb = _workspace(cfg, B, cfg.chunk, ws, V.device)
+    fresh = []
+    ws, wsb = _workspace(cfg, B, cfg.chunk, ws, V.device, fresh)
     c = _cfg(cfg)
     _check(load().fwpkm_stream_flush(ctypes.byref(c), B, _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(state),
                                      ctypes.byref(pos), _ptr(ws), wsb, _stream(stream)))
+    _mine(stream, fresh)

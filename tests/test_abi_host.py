@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_empty_error():
-    assert fwpkm.abi_version() == 2
+    assert fwpkm.abi_version() == 3
     assert fwpkm.load().fwpkm_last_error() is not None
 
 
@@ -234,3 +234,31 @@ def test_forward_seq_backward_rejects_before_launch():
                fake, None, fake, fake, None, fake, 1 << 30, None) == fwpkm.EINVAL
     assert _rc("fwpkm_forward_seq_backward", ctypes.byref(c), 1, 4, 0, fake, fake, fake, None, fake, fake, fake,
                fake, fake, fake, fake, None, fake, 1 << 30, None) == fwpkm.EINVAL  # passes = 0
+
+
+def _raw_ws(cfg, B, T):
+    c = fwpkm.cfg_struct(cfg)
+    out = ctypes.c_size_t(0)
+    assert _rc("fwpkm_workspace_bytes", ctypes.byref(c), B, T, ctypes.byref(out)) == fwpkm.OK
+    return out.value
+
+
+def test_debug_overrides_need_the_debug_switch(monkeypatch):
+    """FWPKM_SCORE_PATH=rows sizes the workspace for whole rows of distances,
+    but only while FWPKM_DEBUG is "1"."""
+    cfg = FwpkmConfig(n=256, heads=4, d_q=128, d_v=64, k_half=16, k=16, chunk=256)
+    B, T = 8, 1024
+    monkeypatch.delenv("FWPKM_SCORE_PATH", raising=False)
+    monkeypatch.setenv("FWPKM_DEBUG", "1")
+    base = _raw_ws(cfg, B, T)
+    monkeypatch.setenv("FWPKM_SCORE_PATH", "rows")
+    assert _raw_ws(cfg, B, T) > base
+    monkeypatch.setenv("FWPKM_DEBUG", "0")
+    assert _raw_ws(cfg, B, T) == base
+    monkeypatch.delenv("FWPKM_DEBUG")
+    assert _raw_ws(cfg, B, T) == base
+
+
+def test_release_streams_with_nothing_to_release():
+    assert _rc("fwpkm_release_streams") == fwpkm.OK
+    assert _rc("fwpkm_release_streams") == fwpkm.OK

@@ -106,3 +106,46 @@ def test_caller_side_stream(path):
     torch.cuda.synchronize()
     for k, x in got.items():
         assert torch.equal(x.cpu().view(-1).view(torch.uint8), ref[k].view(-1).view(torch.uint8)), k
+
+
+def test_side_stream_workspace_not_reused_early(monkeypatch):
+    """A call on a side stream with the workspace and outputs allocated by
+    the binding: when the call returns the binding drops its workspace.  A
+    block of the same size allocated at once on the current stream (which
+    does not wait for the side stream, still busy) must not be any block the
+    call uses, or work on the current stream could overwrite it while the
+    call still runs.  The blocks are compared by address; nothing is written
+    to them."""
+    os.environ["FWPKM_SCORE_PATH"] = "sweep"
+    cfg, B, T = C(), 4, 2048
+    ref = run(cfg, B, T, 1, 63, False, False)
+    q, v, g, _ = make_tokens(cfg, B, T, 63, "gauss")
+    K1, K2, V = (x.to(DEV).contiguous() for x in make_state(cfg, B, 63, std=0.5))
+    qd, vd, gd = (x.to(DEV).contiguous() for x in (q, v, g))
+    taken = []
+    new = fwpkm._new
+
+    def spy(fresh, shape, dtype, device):
+        t = new(fresh, shape, dtype, device)
+        taken.append((t.data_ptr(), t.numel() * t.element_size()))
+        return t
+
+    monkeypatch.setattr(fwpkm, "_new", spy)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)  # keep the side stream busy past the call's return
+    out = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, K1, K2, V, stream=side, want_vhat=True)
+    assert taken, "the binding allocated nothing"
+    later = [torch.empty(nb, dtype=torch.uint8, device=DEV) for _, nb in taken]
+    busy = not side.query()
+    for t in later:
+        for p, nb in taken:
+            assert not (p <= t.data_ptr() < p + nb), "a block of the running call was handed out again"
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    print(f"  side stream still busy at the check: {busy}")
+    got = {"o": out["o"], "vhat": out["vhat"], "K1": K1, "K2": K2, "V": V}
+    for k, x in got.items():
+        assert torch.equal(x.cpu().view(-1).view(torch.uint8), ref[k].view(-1).view(torch.uint8)), k
+    del later
