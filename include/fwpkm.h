@@ -274,6 +274,29 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fwpkm_forward_seq for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, hosts that forbid
+ * allocation): the same computation, the same arguments without the
+ * workspace, the same results bit for bit.  Its scratch is a fixed device
+ * array of FWPKM_STATIC_SCRATCH_BYTES inside the library, one per GPU it
+ * runs on (the device of `stream`), held until the process ends; the
+ * call allocates and frees nothing and creates no stream or event: every
+ * kernel runs on `stream`, one at a time (the single-stream schedule).
+ * Returns FWPKM_EWORKSPACE, before enqueueing anything, when the call would
+ * need more scratch than that (fwpkm_workspace_bytes(cfg, B, min(T, C))
+ * bounds what it needs), and FWPKM_EINVAL while kernel timing is on.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * behind: calls that overlap on one GPU (on different streams, or from
+ * different threads) race; calls ordered on one stream do not.  The scratch
+ * needs no initialisation.
+ */
+#define FWPKM_STATIC_SCRATCH_BYTES ((size_t)512 << 20)
+int fwpkm_forward_seq_static(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
+                             const void* q, const void* v, const float* g, const void* v_next,
+                             void* K1, void* K2, void* V,
+                             float* o, float* vhat, void* stream);
+
+/*
  * Gradients of fwpkm_forward_seq's output o (of its last pass) with respect to
  * q, v and g, for the upstream gradient dO[B][T][d_v] float, by replay: call
  * it with the state (K1, K2, V) that fwpkm_forward_seq started from.  It runs

@@ -180,6 +180,41 @@ hipError_t aux_streams(hipStream_t caller, Aux** out) {
     return hipSuccess;
 }
 
+// Scratch of fwpkm_forward_seq_static, for callers that cannot allocate:
+// a file-scope device array, one copy per GPU the library runs on, held
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a handle): static_scratch() resolves each
+// device's copy once, with that device current, and every later use goes
+// through the resolved pointer.
+constexpr size_t kStaticScratchBytes = FWPKM_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(hipStream_t caller, void** out) {
+    static std::mutex mu;
+    static void* per_dev[64] = {};
+    int dev = 0;
+    hipError_t e = stream_device(caller, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!per_dev[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        per_dev[dev] = p;
+    }
+    *out = per_dev[dev];
+    return hipSuccess;
+}
+
 // Environment overrides for tests, sweeps and profiling, read only while
 // FWPKM_DEBUG=1 (otherwise NULL): FWPKM_SINGLE_STREAM, FWPKM_SCORE_PATH,
 // FWPKM_KGRAD_SPLIT, FWPKM_DECODE.
@@ -869,7 +904,8 @@ struct SeqGrad {
 
 int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q, const void* v,
                      const float* g, const void* v_next, void* K1, void* K2, void* V, float* o, float* vhat,
-                     int32_t* usage, const SeqGrad* grad, void* ws, size_t ws_bytes, void* stream) {
+                     int32_t* usage, const SeqGrad* grad, void* ws, size_t ws_bytes, void* stream,
+                     bool use_static = false) {
     Plan p;
     int rc = make_plan(cfg, &p);
     if (rc) return rc;
@@ -884,6 +920,13 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     if (static_cast<int64_t>(B) * Cm * p.H * p.k > 2147483647LL) return fail(FWPKM_EUNSUPPORTED, "B*C*heads*k too large");
     const Layout L = layout(p, B, Cm, true, true, 2);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (use_static) {
+        if (L.total > kStaticScratchBytes)
+            return fail(FWPKM_EWORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                        L.total, kStaticScratchBytes);
+        HIP_TRY(static_scratch(s, &ws));
+        ws_bytes = kStaticScratchBytes;
+    }
     rc = check_ws(ws, ws_bytes, L.total);
     if (rc) return rc;
     // The key path (scoring, selection, usage statistics, key step) stays on
@@ -901,14 +944,15 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
     // concurrency slows it, 7.99 -> 8.15 ms, so there they stay.  The
     // slot/weight lists and the sort buffers alternate between two sets, so
     // chunk c+1's selection and sort only wait for chunk c-1's write.  With
-    // kernel timing on, or with the debug
+    // kernel timing on, in fwpkm_forward_seq_static, or with the debug
     // override FWPKM_SINGLE_STREAM=1, everything stays on `stream` (same
     // work, one kernel at a time) and no stream or event of the library is
     // used.
     const char* env_single = debug_env("FWPKM_SINGLE_STREAM");
     // the replay for gradients keeps every kernel in order on one stream:
     // a chunk's gradient reads V and K before that chunk's write
-    const bool single = timing().on || (env_single && env_single[0] == '1') || grad != nullptr;
+    const bool single =
+        use_static || timing().on || (env_single && env_single[0] == '1') || grad != nullptr;
     Aux none;  // no events: every record and wait below is skipped when single
     Aux* ax = &none;
     if (!single) HIP_TRY(aux_streams(s, &ax));
@@ -1087,6 +1131,15 @@ int fwpkm_forward_seq_backward(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32
     const SeqGrad grad{dO, dq, dv, dg};
     return forward_seq_impl(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, nullptr, nullptr, &grad, ws, ws_bytes,
                             stream);
+}
+
+int fwpkm_forward_seq_static(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes, const void* q,
+                             const void* v, const float* g, const void* v_next, void* K1, void* K2, void* V,
+                             float* o, float* vhat, void* stream) {
+    // kernel timing creates its events on demand: not in a call that must not allocate
+    if (timing().on) return fail(FWPKM_EINVAL, "fwpkm_forward_seq_static does not run while kernel timing is on");
+    return forward_seq_impl(cfg, B, T, passes, q, v, g, v_next, K1, K2, V, o, vhat, nullptr, nullptr, nullptr, 0,
+                            stream, true);
 }
 
 int fwpkm_release_streams(void) {

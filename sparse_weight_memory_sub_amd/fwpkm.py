@@ -28,7 +28,7 @@ EXPORTS = ("fwpkm_abi_version", "fwpkm_last_error", "fwpkm_workspace_bytes",
            "fwpkm_retrieve_backward", "fwpkm_forward_seq_backward", "fwpkm_forward_seq_usage",
            "fwpkm_usage_metrics",
            "fwpkm_stream_state_bytes", "fwpkm_stream_step", "fwpkm_stream_flush",
-           "fwpkm_release_streams", "fwpkm_timing_enable", "fwpkm_timing_read")
+           "fwpkm_forward_seq_static", "fwpkm_release_streams", "fwpkm_timing_enable", "fwpkm_timing_read")
 
 # kernel families of fwpkm_timing_read, in fwpkm_kernel order
 KERNELS = ("knorm", "score_select", "gather", "resid", "sort", "scatter", "pbar",
@@ -97,13 +97,14 @@ def load(path: str = LIB_PATH):
         lib.fwpkm_retrieve_backward.argtypes = [C, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.fwpkm_forward_seq_backward.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         lib.fwpkm_stream_flush.argtypes = [C, i32, P, P, P, P, P, SP, P, sz, P]
+        lib.fwpkm_forward_seq_static.argtypes = [C, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
         lib.fwpkm_release_streams.argtypes = []
         lib.fwpkm_timing_enable.argtypes = [i32]
         lib.fwpkm_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         for f in (lib.fwpkm_workspace_bytes, lib.fwpkm_retrieve, lib.fwpkm_chunk_update, lib.fwpkm_forward_seq,
                   lib.fwpkm_stream_state_bytes, lib.fwpkm_stream_step, lib.fwpkm_stream_flush,
                   lib.fwpkm_forward_seq_usage, lib.fwpkm_usage_metrics, lib.fwpkm_retrieve_backward,
-                  lib.fwpkm_forward_seq_backward, lib.fwpkm_release_streams,
+                  lib.fwpkm_forward_seq_backward, lib.fwpkm_release_streams, lib.fwpkm_forward_seq_static,
                   lib.fwpkm_timing_enable, lib.fwpkm_timing_read):
             f.restype = ctypes.c_int
         _lib = lib
@@ -325,6 +326,35 @@ def fwpkm_forward_seq(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_n
         _check(load().fwpkm_forward_seq_usage(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
                                               _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat),
                                               _ptr(usage), _ptr(ws), wsb, _stream(stream)))
+    _mine(stream, fresh)
+    return {"o": o, "vhat": vhat}
+
+
+def fwpkm_forward_seq_static(cfg: FwpkmConfig, q, v, g, K1, K2, V, passes: int = 1, v_next=None, o=None,
+                             vhat=None, stream=None, want_vhat: bool = False):
+    """fwpkm_forward_seq with the library's static scratch in place of a
+    workspace (the library allocates nothing; outputs not given are
+    allocated here, by torch).  Returns dict(o, vhat) of the last pass."""
+    sd = cfg.torch_dtype
+    B, T = g.shape
+    H, dq, dv = cfg.heads, cfg.d_q, cfg.d_v
+    dev = g.device
+    _dev(q, "q", sd, (B, T, H, dq)); _dev(v, "v", sd, (B, T, dv)); _dev(g, "g", torch.float32, (B, T))
+    if v_next is not None:
+        _dev(v_next, "v_next", sd, (B, dv))
+    _dev(K1, "K1", sd, (B, H, cfg.n, dq // 2)); _dev(K2, "K2", sd, (B, H, cfg.n, dq // 2))
+    _dev(V, "V", sd, (B, cfg.N, dv))
+    fresh = []
+    o = _new(fresh, (B, T, dv), torch.float32, dev) if o is None else o
+    _dev(o, "o", torch.float32, (B, T, dv))
+    if vhat is None and want_vhat:
+        vhat = _new(fresh, (B, T, dv), torch.float32, dev)
+    if vhat is not None:
+        _dev(vhat, "vhat", torch.float32, (B, T, dv))
+    c = _cfg(cfg)
+    _check(load().fwpkm_forward_seq_static(ctypes.byref(c), B, T, int(passes), _ptr(q), _ptr(v), _ptr(g),
+                                           _ptr(v_next), _ptr(K1), _ptr(K2), _ptr(V), _ptr(o), _ptr(vhat),
+                                           _stream(stream)))
     _mine(stream, fresh)
     return {"o": o, "vhat": vhat}
 

@@ -262,3 +262,15 @@ def test_debug_overrides_need_the_debug_switch(monkeypatch):
 def test_release_streams_with_nothing_to_release():
     assert _rc("fwpkm_release_streams") == fwpkm.OK
     assert _rc("fwpkm_release_streams") == fwpkm.OK
+
+
+def test_static_scratch_refuses_calls_beyond_it():
+    """fwpkm_forward_seq_static returns FWPKM_EWORKSPACE, before touching the
+    GPU, for a call needing more than FWPKM_STATIC_SCRATCH_BYTES."""
+    wl = WORKLOADS["million"]
+    c = fwpkm.cfg_struct(wl.cfg)
+    P = ctypes.c_void_p(256)
+    rc = _rc("fwpkm_forward_seq_static", ctypes.byref(c), 2 * wl.B, wl.T, 1, P, P, P, None, P, P, P, P, None, None)
+    assert rc == fwpkm.EWORKSPACE
+    msg = fwpkm.load().fwpkm_last_error().decode()
+    assert "static scratch holds 536870912" in msg, msg
