@@ -59,6 +59,9 @@ def parse():
                     help="time fwpkm_forward_seq_backward (replayed pass with gradients w.r.t. q, v, g)")
     ap.add_argument("--usage", action="store_true",
                     help="time forward_seq with row-contribution counting and the addressing metrics")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="measure the HBM rates of random 1 KiB value rows (read; read-modify-write at several "
+                         "depths, from registers and staged in LDS) and of a sequential copy")
     return ap.parse_args()
 
 
@@ -83,6 +86,26 @@ def algorithmic(cfg, B, Tc, n_tgt, U, passes_write_o=True):
     kgrad_flops = 2.0 * 2 * B * H * 2 * n * Tc * dh  # distance recompute + a^T q
     return {"gather": gather, "scatter": scatter, "score_select": score_flops,
             "score_rowstat": score_flops, "kgrad": kgrad_flops}
+
+
+def layer_bytes_per_token(cfg, U):
+    """Algorithmic HBM bytes per token of the whole layer step (retrieval and
+    chunk write), with U unique value rows written per chunk and sequence:
+    the compulsory traffic the roofline of the layer's tokens/s is priced on."""
+    es = 2 if cfg.store == "bf16" else 4
+    H, k, dv, dq, n, C = cfg.heads, cfg.k, cfg.d_v, cfg.d_q, cfg.n, cfg.chunk
+    retrieve = (H * k * dv * es          # selected value rows
+                + H * dq * es            # q
+                + dv * es + 4            # v and the gate
+                + 4 * dv + 4 * dv        # o, and v_hat / residual
+                + 8 * H * k              # slot ids and weights
+                + H * n * dq * es / C)   # both codebooks, read once per chunk
+    update = (4 * dv + dv * es           # residual and target in
+              + 2 * U * dv * es / C      # read-modify-write of the written rows
+              + 16 * H * k               # sorted read list
+              + H * dq * es              # q again for the key step
+              + 2 * H * n * dq * es / C) # codebooks read and written
+    return retrieve + update
 
 
 def src_hash(*names):
@@ -318,6 +341,141 @@ def backward_bench(args, cfg, wl, B, T, q, v, g, K1, K2, V):
     print(json.dumps(result), flush=True)
 
 
+def ceiling_bench(args):
+    """Rates HBM sustains for the value rows' access patterns: 16 sequences'
+    value tables of 2^20 rows of 1 KiB (16 GiB), with 62080 distinct random
+    rows per table, the rows the 2^20-slot layer writes per chunk (about a
+    GB).  Sorted: each table's rows in ascending order, 64 consecutive rows
+    per wavefront (the value write's order); shuffled: the same rows in
+    random order (the gather's).  Prints one JSON line."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "sparse_weight_memory_sub_amd", "probe", "libfwpkm_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with `python -m sparse_weight_memory_sub_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.fwpkm_probe_rows.argtypes = [i32, i32, P, i32, i32, P, P, P, i32, ctypes.POINTER(i32)]
+    lib.fwpkm_probe_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    dev = torch.device("cuda:0")
+    seqs, rows_per, U, per = 16, 1 << 20, 62080, 64
+    base = torch.empty(seqs * rows_per * 1024, dtype=torch.uint8, device=dev)
+    gen = torch.Generator().manual_seed(11)
+    sorted_rows = torch.cat([torch.randperm(rows_per, generator=gen)[:U].sort().values + s * rows_per
+                             for s in range(seqs)]).to(torch.int32)
+    shuffled = sorted_rows[torch.randperm(sorted_rows.numel(), generator=gen)]
+    nrows = sorted_rows.numel()
+    assert int(sorted_rows.max()) < base.numel() // 1024 and int(sorted_rows.min()) >= 0
+    lists = {"sorted": sorted_rows.to(dev), "shuffled": shuffled.to(dev)}
+    waves = (nrows + per - 1) // per
+    out = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            fn()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / reps
+
+    def rows_fn(mode, R, lst):
+        def f():
+            rc = lib.fwpkm_probe_rows(mode, R, ctypes.c_void_p(lst.data_ptr()), nrows, per,
+                                      ctypes.c_void_p(base.data_ptr()), ctypes.c_void_p(out.data_ptr()), sp, 0,
+                                      None)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: hip error {rc}")
+        return f
+
+    names = {0: "read", 1: "rmw", 2: "rmw-pipelined", 3: "rmw-lds"}
+    depths = {0: (1, 2, 4, 8, 16), 1: (1, 2, 4, 8, 16), 2: (1, 2, 4, 8), 3: (4, 8, 16, 32)}
+    table = []
+    for order in ("sorted", "shuffled"):
+        for mode in (0, 1, 2, 3):
+            for R in depths[mode]:
+                regs = ctypes.c_int(0)
+                lib.fwpkm_probe_rows(mode, R, None, 0, per, None, None, None, 1, ctypes.byref(regs))
+                ms = timed(rows_fn(mode, R, lists[order]))
+                nbytes = nrows * 1024 * (1 if mode == 0 else 2)
+                gbs = nbytes / (ms / 1e3) / 1e9
+                table.append({"order": order, "pattern": names[mode], "rows_in_flight": R, "vgprs": regs.value,
+                              "ms": ms, "GB/s": gbs})
+                log(f"{order:8s} {names[mode]:14s} R={R:2d} vgprs={regs.value:3d}: {ms * 1e3:7.1f} us, {gbs:7.1f} GB/s")
+    half = 1 << 30
+
+    def copy():
+        rc = lib.fwpkm_probe_copy(ctypes.c_void_p(base.data_ptr()), ctypes.c_void_p(base.data_ptr() + half), half, sp)
+        if rc != 0:
+            raise RuntimeError(f"copy launch failed: hip error {rc}")
+
+    ms = timed(copy)
+    copy_gbs = 2 * half / (ms / 1e3) / 1e9
+    log(f"sequential copy of 1 GiB: {ms * 1e3:.1f} us, {copy_gbs:.1f} GB/s (read + write)")
+    best = {}
+    for r in table:
+        key = (r["order"], "read" if r["pattern"] == "read" else "rmw")
+        if key not in best or r["GB/s"] > best[key]["GB/s"]:
+            best[key] = r
+    result = {"metric": "HBM GB/s of random 1 KiB value rows (ceilings of the value-row kernels)",
+              "value": best[("sorted", "rmw")]["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": 5, "warmup": 2,
+              "higher_is_better": True, "data": "synthetic",
+              "config": {"workload": "value-row-ceiling", "tables": seqs, "rows_per_table": rows_per,
+                         "row_bytes": 1024, "rows_touched_per_table": U, "rows_per_wavefront": per,
+                         "footprint_bytes": base.numel()},
+              "sequential_copy_GBs": copy_gbs,
+              "best": {f"{k[0]}-{k[1]}": v for k, v in best.items()}, "table": table}
+    print(json.dumps(result), flush=True)
+
+
+GOLDEN_RECALL = os.path.join(ROOT, "tests", "golden", "long_recall.json")
+
+
+def planted_recall_report(cfg, wl, passes, q, v, g, start_state, extra):
+    """One fwpkm_forward_seq of `passes` passes from the workload's initial
+    state; recall of the planted bindings at their first and last occurrence
+    in the last pass, beside the CPU oracle's recall for the same inputs and
+    pass count (stored by tests/golden/make_long_recall.py, when it was made
+    for this workload)."""
+    import torch
+    from sparse_weight_memory_sub_amd import fwpkm
+    from sparse_weight_memory_sub_amd.workloads import planted_recall
+
+    K1, K2, V = (x.clone() for x in start_state)
+    out = fwpkm.fwpkm_forward_seq(cfg, q, v, g, K1, K2, V, passes=passes, want_vhat=True)
+    torch.cuda.synchronize()
+    pv, pos = extra["plant_v"], extra["plant_pos"]
+    vh = out["vhat"][0]
+    first = vh[pos.min(1).values.to(vh.device)].cpu()
+    last = vh[pos.max(1).values.to(vh.device)].cpu()
+    rf, af, _ = planted_recall(first, pv)
+    rl, al, _ = planted_recall(last, pv)
+    rep = {"passes": passes, "bindings": int(pv.shape[0]), "reps": int(pos.shape[1]),
+           "gpu_first": rf, "gpu_last": rl, "oracle_first": None, "oracle_last": None,
+           "definition": "share of bindings whose v_hat at the binding's first (last) occurrence in the last "
+                         "pass is closest in cosine to its own z-scored value among all bindings' values"}
+    try:
+        gold = json.load(open(GOLDEN_RECALL))
+        ok = gold.get("T") == wl.T and gold.get("seed") == wl.seed and str(passes) in gold["passes"]
+    except (OSError, ValueError, KeyError):
+        ok = False
+    if ok:
+        gp = gold["passes"][str(passes)]
+        rep["oracle_first"], rep["oracle_last"] = gp["recall_first"], gp["recall_last"]
+        rep["agree_first"] = sum(a == b for a, b in zip(af, gp["argmax_first"]))
+        rep["agree_last"] = sum(a == b for a, b in zip(al, gp["argmax_last"]))
+    log(f"recall after {passes} pass(es): GPU first {rf:.4f} last {rl:.4f}; oracle first "
+        f"{rep['oracle_first']} last {rep['oracle_last']}")
+    return rep
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -331,6 +489,9 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.ceiling:
+        ceiling_bench(args)
+        return
     wl = WORKLOADS[args.workload]
     cfg, B, T = wl.cfg, wl.B, wl.T
     if args.score or args.no_gate_weight:
@@ -343,8 +504,12 @@ def main():
     torch.cuda.set_device(dev)
 
     t0 = time.time()
-    q, v, g, _ = make_tokens(cfg, B, T, wl.seed, wl.kind)
-    K1, K2, V = make_state(cfg, B, wl.seed, device=dev)
+    q, v, g, extra = make_tokens(cfg, B, T, wl.seed, wl.kind)
+    planted = wl.kind == "planted"
+    # the planted workload's state is drawn on the host, as the oracle's
+    # recall run draws it, so the two recalls start from the same bits
+    K1, K2, V = make_state(cfg, B, wl.seed, device="cpu" if planted else dev)
+    K1, K2, V = (x.to(dev) for x in (K1, K2, V))
     q, v, g = q.to(dev), v.to(dev), g.to(dev)
     log(f"workload {wl.name}: B={B} T={T} N={cfg.N} H={cfg.heads} d_q={cfg.d_q} d_v={cfg.d_v} "
         f"k={cfg.k} C={cfg.chunk} {cfg.store}; inputs ready in {time.time() - t0:.1f}s")
@@ -361,8 +526,9 @@ def main():
 
     want_cpu = not (args.no_cpu_baseline or args.profile_only)
     if want_cpu:
-        ns = args.cpu_seqs or 5
+        ns = min(args.cpu_seqs or 5, B)
         pristine = [x[:ns].cpu() for x in (K1, K2, V)]
+    start_state = [x.clone() for x in (K1, K2, V)] if planted and not args.profile_only else None
 
     o = torch.empty((B, T, cfg.d_v), dtype=torch.float32, device=dev)
     ws = torch.empty(fwpkm.workspace_bytes(cfg, B, T), dtype=torch.uint8, device=dev)
@@ -472,17 +638,29 @@ def main():
                               "unit": "TFLOP/s", "frac": d["frac_mfma_peak"],
                               "traffic": traffic_from_profiles(dom, wl.name),
                               "flops_per_launch": d["algorithmic_flops"], "avg_launch_ms": d["avg_ms"]}
+    bpt = layer_bytes_per_token(cfg, U)
+    roof_tps = HBM_PEAK_GBS * 1e9 / bpt
+    result["roofline"]["layer_bytes_per_token"] = bpt
+    result["roofline"]["layer_roofline_tokens_per_s"] = roof_tps
+    result["roofline"]["layer_frac"] = value / roof_tps
     result["kernels"] = kernels
     result["unique_rows_per_chunk_seq"] = U
     result["reads_per_chunk_seq"] = n_tgt * cfg.heads * cfg.k
     rl = result["roofline"]
-    log(f"dominant kernel {dom}: {rl['achieved']:.1f} {rl['unit']} ({100 * rl['frac']:.1f}% of peak); U={U:.0f}")
+    log(f"dominant kernel {dom}: {rl['achieved']:.1f} {rl['unit']} ({100 * rl['frac']:.1f}% of peak); U={U:.0f}; "
+        f"layer {value:.4g} of {roof_tps:.4g} tokens/s at {bpt:.0f} B/token ({100 * rl['layer_frac']:.1f}%)")
+
+    # --- planted bindings: recall after `passes` passes from the initial state ---
+    if start_state is not None:
+        result["recall"] = planted_recall_report(cfg, wl, passes, q, v, g, start_state, extra)
+        del start_state
 
     # --- CPU oracle on a bounded sample of the same workload ---
     if want_cpu:
         import oracle
-        ns = args.cpu_seqs or 5
-        nc = args.cpu_chunks or nchunks
+        ns = min(args.cpu_seqs or 5, B)
+        # about ten seconds of oracle work: the long sequence's first 16 chunks
+        nc = args.cpu_chunks or (min(nchunks, 16) if planted else nchunks)
         qs, vs, gs = (x[:ns].cpu() for x in (q, v, g))
         threads = oracle.num_threads()
         t1 = time.perf_counter()

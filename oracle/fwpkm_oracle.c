@@ -443,10 +443,14 @@ static void memorise_one(const fwo_cfg* c, int32_t Tc, int32_t n_tgt,
  */
 static void address_one(const fwo_cfg* c, int32_t Tc, const double* dist, size_t dist_stride,
                         const void* q_b, size_t q_stride_tok, size_t q_off,
-                        void* Kh, double* p, double* lp, double* m, double* grad) {
+                        void* Kh, double* p, double* lp, double* m, int inner) {
+    /* inner != 0 spreads each loop below over OpenMP threads: every value is
+     * still one thread's sum in the order written, so the result does not
+     * depend on the thread count */
     const int n = c->n, dh = c->d_q / 2;
     const double eps = c->idw_eps;
     const int dot = c->score == FWO_SCORE_DOT;
+    #pragma omp parallel for schedule(static) if(inner)
     for (int t = 0; t < Tc; ++t) {
         const double* d = dist + (size_t)t * dist_stride;
         double smax = -INFINITY;
@@ -458,32 +462,40 @@ static void address_one(const fwo_cfg* c, int32_t Tc, const double* dist, size_t
         for (int i = 0; i < n; ++i) z += exp((dot ? d[i] : -log(eps + d[i])) - smax);
         for (int i = 0; i < n; ++i) p[(size_t)t * n + i] = exp((dot ? d[i] : -log(eps + d[i])) - smax) / z;
     }
+    #pragma omp parallel for schedule(static) if(inner)
     for (int i = 0; i < n; ++i) {
         double s = 0.0;
         for (int t = 0; t < Tc; ++t) s += p[(size_t)t * n + i];
         lp[i] = log(s / Tc);
     }
+    #pragma omp parallel for schedule(static) if(inner)
     for (int t = 0; t < Tc; ++t) {
         double s = 0.0;
         for (int i = 0; i < n; ++i) s += p[(size_t)t * n + i] * lp[i];
         m[t] = s;
     }
-    for (int i = 0; i < n; ++i) {
-        for (int u = 0; u < dh; ++u) grad[u] = 0.0;
-        for (int t = 0; t < Tc; ++t) {
-            const double dLds = p[(size_t)t * n + i] * (lp[i] - m[t]) / Tc;
-            /* ds/dK_i: 2 (q - K_i) / (eps + d) for IDW, q for the dot product */
-            const double scale = dot ? 1.0 : 2.0 / (eps + dist[(size_t)t * dist_stride + i]);
+    #pragma omp parallel if(inner)
+    {
+        double* grad = (double*)malloc(sizeof(double) * (size_t)dh);
+        #pragma omp for schedule(static)
+        for (int i = 0; i < n; ++i) {
+            for (int u = 0; u < dh; ++u) grad[u] = 0.0;
+            for (int t = 0; t < Tc; ++t) {
+                const double dLds = p[(size_t)t * n + i] * (lp[i] - m[t]) / Tc;
+                /* ds/dK_i: 2 (q - K_i) / (eps + d) for IDW, q for the dot product */
+                const double scale = dot ? 1.0 : 2.0 / (eps + dist[(size_t)t * dist_stride + i]);
+                for (int u = 0; u < dh; ++u) {
+                    const double qu = ld(q_b, (size_t)t * q_stride_tok + q_off + u, c->store);
+                    const double ku = dot ? 0.0 : ld(Kh, (size_t)i * dh + u, c->store);
+                    grad[u] += dLds * scale * (qu - ku);
+                }
+            }
             for (int u = 0; u < dh; ++u) {
-                const double qu = ld(q_b, (size_t)t * q_stride_tok + q_off + u, c->store);
-                const double ku = dot ? 0.0 : ld(Kh, (size_t)i * dh + u, c->store);
-                grad[u] += dLds * scale * (qu - ku);
+                const size_t ki = (size_t)i * dh + u;
+                st(Kh, ki, c->store, ld(Kh, ki, c->store) - c->lr_k * grad[u]);
             }
         }
-        for (int u = 0; u < dh; ++u) {
-            const size_t ki = (size_t)i * dh + u;
-            st(Kh, ki, c->store, ld(Kh, ki, c->store) - c->lr_k * grad[u]);
-        }
+        free(grad);
     }
 }
 
@@ -541,12 +553,15 @@ static void chunk_write(const fwo_cfg* c, int32_t B, int32_t Tc, int32_t n_tgt,
     }
 
     if (!c->use_addr) return;
-    #pragma omp parallel
+    /* one codebook per thread when there are enough of them; otherwise one
+     * codebook at a time with its loops spread over the threads (the same
+     * arithmetic either way) */
+    const int inner = B * H * 2 < fwo_num_threads();
+    #pragma omp parallel if(!inner)
     {
         double* p = (double*)malloc(sizeof(double) * (size_t)Tc * n);
         double* lp = (double*)malloc(sizeof(double) * (size_t)n);
         double* m = (double*)malloc(sizeof(double) * (size_t)Tc);
-        double* grad = (double*)malloc(sizeof(double) * (size_t)dh);
         #pragma omp for collapse(3) schedule(dynamic, 1)
         for (int b = 0; b < B; ++b)
             for (int h = 0; h < H; ++h)
@@ -555,9 +570,9 @@ static void chunk_write(const fwo_cfg* c, int32_t B, int32_t Tc, int32_t n_tgt,
                     void* Kh = (char*)(half == 0 ? K1 : K2) + (((size_t)b * H + h) * n * dh) * es;
                     address_one(c, Tc, dist, (size_t)H * n,
                                 (const char*)q + (size_t)b * q_seq_stride * es, (size_t)H * dq,
-                                (size_t)h * dq + (size_t)half * dh, Kh, p, lp, m, grad);
+                                (size_t)h * dq + (size_t)half * dh, Kh, p, lp, m, inner);
                 }
-        free(p); free(lp); free(m); free(grad);
+        free(p); free(lp); free(m);
     }
 }
 

@@ -50,13 +50,31 @@ def _compile(src: str, hipcc: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "rows_probe.hip")
+PROBE_OUT = os.path.join(HERE, "probe", "libfwpkm_probe.so")
+
+
+def build_probe(hipcc: str) -> str:
+    """The measurement library of bench.py --ceiling (not part of the layer)."""
+    tmp = PROBE_OUT + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for rows_probe.hip:\n" + r.stderr)
+    os.replace(tmp, PROBE_OUT)
+    return PROBE_OUT
+
+
 def build(verbose: bool = True) -> str:
-    """Compile every HIP source for gfx950 and link libfwpkm.so (always rebuilds)."""
+    """Compile every HIP source for gfx950 and link libfwpkm.so (always
+    rebuilds), and the measurement library of bench.py --ceiling."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", "8"))))
     with cf.ThreadPoolExecutor(jobs) as ex:
+        probe = ex.submit(build_probe, hipcc)
         objs = list(ex.map(lambda s: _compile(s, hipcc), SOURCES))
+        probe.result()
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -200,6 +200,26 @@ def make_tokens(cfg: FwpkmConfig, B: int, T: int, seed: int, kind: str = "gauss"
     return _store(q, cfg), _store(v, cfg), g.float().contiguous(), extra
 
 
+def planted_recall(vhat_at, plant_v, eps: float = 1e-5):
+    """Recall of planted bindings (an evaluation of the 'planted' inputs, not
+    part of the layer): vhat_at[b] is the layer's retrieved value at one
+    occurrence of binding b's query; binding b counts as recalled when its
+    own z-scored value z(v*_b) (per row over d_v, population variance, eps)
+    is the closest in cosine of all bindings' values.  Returns (recall,
+    argmax per binding, margin per binding: cosine to the closest value
+    minus cosine to the runner-up)."""
+    pv = plant_v.double()
+    z = (pv - pv.mean(-1, keepdim=True)) / torch.sqrt(pv.var(-1, unbiased=False, keepdim=True) + eps)
+    zn = z / z.norm(dim=-1, keepdim=True)
+    vh = vhat_at.double()
+    vh = vh / vh.norm(dim=-1, keepdim=True).clamp_min(1e-300)
+    cos = vh @ zn.T
+    top = torch.topk(cos, 2, dim=-1)
+    arg = top.indices[:, 0]
+    hit = arg == torch.arange(pv.shape[0])
+    return float(hit.double().mean()), arg.tolist(), (top.values[:, 0] - top.values[:, 1]).tolist()
+
+
 def make_workload(name: str, device="cpu", state_device=None, B=None, T=None):
     """Inputs of a named workload: dict(q, v, g, K1, K2, V, extra) with the
     per-token tensors on the CPU and the state on `state_device` (default:

@@ -14,14 +14,18 @@ checks sampled outputs that it can compute one by one:
 Value-row writes are compared on the rows the oracle wrote; every other row
 must be bit-unchanged.
 """
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from parity import TIE_REL, close, compare_indices, rtol_for, token_set_match
+from parity import ARITH_K, ARITH_V, TIE_REL, close, compare_indices, rtol_for, token_set_match, ulp_check
 from sparse_weight_memory_sub_amd import fwpkm
-from sparse_weight_memory_sub_amd.workloads import WORKLOADS, make_state, make_tokens
+from sparse_weight_memory_sub_amd.workloads import WORKLOADS, make_state, make_tokens, planted_recall
 
 pytestmark = pytest.mark.gpu
 
@@ -82,10 +86,13 @@ def replay_with_oracle(cfg, q, v, g, K1d, K2d, Vd, n_chunks, v_next=None):
         m = token_set_match(gi, ora["idx"])
         # Every differing list was checked valid within TIE_REL above.  With
         # |q|^2 far above the spread of the distances (the clustered queries of
-        # the 2^20-slot workload) adjacent products are often within 1e-6, so
-        # the count is reported; the bound only catches gross breakage.
-        print(f"  chunk {c}: differing lists {near} (oracle flags {int(ora['tie'].sum())}) of {exact.size}")
-        assert near <= 0.25 * exact.size, f"chunk {c}: {near} near-tie tokens"
+        # the 2^20-slot workload) adjacent products are often within 1e-6: about
+        # 2% of the lists differ there, and more than 5% would mean a change in
+        # the scoring's rounding, not ties.
+        flagged = int(ora["tie"].sum())
+        print(f"  chunk {c}: differing lists {near} (oracle flags {flagged}) of {exact.size}")
+        assert near <= 0.05 * exact.size, (f"chunk {c}: {near} of {exact.size} (token, head) lists differ from "
+                                           f"the oracle's (all valid near-ties; oracle flags {flagged})")
         close(r["w"].cpu().numpy(), ora["w"], 1e-4, mask=exact, what=f"w chunk {c}")
         close(r["o"].cpu().numpy(), ora["o"], 1e-4, mask=m, what=f"o chunk {c}")
         outs.append(r["o"])
@@ -117,9 +124,13 @@ def replay_with_oracle(cfg, q, v, g, K1d, K2d, Vd, n_chunks, v_next=None):
         print(f"  chunk {c}: near ties {near}, rows written {rows.size}, max N_read {int(nro.max())}")
         close(Vg_rows, Vo_rows, rt, what=f"V rows chunk {c}")
         delta_norm(Vg_rows - V0_rows, Vo_rows - V0_rows, f"dV chunk {c}")
+        if cfg.store == "bf16":
+            ulp_check(Vg_rows, Vo_rows, V0_rows, f"V rows chunk {c}", ARITH_V)
         for Kd, Ko, K0, nm in ((K1d, K1o, s_K1, "K1"), (K2d, K2o, s_K2, "K2")):
             close(f64(Kd), f64(Ko), rt, what=f"{nm} chunk {c}")
             delta_norm(f64(Kd) - f64(K0), f64(Ko) - f64(K0), f"d{nm} chunk {c}")
+            if cfg.store == "bf16":
+                ulp_check(f64(Kd), f64(Ko), f64(K0), f"{nm} chunk {c}", ARITH_K)
         del V_old
     return torch.cat(outs, 1), near_total
 
@@ -234,3 +245,58 @@ def test_long_context_recall_agrees_with_oracle():
     bad = (err > 2e-2).any(-1)
     print(f"  tokens beyond 2e-2: {int(bad.sum())} of {bad.size}")
     assert bad.mean() <= 0.02
+
+
+GOLDEN_RECALL = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "long_recall.json")
+
+
+def _digest(*ts):
+    h = hashlib.sha256()
+    for t in ts:
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
+def test_long_context_full_size_recall_agrees_with_oracle():
+    """The long-context workload at its stated size: one sequence of 131072
+    tokens, 2^20 slots, 64 bindings each planted 16 times, run for 1, 2 and
+    4 passes from the same initial state.  The recall of the planted values
+    at each binding's first and last occurrence in the last pass must agree
+    with the CPU oracle's for the same inputs (stored by
+    golden/make_long_recall.py, which runs the oracle alone) to within one
+    binding in 64.  Four single-pass calls carrying the state must also equal
+    one four-pass call bit for bit."""
+    gold = json.load(open(GOLDEN_RECALL))
+    wl = WORKLOADS["long"]
+    cfg, T = wl.cfg, wl.T
+    q, v, g, extra = make_tokens(cfg, 1, T, wl.seed, wl.kind)
+    K1, K2, V = make_state(cfg, 1, wl.seed)
+    assert gold["T"] == T and gold["seed"] == wl.seed
+    assert gold["digest_tokens"] == _digest(q, v, g) and gold["digest_state"] == _digest(K1, K2, V), \
+        "the stored oracle recall was made from other inputs"
+    pv, pos = extra["plant_v"], extra["plant_pos"]
+    first, last = pos.min(1).values, pos.max(1).values
+    qd, vd, gd = (x.to(DEV) for x in (q, v, g))
+    state = [x.to(DEV) for x in (K1, K2, V)]
+    start = [x.clone() for x in state]
+    nb = pv.shape[0]
+    for p in range(1, 5):
+        out = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, *state, passes=1, want_vhat=True)
+        torch.cuda.synchronize()
+        vh = out["vhat"][0]
+        rf, af, _ = planted_recall(vh[first.to(DEV)].cpu(), pv)
+        rl, al, _ = planted_recall(vh[last.to(DEV)].cpu(), pv)
+        gp = gold["passes"][str(p)]
+        agree_f = sum(a == b for a, b in zip(af, gp["argmax_first"]))
+        agree_l = sum(a == b for a, b in zip(al, gp["argmax_last"]))
+        print(f"  pass {p}: recall first GPU {rf:.4f} oracle {gp['recall_first']:.4f} (same answer for "
+              f"{agree_f}/{nb}); last GPU {rl:.4f} oracle {gp['recall_last']:.4f} ({agree_l}/{nb})", flush=True)
+        if p in (1, 2, 4):
+            assert abs(rf - gp["recall_first"]) <= 1.0 / nb + 1e-9, f"pass {p}: first-occurrence recall"
+            assert abs(rl - gp["recall_last"]) <= 1.0 / nb + 1e-9, f"pass {p}: last-occurrence recall"
+        del out, vh
+    four = fwpkm.fwpkm_forward_seq(cfg, qd, vd, gd, *start, passes=4)
+    torch.cuda.synchronize()
+    for a, b in zip(start, state):
+        assert torch.equal(a, b), "four single-pass calls differ from one four-pass call"
+    del four

@@ -662,3 +662,28 @@ def test_pair_p_matches_selected():
     P = oracle.pair_p(cfg, q, K1, K2, r["idx"])
     np.testing.assert_array_equal(P, r["P"])
     assert (np.diff(P, axis=-1) >= 0).all()
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 4)])
+def test_oracle_results_do_not_depend_on_thread_count(B, H):
+    """The oracle spreads work over OpenMP threads (sequences and tokens; the
+    addressing step codebook by codebook, or inside one codebook when there
+    are fewer codebooks than threads) without changing any sum's order: one
+    thread and many give the same bits."""
+    cfg = FwpkmConfig(n=128, heads=H, d_q=64, d_v=64, k_half=8, k=8, chunk=128, store="bf16", lr_k=20.0)
+    q, v, g, K1, K2, V = _rand_problem(cfg, B, 300, seed=91)
+    threads = oracle.num_threads()
+    try:
+        oracle.set_threads(1)
+        one = oracle.forward_seq(cfg, q, v, g, K1, K2, V, passes=2)
+        oracle.set_threads(max(threads, 4))
+        many = oracle.forward_seq(cfg, q, v, g, K1, K2, V, passes=2)
+    finally:
+        oracle.set_threads(threads)
+    for k in ("o", "vhat", "K1", "K2", "V"):
+        assert np.array_equal(one[k], many[k]), k
+    assert not np.array_equal(one["K1"], _np_store(K1)), "the key step did not move K1"
+
+
+def _np_store(x):
+    return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
