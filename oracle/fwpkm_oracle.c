@@ -365,8 +365,10 @@ int fwo_retrieve(const fwo_cfg* c, int32_t B, int32_t T,
  *   grad_{V_i} L_mem = sum over reads (t,h,j) of row i of (w/H) g_t (v_hat_t - y_t);
  *   grad_agg V_i = grad_{V_i} L_mem / N_read,i;  V_i <- V_i - lr_v grad_agg V_i.
  * tgt_row(t) gives the raw target of token t (t < n_tgt).
- * A slot id outside [0, N) names no row: the read is skipped (the library's
- * boundary takes such ids as a caller error and skips them the same way).
+ * G_i and N_read,i sum over the reads whose slot id is i, for the rows
+ * i in [0, N): a slot id outside [0, N) is the read of no row, so it adds to
+ * no G_i and no N_read,i (every retrieval's ids are in range; a list given
+ * from outside may not be).
  */
 static void memorise_one(const fwo_cfg* c, int32_t Tc, int32_t n_tgt,
                          const float* g_b, const void* tgt_b, size_t tgt_stride_tok,

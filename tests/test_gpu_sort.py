@@ -1,7 +1,7 @@
 """GPU: the value write over planted slot lists -- long runs of one row,
-ragged read counts across sort tiles, and out-of-range slot
-ids, which the boundary skips (the oracle skips them the same way).  N_read
-must be exact and V within tolerance of the oracle."""
+ragged read counts across sort tiles, and out-of-range slot ids (the read
+of no row: they add to no row's sum and no row's read count).  N_read must
+be exact and V within tolerance of the oracle."""
 import numpy as np
 import pytest
 import torch

@@ -214,8 +214,8 @@ def test_value_write_equals_dense_matmul_over_read_counts(H, k, znorm, gate):
 
 
 def test_value_write_skips_out_of_range_ids():
-    """Slot ids outside [0, N) (a caller error the boundary skips) name no
-    row: the write equals the dense formula over the valid reads alone."""
+    """Slot ids outside [0, N) name no row: the write equals the dense
+    formula over the reads of rows 0..N-1 alone."""
     cfg = FwpkmConfig(n=5, heads=2, d_q=4, d_v=3, k_half=3, k=3, chunk=10, use_addr=False)
     B, Tc = 1, 10
     q, v, g, K1, K2, V = _rand_problem(cfg, B, Tc, seed=31)
