@@ -21,6 +21,19 @@ namespace fwpkm {
 
 namespace {
 
+// Runs whose value rows a wavefront requests at once.  Random
+// read-modify-writes of 1 KiB rows reach their full rate only with many rows
+// in flight; a 64-read piece holds about 60 runs at the 2^20-slot layer, so
+// 16 rows per request take four round trips per wavefront, at 102 VGPRs (five
+// wavefronts per SIMD).  Measured per chunk of that layer: 462 us with the
+// earlier two-row pipeline, 431-435 us with 16; 10 or 12 rows (more
+// wavefronts, more round trips) 451-465 us; the first residual row requested
+// one or two runs ahead, or two reads of a long run per step, cost the fifth
+// wavefront and did not pay.
+constexpr int kScatterRuns = 16;
+// Pieces whose partials k_fixup requests at once.
+constexpr int kFixupAhead = 8;
+
 template <int STORE, int EPL>
 __device__ __forceinline__ void ld_row(const void* base, size_t off, float (&x)[EPL]) {
     if constexpr (STORE == kF32) {
@@ -186,7 +199,7 @@ __device__ __forceinline__ void apply_row(const ScatterArgs& a, int b, uint32_t 
     finish_row<STORE, EPL>(a, b, slot, count, v, acc);
 }
 
-template <int STORE, int EPL>
+template <int STORE, int EPL, int R>
 __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
     const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -228,14 +241,9 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
     };
     auto w_at = [&](int j) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), j)); };
 
-    // Runs are processed in order, software-pipelined: the row and first
-    // residual of run j+1 are requested before run j is computed and stored,
-    // so the loads do not queue behind run j's store.  Two register sets,
-    // used alternately, hold the requested data.
-    struct Pending {
-        RawRow<STORE, EPL> v;
-        float x[EPL];
-    };
+    // Runs are processed in order, in batches of up to R: the value rows of
+    // a batch's runs are all requested first, then each run is summed in
+    // list order and its row written.
     auto run_end = [&](int s0) {
         const uint64_t tm = tb & (~0ull << s0);
         return tm != 0ull ? (__ffsll(static_cast<unsigned long long>(tm)) - 1) : nvalid - 1;
@@ -248,11 +256,7 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
         const bool whole = ((hb >> s0) & 1ull) && ((tb >> e0) & 1ull) && slot < a.N;
         return whole ? slot : 0u;
     };
-    auto request = [&](int s0, Pending& pd) {
-        ld_raw<STORE, EPL>(Vb + (row_of(s0) * vrow + vlane), 0, pd.v);
-        ld_f32<EPL>(rrow_at(s0), pd.x);
-    };
-    auto finish = [&](int s0, int e, Pending& pd) {
+    auto finish = [&](int s0, int e, const RawRow<STORE, EPL>& vraw, const float (&x0)[EPL]) {
         const bool ends_here = (tb >> e) & 1ull;
         const bool starts_here = (hb >> s0) & 1ull;
         const uint32_t slot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), s0));
@@ -262,32 +266,18 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
         if (whole && e == s0) {
             // a row read once: V - lr w r
             float v[EPL];
-            unpack<STORE, EPL>(pd.v, v);
+            unpack<STORE, EPL>(vraw, v);
             const float sw = a.lr * w0;
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) v[i] = fmaf(-sw, pd.x[i], v[i]);
+            for (int i = 0; i < EPL; ++i) v[i] = fmaf(-sw, x0[i], v[i]);
             st_row<STORE, EPL>(vp, 0, v);
             if (a.n_read && lane == 0) a.n_read[static_cast<size_t>(b) * a.N + slot] = 1;
             return;
         }
         float acc[EPL];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) acc[i] = w0 * pd.x[i];
-        int j = s0 + 1;
-        for (; j + 4 <= e + 1; j += 4) {
-            float y[4][EPL];
-            float ww[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ww[u] = w_at(j + u);
-                ld_f32<EPL>(rrow_at(j + u), y[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww[u], y[u][i], acc[i]);
-        }
-        for (; j <= e; ++j) {
+        for (int i = 0; i < EPL; ++i) acc[i] = w0 * x0[i];
+        for (int j = s0 + 1; j <= e; ++j) {
             float y[EPL];
             const float ww = w_at(j);
             ld_f32<EPL>(rrow_at(j), y);
@@ -297,7 +287,7 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
         if (starts_here && ends_here) {
             if (whole) {
                 float v[EPL];
-                unpack<STORE, EPL>(pd.v, v);
+                unpack<STORE, EPL>(vraw, v);
                 const float sc = a.lr * __builtin_amdgcn_rcpf(static_cast<float>(e - s0 + 1));
 #pragma unroll
                 for (int i = 0; i < EPL; ++i) v[i] = fmaf(-sc, acc[i], v[i]);
@@ -315,21 +305,30 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
         }
     };
 
-    // (the request after the last run repeats it: every iteration issues the
-    // same loads, so the waits before a run's use count only the newer ones)
-    Pending pa, pb;
-    int s = 0;
-    if (s < nvalid) request(s, pa);
-    while (s < nvalid) {
-        int e = run_end(s);
-        request(e + 1 < nvalid ? e + 1 : s, pb);
-        finish(s, e, pa);
-        s = e + 1;
-        if (s >= nvalid) break;
-        e = run_end(s);
-        request(e + 1 < nvalid ? e + 1 : s, pa);
-        finish(s, e, pb);
-        s = e + 1;
+    // run starts: position 0 and every position after a run's last one
+    uint64_t rem = nvalid > 0 ? (((tb << 1) | 1ull) & (nvalid == 64 ? ~0ull : ((1ull << nvalid) - 1ull))) : 0ull;
+    while (rem) {
+        int st[R], en[R];
+        RawRow<STORE, EPL> vr[R];
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (rem) {
+                st[j] = __ffsll(static_cast<unsigned long long>(rem)) - 1;
+                rem &= rem - 1ull;
+                en[j] = run_end(st[j]);
+                ld_raw<STORE, EPL>(Vb + (row_of(st[j]) * vrow + vlane), 0, vr[j]);
+                n = j + 1;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (j < n) {
+                float r0[EPL];
+                ld_f32<EPL>(rrow_at(st[j]), r0);
+                finish(st[j], en[j], vr[j], r0);
+            }
+        }
     }
 }
 
@@ -346,14 +345,26 @@ __global__ __launch_bounds__(256) void k_fixup(ScatterArgs a) {
     if (start < 0) return;
     float acc[EPL];
     ld_f32<EPL>(a.pt + (base + p) * a.dv + static_cast<size_t>(lane) * EPL, acc);
+    // the following pieces' partials, in piece order; a long run crosses
+    // many pieces, so kFixupAhead of them are requested at a time (the sum
+    // stops at the piece where the run ends)
     int end = -1;
-    for (int q = p + 1; q < a.pieces; ++q) {
-        float x[EPL];
-        ld_f32<EPL>(a.ph + (base + q) * a.dv + static_cast<size_t>(lane) * EPL, x);
+    for (int q = p + 1; end < 0 && q < a.pieces; q += kFixupAhead) {
+        float x[kFixupAhead][EPL];
+        int ends[kFixupAhead];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) acc[i] += x[i];
-        end = a.ph_end[base + q];
-        if (end >= 0) break;
+        for (int u = 0; u < kFixupAhead; ++u)
+            if (q + u < a.pieces) {
+                ends[u] = a.ph_end[base + q + u];
+                ld_f32<EPL>(a.ph + (base + q + u) * a.dv + static_cast<size_t>(lane) * EPL, x[u]);
+            }
+#pragma unroll
+        for (int u = 0; u < kFixupAhead; ++u)
+            if (end < 0 && q + u < a.pieces) {
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) acc[i] += x[u][i];
+                end = ends[u];
+            }
     }
     if (end < 0) return;  // unreachable for a well-formed list: the last position ends a run
     const uint32_t slot = a.keys[static_cast<size_t>(b) * a.M + start];
@@ -383,7 +394,7 @@ template <int STORE, int EPL>
 hipError_t scatter_t(const ScatterArgs& a, hipStream_t s) {
     const int64_t waves = static_cast<int64_t>(a.B) * a.pieces;
     const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
-    hipLaunchKernelGGL((k_scatter<STORE, EPL>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_scatter<STORE, EPL, kScatterRuns>), dim3(grid), dim3(256), 0, s, a);
     hipLaunchKernelGGL((k_fixup<STORE, EPL>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
