@@ -59,6 +59,12 @@ def parse():
                     help="time fwpkm_forward_seq_backward (replayed pass with gradients w.r.t. q, v, g)")
     ap.add_argument("--usage", action="store_true",
                     help="time forward_seq with row-contribution counting and the addressing metrics")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print per-kernel tables of a rocprofv3 --kernel-trace CSV output directory and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="HBM bytes per kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE CSV output directories "
+                         "of a --profile-only run with one kernel at a time; writes profiles/<family>_<workload>_pmc.json "
+                         "and prints a table")
     ap.add_argument("--ceiling", action="store_true",
                     help="measure the HBM rates of random 1 KiB value rows (read; read-modify-write at several "
                          "depths, from registers and staged in LDS) and of a sequential copy")
@@ -435,6 +441,120 @@ def ceiling_bench(args):
     print(json.dumps(result), flush=True)
 
 
+# kernel families of the library's timing (fwpkm_timing_read), by kernel name
+def kernel_family(name):
+    import re
+    n = name.replace("(anonymous namespace)", "").split("(")[0]
+    if "k_scatter" in n or "k_fixup" in n:
+        return "scatter"
+    if "k_gather" in n:
+        return "gather"
+    if "k_sort_" in n:
+        return "sort"
+    m = re.search(r"k_score<\s*\d+\s*,\s*\d+\s*,\s*\d+\s*,\s*(\d+)", n)
+    if m:
+        mode = int(m.group(1))
+        return "score_rowstat" if mode == 4 else ("score_select" if mode & 1 else "score_stats")
+    for key, fam in (("k_kgrad", "kgrad"), ("k_select", "select"), ("k_qt", "qt"), ("k_pbar", "pbar"),
+                     ("k_knorm", "knorm"), ("k_rows", "score_select"), ("k_row_", "score_rowstat")):
+        if key in n:
+            return fam
+    return None
+
+
+def _rocprof_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def summarize_trace(directory):
+    """Per-kernel dispatch counts and mean durations of a rocprofv3 kernel
+    trace, and the per-chunk-step time of each kernel family (one gather
+    launch per chunk step of B sequences, or two half-batch ones)."""
+    rows = _rocprof_rows(directory, "kernel_trace.csv")
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(name, []).append(dt)
+    lines = ["| kernel | dispatches | avg us | total ms |", "|---|---|---|---|"]
+    for name, ts in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("fwpkm::", "")
+        lines.append(f"| `{short}` | {len(ts)} | {sum(ts) / len(ts):.1f} | {sum(ts) / 1e3:.2f} |")
+    fam = {}
+    for name, ts in per.items():
+        f = kernel_family(name)
+        if f:
+            fam[f] = fam.get(f, 0.0) + sum(ts)
+    steps = sum(1 for r in rows if "k_select<" in r["Kernel_Name"] or "k_select_gather" in r["Kernel_Name"]
+                or "k_select_rows" in r["Kernel_Name"])
+    if steps:
+        lines += ["", f"Per chunk step ({steps} selections):", "", "| family | us per chunk step |", "|---|---|"]
+        for f, t in sorted(fam.items(), key=lambda kv: -kv[1]):
+            lines.append(f"| {f} | {t / steps:.1f} |")
+    print("\n".join(lines))
+
+
+def summarize_pmc(fetch_dir, write_dir, workload):
+    """HBM bytes per kernel family launch from FETCH_SIZE and WRITE_SIZE
+    passes (KiB per dispatch), scaled by what the same counters read for the
+    calibration kernel of --profile-only (torch.neg over 2^28 float32: 1 GiB
+    read, 1 GiB written).  Assumes one launch per family per chunk step (one
+    kernel at a time, full batches)."""
+    def per_kernel(directory, counter):
+        vals = {}
+        for r in _rocprof_rows(directory, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    def calib(vals):
+        c = [v for (_, n), v in vals.items() if "neg" in n]
+        if not c:
+            raise SystemExit("no calibration dispatch (torch.neg) in the counter output")
+        return gib_kib / (sum(c) / len(c))
+    fs, wsc = calib(fetch), calib(write)
+    def family_totals(vals):
+        tot, steps = {}, 0
+        for (_, n), v in vals.items():
+            f = kernel_family(n)
+            if f:
+                tot[f] = tot.get(f, 0.0) + v
+            if "k_select<" in n:
+                steps += 1
+        return tot, steps
+    ft, steps = family_totals(fetch)
+    wt, steps_w = family_totals(write)
+    if not steps or steps != steps_w:
+        raise SystemExit(f"chunk steps differ between the passes ({steps}, {steps_w})")
+    print(f"fetch scale {fs:.4f}, write scale {wsc:.4f}; {steps} chunk steps")
+    print("| family | FETCH_SIZE KiB/step (raw) | WRITE_SIZE KiB/step (raw) | HBM bytes/step (scaled) |")
+    print("|---|---|---|---|")
+    for f in sorted(ft):
+        fk, wk = ft[f] / steps, wt.get(f, 0.0) / steps
+        hbm = (fk * fs + wk * wsc) * 1024
+        print(f"| {f} | {fk:.0f} | {wk:.0f} | {hbm / 1e6:.1f} MB |")
+        if f in KERNEL_SRC:
+            out = {"kernel": f, "workload": workload, "src_hash": src_hash(*KERNEL_SRC[f]),
+                   "hbm_bytes_per_launch": hbm, "fetch_scale": fs, "write_scale": wsc,
+                   "fetch_kib_raw": fk, "write_kib_raw": wk,
+                   "command": "FWPKM_DEBUG=1 FWPKM_SINGLE_STREAM=1 rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) "
+                              "--output-format csv -d <dir> -o run -- python3 -u bench.py --profile-only "
+                              f"--workload {workload} --steps 2 --warmup 1"}
+            with open(os.path.join(ROOT, "profiles", f"{f}_{workload}_pmc.json"), "w") as fh:
+                json.dump(out, fh, indent=1)
+
+
 GOLDEN_RECALL = os.path.join(ROOT, "tests", "golden", "long_recall.json")
 
 
@@ -478,6 +598,12 @@ def planted_recall_report(cfg, wl, passes, q, v, g, start_state, extra):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "the FwPKM layer benchmark runs on one GPU; --gpus must be 1",
                           "requested_gpus": args.gpus}))
