@@ -475,13 +475,16 @@ def _rocprof_rows(directory, suffix):
 
 
 def summarize_trace(directory):
-    """Per-kernel dispatch counts and mean durations of a rocprofv3 kernel
-    trace, and the per-chunk-step time of each kernel family (one gather
-    launch per chunk step of B sequences, or two half-batch ones)."""
+    """Per-kernel dispatch counts and mean durations of the library's kernels
+    in a rocprofv3 kernel trace, and the per-chunk-step time of each kernel
+    family (one gather launch per chunk step of B sequences, or two
+    half-batch ones)."""
     rows = _rocprof_rows(directory, "kernel_trace.csv")
     per = {}
     for r in rows:
         name = r["Kernel_Name"]
+        if "fwpkm::" not in name:
+            continue  # the input generation's and the row-count measurement's kernels
         dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         per.setdefault(name, []).append(dt)
     lines = ["| kernel | dispatches | avg us | total ms |", "|---|---|---|---|"]

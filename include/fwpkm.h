@@ -425,13 +425,13 @@ typedef enum {
     FWPKM_K_RESID = 3,          /* residual of fwpkm_chunk_update                  */
     FWPKM_K_SORT = 4,           /* radix sort of the read list (all passes)        */
     FWPKM_K_SCATTER = 5,        /* read-count-normalised value-row write           */
-    FWPKM_K_PBAR = 6,           /* log of the usage marginals                      */
+    FWPKM_K_PBAR = 6,           /* usage partials from stored scores (row path)    */
     FWPKM_K_SWEEP_STATS = 7,    /* usage sums of fwpkm_chunk_update                */
     FWPKM_K_SWEEP_ROWSTAT = 8,  /* row statistic of the entropy gradient           */
     FWPKM_K_KGRAD = 9,          /* sub-key gradient step                           */
     FWPKM_K_FILL = 10,          /* zero fill of n_read                             */
     FWPKM_K_SELECT = 11,        /* per-half top-k', product top-k, weights         */
-    FWPKM_K_QT = 12,            /* transposed query halves for the sub-key step    */
+    FWPKM_K_QT = 12,            /* transposed query halves (rescoring statistic)   */
     FWPKM_K_PEND = 13,          /* copies into a stream's pending chunk            */
     FWPKM_K_USAGE = 14,         /* row-contribution counts and addressing metrics  */
     FWPKM_K_BACKWARD = 15,      /* gradient of the retrieval output                */

@@ -589,6 +589,12 @@ int memorise(const Plan& p, const Layout& L, void* ws, int B, int Tc, int n_tgt,
 // partial sums too (on the rows path they are taken here from the stored
 // rows); otherwise a stats scoring pass computes all of them first.
 // knorm holds ||K_i||^2 of the current codebooks; the key step rewrites it.
+// The transposed queries of the key step (written by the row statistic's
+// launch).
+QtArgs qt_args(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride) {
+    return QtArgs{q, q_bstride, at<void>(ws, L.qT), B, Tc, (Tc + 31) / 32 * 32, p.H, p.dh};
+}
+
 int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void* q, int64_t q_bstride,
             void* K1, void* K2, bool have_stats, float* knorm, hipStream_t s, hipEvent_t before_kstep = nullptr) {
     const bool rows = use_rows(p, B, Tc);
@@ -601,46 +607,50 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
         if (rows) a.erow = at<uint32_t>(ws, L.erow);
         TimedLaunch tl(FWPKM_K_SWEEP_STATS, s);
         HIP_TRY(launch_score(a, p.store, s));
-        if (rows) HIP_TRY(launch_row_stats(a, 0, s));
+        if (rows) HIP_TRY(launch_row_stats(a, 0, p.store, s));
     }
-    PbarArgs pa{at<float>(ws, L.part), at<float>(ws, L.lp), B, p.H, p.n, 0, Tc};
-    {
-        const int tile = stat_tile(p, B, Tc);
-        pa.ntiles = (Tc + tile - 1) / tile;
-    }
-    {
+    if (have_stats && rows) {
+        // the selection left Z (and M): the per-tile usage partials
+        ScoreArgs ca = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreRows);
+        ca.erow = at<uint32_t>(ws, L.erow);
+        ca.part = at<float>(ws, L.part);
+        ca.Z = at<float>(ws, L.Z);
+        ca.M = at<float>(ws, L.M);
         TimedLaunch tl(FWPKM_K_PBAR, s);
-        if (have_stats && rows) {
-            // the selection left Z (and M): the per-tile usage partials, then pbar
-            ScoreArgs ca = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreRows);
-            ca.erow = at<uint32_t>(ws, L.erow);
-            ca.part = at<float>(ws, L.part);
-            ca.Z = at<float>(ws, L.Z);
-            ca.M = at<float>(ws, L.M);
-            HIP_TRY(launch_row_stats(ca, 2, s));
-        }
-        HIP_TRY(launch_pbar(pa, s));
+        HIP_TRY(launch_row_stats(ca, 2, p.store, s));
     }
+    // the row statistic forms ln pbar from the usage partials itself and
+    // leaves it for the key step
     ScoreArgs ra = score_args(p, B, Tc, q, q_bstride, K1, K2, knorm, kScoreRowStat);
     ra.lp = at<float>(ws, L.lp);
+    ra.part = at<float>(ws, L.part);
+    {
+        const int tile = stat_tile(p, B, Tc);
+        ra.pbar_ntiles = (Tc + tile - 1) / tile;
+    }
     ra.Z = at<float>(ws, L.Z);
     ra.M = at<float>(ws, L.M);
     ra.m = at<float>(ws, L.m);
+    // the transposed queries the key step reads: extra workgroups of the row
+    // statistic's launch on the stored-score path; a launch of their own
+    // after a rescoring statistic, which has just brought the queries into
+    // the last-level cache
+    const QtArgs qa = qt_args(p, L, ws, B, Tc, q, q_bstride);
     {
         TimedLaunch tl(FWPKM_K_SWEEP_ROWSTAT, s);
         if (rows) {
+            ra.qt = qa;
             ra.erow = at<uint32_t>(ws, L.erow);
-            HIP_TRY(launch_row_stats(ra, 1, s));
+            HIP_TRY(launch_row_stats(ra, 1, p.store, s));
         } else {
             HIP_TRY(launch_score(ra, p.store, s));
         }
     }
-    const int Tp = (Tc + 31) / 32 * 32;
-    {
-        QtArgs qa{q, q_bstride, at<void>(ws, L.qT), B, Tc, Tp, p.H, p.dh};
+    if (!rows) {
         TimedLaunch tl(FWPKM_K_QT, s);
         HIP_TRY(launch_qt(qa, p.store, s));
     }
+    const int Tp = (Tc + 31) / 32 * 32;
     KgradArgs ka{};
     ka.q = q; ka.q_bstride = q_bstride; ka.qT = at<void>(ws, L.qT); ka.Tp = Tp;
     ka.K1 = K1; ka.K2 = K2; ka.knorm = knorm;

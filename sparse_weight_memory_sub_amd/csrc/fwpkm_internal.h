@@ -144,6 +144,14 @@ __device__ __forceinline__ float unord_f32(uint32_t u) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
+// ln pbar_i = ln((sum over the tiles, in order, of part[tile][i]) / Tc):
+// the usage marginal of sub-key i from its per-tile partial sums.
+__device__ __forceinline__ float log_pbar(const float* part, int ntiles, int n, int i, int Tc) {
+    float s = 0.f;
+    for (int t = 0; t < ntiles; ++t) s += part[static_cast<size_t>(t) * n + i];
+    return logf(s / static_cast<float>(Tc));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += xor_lane(x, o);
@@ -201,6 +209,73 @@ constexpr int kGatherPart = 16;         // gather: entries summed per part (part
 constexpr int kGatherSplitBelow = 1024; // gather: one wavefront per part below this many tokens
 constexpr int kScoreTokMax = 256;
 
+// Transposed query halves of a chunk, qT[bhh][d][t'] for t' < Tp (Tp = Tc
+// rounded up to 32; zeros past Tc), the token-contiguous operand of the sum
+// over tokens in the key step.  Within each 32-token block the tokens are
+// stored in groups of four in the order 0, 4, 1, 5, 2, 6, 3, 7 (group j =
+// tokens 4j..4j+3), so that tokens 4g..4g+3 and 16+4g..16+4g+3 -- the eight
+// k-elements lane group g of an MFMA operand holds -- are adjacent.  64x64
+// tiles through LDS, one per workgroup of 256 or 1024 threads: tile (bx, by) of
+// (tokens, d) of query half bz = (b*H + h)*2 + half.
+struct QtArgs {
+    const void* q;        // token t of sequence b at q + b*q_bstride + t*H*2*dh
+    int64_t q_bstride;
+    void* qT;             // [B][H][2][dh][Tp]
+    int B, Tc, Tp, H, dh;
+};
+
+__host__ __device__ constexpr int qt_pos(int t) {
+    const int blk = t & ~31, grp = (t >> 2) & 7;
+    return blk + (((grp & 3) << 1) | (grp >> 2)) * 4 + (t & 3);
+}
+
+template <int STORE>
+__host__ __device__ constexpr int qt_tile_bytes() {
+    return 64 * 65 * Store<STORE>::kBytes;
+}
+
+// Tiles of the transposed queries: (tokens, d) tiles x bz.
+inline int64_t qt_tiles(const QtArgs& a) {
+    return static_cast<int64_t>((a.Tp + 63) / 64) * ((a.dh + 63) / 64) * a.B * a.H * 2;
+}
+
+template <int STORE, int GROUPS>
+__device__ __forceinline__ void qt_tile(const QtArgs& a, int bx, int by, int bz, unsigned char* lds) {
+    using E = typename Store<STORE>::T;
+    static_assert(GROUPS == 4 || GROUPS == 16, "256 or 1024 threads");
+    constexpr int PER = 64 / GROUPS;  // rows of the tile per 64-thread group
+    E (*tile)[65] = reinterpret_cast<E (*)[65]>(lds);
+    const int t0 = bx * 64, d0 = by * 64;
+    const int bhh = bz;
+    const int half = bhh & 1, bh = bhh >> 1;
+    const int h = bh % a.H, b = bh / a.H;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const E* q = static_cast<const E*>(a.q) + static_cast<size_t>(b) * a.q_bstride + h * 2 * a.dh + half * a.dh;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int tl = ty * PER + i, t = t0 + tl, d = d0 + tx;
+        E v{};
+        if (t < a.Tc && d < a.dh) v = q[static_cast<size_t>(t) * a.H * 2 * a.dh + d];
+        tile[tl][tx] = v;
+    }
+    __syncthreads();
+    E* out = static_cast<E*>(a.qT) + static_cast<size_t>(bhh) * a.dh * a.Tp;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int dl = ty * PER + i, d = d0 + dl, t = t0 + tx;
+        if (d < a.dh && t < a.Tp) out[static_cast<size_t>(d) * a.Tp + qt_pos(t)] = tile[tx][dl];
+    }
+}
+
+// Linear tile index -> (bx, by, bz) of qt_tile.
+template <int STORE, int GROUPS>
+__device__ __forceinline__ void qt_tile_linear(const QtArgs& a, int64_t i, unsigned char* lds) {
+    const int tb = (a.Tp + 63) / 64, db = (a.dh + 63) / 64;
+    const int bz = static_cast<int>(i / (tb * db));
+    const int rem = static_cast<int>(i % (tb * db));
+    qt_tile<STORE, GROUPS>(a, rem % tb, rem / tb, bz, lds);
+}
+
 struct ScoreArgs {
     const void* q;        // token t of sequence b at q + b*q_bstride + t*H*d_q
     int64_t q_bstride;
@@ -215,7 +290,14 @@ struct ScoreArgs {
     int cap;
     float* qn;            // [B][H][2][Tc]  ||q_half||^2
     float* part;          // [B][H][2][ceil(Tc/tile)][n]
-    const float* lp;      // [B][H][2][n]   log pbar
+    float* lp;            // [B][H][2][n]   log pbar (row statistic: computed from part, written by
+                          //   one workgroup per (sequence, head, half) for the key step)
+    int pbar_ntiles;      // row statistic: tiles of the usage partials in part
+    QtArgs qt;            // row statistic from stored rows, qt.qT non-NULL: the launch also writes
+                          //   the chunk's transposed queries (qt_tiles(qt) workgroups after the
+                          //   statistic's)
+    int stat_blocks;      // row statistic from stored rows: the statistic's workgroups (set by
+                          //   the launcher)
     float* Z;             // [B][H][2][Tc]
     float* m;             // [B][H][2][Tc]
     uint32_t* erow;       // [B][H][2][Tc][n]  e bit patterns (rows mode)
@@ -331,23 +413,11 @@ struct ScatterArgs {
     float lr, inv_h;
 };
 
-struct PbarArgs {
-    const float* part;    // [B][H][2][ntiles][n]
-    float* lp;            // [B][H][2][n]
-    int B, H, n, ntiles, Tc;
-};
-
-struct QtArgs {
-    const void* q;        // token t of sequence b at q + b*q_bstride + t*H*2*dh
-    int64_t q_bstride;
-    void* qT;             // [B][H][2][dh][Tp]
-    int B, Tc, Tp, H, dh;
-};
 
 struct KgradArgs {
     const void* q;
     int64_t q_bstride;
-    const void* qT;       // [B][H][2][dh][Tp] (k_qt)
+    const void* qT;       // [B][H][2][dh][Tp] (written in tiles of qt_tile)
     int Tp;
     void* K1;
     void* K2;
@@ -426,8 +496,8 @@ int score_tile(int B, int H, int Tc, bool dot);
 int device_cus();
 // Statistics of stored rows (rows mode): what = 0 writes Z (and M for dot
 // scoring) and the per-64-token usage partials into part; what = 1 writes m
-// (needs lp).
-hipError_t launch_row_stats(const ScoreArgs& a, int what, hipStream_t s);
+// (needs lp), with the transposed queries of a.qt when a.qt.qT is set.
+hipError_t launch_row_stats(const ScoreArgs& a, int what, int store, hipStream_t s);
 // Gradient of the retrieval output w.r.t. q, v and g for T tokens of B
 // sequences; per-sequence strides in elements:
 //   q, dq (f32):         + b*q_bstride + (t*H + h)*2*dh
@@ -480,9 +550,9 @@ hipError_t launch_usage_metrics(int32_t* usage, int B, int64_t N, void* scratch,
 // height rows of width_bytes (a multiple of 4) from src + y*spitch to dst + y*dpitch
 hipError_t launch_copy2d(void* dst, int64_t dpitch, const void* src, int64_t spitch, int64_t width_bytes,
                          int64_t height, hipStream_t s);
-hipError_t launch_pbar(const PbarArgs& a, hipStream_t s);
-hipError_t launch_qt(const QtArgs& a, int store, hipStream_t s);
 hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s);
+// the transposed query halves alone (tiles of qt_tile)
+hipError_t launch_qt(const QtArgs& a, int store, hipStream_t s);
 
 constexpr int kSortItems = 8;                  // entries per thread
 constexpr int kSortTile = 256 * kSortItems;    // entries per sort workgroup

@@ -13,7 +13,7 @@
 // wavefront owns 16 keys and walks the chunk's tokens in blocks of 32.  Each
 // block is staged in LDS twice by direct global-to-LDS loads, double-buffered:
 // the query rows (d_h-contiguous) and the same rows transposed
-// (token-contiguous, written once per chunk by k_qt).  Per block:
+// (token-contiguous, written once per chunk in tiles of qt_tile).  Per block:
 //  1. recompute the 32x16 distance tile on the matrix cores (same operands,
 //     order and roundings as the scoring sweep, so the values are bitwise
 //     the same);
@@ -30,17 +30,6 @@
 namespace fwpkm {
 
 namespace {
-
-// log pbar_i from the per-tile partial sums, tiles added in order.
-__global__ __launch_bounds__(256) void k_pbar(PbarArgs a) {
-    const int bhh = blockIdx.y;
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= a.n) return;
-    const float* part = a.part + static_cast<size_t>(bhh) * a.ntiles * a.n + i;
-    float s = 0.f;
-    for (int t = 0; t < a.ntiles; ++t) s += part[static_cast<size_t>(t) * a.n];
-    a.lp[static_cast<size_t>(bhh) * a.n + i] = logf(s / static_cast<float>(a.Tc));
-}
 
 // ||K_i||^2 for every sub-key.  Sixteen lanes per key; lane r adds the
 // squares of columns r, r+16, r+32, ... in order, then the sixteen partial
@@ -74,42 +63,14 @@ __global__ __launch_bounds__(256) void k_knorm(KnormArgs a) {
     if (valid && r == 0) a.knorm[key] = x;
 }
 
-// Transposed query halves of a chunk, qT[bhh][d][t'] for t' < Tp (Tp = Tc
-// rounded up to 32; zeros past Tc), the token-contiguous operand of the sum
-// over tokens in k_kgrad.  Within each 32-token block the tokens are stored
-// in groups of four in the order 0, 4, 1, 5, 2, 6, 3, 7 (group j = tokens
-// 4j..4j+3), so that tokens 4g..4g+3 and 16+4g..16+4g+3 -- the eight
-// k-elements lane group g of an MFMA operand holds -- are adjacent.  64x64
-// tiles through LDS.
-__host__ __device__ constexpr int qt_pos(int t) {
-    const int blk = t & ~31, grp = (t >> 2) & 7;
-    return blk + (((grp & 3) << 1) | (grp >> 2)) * 4 + (t & 3);
-}
 
+// The chunk's transposed query halves in a launch of their own, one 64 x 64
+// tile per 256-thread workgroup (the scoring path, whose row-statistic
+// workgroups are too large and hold too much LDS to carry these tiles well).
 template <int STORE>
 __global__ __launch_bounds__(256) void k_qt(QtArgs a) {
-    using E = typename Store<STORE>::T;
-    __shared__ E tile[64][65];
-    const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
-    const int bhh = blockIdx.z;
-    const int half = bhh & 1, bh = bhh >> 1;
-    const int h = bh % a.H, b = bh / a.H;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    const E* q = static_cast<const E*>(a.q) + static_cast<size_t>(b) * a.q_bstride + h * 2 * a.dh + half * a.dh;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-        const int tl = ty * 16 + i, t = t0 + tl, d = d0 + tx;
-        E v{};
-        if (t < a.Tc && d < a.dh) v = q[static_cast<size_t>(t) * a.H * 2 * a.dh + d];
-        tile[tl][tx] = v;
-    }
-    __syncthreads();
-    E* out = static_cast<E*>(a.qT) + static_cast<size_t>(bhh) * a.dh * a.Tp;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-        const int dl = ty * 16 + i, d = d0 + dl, t = t0 + tx;
-        if (d < a.dh && t < a.Tp) out[static_cast<size_t>(d) * a.Tp + qt_pos(t)] = tile[tx][dl];
-    }
+    __shared__ __align__(16) unsigned char tile[qt_tile_bytes<STORE>()];
+    qt_tile<STORE, 4>(a, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
 
 // Split partials: [B*H*2][split][n][dh] sums over the split's tokens of
@@ -206,7 +167,7 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     const int eps_bits = __float_as_int(a.eps);
     const FragBase<STORE, DHS> fq(r, g);
     // transposed-tile offsets of the operand column d = 16c + r: tokens 4g..4g+3
-    // and 16+4g..16+4g+3 of the block, adjacent in the k_qt order (one 16-byte
+    // and 16+4g..16+4g+3 of the block, adjacent in the qt_tile order (one 16-byte
     // chunk for bf16, two for fp32)
     uint32_t tb0, tb1;
     {
@@ -527,12 +488,6 @@ hipError_t kgrad_s(const KgradArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_pbar(const PbarArgs& a, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>((a.n + 255) / 256), static_cast<unsigned>(a.B * a.H * 2));
-    hipLaunchKernelGGL(k_pbar, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s) {
     const int64_t keys = static_cast<int64_t>(a.B) * a.H * 2 * a.n;
     const unsigned grid = static_cast<unsigned>((keys + 15) / 16);
@@ -541,16 +496,16 @@ hipError_t launch_knorm(const KnormArgs& a, int store, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s) {
+    return store == kBF16 ? kgrad_s<kBF16>(a, s) : kgrad_s<kF32>(a, s);
+}
+
 hipError_t launch_qt(const QtArgs& a, int store, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>((a.Tp + 63) / 64), static_cast<unsigned>((a.dh + 63) / 64),
                     static_cast<unsigned>(a.B * a.H * 2));
     if (store == kBF16) hipLaunchKernelGGL(k_qt<kBF16>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_qt<kF32>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
-}
-
-hipError_t launch_kgrad(const KgradArgs& a, int store, hipStream_t s) {
-    return store == kBF16 ? kgrad_s<kBF16>(a, s) : kgrad_s<kF32>(a, s);
 }
 
 }  // namespace fwpkm

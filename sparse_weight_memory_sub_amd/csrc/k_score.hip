@@ -200,7 +200,14 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
     float mrow[4] = {0.f, 0.f, 0.f, 0.f};  // dot scoring: the row maximum M_t of s
     uint32_t tau[4] = {0u, 0u, 0u, 0u};
     if constexpr (ROW) {
-        for (int i = threadIdx.x; i < n; i += 64 * NW) lps[i] = a.lp[static_cast<size_t>(bhh) * n + i];
+        // log pbar_i from the per-tile usage partials, tiles added in order;
+        // the first tile's workgroup also leaves it for the key step
+        const float* pp = a.part + static_cast<size_t>(bhh) * a.pbar_ntiles * n;
+        for (int i = threadIdx.x; i < n; i += 64 * NW) {
+            const float l = log_pbar(pp, a.pbar_ntiles, n, i, Tc);
+            lps[i] = l;
+            if (tile == 0) a.lp[static_cast<size_t>(bhh) * n + i] = l;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (rv[i]) {
@@ -543,15 +550,38 @@ __global__ __launch_bounds__(256) void k_row_colsum(ScoreArgs a) {
             ((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane];
 }
 
-// Row statistic m_t = sum_i p_ti ln pbar_i from stored rows.
-template <bool DOT>
-__global__ __launch_bounds__(256) void k_row_m(ScoreArgs a) {
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= static_cast<int64_t>(a.B) * a.H * 2 * a.Tc) return;
+// Row statistic m_t = sum_i p_ti ln pbar_i from stored rows.  One workgroup
+// per kRowMRows rows of one (sequence, head, half): it first forms ln pbar
+// from the usage partials in LDS (the first group also leaves it for the key
+// step), then one wavefront per row.  Workgroups past a.stat_blocks write
+// the chunk's transposed queries instead.
+constexpr int kRowMRows = 16;
+template <int STORE, bool DOT>
+__global__ __launch_bounds__(64 * kRowMRows) void k_row_m(ScoreArgs a) {
+    constexpr int LDS = kNplMax * 64 * 4 > qt_tile_bytes<STORE>() ? kNplMax * 64 * 4 : qt_tile_bytes<STORE>();
+    __shared__ __align__(16) unsigned char lds[LDS];
+    if (static_cast<int>(blockIdx.x) >= a.stat_blocks) {
+        qt_tile_linear<STORE, kRowMRows>(a.qt, static_cast<int64_t>(blockIdx.x) - a.stat_blocks, lds);
+        return;
+    }
+    float* lps = reinterpret_cast<float*>(lds);
+    const int groups = (a.Tc + kRowMRows - 1) / kRowMRows;
+    const int bhh = static_cast<int>(blockIdx.x / groups), grp = static_cast<int>(blockIdx.x % groups);
     const int lane = threadIdx.x & 63, n = a.n;
-    const int bhh = static_cast<int>(row / a.Tc);
+    {
+        const float* pp = a.part + static_cast<size_t>(bhh) * a.pbar_ntiles * n;
+        for (int i = threadIdx.x; i < n; i += 64 * kRowMRows) {
+            const float l = log_pbar(pp, a.pbar_ntiles, n, i, a.Tc);
+            lps[i] = l;
+            if (grp == 0) a.lp[static_cast<size_t>(bhh) * n + i] = l;
+        }
+    }
+    __syncthreads();
+    const int t = grp * kRowMRows + (threadIdx.x >> 6);
+    if (t >= a.Tc) return;
+    const int64_t row = static_cast<int64_t>(bhh) * a.Tc + t;
     const uint32_t* e = a.erow + static_cast<size_t>(row) * n;
-    const float* lp = a.lp + static_cast<size_t>(bhh) * n;
+    const float* lp = lps;
     const float M = DOT ? a.M[row] : 0.f;
     // every load in flight first, then the sum over sub-keys lane, lane+64, ... in order
     uint32_t ev[kNplMax];
@@ -993,7 +1023,7 @@ hipError_t score_w(const ScoreArgs& a, hipStream_t s) {
         attr_set = true;
     }
     const int ntiles = (a.Tc + 16 * NW - 1) / (16 * NW);
-    const unsigned grid = static_cast<unsigned>(a.B) * a.H * 2 * ntiles;
+    const unsigned grid = static_cast<unsigned>(a.B * a.H * 2 * ntiles);
     hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE, NW, DOT>), dim3(grid), dim3(64 * NW), lds, s, a);
     return hipGetLastError();
 }
@@ -1072,7 +1102,7 @@ int score_tile(int B, int H, int Tc, bool dot) {
     return kScoreTokMin;
 }
 
-hipError_t launch_row_stats(const ScoreArgs& a, int what, hipStream_t s) {
+hipError_t launch_row_stats(const ScoreArgs& a, int what, int store, hipStream_t s) {
     const int64_t rows = static_cast<int64_t>(a.B) * a.H * 2 * a.Tc;
     const unsigned rgrid = static_cast<unsigned>((rows + 3) / 4);
     if (what == 0 || what == 2) {  // Z (and M) unless the selection left them, then the usage partials
@@ -1085,9 +1115,18 @@ hipError_t launch_row_stats(const ScoreArgs& a, int what, hipStream_t s) {
             if (what == 0) hipLaunchKernelGGL(k_row_z<false>, dim3(rgrid), dim3(256), 0, s, a);
             hipLaunchKernelGGL(k_row_colsum<false>, dim3(cgrid), dim3(256), 0, s, a);
         }
-    } else {  // the row statistic m
-        if (a.dot) hipLaunchKernelGGL(k_row_m<true>, dim3(rgrid), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(k_row_m<false>, dim3(rgrid), dim3(256), 0, s, a);
+    } else {  // the row statistic m (and the transposed queries)
+        ScoreArgs b = a;
+        b.stat_blocks = a.B * a.H * 2 * ((a.Tc + kRowMRows - 1) / kRowMRows);
+        const unsigned mgrid = static_cast<unsigned>(b.stat_blocks + (a.qt.qT ? qt_tiles(a.qt) : 0));
+        const dim3 blk(64 * kRowMRows);
+        if (store == kBF16) {
+            if (a.dot) hipLaunchKernelGGL((k_row_m<kBF16, true>), dim3(mgrid), blk, 0, s, b);
+            else hipLaunchKernelGGL((k_row_m<kBF16, false>), dim3(mgrid), blk, 0, s, b);
+        } else {
+            if (a.dot) hipLaunchKernelGGL((k_row_m<kF32, true>), dim3(mgrid), blk, 0, s, b);
+            else hipLaunchKernelGGL((k_row_m<kF32, false>), dim3(mgrid), blk, 0, s, b);
+        }
     }
     return hipGetLastError();
 }
