@@ -393,6 +393,10 @@ struct SortArgs {
     int first;
     uint32_t N;           // slot ids >= N (or < 0) become the sentinel key N
     int items;            // entries per thread: kSortItems or kSortItemsSmall
+    int passes;           // 8-bit passes over the keys
+    int fuse;             // counts of pass p+1 built by pass p's scatter (integer atomics into
+                          //   counts + (p+1)*pass_stride); only pass 0 has a count launch
+    int64_t pass_stride;  // entries between the passes' count arrays (fuse)
 };
 
 struct ScatterArgs {
@@ -561,6 +565,7 @@ constexpr int kSortTile = 256 * kSortItems;    // entries per sort workgroup
 constexpr int kSortItemsSmall = 2;
 constexpr int kSortTileSmall = 256 * kSortItemsSmall;
 constexpr int kSortMinTiles = 128;
+constexpr int kSortFuseTiles = 64;             // at most B*tiles for next-pass counts by the scatters
 inline int sort_items(int B, int M) {
     return static_cast<long long>(B) * ((M + kSortTile - 1) / kSortTile) < kSortMinTiles ? kSortItemsSmall
                                                                                           : kSortItems;

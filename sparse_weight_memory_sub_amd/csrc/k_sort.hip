@@ -42,7 +42,11 @@ __global__ __launch_bounds__(256) void k_sort_count(SortArgs a) {
         if (pos < a.M) atomicAdd(&hist[(load_key(a, b, pos) >> a.shift) & 255u], 1u);
     }
     __syncthreads();
-    a.counts[(static_cast<size_t>(b) * a.tiles + tile) * 256 + threadIdx.x] = hist[threadIdx.x];
+    const size_t row = (static_cast<size_t>(b) * a.tiles + tile) * 256 + threadIdx.x;
+    a.counts[row] = hist[threadIdx.x];
+    // the later passes' counts start from zero: their scatters add to them
+    if (a.fuse)
+        for (int p = 1; p < a.passes; ++p) a.counts[static_cast<size_t>(p) * a.pass_stride + row] = 0u;
 }
 
 template <int ITEMS>
@@ -126,6 +130,11 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
         cnt[3][d] = c0 + c1 + c2;
     }
     __syncthreads();
+    // with fuse, the next pass's per-tile digit counts: each element adds one
+    // to (its tile after this pass, its next digit) -- integer sums, so the
+    // counts are exact in any order
+    const bool next = a.fuse && a.shift + 8 < 8 * a.passes;
+    uint32_t* cnext = a.counts + a.pass_stride + static_cast<size_t>(b) * a.tiles * 256;  // a.counts: this pass's
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
         const int pos = wbase + r * 64 + lane;
@@ -134,6 +143,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
             const uint32_t g = toff[d] + cnt[wave][d] + loc[r];
             a.kout[static_cast<size_t>(b) * a.M + g] = key[r];
             a.vout[static_cast<size_t>(b) * a.M + g] = val[r];
+            if (next) atomicAdd(&cnext[(g / (256 * ITEMS)) * 256 + ((key[r] >> (a.shift + 8)) & 255u)], 1u);
         }
     }
 }
@@ -142,12 +152,16 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
 
 hipError_t launch_sort_pass(const SortArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.tiles), static_cast<unsigned>(a.B));
+    // with fuse, the scatter of the pass before has counted this pass's digits
+    SortArgs c = a;
+    const bool count = a.first || !a.fuse;
+    if (a.fuse) c.counts = a.counts + static_cast<size_t>(a.shift / 8) * a.pass_stride;
     if (a.items == kSortItemsSmall) {
-        hipLaunchKernelGGL(k_sort_count<kSortItemsSmall>, grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(k_sort_scatter<kSortItemsSmall>, grid, dim3(256), 0, s, a);
+        if (count) hipLaunchKernelGGL(k_sort_count<kSortItemsSmall>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_sort_scatter<kSortItemsSmall>, grid, dim3(256), 0, s, c);
     } else if (a.items == kSortItems) {
-        hipLaunchKernelGGL(k_sort_count<kSortItems>, grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(k_sort_scatter<kSortItems>, grid, dim3(256), 0, s, a);
+        if (count) hipLaunchKernelGGL(k_sort_count<kSortItems>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_sort_scatter<kSortItems>, grid, dim3(256), 0, s, c);
     } else {
         return hipErrorInvalidValue;
     }
