@@ -246,17 +246,24 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
         float av[8];  // a_ti of this wave's keys for the block's tokens
         if (active) {
             const float* tq = reinterpret_cast<const float*>(cur + QB);
+            // the two 16-token halves' distance tiles side by side: two
+            // independent accumulation chains, each in k-block order
+            f32x4_t accs[2];
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accs[sub][i] = kn;
+#pragma unroll
+            for (int s = 0; s < DHS; ++s) {
+                Frag<STORE> A0, A1;
+                lds_frag<STORE, DHS>(A0, cur, fq, 0, s);
+                lds_frag<STORE, DHS>(A1, cur, fq, 1, s);
+                mma(A0, Bk[s], accs[0]);
+                mma(A1, Bk[s], accs[1]);
+            }
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
-                f32x4_t acc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = kn;
-                Frag<STORE> A[2];
-#pragma unroll
-                for (int s = 0; s < DHS; ++s) {
-                    lds_frag<STORE, DHS>(A[s & 1], cur, fq, sub, s);
-                    mma(A[s & 1], Bk[s], acc);
-                }
+                const f32x4_t acc = accs[sub];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = sub * 16 + 4 * g + i;
@@ -290,13 +297,21 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
                 }
                 Ahi.v = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
                 Alo.v = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+                // four column tiles at a time: their operands requested
+                // together, then the high parts, then the low parts (each
+                // accumulator still takes high before low)
+                constexpr int G = NCT % 4 == 0 ? 4 : 1;
 #pragma unroll
-                for (int c = 0; c < NCT; ++c) {
-                    const unsigned char* tp = tbuf + static_cast<uint32_t>(c * 16 * CPRT * 16);
-                    Frag<kBF16> Bq;
-                    Bq.v = *reinterpret_cast<const u32x4_t*>(tp + tb0);
-                    mma(Ahi, Bq, gacc[c]);
-                    mma(Alo, Bq, gacc[c]);
+                for (int c0 = 0; c0 < NCT; c0 += G) {
+                    Frag<kBF16> Bq[G];
+#pragma unroll
+                    for (int j = 0; j < G; ++j)
+                        Bq[j].v = *reinterpret_cast<const u32x4_t*>(
+                            tbuf + static_cast<uint32_t>((c0 + j) * 16 * CPRT * 16) + tb0);
+#pragma unroll
+                    for (int j = 0; j < G; ++j) mma(Ahi, Bq[j], gacc[c0 + j]);
+#pragma unroll
+                    for (int j = 0; j < G; ++j) mma(Alo, Bq[j], gacc[c0 + j]);
                 }
             } else {
                 Frag<kF32> A;

@@ -102,17 +102,25 @@ __device__ __forceinline__ void mma(const Frag<kF32>& a, const Frag<kF32>& b, f3
 // ---------------------------------------------------------------------------
 //
 // A tile of ROWS rows of CPR 16-byte chunks is stored row after row, with
-// the chunk index of row R permuted by an xor, chunk c at R*CPR + (c ^ swz(R)),
-// swz(R) = R & 15 for CPR >= 16 and (R / (16 / CPR)) & (CPR - 1) for CPR = 4
-// or 8.  A 16-byte read is served sixteen lanes at a time across all banks
-// (sixteen 16-byte bank groups), and these sixteen lanes read the same chunk
-// of sixteen consecutive rows; with the swizzle those land in sixteen
-// distinct bank groups for every row width.
+// the chunk index of row R permuted by an xor, chunk c at R*CPR + (c ^ swz(R)).
+// The sixteen lanes r = 0..15 of a lane group read the same chunk of sixteen
+// consecutive rows.  The swizzle puts those reads in sixteen distinct
+// 16-byte bank groups of 256 bytes, and each half (lanes r = 0..7, 8..15) in
+// eight distinct groups of 128 bytes, so a 16-byte read meets no bank
+// conflict whether the LDS serves it sixteen or eight lanes at a time:
+//   CPR >= 16: swz(R) = R & 15;
+//   CPR = 8:   swz(R) = ((R >> 1) ^ (R << 2)) & 7;
+//   CPR = 4:   swz(R) = ((R >> 2) ^ (R >> 1)) & 3.
+// (Measured on the key step's 4-chunk transposed tile: (R >> 2) & 3, which
+// is conflict-free only sixteen lanes at a time, left the LDS with bank
+// conflicts in most of its busy cycles.)
 
 template <int CPR, bool NARROW = false>
 __device__ __forceinline__ int swz(int R) {
+    static_assert(CPR == 4 || CPR == 8 || CPR >= 16, "rows of 4, 8 or at least 16 chunks");
     if constexpr (CPR >= 16) return R & 15;
-    else return (R / (16 / CPR)) & (CPR - 1);
+    else if constexpr (CPR == 8) return ((R >> 1) ^ (R << 2)) & 7;
+    else return ((R >> 2) ^ (R >> 1)) & 3;
 }
 
 // Copies rows [0, ROWS) of a strided source (row R at src + R*stride bytes;
