@@ -61,10 +61,16 @@ def parse():
                     help="time forward_seq with row-contribution counting and the addressing metrics")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print per-kernel tables of a rocprofv3 --kernel-trace CSV output directory and exit")
+    ap.add_argument("--last-call", action="store_true",
+                    help="with --summarize-trace: only the last forward_seq call of the trace (from its sub-key "
+                         "norms on), with each stream's gaps and the chunk period")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="HBM bytes per kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE CSV output directories "
                          "of a --profile-only run with one kernel at a time; writes profiles/<family>_<workload>_pmc.json "
                          "and prints a table")
+    ap.add_argument("--prequeue", action="store_true",
+                    help="also time one step queued whole behind a sleep kernel before the GPU starts it "
+                         "(the device-side time, without the host's enqueue pace)")
     ap.add_argument("--ceiling", action="store_true",
                     help="measure the HBM rates of random 1 KiB value rows (read; read-modify-write at several "
                          "depths, from registers and staged in LDS) and of a sequential copy")
@@ -474,12 +480,56 @@ def _rocprof_rows(directory, suffix):
     return rows
 
 
-def summarize_trace(directory):
+def _short_kernel(name):
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("fwpkm::", "")
+
+
+def _call_timeline(rows):
+    """The last call's kernels (from its last k_knorm on): span, time with
+    any kernel running, per-stream kernel time and gaps, chunk period."""
+    rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
+    kn = [i for i, r in enumerate(rows) if "k_knorm" in r["Kernel_Name"]]
+    seg = rows[kn[-1]:] if kn else rows
+    iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in seg)
+    busy, (cs, ce) = 0, iv[0]
+    for a, b in iv[1:]:
+        if a > ce:
+            busy += ce - cs
+            cs, ce = a, b
+        else:
+            ce = max(ce, b)
+    busy += ce - cs
+    span = max(b for _, b in iv) - iv[0][0]
+    lines = ["", f"Last call: {len(seg)} kernels over {span / 1e6:.3f} ms, some kernel running for "
+             f"{busy / 1e6:.3f} ms.", "", "| stream (queue) | kernels | kernel time ms | gaps ms | median gap us |",
+             "|---|---|---|---|---|"]
+    byq = {}
+    for r in seg:
+        byq.setdefault(r["Queue_Id"], []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r))
+    for q, L in sorted(byq.items()):
+        L.sort(key=lambda x: x[0])
+        gaps = sorted(b[0] - a[1] for a, b in zip(L, L[1:]))
+        med = gaps[len(gaps) // 2] / 1e3 if gaps else 0.0
+        lines.append(f"| {q} | {len(L)} | {sum(e - s for s, e, _ in L) / 1e6:.3f} | {sum(gaps) / 1e6:.3f} | {med:.1f} |")
+    sel = [int(r["Start_Timestamp"]) for r in seg if "k_select" in r["Kernel_Name"] and "ovf" not in r["Kernel_Name"]]
+    if len(sel) > 1:
+        per = [(b - a) / 1e3 for a, b in zip(sel, sel[1:])]
+        lines += ["", f"Chunk period (one selection launch to the next): mean {sum(per) / len(per):.1f} us, "
+                  f"min {min(per):.1f}, max {max(per):.1f}."]
+    return seg, lines
+
+
+def summarize_trace(directory, last_call=False):
     """Per-kernel dispatch counts and mean durations of the library's kernels
     in a rocprofv3 kernel trace, and the per-chunk-step time of each kernel
     family (one gather launch per chunk step of B sequences, or two
-    half-batch ones)."""
+    half-batch ones).  last_call: the last forward_seq call only, with its
+    streams' gaps."""
     rows = _rocprof_rows(directory, "kernel_trace.csv")
+    rows = [r for r in rows if "fwpkm::" in r["Kernel_Name"]]
+    extra = []
+    if last_call:
+        rows, extra = _call_timeline(rows)
     per = {}
     for r in rows:
         name = r["Kernel_Name"]
@@ -489,7 +539,7 @@ def summarize_trace(directory):
         per.setdefault(name, []).append(dt)
     lines = ["| kernel | dispatches | avg us | total ms |", "|---|---|---|---|"]
     for name, ts in sorted(per.items(), key=lambda kv: -sum(kv[1])):
-        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("fwpkm::", "")
+        short = _short_kernel(name)
         lines.append(f"| `{short}` | {len(ts)} | {sum(ts) / len(ts):.1f} | {sum(ts) / 1e3:.2f} |")
     fam = {}
     for name, ts in per.items():
@@ -502,7 +552,7 @@ def summarize_trace(directory):
         lines += ["", f"Per chunk step ({steps} selections):", "", "| family | us per chunk step |", "|---|---|"]
         for f, t in sorted(fam.items(), key=lambda kv: -kv[1]):
             lines.append(f"| {f} | {t / steps:.1f} |")
-    print("\n".join(lines))
+    print("\n".join(lines + extra))
 
 
 def summarize_pmc(fetch_dir, write_dir, workload):
@@ -599,10 +649,46 @@ def planted_recall_report(cfg, wl, passes, q, v, g, start_state, extra):
     return rep
 
 
+def prequeued_step(torch, step, stream):
+    """One step enqueued in full while a sleep kernel holds the stream, then
+    timed on the device from the sleep's end: the GPU-side time of the step
+    with every launch already queued, so the host's enqueue pace (several
+    microseconds per launch and per cross-stream event) cannot show.  Valid
+    when the host finished enqueueing before the sleep ended (the sleep is
+    timed from a calibration launch, hence the 10% margin).  The step starts
+    right after a long single-wave kernel, so the clocks may still be
+    ramping: this is a diagnostic beside `value`, not a replacement."""
+    cycles = 1 << 26
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(cycles)
+    b.record(stream)
+    torch.cuda.synchronize()
+    per_cycle_ms = a.elapsed_time(b) / cycles
+    host_est_ms = None
+    for _ in range(2):
+        sleep_ms = max(200.0, 4.0 * (host_est_ms or 0.0))
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(sleep_ms / per_cycle_ms))
+        start.record(stream)
+        h0 = time.perf_counter()
+        step()
+        host_ms = (time.perf_counter() - h0) * 1e3
+        stop.record(stream)
+        torch.cuda.synchronize()
+        host_est_ms = host_ms
+        if host_ms < 0.9 * sleep_ms:
+            break
+    return {"ms_per_step": start.elapsed_time(stop), "host_enqueue_ms": host_ms, "sleep_ms": sleep_ms,
+            "valid": host_ms < 0.9 * sleep_ms}
+
+
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.last_call)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload)
@@ -711,6 +797,9 @@ def main():
                    "score": cfg.score, "gate_weight": cfg.gate_weight,
                    "passes": passes, "storage": cfg.store, "accumulate": "f32", "state": "carried across steps"},
     }
+    if args.prequeue:
+        result["prequeued"] = prequeued_step(torch, step, stream)
+        log(f"prequeued: {result['prequeued']}")
     if args.profile_only:
         print(json.dumps(result), flush=True)
         return
