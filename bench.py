@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--last-call", action="store_true",
                     help="with --summarize-trace: only the last forward_seq call of the trace (from its sub-key "
                          "norms on), with each stream's gaps and the chunk period")
+    ap.add_argument("--decode-calls", nargs=2, type=int, metavar=("FIRST", "COUNT"),
+                    help="with --summarize-trace: the library's kernels of decode calls FIRST .. FIRST+COUNT-1 "
+                         "(calls counted by their scoring launches), per call")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="HBM bytes per kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE CSV output directories "
                          "of a --profile-only run with one kernel at a time; writes profiles/<family>_<workload>_pmc.json "
@@ -555,6 +558,31 @@ def summarize_trace(directory, last_call=False):
     print("\n".join(lines + extra))
 
 
+def summarize_decode_calls(directory, first, count):
+    """Kernel time and launch spacing of decode calls first .. first+count-1
+    of a rocprofv3 kernel trace of `bench.py --decode`; each call starts with
+    one whole-row scoring launch (k_rows)."""
+    rows = sorted((r for r in _rocprof_rows(directory, "kernel_trace.csv") if "fwpkm::" in r["Kernel_Name"]),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if "k_rows<" in r["Kernel_Name"]]
+    if len(starts) <= first + count:
+        raise SystemExit(f"the trace has {len(starts)} calls; {first + count + 1} needed")
+    a, b = starts[first], starts[first + count]
+    win = rows[a:b]
+    per = {}
+    for r in win:
+        per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    tot = sum(sum(v) for v in per.values())
+    wall = (int(rows[b]["Start_Timestamp"]) - int(win[0]["Start_Timestamp"])) / 1e3
+    lines = [f"Calls {first} .. {first + count - 1}: {tot / count:.1f} us of kernels per call, "
+             f"calls {wall / count:.1f} us apart.", "",
+             "| kernel | launches | avg us | us per decode call |", "|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {sum(v) / count:.2f} |")
+    print("\n".join(lines))
+
+
 def summarize_pmc(fetch_dir, write_dir, workload):
     """HBM bytes per kernel family launch from FETCH_SIZE and WRITE_SIZE
     passes (KiB per dispatch), scaled by what the same counters read for the
@@ -688,7 +716,10 @@ def prequeued_step(torch, step, stream):
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.last_call)
+        if args.decode_calls:
+            summarize_decode_calls(args.summarize_trace, *args.decode_calls)
+        else:
+            summarize_trace(args.summarize_trace, args.last_call)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload)

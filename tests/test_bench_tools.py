@@ -105,6 +105,26 @@ def test_summarize_trace_whole(tmp_path, capsys):
     assert "Last call" not in out
 
 
+def test_summarize_decode_calls(tmp_path, capsys):
+    # four decode calls 10 us apart: scoring 3 us, selection and read 5 us;
+    # the third call also runs a 20 us chunk write
+    rows = []
+    for c in range(4):
+        t0 = 1_000 + c * 10_000
+        rows.append(_trace_row("k_rows<1, 8, false>", t0, t0 + 3_000, 1))
+        rows.append(_trace_row("k_select_gather<1, 8>", t0 + 3_000, t0 + 8_000, 1))
+    rows.append(_trace_row("k_scatter<1, 8, 16>", 21_000 + 8_500, 21_000 + 28_500, 1))
+    _write_csv(tmp_path / "run_kernel_trace.csv", rows)
+    bench.summarize_decode_calls(str(tmp_path), 1, 2)  # calls 1 and 2
+    out = capsys.readouterr().out
+    # (3 + 5) * 2 + 20 = 36 us of kernels over 2 calls, starts 10 us apart
+    assert "Calls 1 .. 2: 18.0 us of kernels per call, calls 10.0 us apart." in out
+    assert "| `k_scatter<1, 8, 16>` | 1 | 20.00 | 10.00 |" in out
+    assert "| `k_rows<1, 8, false>` | 2 | 3.00 | 3.00 |" in out
+    with pytest.raises(SystemExit):
+        bench.summarize_decode_calls(str(tmp_path), 2, 2)  # needs a fifth call's start
+
+
 def _pmc_row(dispatch, name, counter, value):
     return {"Dispatch_Id": dispatch, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value}
 
