@@ -655,6 +655,28 @@ def test_near_tie_flag_on_duplicate_keys():
     assert (r["idx"][..., 0] // cfg.n == 0).all()
 
 
+def test_near_tie_flag_threshold():
+    """The flag marks a decision whose two alternatives differ by less than
+    tie_rel relative to the larger (eps + d): one query whose only close call
+    is half 1's boundary between the kept 2nd sub-key (d = 1) and the dropped
+    3rd (d = 1.0005^2), a relative gap of about 9.98e-4, is flagged for
+    tie_rel just above that gap and not just below it."""
+    cfg = FwpkmConfig(n=4, heads=1, d_q=2, d_v=2, k_half=2, k=1, chunk=4)
+    q, v, g, K1, K2, V = _rand_problem(cfg, 1, 1, seed=8)
+    q.zero_()
+    K1.copy_(torch.tensor([0.0, 1.0, 1.0005, 3.0]).view(1, 1, 4, 1))
+    K2.copy_(torch.tensor([0.0, 2.0, 4.0, 6.0]).view(1, 1, 4, 1))
+    eps = cfg.idw_eps
+    d_in, d_out = float(K1[0, 0, 1, 0]) ** 2, float(K1[0, 0, 2, 0]) ** 2
+    gap = ((eps + d_out) - (eps + d_in)) / (eps + d_out)
+    assert 9.9e-4 < gap < 1.0e-3
+    below = oracle.retrieve(cfg, q, v, g, K1, K2, V, tie_rel=0.97 * gap)
+    above = oracle.retrieve(cfg, q, v, g, K1, K2, V, tie_rel=1.03 * gap)
+    assert not below["tie"].any() and above["tie"].all()
+    # the kept pair is (0, 0) either way: the flag reports, it does not decide
+    assert below["idx"][0, 0, 0, 0] == 0 and above["idx"][0, 0, 0, 0] == 0
+
+
 def test_pair_p_matches_selected():
     cfg = FwpkmConfig(n=8, heads=2, d_q=6, d_v=2, k_half=4, k=4, chunk=4, store="bf16")
     q, v, g, K1, K2, V = _rand_problem(cfg, 2, 3, seed=7)
