@@ -14,7 +14,11 @@
 // workgroup derives its digit offsets from all tiles' histograms (elements
 // of smaller digits anywhere, plus elements of its digit in earlier tiles)
 // and places its elements by a stable rank inside the tile from wavefront
-// ballots, wavefronts in order.
+// ballots, wavefronts in order.  With SortArgs::fuse (a small sort: few
+// tiles in all) only the first pass has a count launch: each scatter adds
+// one per element to the next pass's histogram of the tile the element
+// lands in, with integer atomics (exact in any order), and the first count
+// launch zeroes those histograms.
 #include "fwpkm_internal.h"
 
 namespace fwpkm {
