@@ -6,7 +6,9 @@ checks sampled outputs that it can compute one by one:
 * the run the benchmark times (fwpkm_forward_seq over the whole batch) is
   tied bit for bit to a chunk-by-chunk replay of one sampled sequence
   (sequences share nothing, and forward_seq equals retrieve + chunk_update
-  per chunk);
+  per chunk; the replay may score by whole rows where the batch sweeps,
+  which orders the key step's fp32 statistics differently, and the bf16
+  rounding of the stored keys absorbs that here);
 * every chunk of that replay is compared with the oracle started from the
   GPU's own state before the chunk, so a near-tie decided differently in one
   chunk cannot cascade into later ones.
