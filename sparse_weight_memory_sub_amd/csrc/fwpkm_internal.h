@@ -152,6 +152,11 @@ __device__ __forceinline__ float log_pbar(const float* part, int ntiles, int n, 
     return logf(s / static_cast<float>(Tc));
 }
 
+// The median of a, b, c, written so that the compiler emits one v_med3_u32.
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+    return max(min(a, b), min(max(a, b), c));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += xor_lane(x, o);

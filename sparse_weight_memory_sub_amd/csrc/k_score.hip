@@ -288,14 +288,14 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
                         }
                         if constexpr (ROW) macc[i] = fmaf(DOT ? __expf(acc[i] - mrow[i]) : fast_rcp(e), lpk, macc[i]);
                         if constexpr (SEL) {
-                            // keep the MK smallest of this lane, ascending
-                            uint32_t x = eb;
+                            // keep the MK smallest of this lane, ascending: with the
+                            // list sorted, entry m becomes the median of (entry m-1,
+                            // entry m, x) -- one v_med3_u32 each -- and entry 0 the
+                            // smaller of itself and x (the same values as inserting
+                            // x by compare-and-swap down the list)
 #pragma unroll
-                            for (int m = 0; m < MK; ++m) {
-                                const uint32_t lo = min(keep[i][m], x);
-                                x = max(keep[i][m], x);
-                                keep[i][m] = lo;
-                            }
+                            for (int m = MK - 1; m >= 1; --m) keep[i][m] = med3_u32(keep[i][m - 1], keep[i][m], eb);
+                            keep[i][0] = min(keep[i][0], eb);
                         }
                     } else {
                         if constexpr (STATS) cs = fmaf(DOT ? __expf(acc[i] - mrow[i]) : fast_rcp(e), zinv[i], cs);
