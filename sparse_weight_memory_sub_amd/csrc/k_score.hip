@@ -737,6 +737,10 @@ __device__ void half_topk(const SelectArgs& a, int b, int t, int h, int half, ui
 // tau with at least kh values of the row <= tau, so every value <= tau is a
 // candidate (about kh of them) and one sort of the candidates finishes.
 // More than 64 candidates (many equal values) fall back to a radix select.
+// The loops run over all kNplMax entries of a lane without a branch (past
+// the row's end a lane holds the padding ~0, which is never a candidate):
+// a branch per entry made the wavefront wait for each candidate's LDS store
+// at the join (measured in decode: the candidate pass 1.1 us of the 14.5).
 __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, uint64_t* buf, float* out_e,
                               int* out_i) {
     const int lane = lane_id();
@@ -747,7 +751,8 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
 #pragma unroll
     for (int j = 0; j < kNplMax; ++j) {
         const int i = j * 64 + lane;
-        u[j] = (j < npl && i < n) ? e[i] : 0xffffffffu;
+        const uint32_t x = e[min(i, n - 1)];  // in bounds for every lane: no branch around the load
+        u[j] = i < n ? x : 0xffffffffu;
         const uint32_t lo = min(m0, u[j]), hi = max(m0, u[j]);
         m0 = lo;
         m1 = min(m1, hi);
@@ -758,16 +763,20 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
         if (a.dot) {
             float mx = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < kNplMax; ++j)
-                if (j < npl && j * 64 + lane < n) mx = fmaxf(mx, -unord_f32(u[j]));
+            for (int j = 0; j < kNplMax; ++j) {
+                const float sv = -unord_f32(u[j]);
+                mx = j * 64 + lane < n ? fmaxf(mx, sv) : mx;
+            }
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, xor_lane(mx, o));
             M = mx;
         }
         float z = 0.f;
 #pragma unroll
-        for (int j = 0; j < kNplMax; ++j)
-            if (j < npl && j * 64 + lane < n) z += a.dot ? row_weight<true>(u[j], M) : row_weight<false>(u[j], 0.f);
+        for (int j = 0; j < kNplMax; ++j) {
+            const float wv = a.dot ? row_weight<true>(u[j], M) : row_weight<false>(u[j], 0.f);
+            z = j * 64 + lane < n ? z + wv : z;
+        }
         z = wave_sum(z);
         if (lane == 0) {
             a.Z[row] = z;
@@ -781,13 +790,11 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
     uint32_t total = 0u;
 #pragma unroll
     for (int j = 0; j < kNplMax; ++j) {
-        if (j < npl) {
-            const bool c = u[j] <= tau;
-            const uint64_t bm = ballot(c);
-            const uint32_t pos = total + static_cast<uint32_t>(__popcll(bm & lt));
-            if (c && pos < 64u) buf[pos] = (static_cast<uint64_t>(u[j]) << 32) | static_cast<uint32_t>(j * 64 + lane);
-            total += static_cast<uint32_t>(__popcll(bm));
-        }
+        const bool c = u[j] <= tau && j * 64 + lane < n;
+        const uint64_t bm = ballot(c);
+        const uint32_t pos = total + static_cast<uint32_t>(__popcll(bm & lt));
+        if (c && pos < 64u) buf[pos] = (static_cast<uint64_t>(u[j]) << 32) | static_cast<uint32_t>(j * 64 + lane);
+        total += static_cast<uint32_t>(__popcll(bm));
     }
     wave_sync();
     uint64_t key[1];
@@ -807,16 +814,26 @@ __device__ void half_topk_row(const SelectArgs& a, size_t row, uint32_t* hist, u
     wave_sync();
 }
 
+// The product candidates' rank pairs of this lane: entry r is candidate
+// r*64 + lane (a*64 + b of its two per-half ranks; entries past ncand are
+// not used).  Loaded apart from the product top-k, without a condition, so
+// that a caller can request it early and wait for it only where it is used.
+__device__ __forceinline__ void load_ab(const SelectArgs& a, uint32_t (&ab)[kMaxCand / 64]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < kMaxCand / 64; ++r) ab[r] = a.cand_ab.ab[r * 64 + lane];
+}
+
 template <int R>
 __device__ void product_topk(const SelectArgs& a, const float* e1, const int* i1, const float* e2, const int* i2,
-                             int32_t* idx_out, float* w_out, int32_t* usage) {
+                             int32_t* idx_out, float* w_out, int32_t* usage, const uint32_t (&abr)[kMaxCand / 64]) {
     const int lane = lane_id();
     uint64_t key[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int c = r * 64 + lane;
         if (c < a.ncand) {
-            const uint32_t ab = a.cand_ab.ab[c];
+            const uint32_t ab = abr[r];
             const int ia = static_cast<int>(ab >> 6), ib = static_cast<int>(ab & 63u);
             // IDW: P = (eps + d1)(eps + d2); dot: v = -(s1 + s2); smaller is better
             const float P = a.dot ? e1[ia] + e2[ib] : e1[ia] * e2[ib];
@@ -840,6 +857,16 @@ __device__ void product_topk(const SelectArgs& a, const float* e1, const int* i1
         // row contribution of this read (integer atomic: exact in any order)
         if (usage && slot >= 0 && slot < a.n * a.n) atomicAdd(usage + slot, 1);
     }
+}
+
+// The product top-k of one (token, head) with the register width its
+// candidate count needs.
+__device__ __forceinline__ void product_topk_n(const SelectArgs& a, const float* e1, const int* i1, const float* e2,
+                                               const int* i2, int32_t* idx_out, float* w_out, int32_t* usage,
+                                               const uint32_t (&ab)[kMaxCand / 64]) {
+    if (a.ncand <= 64) product_topk<1>(a, e1, i1, e2, i2, idx_out, w_out, usage, ab);
+    else if (a.ncand <= 128) product_topk<2>(a, e1, i1, e2, i2, idx_out, w_out, usage, ab);
+    else product_topk<4>(a, e1, i1, e2, i2, idx_out, w_out, usage, ab);
 }
 
 // Items (token, head) of a launch from which the rare-path items get a
@@ -888,9 +915,9 @@ __global__ __launch_bounds__(256) void k_select_ovf(SelectArgs a) {
             half_topk<STORE>(a, b, t, h, half, hist[wave], buf[wave], se[wave][half], si[wave][half]);
         const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
         int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
-        if (a.ncand <= 64) product_topk<1>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
-        else if (a.ncand <= 128) product_topk<2>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
-        else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
+        uint32_t ab[kMaxCand / 64];
+        load_ab(a, ab);
+        product_topk_n(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u, ab);
         wave_sync();
     }
 }
@@ -911,6 +938,8 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     const int t = static_cast<int>(bt % a.Tc), b = static_cast<int>(bt / a.Tc);
     const size_t row0 = (static_cast<size_t>(b * a.H + h) * 2) * a.Tc + t;  // half 0; half 1 is Tc further
     const int c0 = a.cnt[row0], c1 = a.cnt[row0 + a.Tc];
+    uint32_t ab[kMaxCand / 64];
+    load_ab(a, ab);  // requested with the list counts, used after the sort
     if (lists_fit(a, c0, c1)) {
         // the usual case: both lists fit one register; sort them together
         const int lane = threadIdx.x & 63;
@@ -935,9 +964,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     }
     const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
     int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
-    if (a.ncand <= 64) product_topk<1>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
-    else if (a.ncand <= 128) product_topk<2>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
-    else product_topk<4>(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u);
+    product_topk_n(a, se[wave][0], si[wave][0], se[wave][1], si[wave][1], a.idx + o, a.w + o, u, ab);
 }
 
 // Selection from whole rows (rows mode, a few tokens): two wavefronts per
@@ -950,6 +977,8 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs a) {
     const int wave = threadIdx.x >> 6, slot = wave >> 1, half = wave & 1;
     const int64_t item = static_cast<int64_t>(blockIdx.x) * 2 + slot;  // over B*Tc*H
     const bool live = item < static_cast<int64_t>(a.B) * a.Tc * a.H;
+    uint32_t ab[kMaxCand / 64];
+    load_ab(a, ab);  // requested before the row, used by the product top-k
     int b = 0, t = 0, h = 0;
     if (live) {
         h = static_cast<int>(item % a.H);
@@ -963,9 +992,7 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs a) {
     if (!live || half != 0) return;
     const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
     int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
-    if (a.ncand <= 64) product_topk<1>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
-    else if (a.ncand <= 128) product_topk<2>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
-    else product_topk<4>(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u);
+    product_topk_n(a, se[slot][0], si[slot][0], se[slot][1], si[slot][1], a.idx + o, a.w + o, u, ab);
 }
 
 // Decode: one token's selection and read in one workgroup.  Wavefront 2h+half
@@ -975,6 +1002,15 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs a) {
 // the same order as k_select_rows followed by k_gather_split, so the same bits,
 // with one launch fewer on a path where a launch is a large part of a token.
 // The selection's scratch and the read's parts are never live together.
+// What does not depend on the selection is requested before it, by every
+// wavefront and without a condition (clamped to valid addresses), so that
+// nothing waits for it before its use: the product table, the epilogue's g
+// and v row (used by wavefront 0) and kSgCopy 16-byte pieces per thread of
+// the stream's copies into the pending chunk, stored after the row
+// selection (pieces beyond those by a loop).  Measured per decode call of
+// the 2^20-slot layer (16 tokens, 4 heads): the epilogue's dependent loads
+// and copies had taken 2.4 us and the read's second round trip 1.3 us of
+// the kernel's 14.5 us.  A stream launch only (ga.pq set).
 constexpr int kSgScratch = (kSgWaves * 64 * 8 + kSgWaves * 256 * 4) > (kSgWaves * 512 * 4)
                                ? (kSgWaves * 64 * 8 + kSgWaves * 256 * 4) : (kSgWaves * 512 * 4);
 
@@ -986,25 +1022,40 @@ __global__ __launch_bounds__(64 * kSgWaves) void k_select_gather(SelectArgs a, G
     uint64_t (*buf)[64] = reinterpret_cast<uint64_t (*)[64]>(scratch);
     uint32_t (*hist)[256] = reinterpret_cast<uint32_t (*)[256]>(scratch + kSgWaves * 64 * 8);
     float (*part)[512] = reinterpret_cast<float (*)[512]>(scratch);
-    const int wave = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t tok = blockIdx.x;  // b*Tc + t
     const int t = static_cast<int>(tok % a.Tc), b = static_cast<int>(tok / a.Tc);
+    uint32_t ab[kMaxCand / 64];
+    load_ab(a, ab);
+    const float gt = ga.g[static_cast<size_t>(b) * ga.g_bstride + t];
+    RawRow<STORE, EPL> vraw;
+    ld_raw_row<STORE, EPL>(ga.v, static_cast<size_t>(b) * ga.v_bstride + static_cast<size_t>(t) * ga.dv +
+                                     static_cast<size_t>(lane) * EPL, vraw);
+    const int npieces = pending_pieces<STORE>(ga, t);  // >= 1: q is never empty
+    const int w0 = threadIdx.x, w1 = threadIdx.x + static_cast<int>(blockDim.x);
+    const uint4 cp0 = *pending_src<STORE>(ga, b, t, min(w0, npieces - 1));
+    const uint4 cp1 = *pending_src<STORE>(ga, b, t, min(w1, npieces - 1));
     if (wave < 2 * a.H) {
         const int h = wave >> 1, half = wave & 1;
         const size_t row = ((static_cast<size_t>(b * a.H + h) * 2) + half) * a.Tc + t;
         half_topk_row(a, row, hist[wave], buf[wave], se[h][half], si[h][half]);
     }
+    if (w0 < npieces) *pending_dst<STORE>(ga, b, t, w0) = cp0;
+    if (w1 < npieces) *pending_dst<STORE>(ga, b, t, w1) = cp1;
+    pending_copy<STORE>(ga, b, t, w1 + static_cast<int>(blockDim.x), static_cast<int>(blockDim.x));
+    if (threadIdx.x == 0) ga.pg[static_cast<size_t>(b) * ga.pg_bstride + t] = gt;
     __syncthreads();
     if (wave < a.H) {
         const int h = wave;
         const size_t o = static_cast<size_t>(b) * a.iw_bstride + (static_cast<size_t>(t) * a.H + h) * a.k;
         int32_t* u = a.usage ? a.usage + static_cast<size_t>(b) * a.n * a.n : nullptr;
-        if (a.ncand <= 64) product_topk<1>(a, se[h][0], si[h][0], se[h][1], si[h][1], a.idx + o, a.w + o, u);
-        else if (a.ncand <= 128) product_topk<2>(a, se[h][0], si[h][0], se[h][1], si[h][1], a.idx + o, a.w + o, u);
-        else product_topk<4>(a, se[h][0], si[h][0], se[h][1], si[h][1], a.idx + o, a.w + o, u);
+        product_topk_n(a, se[h][0], si[h][0], se[h][1], si[h][1], a.idx + o, a.w + o, u, ab);
     }
     __syncthreads();  // the slot lists are visible to the workgroup; the scratch is free
-    gather_token_split<STORE, EPL>(ga, tok, part);
+    FinishIn<EPL> fin;
+    fin.gt = gt;
+    widen_raw_row<STORE, EPL>(vraw, fin.vt);
+    gather_token_split<STORE, EPL>(ga, tok, part, &fin);
 }
 
 template <int STORE, int DHS, int MK, int MODE, int NW, bool DOT>
@@ -1169,7 +1220,8 @@ hipError_t select_gather_s(const SelectArgs& a, const GatherArgs& ga, hipStream_
 }
 
 hipError_t launch_select_gather(const SelectArgs& a, const GatherArgs& ga, int store, hipStream_t s) {
-    if (!a.erow || !select_gather_fits(a.H, a.k) || a.B != ga.B || a.Tc != ga.Tc) return hipErrorInvalidValue;
+    if (!a.erow || !ga.pq || !ga.o || ga.r || !select_gather_fits(a.H, a.k) || a.B != ga.B || a.Tc != ga.Tc)
+        return hipErrorInvalidValue;
     return store == kBF16 ? select_gather_s<kBF16>(a, ga, s) : select_gather_s<kF32>(a, ga, s);
 }
 
