@@ -26,8 +26,8 @@
 //                 upper bound of the k'-th smallest e of the row (at least
 //                 k' values are <= tau_t).  Pass 2 recomputes the tile and
 //                 appends every (e, sub-key) with e <= tau_t to the token's
-//                 candidate list in the workspace (positions from an LDS
-//                 counter, so the list order varies; k_select sorts it).
+//                 candidate list in the workspace (positions from a ballot
+//                 of the token row's lanes; k_select sorts the list).
 //  kScoreStats    pass 1 also sums Z_t = sum_i 1/e_ti (written out); pass 2
 //                 forms the per-tile partial sums over tokens of p_ti,
 //                 the pieces of the chunk's marginal usage pbar.
@@ -47,8 +47,10 @@ namespace fwpkm {
 
 namespace {
 
-// sub-keys per LDS block: 32 bf16 or 16 fp32 rows (at most 16 KiB for d_h <= 256)
-template <int STORE> constexpr int kKB = (STORE == kBF16) ? 32 : 16;
+// sub-keys per LDS block: 32 bf16 or 16 fp32 rows (at most 16 KiB for d_h <= 256);
+// 64 bf16 rows (32 KiB) for the widest tiles, which hold a compute unit
+// alone and meet at half as many barriers
+template <int STORE, int NW> constexpr int kKB = (STORE == kBF16) ? (NW >= 16 ? 64 : 32) : 16;
 constexpr int kNplMax = 16;    // sub-keys per lane in a row: n <= 1024
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -127,26 +129,32 @@ __device__ __forceinline__ void bitonic_sort_lists(uint64_t (&x)[L]) {
 // k_score
 // ---------------------------------------------------------------------------
 
-// One sweep of a.tile tokens of one (sequence, head, half) against all n
-// sub-keys of that half.  MODE is a combination of kScoreSelect,
-// kScoreStats and kScoreRowStat (the latter alone).
-template <int STORE, int DHS, int MK, int MODE, int NW, bool DOT>
+// One sweep of a tile of 16*NW*TG tokens of one (sequence, head, half)
+// against all n sub-keys of that half.  Each wavefront owns TG groups of 16
+// tokens (the MFMA rows); every sub-key fragment it reads from LDS feeds the
+// MFMAs of all TG groups, so two groups halve the LDS reads per distance.
+// Each group's arithmetic is that of a wavefront of its own (the same MFMA
+// order per accumulator; per-token and per-column sums over the groups in
+// token order).  MODE is a combination of kScoreSelect, kScoreStats and
+// kScoreRowStat (the latter alone).
+template <int STORE, int DHS, int MK, int MODE, int NW, int TG, bool DOT>
 __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
+    static_assert(TG >= 1 && TG <= 4, "a workgroup's counters are zeroed by one thread per token");
     constexpr int ES = Store<STORE>::kBytes;
-    constexpr int KB = kKB<STORE>;
+    constexpr int KB = kKB<STORE, NW>;
     constexpr int CPR = 32 * DHS * ES / 16;
     constexpr int BLK_BYTES = KB * CPR * 16;
     constexpr bool SEL = (MODE & kScoreSelect) != 0;
     constexpr bool STATS = (MODE & kScoreStats) != 0;
     constexpr bool ROW = (MODE & kScoreRowStat) != 0;
     constexpr int NPASS = (SEL || STATS) ? 2 : 1;
+    constexpr int NG = NW * TG;  // 16-token groups of the workgroup
+    constexpr int TT = 16 * NG;  // tokens of the workgroup
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* kbuf = smem;                                            // [2][BLK_BYTES]
     float* kns = reinterpret_cast<float*>(smem + 2 * BLK_BYTES);           // [n]  ||K_i||^2
-    constexpr int TT = 16 * NW;  // tokens of the workgroup, 16 per wavefront
-    float* colbuf = kns + a.n;                                             // [2][NW][KB] (stats)
-    uint32_t* ccnt = reinterpret_cast<uint32_t*>(colbuf + (STATS ? 2 * NW * KB : 0));  // [TT] (select)
-    float* lps = reinterpret_cast<float*>(ccnt + (SEL ? TT : 0));         // [n]  log pbar (row statistic)
+    float* colbuf = kns + a.n;                                             // [2][NG][KB] (stats)
+    float* lps = colbuf + (STATS ? 2 * NG * KB : 0);                       // [n]  log pbar (row statistic)
 
     const int n = a.n, H = a.H, Tc = a.Tc;
     const int ntiles = (Tc + TT - 1) / TT;
@@ -157,48 +165,62 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
     const int h = bh % H, b = bh / H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int tw0 = tile * TT + wave * 16;  // first token of this wavefront
+    const int tw0 = tile * TT + wave * 16 * TG;  // first token of this wavefront; group j from tw0 + 16 j
     const int nblk = (n + KB - 1) / KB;
     const unsigned char* Kg = static_cast<const unsigned char*>(half ? a.K2 : a.K1) +
                               static_cast<size_t>(bh) * n * (32 * DHS) * ES;
     const size_t rowbase = static_cast<size_t>(bhh) * Tc;
     for (int i = threadIdx.x; i < n; i += 64 * NW) kns[i] = a.knorm[static_cast<size_t>(bhh) * n + i];
 
-    // query fragments of token tw0 + r (zero past the chunk), then -2 q
-    Frag<STORE> A[DHS];
-    const int tok = tw0 + r;
-    const bool tv = tok < Tc;
-    {
+    // query fragments of token tw0 + 16 j + r (zero past the chunk), then -2 q
+    Frag<STORE> A[TG][DHS];
+    float qe[TG][4];
+    bool rv[TG][4];
+    const int eps_bits = __float_as_int(a.eps);
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+        const int tok = tw0 + 16 * j + r;
+        const bool tv = tok < Tc;
         const unsigned char* qrow = static_cast<const unsigned char*>(a.q) +
             (static_cast<size_t>(b) * a.q_bstride + static_cast<size_t>(tv ? tok : 0) * H * (64 * DHS) +
              h * (64 * DHS) + half * (32 * DHS)) * ES;
-        load_row_frags<STORE, DHS>(A, qrow, g);
-    }
-    float qsq = 0.f;
+        load_row_frags<STORE, DHS>(A[j], qrow, g);
+        float qsq = 0.f;
 #pragma unroll
-    for (int s = 0; s < DHS; ++s) {
-        if (!tv) frag_zero<STORE>(A[s]);
-        qsq += frag_sumsq<STORE>(A[s]);
-        if constexpr (!DOT) frag_scale_m2(A[s]);  // dot scores use q itself
+        for (int s = 0; s < DHS; ++s) {
+            if (!tv) frag_zero<STORE>(A[j][s]);
+            qsq += frag_sumsq<STORE>(A[j][s]);
+            if constexpr (!DOT) frag_scale_m2(A[j][s]);  // dot scores use q itself
+        }
+        qsq += xor_lane(qsq, 16);
+        qsq += xor_lane(qsq, 32);
+        if ((SEL || STATS) && a.qn && g == 0 && tv) a.qn[rowbase + tok] = qsq;
+        // this lane's output rows: tokens tw0 + 16 j + 4g + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qe[j][i] = __shfl(qsq, 4 * g + i, 64) + a.eps;
+            rv[j][i] = tw0 + 16 * j + 4 * g + i < Tc;
+        }
     }
-    qsq += xor_lane(qsq, 16);
-    qsq += xor_lane(qsq, 32);
-    if ((SEL || STATS) && a.qn && g == 0 && tv) a.qn[rowbase + tok] = qsq;
-    // this lane's output rows: tokens tw0 + 4g + i
-    const int eps_bits = __float_as_int(a.eps);
     const FragBase<STORE, DHS> fb(r, g);
-    float qe[4];
-    bool rv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        qe[i] = __shfl(qsq, 4 * g + i, 64) + a.eps;
-        rv[i] = tw0 + 4 * g + i < Tc;
-    }
+    // this lane's group of sixteen lanes (the lanes of one token row) in a
+    // wavefront ballot, low and high words
+    const uint32_t gm_lo = (g == 0) ? 0x0000ffffu : (g == 1 ? 0xffff0000u : 0u);
+    const uint32_t gm_hi = (g == 2) ? 0x0000ffffu : (g == 3 ? 0xffff0000u : 0u);
+    uint32_t ncand[TG][4];  // candidates appended so far to each of the lane's token lists
 
-    float zinv[4] = {0.f, 0.f, 0.f, 0.f};  // 1/Z_t of the selection pass (0 past the chunk)
-    float zrow[4] = {1.f, 1.f, 1.f, 1.f};  // Z_t from the workspace (row statistic)
-    float mrow[4] = {0.f, 0.f, 0.f, 0.f};  // dot scoring: the row maximum M_t of s
-    uint32_t tau[4] = {0u, 0u, 0u, 0u};
+    float zinv[TG][4], zrow[TG][4], mrow[TG][4];  // 1/Z_t of the selection pass (0 past the chunk);
+    uint32_t tau[TG][4];                          // Z_t from the workspace; dot scoring's row maximum M_t
+#pragma unroll
+    for (int j = 0; j < TG; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            zinv[j][i] = 0.f;
+            zrow[j][i] = 1.f;
+            mrow[j][i] = 0.f;
+            tau[j][i] = 0u;
+            ncand[j][i] = 0u;
+        }
     if constexpr (ROW) {
         // log pbar_i from the per-tile usage partials, tiles added in order;
         // the first tile's workgroup also leaves it for the key step
@@ -209,26 +231,32 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
             if (tile == 0) a.lp[static_cast<size_t>(bhh) * n + i] = l;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (rv[i]) {
-                zrow[i] = a.Z[rowbase + tw0 + 4 * g + i];
-                if constexpr (DOT) mrow[i] = a.M[rowbase + tw0 + 4 * g + i];
-            }
+        for (int j = 0; j < TG; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (rv[j][i]) {
+                    zrow[j][i] = a.Z[rowbase + tw0 + 16 * j + 4 * g + i];
+                    if constexpr (DOT) mrow[j][i] = a.M[rowbase + tw0 + 16 * j + 4 * g + i];
+                }
     }
 
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-        float zacc[4] = {0.f, 0.f, 0.f, 0.f}, macc[4] = {0.f, 0.f, 0.f, 0.f};
-        // dot scoring's Z: a running maximum and the sum of exp(s - max) per lane
-        float zmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        uint32_t keep[4][MK];
+        float zacc[TG][4], macc[TG][4];
+        float zmax[TG][4];  // dot scoring's Z: a running maximum and the sum of exp(s - max) per lane
+        uint32_t keep[TG][4][MK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < TG; ++j)
 #pragma unroll
-            for (int m = 0; m < MK; ++m) keep[i][m] = 0xffffffffu;
+            for (int i = 0; i < 4; ++i) {
+                zacc[j][i] = 0.f;
+                macc[j][i] = 0.f;
+                zmax[j][i] = -INFINITY;
+#pragma unroll
+                for (int m = 0; m < MK; ++m) keep[j][i][m] = 0xffffffffu;
+            }
 
-        __syncthreads();  // the previous pass is done with kbuf / ccnt
-        if (SEL && pass == 1 && static_cast<int>(threadIdx.x) < TT) ccnt[threadIdx.x] = 0u;
+        __syncthreads();  // the previous pass is done with kbuf
         dma_rows<CPR, KB, NW, false>(kbuf, Kg, CPR * 16, n, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -239,18 +267,21 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
                 dma_rows<CPR, KB, NW, false>(kbuf + (cur ^ 1) * BLK_BYTES, Kg + static_cast<size_t>(blk + 1) * KB * CPR * 16,
                                              CPR * 16, n - (blk + 1) * KB, wave, lane);
             const unsigned char* kb = kbuf + cur * BLK_BYTES;
-            float colv[KB / 16];
+            float colv[TG][KB / 16];
 #pragma unroll
             for (int ct = 0; ct < KB / 16; ++ct) {
-                colv[ct] = 0.f;
+#pragma unroll
+                for (int j = 0; j < TG; ++j) colv[j][ct] = 0.f;
                 if (blk * KB + ct * 16 >= n) continue;  // partial last block (n % 16 == 0)
                 const int key = blk * KB + ct * 16 + r;
                 const float knv = DOT ? 0.f : kns[key];
-                f32x4_t acc;
+                f32x4_t acc[TG];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = knv;
+                for (int j = 0; j < TG; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] = knv;
                 // k-blocks in pairs, the next pair's LDS reads in flight under
-                // this pair's MFMAs
+                // this pair's MFMAs; each fragment feeds every group
                 constexpr int NP = (DHS + 1) / 2;
                 Frag<STORE> Bf[2][2];
                 lds_frag<STORE, DHS>(Bf[0][0], kb, fb, ct, 0);
@@ -261,141 +292,179 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
                         lds_frag<STORE, DHS>(Bf[(sp + 1) & 1][0], kb, fb, ct, 2 * sp + 2);
                         lds_frag<STORE, DHS>(Bf[(sp + 1) & 1][1], kb, fb, ct, 2 * sp + 3);
                     }
-                    mma(A[2 * sp], Bf[sp & 1][0], acc);
-                    if (2 * sp + 1 < DHS) mma(A[2 * sp + 1], Bf[sp & 1][1], acc);
+#pragma unroll
+                    for (int j = 0; j < TG; ++j) mma(A[j][2 * sp], Bf[sp & 1][0], acc[j]);
+                    if (2 * sp + 1 < DHS)
+#pragma unroll
+                        for (int j = 0; j < TG; ++j) mma(A[j][2 * sp + 1], Bf[sp & 1][1], acc[j]);
+                }
+                if constexpr (STORE == kBF16) {
+                    // keep two fragment reads in flight ahead of the MFMAs
+                    // (left alone, the scheduler waits for each read just
+                    // before its MFMA): the key norm and fragments 0 and 1
+                    // first, then one read after each MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, DOT ? 2 : 3, 0);
+#pragma unroll
+                    for (int s = 0; s < DHS; ++s) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, TG, 0);
+                        if (s + 2 < DHS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
                 }
                 float lpk = 0.f;
                 if constexpr (ROW) lpk = lps[key];
-                float cs = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // e = max(eps + d, eps): the large ||q||^2 enters with one
-                    // rounding at the end; a signed-integer max of the bit
-                    // patterns orders these floats exactly (eps > 0)
-                    // dot scoring: smaller ord(-s) is better, p ~ exp(s - M)
-                    const uint32_t eb = DOT ? ord_f32(-acc[i])
-                                            : static_cast<uint32_t>(max(__float_as_int(qe[i] + acc[i]), eps_bits));
-                    const float e = __uint_as_float(eb);
-                    if (pass == 0) {
-                        if constexpr (STATS) {
-                            if constexpr (DOT) {
-                                const float mx = fmaxf(zmax[i], acc[i]);
-                                zacc[i] = zacc[i] * __expf(zmax[i] - mx) + __expf(acc[i] - mx);
-                                zmax[i] = mx;
-                            } else {
-                                zacc[i] += fast_rcp(e);
+                for (int j = 0; j < TG; ++j) {
+                    float cs = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // e = max(eps + d, eps): the large ||q||^2 enters with one
+                        // rounding at the end; a signed-integer max of the bit
+                        // patterns orders these floats exactly (eps > 0)
+                        // dot scoring: smaller ord(-s) is better, p ~ exp(s - M)
+                        const float x = acc[j][i];
+                        const uint32_t eb = DOT ? ord_f32(-x)
+                                                : static_cast<uint32_t>(max(__float_as_int(qe[j][i] + x), eps_bits));
+                        const float e = __uint_as_float(eb);
+                        if (pass == 0) {
+                            if constexpr (STATS) {
+                                if constexpr (DOT) {
+                                    const float mx = fmaxf(zmax[j][i], x);
+                                    zacc[j][i] = zacc[j][i] * __expf(zmax[j][i] - mx) + __expf(x - mx);
+                                    zmax[j][i] = mx;
+                                } else {
+                                    zacc[j][i] += fast_rcp(e);
+                                }
                             }
-                        }
-                        if constexpr (ROW) macc[i] = fmaf(DOT ? __expf(acc[i] - mrow[i]) : fast_rcp(e), lpk, macc[i]);
-                        if constexpr (SEL) {
-                            // keep the MK smallest of this lane, ascending: with the
-                            // list sorted, entry m becomes the median of (entry m-1,
-                            // entry m, x) -- one v_med3_u32 each -- and entry 0 the
-                            // smaller of itself and x (the same values as inserting
-                            // x by compare-and-swap down the list)
+                            if constexpr (ROW)
+                                macc[j][i] = fmaf(DOT ? __expf(x - mrow[j][i]) : fast_rcp(e), lpk, macc[j][i]);
+                            if constexpr (SEL) {
+                                // keep the MK smallest of this lane, ascending: with the
+                                // list sorted, entry m becomes the median of (entry m-1,
+                                // entry m, x) -- one v_med3_u32 each -- and entry 0 the
+                                // smaller of itself and x (the same values as inserting
+                                // x by compare-and-swap down the list)
 #pragma unroll
-                            for (int m = MK - 1; m >= 1; --m) keep[i][m] = med3_u32(keep[i][m - 1], keep[i][m], eb);
-                            keep[i][0] = min(keep[i][0], eb);
-                        }
-                    } else {
-                        if constexpr (STATS) cs = fmaf(DOT ? __expf(acc[i] - mrow[i]) : fast_rcp(e), zinv[i], cs);
-                        if constexpr (SEL) {
-                            if (eb <= tau[i]) {
-                                const uint32_t pos = atomicAdd(&ccnt[wave * 16 + 4 * g + i], 1u);
-                                if (pos < static_cast<uint32_t>(a.cap))
-                                    a.cand[(rowbase + tw0 + 4 * g + i) * a.cap + pos] =
-                                        (static_cast<uint64_t>(eb) << 32) | static_cast<uint32_t>(key);
+                                for (int m = MK - 1; m >= 1; --m)
+                                    keep[j][i][m] = med3_u32(keep[j][i][m - 1], keep[j][i][m], eb);
+                                keep[j][i][0] = min(keep[j][i][0], eb);
+                            }
+                        } else {
+                            if constexpr (STATS) cs = fmaf(DOT ? __expf(x - mrow[j][i]) : fast_rcp(e), zinv[j][i], cs);
+                            if constexpr (SEL) {
+                                // append (e, sub-key) to the token's list when e <= tau:
+                                // positions from a ballot of the sixteen lanes of the
+                                // token row, in lane (sub-key) order
+                                const bool hit = eb <= tau[j][i];
+                                const uint64_t m = ballot(hit);
+                                if (m != 0u) {
+                                    const uint32_t lo = static_cast<uint32_t>(m) & gm_lo;
+                                    const uint32_t hi = static_cast<uint32_t>(m >> 32) & gm_hi;
+                                    const uint32_t pos =
+                                        ncand[j][i] + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+                                    if (hit && pos < static_cast<uint32_t>(a.cap))
+                                        a.cand[(rowbase + tw0 + 16 * j + 4 * g + i) * a.cap + pos] =
+                                            (static_cast<uint64_t>(eb) << 32) | static_cast<uint32_t>(key);
+                                    ncand[j][i] += __popc(lo) + __popc(hi);
+                                }
                             }
                         }
                     }
+                    colv[j][ct] = cs;
                 }
-                colv[ct] = cs;
             }
             if (STATS && pass == 1) {
-                // sum over this wavefront's 16 tokens: across the four lane groups
+                // sum over each group's 16 tokens: across the four lane groups
 #pragma unroll
-                for (int ct = 0; ct < KB / 16; ++ct) {
-                    float x = colv[ct];
-                    x += xor_lane(x, 16);
-                    x += xor_lane(x, 32);
-                    if (g == 0) colbuf[(cur * NW + wave) * KB + ct * 16 + r] = x;
-                }
+                for (int j = 0; j < TG; ++j)
+#pragma unroll
+                    for (int ct = 0; ct < KB / 16; ++ct) {
+                        float x = colv[j][ct];
+                        x += xor_lane(x, 16);
+                        x += xor_lane(x, 32);
+                        if (g == 0) colbuf[(cur * NG + wave * TG + j) * KB + ct * 16 + r] = x;
+                    }
             }
             __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next block has landed
             __syncthreads();
             if (STATS && pass == 1 && threadIdx.x < KB && blk * KB + static_cast<int>(threadIdx.x) < n) {
-                // this tile's partial of pbar for the block's sub-keys, waves in order
-                const float* cb = colbuf + cur * NW * KB + threadIdx.x;
+                // this tile's partial of pbar for the block's sub-keys, groups in token order
+                const float* cb = colbuf + cur * NG * KB + threadIdx.x;
                 float s = cb[0];
 #pragma unroll
-                for (int w = 1; w < NW; ++w) s += cb[w * KB];
+                for (int w = 1; w < NG; ++w) s += cb[w * KB];
                 a.part[(static_cast<size_t>(bhh) * ntiles + tile) * n + blk * KB + threadIdx.x] = s;
             }
         }
 
         if (pass == 0) {
-            if constexpr (STATS) {
-                // Z_t over the sixteen lanes that share token 4g+i
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = zacc[i];
-                    if constexpr (DOT) {
-                        // merge (max, sum) pairs: sum' = sum e^(max - M) + sum2 e^(max2 - M)
-                        float mx = zmax[i];
+            for (int j = 0; j < TG; ++j) {
+                const size_t row0 = rowbase + tw0 + 16 * j + 4 * g;
+                if constexpr (STATS) {
+                    // Z_t over the sixteen lanes that share token 4g+i
 #pragma unroll
-                        for (int o = 1; o <= 8; o <<= 1) {
-                            const float m2 = xor_lane(mx, o), x2 = xor_lane(x, o);
-                            const float M = fmaxf(mx, m2);
-                            x = x * __expf(mx - M) + x2 * __expf(m2 - M);
-                            mx = M;
+                    for (int i = 0; i < 4; ++i) {
+                        float x = zacc[j][i];
+                        if constexpr (DOT) {
+                            // merge (max, sum) pairs: sum' = sum e^(max - M) + sum2 e^(max2 - M)
+                            float mx = zmax[j][i];
+#pragma unroll
+                            for (int o = 1; o <= 8; o <<= 1) {
+                                const float m2 = xor_lane(mx, o), x2 = xor_lane(x, o);
+                                const float M = fmaxf(mx, m2);
+                                x = x * __expf(mx - M) + x2 * __expf(m2 - M);
+                                mx = M;
+                            }
+                            mrow[j][i] = mx;
+                            if (r == 0 && rv[j][i]) a.M[row0 + i] = mx;
+                        } else {
+                            x += xor_lane(x, 1);
+                            x += xor_lane(x, 2);
+                            x += xor_lane(x, 4);
+                            x += xor_lane(x, 8);
                         }
-                        mrow[i] = mx;
-                        if (r == 0 && rv[i]) a.M[rowbase + tw0 + 4 * g + i] = mx;
-                    } else {
+                        zinv[j][i] = rv[j][i] ? fast_rcp(x) : 0.f;
+                        if (r == 0 && rv[j][i]) a.Z[row0 + i] = x;
+                    }
+                }
+                if constexpr (ROW) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = macc[j][i];
                         x += xor_lane(x, 1);
                         x += xor_lane(x, 2);
                         x += xor_lane(x, 4);
                         x += xor_lane(x, 8);
+                        if (r == 0 && rv[j][i]) a.m[row0 + i] = x / zrow[j][i];
                     }
-                    zinv[i] = rv[i] ? fast_rcp(x) : 0.f;
-                    if (r == 0 && rv[i]) a.Z[rowbase + tw0 + 4 * g + i] = x;
                 }
-            }
-            if constexpr (ROW) {
+                if constexpr (SEL) {
+                    // tau = k'-th smallest of the 16*MK values kept by the token's lanes
+                    constexpr int RS = (MK <= 1) ? 1 : (MK <= 2 ? 2 : 4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = macc[i];
-                    x += xor_lane(x, 1);
-                    x += xor_lane(x, 2);
-                    x += xor_lane(x, 4);
-                    x += xor_lane(x, 8);
-                    if (r == 0 && rv[i]) a.m[rowbase + tw0 + 4 * g + i] = x / zrow[i];
-                }
-            }
-            if constexpr (SEL) {
-                // tau = k'-th smallest of the 16*MK values kept by the token's lanes
-                constexpr int RS = (MK <= 1) ? 1 : (MK <= 2 ? 2 : 4);
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t v[RS];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint32_t v[RS];
+                        for (int m = 0; m < RS; ++m) v[m] = (m < MK) ? keep[j][i][m] : 0xffffffffu;
+                        bitonic_sort<RS, 16>(v);
+                        const int kth = a.kh - 1;
+                        uint32_t t = 0u;
 #pragma unroll
-                    for (int m = 0; m < RS; ++m) v[m] = (m < MK) ? keep[i][m] : 0xffffffffu;
-                    bitonic_sort<RS, 16>(v);
-                    const int kth = a.kh - 1;
-                    uint32_t t = 0u;
-#pragma unroll
-                    for (int m = 0; m < RS; ++m)
-                        if (m == kth / 16) t = v[m];
-                    t = static_cast<uint32_t>(__shfl(static_cast<int>(t), 16 * g + (kth % 16), 64));
-                    tau[i] = rv[i] ? t : 0u;  // rows past the chunk collect nothing
+                        for (int m = 0; m < RS; ++m)
+                            if (m == kth / 16) t = v[m];
+                        t = static_cast<uint32_t>(__shfl(static_cast<int>(t), 16 * g + (kth % 16), 64));
+                        tau[j][i] = rv[j][i] ? t : 0u;  // rows past the chunk collect nothing
+                    }
                 }
             }
         }
     }
     if constexpr (SEL) {
-        __syncthreads();
-        const int t = tile * TT + static_cast<int>(threadIdx.x);
-        if (static_cast<int>(threadIdx.x) < TT && t < Tc) a.cnt[rowbase + t] = static_cast<int32_t>(ccnt[threadIdx.x]);
+#pragma unroll
+        for (int j = 0; j < TG; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (r == 0 && rv[j][i]) a.cnt[rowbase + tw0 + 16 * j + 4 * g + i] = static_cast<int32_t>(ncand[j][i]);
     }
 }
 
@@ -1058,35 +1127,35 @@ __global__ __launch_bounds__(64 * kSgWaves) void k_select_gather(SelectArgs a, G
     gather_token_split<STORE, EPL>(ga, tok, part, &fin);
 }
 
-template <int STORE, int DHS, int MK, int MODE, int NW, bool DOT>
+template <int STORE, int DHS, int MK, int MODE, int NW, int TG, bool DOT>
 hipError_t score_w(const ScoreArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
-    constexpr int KB = kKB<STORE>;
+    constexpr int KB = kKB<STORE, NW>;
+    constexpr int NG = NW * TG;
     constexpr size_t BLK_BYTES = static_cast<size_t>(KB) * DHS * 32 * ES;
-    const size_t lds = 2 * BLK_BYTES + static_cast<size_t>(a.n) * 4 + ((MODE & kScoreStats) ? 2 * NW * KB * 4 : 0) +
-                       ((MODE & kScoreSelect) ? 16 * NW * 4 : 0) +
+    const size_t lds = 2 * BLK_BYTES + static_cast<size_t>(a.n) * 4 + ((MODE & kScoreStats) ? 2 * NG * KB * 4 : 0) +
                        ((MODE & kScoreRowStat) ? static_cast<size_t>(a.n) * 4 : 0);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK, MODE, NW, DOT>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<STORE, DHS, MK, MODE, NW, TG, DOT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int ntiles = (a.Tc + 16 * NW - 1) / (16 * NW);
+    const int ntiles = (a.Tc + 16 * NG - 1) / (16 * NG);
     const unsigned grid = static_cast<unsigned>(a.B * a.H * 2 * ntiles);
-    hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE, NW, DOT>), dim3(grid), dim3(64 * NW), lds, s, a);
+    hipLaunchKernelGGL((k_score<STORE, DHS, MK, MODE, NW, TG, DOT>), dim3(grid), dim3(64 * NW), lds, s, a);
     return hipGetLastError();
 }
 
 template <int STORE, int DHS, int MK, int MODE>
 hipError_t score_t(const ScoreArgs& a, hipStream_t s) {
     // dot-product scoring (an ablation) is built for 64-token tiles only
-    if (a.dot) return score_w<STORE, DHS, MK, MODE, 4, true>(a, s);
+    if (a.dot) return score_w<STORE, DHS, MK, MODE, 4, 1, true>(a, s);
     switch (a.tile) {
-        case 64: return score_w<STORE, DHS, MK, MODE, 4, false>(a, s);
-        case 128: return score_w<STORE, DHS, MK, MODE, 8, false>(a, s);
-        case 256: return score_w<STORE, DHS, MK, MODE, 16, false>(a, s);
+        case 64: return score_w<STORE, DHS, MK, MODE, 4, 1, false>(a, s);
+        case 128: return score_w<STORE, DHS, MK, MODE, 8, 1, false>(a, s);
+        case 256: return score_w<STORE, DHS, MK, MODE, 16, 1, false>(a, s);
     }
     return hipErrorInvalidValue;
 }
