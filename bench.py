@@ -71,6 +71,10 @@ def parse():
                     help="HBM bytes per kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE CSV output directories "
                          "of a --profile-only run with one kernel at a time; writes profiles/<family>_<workload>_pmc.json "
                          "and prints a table")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="MFMA work and busy fraction per scoring, row-statistic and key-step kernel from a rocprofv3 "
+                         "--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "
+                         "GRBM_GUI_ACTIVE CSV output directory; prints a table")
     ap.add_argument("--prequeue", action="store_true",
                     help="also time one step queued whole behind a sleep kernel before the GPU starts it "
                          "(the device-side time, without the host's enqueue pace)")
@@ -636,6 +640,39 @@ def summarize_pmc(fetch_dir, write_dir, workload):
                 json.dump(out, fh, indent=1)
 
 
+def summarize_mfma(directory):
+    """Matrix-core work of the scoring, row-statistic and key-step kernels
+    from one rocprofv3 --pmc pass of SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F32 and
+    GRBM_GUI_ACTIVE: per kernel, the executed MFMA flops per dispatch (MOPS
+    x 512, recomputes included), their rate over the dispatch's duration
+    against the dense bf16 peak, and the MFMA-busy fraction
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).
+    Counter values are summed over the instances rocprofv3 reports."""
+    acc, disp, dur = {}, {}, {}
+    for r in _rocprof_rows(directory, "counter_collection.csv"):
+        n = r["Kernel_Name"]
+        if not any(k in n for k in ("k_score<", "k_kgrad<", "k_rows<")):
+            continue
+        k = _short_kernel(n)
+        c = acc.setdefault(k, {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        seen = disp.setdefault(k, set())
+        if r["Dispatch_Id"] not in seen:
+            seen.add(r["Dispatch_Id"])
+            dur[k] = dur.get(k, 0.0) + (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    print("| kernel | dispatches | avg us | executed GFLOP / dispatch | TFLOP/s | % of bf16 peak | MFMA busy % |")
+    print("|---|---|---|---|---|---|---|")
+    for k in sorted(acc, key=lambda k: -dur[k]):
+        n, c = len(disp[k]), acc[k]
+        us = dur[k] / n
+        flops = (c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)) * 512 / n
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (c["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        tfs = flops / (us * 1e-6) / 1e12
+        print(f"| `{k}` | {n} | {us:.1f} | {flops / 1e9:.2f} | {tfs:.0f} | {100 * tfs / MFMA_PEAK_TFS['bf16']:.1f} "
+              f"| {100 * busy:.1f} |")
+
+
 GOLDEN_RECALL = os.path.join(ROOT, "tests", "golden", "long_recall.json")
 
 
@@ -723,6 +760,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the FwPKM layer benchmark runs on one GPU; --gpus must be 1",

@@ -155,6 +155,26 @@ def test_summarize_pmc_scales(tmp_path, capsys):
     assert "| sort | 80 | 40 | 0.2 MB |" in out
 
 
+def test_summarize_mfma(tmp_path, capsys):
+    # two dispatches of a 10 us sweep, each executing 2^30 bf16 MFMA flops
+    # (2^21 MOPS of 512): 107.4 TFLOP/s, 4.3% of 2500; GRBM_GUI_ACTIVE of
+    # 8 XCDs x 24000 cycles, MFMA busy 6144000 cycles = 25% of 24000 x 1024 SIMDs
+    rows = []
+    for d in (1, 2):
+        base = {"Kernel_Name": NS + "k_score<1, 8, 3, 3, 16, 1, false>(fwpkm::ScoreArgs)",
+                "Start_Timestamp": 1_000_000 * d, "End_Timestamp": 1_000_000 * d + 10_000}
+        for counter, value in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1 << 21), ("SQ_INSTS_VALU_MFMA_MOPS_F32", 0),
+                               ("SQ_VALU_MFMA_BUSY_CYCLES", 6_144_000), ("GRBM_GUI_ACTIVE", 8 * 24_000)):
+            rows.append({**_pmc_row(d, base["Kernel_Name"], counter, value), **base})
+        # a kernel outside the MFMA families is left out
+        rows.append({**base, **_pmc_row(10 + d, NS + "k_gather<1, 8>(fwpkm::GatherArgs)", "GRBM_GUI_ACTIVE", 8)})
+    _write_csv(tmp_path / "run_counter_collection.csv", rows)
+    bench.summarize_mfma(str(tmp_path))
+    out = capsys.readouterr().out
+    assert "| `k_score<1, 8, 3, 3, 16, 1, false>` | 2 | 10.0 | 1.07 | 107 | 4.3 | 25.0 |" in out
+    assert "k_gather" not in out
+
+
 @pytest.mark.parametrize("name,worst", [("million", 437_252), ("mid", 120_324), ("long", 115_460)])
 def test_layer_bytes_worst_case(name, worst):
     cfg = WORKLOADS[name].cfg
