@@ -1078,6 +1078,7 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                 ga.r = at<float>(ws, L.r) + bo * Tc * p.dv;
                 ga.B = nb; ga.Tc = Tc; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
                 ga.znorm = p.znorm; ga.znorm_eps = p.zeps; ga.gate_w = p.gate;
+                ga.keep_b0 = gather_keep_from(nb, Tc, p.H, p.k, p.dv, p.es);
                 {
                     TimedLaunch tl(FWPKM_K_GATHER, sv);
                     HIP_TRY(launch_gather(ga, p.store, sv));

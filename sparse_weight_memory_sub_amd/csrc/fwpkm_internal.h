@@ -371,7 +371,23 @@ struct GatherArgs {
     int znorm;
     float znorm_eps;
     int gate_w;           // 1: r = g (vhat - y); 0: r = vhat - y
+    int keep_b0;          // k_gather: sequences b >= keep_b0 read value rows with cache-allocating
+                          //   loads, earlier ones with streaming (non-temporal) loads
 };
+
+// Capacity of the memory-side last-level cache (MI355X: 256 MB).
+constexpr int64_t kLastLevelCacheBytes = int64_t{256} << 20;
+
+// The first sequence of a chunk-gather launch of B sequences whose value rows
+// are read into the last-level cache.  The value write that follows reads the
+// same rows again; of a launch larger than the cache, only the rows read last
+// (its last sequences, up to the cache's capacity) are still there by then,
+// so the earlier sequences' rows are streamed past it.
+inline int gather_keep_from(int B, int Tc, int H, int k, int dv, int es) {
+    const int64_t per_seq = static_cast<int64_t>(Tc) * H * k * dv * es;
+    const int64_t fit = per_seq > 0 ? kLastLevelCacheBytes / per_seq : B;
+    return static_cast<int>(std::max<int64_t>(0, B - std::max<int64_t>(fit, 1)));
+}
 
 struct ResidArgs {        // r = g (vhat - z(tgt)) for t < n_tgt
     const float* vhat;    // vhat + b*vhat_bstride + t*dv

@@ -16,7 +16,10 @@
 // still in the 256 MB last-level cache.  Measured per chunk of the 2^20-slot
 // layer (serialized timing): gather 198 -> 215 us, write 440 -> 408 us, with
 // the overlapped step unchanged; non-temporal loads had been chosen when the
-// gather was timed alone.
+// gather was timed alone.  The chunk gather streams (non-temporal loads) the
+// rows of the sequences that would leave the cache before the write reaches
+// them (GatherArgs::keep_b0): at that layer gather 214 -> 204 us, the write
+// unchanged, the overlapped step 7.71 -> 7.62 ms.
 constexpr bool kGatherNt = false;
 
 namespace fwpkm {
@@ -49,7 +52,7 @@ __device__ __forceinline__ void zscore(float (&y)[EPL], int dv, float eps) {
 // wavefronts share the chip with the key path; 8.15 -> 8.09 ms per step at
 // million), 8 for the few-token gather (16 makes decode's 9.8 -> 15.9 us).
 // The rows of a part are summed in the same order either way.
-template <int STORE, int EPL, int ROWS>
+template <int STORE, int EPL, int ROWS, bool NT = kGatherNt>
 __device__ __forceinline__ void gather_part(const GatherArgs& a, size_t vb, size_t col, int32_t sl, float wt, int base,
                                             int cnt, float (&acc)[EPL]) {
 #pragma unroll
@@ -62,7 +65,7 @@ __device__ __forceinline__ void gather_part(const GatherArgs& a, size_t vb, size
         for (int u = 0; u < ROWS; ++u) {
             const int s = __builtin_amdgcn_readlane(sl, base + j + u);
             ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), base + j + u));
-            ldrow<STORE, EPL, kGatherNt>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
+            ldrow<STORE, EPL, NT>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
         }
 #pragma unroll
         for (int u = 0; u < ROWS; ++u)
@@ -73,7 +76,7 @@ __device__ __forceinline__ void gather_part(const GatherArgs& a, size_t vb, size
         float x[EPL];
         const int s = __builtin_amdgcn_readlane(sl, base + j);
         const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), base + j));
-        ldrow<STORE, EPL, kGatherNt>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
+        ldrow<STORE, EPL, NT>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) acc[i] = fmaf(ww, x[i], acc[i]);
     }

@@ -38,13 +38,21 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
     }
     const size_t vb = static_cast<size_t>(b) * static_cast<size_t>(a.N) * a.dv;
     const size_t col = static_cast<size_t>(lane) * EPL;
+    // rows the value write will find in the last-level cache are read into
+    // it; the others stream (gather_keep_from)
+    const bool keep = b >= a.keep_b0;
     float tot[EPL];
 #pragma unroll
     for (int p = 0; p < 256 / kGatherPart; ++p) {
         const int e0 = p * kGatherPart;
         if (e0 >= HK) break;
         float acc[EPL];
-        gather_part<STORE, EPL, 16>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64, min(kGatherPart, HK - e0), acc);
+        if (keep)
+            gather_part<STORE, EPL, 16, false>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
+                                               min(kGatherPart, HK - e0), acc);
+        else
+            gather_part<STORE, EPL, 16, true>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
+                                              min(kGatherPart, HK - e0), acc);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) tot[i] = (p == 0) ? acc[i] : tot[i] + acc[i];
     }
