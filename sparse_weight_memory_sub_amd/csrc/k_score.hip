@@ -135,7 +135,9 @@ __device__ __forceinline__ void bitonic_sort_lists(uint64_t (&x)[L]) {
 // MFMAs of all TG groups, so two groups halve the LDS reads per distance.
 // Each group's arithmetic is that of a wavefront of its own (the same MFMA
 // order per accumulator; per-token and per-column sums over the groups in
-// token order).  MODE is a combination of kScoreSelect, kScoreStats and
+// token order).  The launches use one group per wavefront: two (170
+// registers, two wavefronts per SIMD) made the 2^20-slot sweep slower,
+// 128 -> 170 us.  MODE is a combination of kScoreSelect, kScoreStats and
 // kScoreRowStat (the latter alone).
 template <int STORE, int DHS, int MK, int MODE, int NW, int TG, bool DOT>
 __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
