@@ -288,7 +288,11 @@ int fwpkm_forward_seq(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes
  * Every call on one GPU shares that GPU's scratch and leaves its contents
  * behind: calls that overlap on one GPU (on different streams, or from
  * different threads) race; calls ordered on one stream do not.  The scratch
- * needs no initialisation.
+ * needs no initialisation.  Capturing fwpkm calls into a HIP graph is not
+ * supported: on the test GPU, replays of a captured call of one chunk
+ * reproduced the eager results, replays of a captured call of several
+ * chunks did not (the cause is not established); enqueue the calls on a
+ * stream.
  */
 #define FWPKM_STATIC_SCRATCH_BYTES ((size_t)512 << 20)
 int fwpkm_forward_seq_static(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
