@@ -638,22 +638,24 @@ int address(const Plan& p, const Layout& L, void* ws, int B, int Tc, const void*
     ra.Z = at<float>(ws, L.Z);
     ra.M = at<float>(ws, L.M);
     ra.m = at<float>(ws, L.m);
-    // the transposed queries the key step reads: extra workgroups of the row
-    // statistic's launch on the stored-score path; a launch of their own
-    // after a rescoring statistic, which has just brought the queries into
-    // the last-level cache
+    // fp32 storage: the transposed queries the key step reads, extra
+    // workgroups of the row statistic's launch on the stored-score path, a
+    // launch of their own after a rescoring statistic (which has just brought
+    // the queries into the last-level cache); bf16 storage: none (the key
+    // step reads its query tiles transposed from LDS)
+    const bool want_qt = p.store == kF32;
     const QtArgs qa = qt_args(p, L, ws, B, Tc, q, q_bstride);
     {
         TimedLaunch tl(FWPKM_K_SWEEP_ROWSTAT, s);
         if (rows) {
-            ra.qt = qa;
+            if (want_qt) ra.qt = qa;
             ra.erow = at<uint32_t>(ws, L.erow);
             HIP_TRY(launch_row_stats(ra, 1, p.store, s));
         } else {
             HIP_TRY(launch_score(ra, p.store, s));
         }
     }
-    if (!rows) {
+    if (!rows && want_qt) {
         TimedLaunch tl(FWPKM_K_QT, s);
         HIP_TRY(launch_qt(qa, p.store, s));
     }

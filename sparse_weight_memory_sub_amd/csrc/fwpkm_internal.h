@@ -442,7 +442,7 @@ struct ScatterArgs {
 struct KgradArgs {
     const void* q;
     int64_t q_bstride;
-    const void* qT;       // [B][H][2][dh][Tp] (written in tiles of qt_tile)
+    const void* qT;       // [B][H][2][dh][Tp] (written in tiles of qt_tile); fp32 storage only
     int Tp;
     void* K1;
     void* K2;

@@ -11,17 +11,19 @@
 //
 // k_kgrad: one workgroup per 64 sub-keys of one (sequence, head, half); each
 // wavefront owns 16 keys and walks the chunk's tokens in blocks of 32.  Each
-// block is staged in LDS twice by direct global-to-LDS loads, double-buffered:
-// the query rows (d_h-contiguous) and the same rows transposed
-// (token-contiguous, written once per chunk in tiles of qt_tile).  Per block:
+// block's query rows (d_h-contiguous) are staged in LDS by direct
+// global-to-LDS loads, double-buffered; for fp32 storage also the same rows
+// transposed (token-contiguous, written once per chunk in tiles of qt_tile).
+// Per block:
 //  1. recompute the 32x16 distance tile on the matrix cores (same operands,
 //     order and roundings as the scoring sweep, so the values are bitwise
 //     the same);
 //  2. form a_ti for its keys;
 //  3. accumulate sum_t a_ti q_t on the matrix cores (keys x tokens times
-//     tokens x d_h from the transposed tile; for bf16 storage a_ti is split
-//     into a bf16 high part and a bf16 low part, two MFMAs, about 16 bits of
-//     a_ti).
+//     tokens x d_h; for bf16 storage the tokens x d_h operand comes from the
+//     query tile itself through gfx950's transposing LDS reads, and a_ti is
+//     split into a bf16 high part and a bf16 low part, two MFMAs, about 16
+//     bits of a_ti; for fp32 from the transposed tile).
 // Then K_i <- K_i - lr (sum_t a_ti q_t - (sum_t a_ti) K_i), rounded to the
 // storage type, and ||K_i||^2 of the stored key is written for the next
 // chunk's scoring.  Every key is read and written by one wavefront only.
@@ -130,6 +132,9 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     constexpr int CPRT = 32 * ES / 16;        // chunks per transposed row (narrow image, DH rows)
     constexpr int QB = 32 * CPRQ * 16;        // bytes of one query tile
     constexpr int QBUF = QB + 3 * 32 * 4;     // a query tile + qn, 1/Z, m of its 32 tokens
+    // bf16: the sum over tokens takes its query operand from the query tile
+    // itself by transposing LDS reads; fp32: from a transposed tile
+    constexpr bool TR = STORE == kBF16;
     const int n = a.n, H = a.H, Tc = a.Tc;
 
     const int nkb = (n + 63) / 64;
@@ -169,16 +174,27 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     // transposed-tile offsets of the operand column d = 16c + r: tokens 4g..4g+3
     // and 16+4g..16+4g+3 of the block, adjacent in the qt_tile order (one 16-byte
     // chunk for bf16, two for fp32)
-    uint32_t tb0, tb1;
-    {
+    uint32_t tb0 = 0, tb1 = 0;
+    // bf16, by transposing reads of the query tile: a read hands lane r of a
+    // 16-lane group component r % 4 of the 8 bytes addressed by lanes
+    // r / 4, 4 + r / 4, 8 + r / 4 and 12 + r / 4.  So lane m of group g
+    // addresses columns 16c + 4(m % 4) .. +3 of token row 4g + m / 4 (and
+    // of row 16 + 4g + m / 4), and lane r receives column 16c + r of tokens
+    // 4g..4g+3 (16+4g..16+4g+3): the eight k-elements of the a_ti fragment,
+    // in its order.  Column chunk 2c + (m % 4) / 2 of a row R sits at chunk
+    // position (2c + (m % 4) / 2) ^ swz(R) = 2c ^ tk (the image's swizzle).
+    uint32_t trow1 = 0, trow2 = 0;
+    int tk1 = 0, tk2 = 0;
+    if constexpr (TR) {
+        const int R1 = 4 * g + (r >> 2), R2 = R1 + 16, u = r & 3;
+        trow1 = static_cast<uint32_t>(R1 * CPRQ * 16 + (u & 1) * 8);
+        trow2 = static_cast<uint32_t>(R2 * CPRQ * 16 + (u & 1) * 8);
+        tk1 = (u >> 1) ^ swz<CPRQ>(R1);
+        tk2 = (u >> 1) ^ swz<CPRQ>(R2);
+    } else {
         const int f = swz<CPRT, true>(r);
-        if constexpr (STORE == kBF16) {
-            tb0 = static_cast<uint32_t>(r * CPRT + (g ^ f)) * 16u;
-            tb1 = tb0;
-        } else {
-            tb0 = static_cast<uint32_t>(r * CPRT + ((2 * g) ^ f)) * 16u;
-            tb1 = static_cast<uint32_t>(r * CPRT + ((2 * g + 1) ^ f)) * 16u;
-        }
+        tb0 = static_cast<uint32_t>(r * CPRT + ((2 * g) ^ f)) * 16u;
+        tb1 = static_cast<uint32_t>(r * CPRT + ((2 * g + 1) ^ f)) * 16u;
     }
 
     constexpr int NCT = DHS * 2;  // 16-wide column tiles of d_h
@@ -198,13 +214,22 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
     const int nblk = SPLIT ? min(a.per, (Tc + 31) / 32 - b0) : (Tc + 31) / 32;
     auto tok_block = [&](int bi) { return (b0 + (bi + kb) % nblk) * 32; };
     // LDS: two query tiles (with their token statistics), used in turn, and
-    // one transposed tile
+    // (fp32) one transposed tile
     unsigned char* tbuf = smem + 2 * QBUF;
     auto stage_q = [&](unsigned char* buf, int tb) {
-        dma_rows<CPRQ, 32, 4, false>(buf, qbase + static_cast<size_t>(tb) * qstride, qstride, Tc - tb, wave, lane);
+        const int nv = Tc - tb;
+        dma_rows<CPRQ, 32, 4, false>(buf, qbase + static_cast<size_t>(tb) * qstride, qstride, nv, wave, lane);
+        if constexpr (TR) {
+            // the rows past the chunk hold zeros: the transposing reads hand
+            // them to the sum over tokens, whose a_ti are 0 there
+            if (nv < 32)
+                for (int i = static_cast<int>(threadIdx.x); i < (32 - nv) * CPRQ; i += 256)
+                    *reinterpret_cast<uint4*>(buf + (static_cast<size_t>(nv) * CPRQ + i) * 16) = make_uint4(0u, 0u, 0u, 0u);
+        }
     };
     auto stage_t = [&](int tb) {
-        dma_rows<CPRT, DH, 4, true>(tbuf, tbase + static_cast<size_t>(tb) * ES, tstride, DH, wave, lane);
+        if constexpr (!TR)
+            dma_rows<CPRT, DH, 4, true>(tbuf, tbase + static_cast<size_t>(tb) * ES, tstride, DH, wave, lane);
     };
     // qn, 1/Z, m of tokens tb..tb+31 (zeros past the chunk), threads 0..95
     auto tq_load = [&](int tb) {
@@ -282,7 +307,7 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the transposed tile has landed
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's parts of the next query tile (and the transposed tile) have landed
         __syncthreads();
         if (active) {
             // sum_t a_ti q_t: keys x tokens (A) times tokens x d_h (B)
@@ -301,13 +326,27 @@ __global__ __launch_bounds__(256, 3) void k_kgrad(KgradArgs a) {
                 // together, then the high parts, then the low parts (each
                 // accumulator still takes high before low)
                 constexpr int G = NCT % 4 == 0 ? 4 : 1;
+                // the read offsets are formed per block (two operations each),
+                // not kept in registers across the loop (the kernel has none
+                // to spare at three workgroups per compute unit)
+                asm volatile("" : "+v"(tk1), "+v"(trow1));
 #pragma unroll
                 for (int c0 = 0; c0 < NCT; c0 += G) {
                     Frag<kBF16> Bq[G];
 #pragma unroll
-                    for (int j = 0; j < G; ++j)
-                        Bq[j].v = *reinterpret_cast<const u32x4_t*>(
-                            tbuf + static_cast<uint32_t>((c0 + j) * 16 * CPRT * 16) + tb0);
+                    for (int j = 0; j < G; ++j) {
+                        const int c = c0 + j;
+                        const uint32_t o1 = trow1 + (static_cast<uint32_t>((2 * c) ^ tk1) << 4);
+                        // rows 16 on: the same swizzle when rows hold 16 or more chunks
+                        const uint32_t o2 = (CPRQ >= 16) ? o1 + 16u * CPRQ * 16u
+                                                         : trow2 + (static_cast<uint32_t>((2 * c) ^ tk2) << 4);
+                        const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4i16_t*)(cur + o1));
+                        const v4i16_t x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4i16_t*)(cur + o2));
+                        const uint2 w1 = __builtin_bit_cast(uint2, x1), w2 = __builtin_bit_cast(uint2, x2);
+                        Bq[j].v = u32x4_t{w1.x, w1.y, w2.x, w2.y};
+                    }
 #pragma unroll
                     for (int j = 0; j < G; ++j) mma(Ahi, Bq[j], gacc[c0 + j]);
 #pragma unroll
@@ -465,7 +504,9 @@ template <int STORE, int DHS, bool DOT>
 hipError_t kgrad_t(const KgradArgs& a, hipStream_t s) {
     constexpr int ES = Store<STORE>::kBytes;
     constexpr int DH = 32 * DHS;
-    constexpr size_t LDS = 2 * (static_cast<size_t>(32) * DH * ES + 3 * 32 * 4) + static_cast<size_t>(DH) * 32 * ES;
+    // two query tiles with their token statistics, and for fp32 the transposed tile
+    constexpr size_t LDS = 2 * (static_cast<size_t>(32) * DH * ES + 3 * 32 * 4) +
+                           (STORE == kF32 ? static_cast<size_t>(DH) * 32 * ES : 0);
     static bool attr_set = false;
     if (!attr_set) {
         for (const void* f : {reinterpret_cast<const void*>(&k_kgrad<STORE, DHS, DOT, false>),

@@ -20,6 +20,7 @@ namespace fwpkm {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short v4i16_t;
 
 template <int STORE> struct Frag;
 template <> struct Frag<kBF16> {
