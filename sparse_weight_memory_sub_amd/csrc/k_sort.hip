@@ -68,6 +68,18 @@ __global__ __launch_bounds__(256) void k_sort_scatter(SortArgs a) {
         const uint32_t* col = a.counts + static_cast<size_t>(b) * a.tiles * 256 + threadIdx.x;
         uint32_t tot = 0u, before = 0u;
         int t = 0;
+        // 32 tiles' counts requested at once (a sequence of 2^16 reads has 32
+        // tiles), then 8 at a time
+        for (; t + 32 <= a.tiles; t += 32) {
+            uint32_t c[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) c[u] = col[static_cast<size_t>(t + u) * 256];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                tot += c[u];
+                before += (t + u < tile) ? c[u] : 0u;
+            }
+        }
         for (; t + 8 <= a.tiles; t += 8) {
             uint32_t c[8];
 #pragma unroll
