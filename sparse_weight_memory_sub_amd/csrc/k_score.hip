@@ -79,7 +79,9 @@ __device__ __forceinline__ void bitonic_sort(K (&x)[R]) {
                         const int p = r * W + ln;
                         const bool up = (p & size) == 0;
                         const K a = x[r], b = x[r2];
-                        const bool sw = up ? (a > b) : (a < b);
+                        // swap if out of order for the direction: one compare
+                        // (equal keys swap or not: the same values either way)
+                        const bool sw = (a > b) == up;
                         x[r] = sw ? b : a;
                         x[r2] = sw ? a : b;
                     }
@@ -93,9 +95,9 @@ __device__ __forceinline__ void bitonic_sort(K (&x)[R]) {
                     const int p = r * W + ln;
                     const bool up = (p & size) == 0;
                     const bool lower = (ln & stride) == 0;
-                    const K mn = x[r] < y ? x[r] : y;
-                    const K mx = x[r] < y ? y : x[r];
-                    x[r] = (lower == up) ? mn : mx;
+                    // keep x when it is the one this lane wants (the smaller
+                    // for the lower lane of an ascending pair): one compare
+                    x[r] = ((x[r] < y) == (lower == up)) ? x[r] : y;
                 }
             }
         }
@@ -117,9 +119,7 @@ __device__ __forceinline__ void bitonic_sort_lists(uint64_t (&x)[L]) {
 #pragma unroll
             for (int l = 0; l < L; ++l) {
                 const uint64_t y = shfl_xor_u64(x[l], stride);
-                const uint64_t mn = x[l] < y ? x[l] : y;
-                const uint64_t mx = x[l] < y ? y : x[l];
-                x[l] = (lower == up) ? mn : mx;
+                x[l] = ((x[l] < y) == (lower == up)) ? x[l] : y;
             }
         }
     }
