@@ -193,6 +193,11 @@ __global__ __launch_bounds__(64 * NW) void k_score(ScoreArgs a) {
             if (!tv) frag_zero<STORE>(A[j][s]);
             qsq += frag_sumsq<STORE>(A[j][s]);
             if constexpr (!DOT) frag_scale_m2(A[j][s]);  // dot scores use q itself
+            // the scaled fragment is formed here: left free, the compiler
+            // keeps the unpacked elements of ||q||^2 live until the loop to
+            // scale them there, and the kernel's peak register count with
+            // them (the 2^20-slot sweep: 112 -> 104)
+            if constexpr (STORE == kBF16) asm volatile("" : "+v"(A[j][s].v));
         }
         qsq += xor_lane(qsq, 16);
         qsq += xor_lane(qsq, 32);
