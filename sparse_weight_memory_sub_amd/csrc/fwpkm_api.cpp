@@ -1081,6 +1081,12 @@ int forward_seq_impl(const fwpkm_cfg* cfg, int32_t B, int32_t T, int32_t passes,
                 ga.B = nb; ga.Tc = Tc; ga.H = p.H; ga.k = p.k; ga.dv = p.dv; ga.N = p.N;
                 ga.znorm = p.znorm; ga.znorm_eps = p.zeps; ga.gate_w = p.gate;
                 ga.keep_b0 = gather_keep_from(nb, Tc, p.H, p.k, p.dv, p.es);
+                // rows held raw (more wavefronts per SIMD) in chunks under
+                // kApartReads reads, where the value path does not already
+                // fill HBM; above, the extra wavefronts only crowd the key
+                // path (A/B, the same bits: 131K-read chunks 1.900 -> 1.832
+                // ms per step, 262K 1.168 -> 1.160, 1M 7.339 -> 7.41)
+                ga.held = reads < kApartReads ? 1 : 0;
                 {
                     TimedLaunch tl(FWPKM_K_GATHER, sv);
                     HIP_TRY(launch_gather(ga, p.store, sv));

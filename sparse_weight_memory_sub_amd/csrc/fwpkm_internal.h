@@ -373,6 +373,8 @@ struct GatherArgs {
     int gate_w;           // 1: r = g (vhat - y); 0: r = vhat - y
     int keep_b0;          // k_gather: sequences b >= keep_b0 read value rows with cache-allocating
                           //   loads, earlier ones with streaming (non-temporal) loads
+    int held;             // k_gather, bf16 storage: 1 holds a round's rows as their raw bf16
+                          //   words (100 rather than 163 registers at d_v = 512), 0 widens them
 };
 
 // Capacity of the memory-side last-level cache (MI355X: 256 MB).

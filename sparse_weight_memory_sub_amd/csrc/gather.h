@@ -203,11 +203,11 @@ struct Bf16Row {
     uint32_t w[(EPL + 1) / 2];
 };
 
-template <int EPL>
+template <int EPL, bool NT = kGatherNt>
 __device__ __forceinline__ void ld_bf16_row(const void* base, size_t off, Bf16Row<EPL>& r) {
     const uint16_t* p = static_cast<const uint16_t*>(base) + off;
     if constexpr (EPL == 8) {
-        const uint4 v = ld16<kGatherNt>(p);
+        const uint4 v = ld16<NT>(p);
         r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else if constexpr (EPL == 4) {
         const uint2 v = *reinterpret_cast<const uint2*>(p);
@@ -267,7 +267,7 @@ __device__ __forceinline__ void widen_raw_row(const RawRow<STORE, EPL>& r, float
     }
 }
 
-template <int EPL, int ROWS>
+template <int EPL, int ROWS, bool NT = kGatherNt>
 __device__ __forceinline__ void gather_part_held(const GatherArgs& a, size_t vb, size_t col, int32_t sl, float wt,
                                                  int base, int cnt, float (&acc)[EPL]) {
 #pragma unroll
@@ -280,7 +280,7 @@ __device__ __forceinline__ void gather_part_held(const GatherArgs& a, size_t vb,
         for (int u = 0; u < ROWS; ++u) {
             const int s = __builtin_amdgcn_readlane(sl, base + j + u);
             ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), base + j + u));
-            ld_bf16_row<EPL>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
+            ld_bf16_row<EPL, NT>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x[u]);
         }
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) fma_bf16_row<EPL>(ww[u], x[u], acc);
@@ -289,7 +289,7 @@ __device__ __forceinline__ void gather_part_held(const GatherArgs& a, size_t vb,
         Bf16Row<EPL> x;
         const int s = __builtin_amdgcn_readlane(sl, base + j);
         const float ww = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), base + j));
-        ld_bf16_row<EPL>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
+        ld_bf16_row<EPL, NT>(a.V, vb + static_cast<size_t>(s) * a.dv + col, x);
         fma_bf16_row<EPL>(ww, x, acc);
     }
 }

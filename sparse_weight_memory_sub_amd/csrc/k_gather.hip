@@ -13,13 +13,15 @@
 // entry order, and the parts are added in order: one wavefront per token
 // for large batches (k_gather), one wavefront per part when the tokens are
 // too few to fill the chip (k_gather_split, decode); both give the same bits.
+// HELD (bf16 storage) keeps a round's rows as their raw words until their
+// multiply-adds: fewer registers and more wavefronts per SIMD, the same bits.
 #include "gather.h"
 
 namespace fwpkm {
 
 namespace {
 
-template <int STORE, int EPL>
+template <int STORE, int EPL, bool HELD>
 __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t tok = static_cast<int64_t>(blockIdx.x) * 4 + wave;
@@ -47,12 +49,21 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
         const int e0 = p * kGatherPart;
         if (e0 >= HK) break;
         float acc[EPL];
-        if (keep)
-            gather_part<STORE, EPL, 16, false>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
-                                               min(kGatherPart, HK - e0), acc);
-        else
-            gather_part<STORE, EPL, 16, true>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
-                                              min(kGatherPart, HK - e0), acc);
+        if constexpr (HELD) {
+            if (keep)
+                gather_part_held<EPL, 16, false>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
+                                                 min(kGatherPart, HK - e0), acc);
+            else
+                gather_part_held<EPL, 16, true>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
+                                                min(kGatherPart, HK - e0), acc);
+        } else {
+            if (keep)
+                gather_part<STORE, EPL, 16, false>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
+                                                   min(kGatherPart, HK - e0), acc);
+            else
+                gather_part<STORE, EPL, 16, true>(a, vb, col, sl[e0 / 64], wt[e0 / 64], e0 % 64,
+                                                  min(kGatherPart, HK - e0), acc);
+        }
 #pragma unroll
         for (int i = 0; i < EPL; ++i) tot[i] = (p == 0) ? acc[i] : tot[i] + acc[i];
     }
@@ -93,7 +104,10 @@ hipError_t gather_t(const GatherArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((k_gather_split<STORE, EPL>), dim3(static_cast<unsigned>(toks)), dim3(64 * nparts), 0, s, a);
     } else {
         const unsigned grid = static_cast<unsigned>((toks + 3) / 4);
-        hipLaunchKernelGGL((k_gather<STORE, EPL>), dim3(grid), dim3(256), 0, s, a);
+        if (STORE == kBF16 && a.held)
+            hipLaunchKernelGGL((k_gather<STORE, EPL, STORE == kBF16>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gather<STORE, EPL, false>), dim3(grid), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
