@@ -29,7 +29,9 @@ namespace {
 // earlier two-row pipeline, 431-435 us with 16; 10 or 12 rows (more
 // wavefronts, more round trips) 451-465 us; the first residual row requested
 // one or two runs ahead, or two reads of a long run per step, cost the fifth
-// wavefront and did not pay.
+// wavefront and did not pay.  Measured again later: 14 rows (94 VGPRs,
+// five round trips) 412 -> 441 us; 20 rows (119 VGPRs, four wavefronts per
+// SIMD) 412 us, the overlapped step no faster.
 constexpr int kScatterRuns = 16;
 // Pieces whose partials k_fixup requests at once.
 constexpr int kFixupAhead = 8;
